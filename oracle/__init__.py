@@ -1,0 +1,118 @@
+"""ctypes wrapper of the fp64 CPU oracle (oracle/dsa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's CPU-baseline leg are the only
+callers.  The GPU library never imports, links or calls it, and it never imports the GPU library.
+
+Every function takes the numpy arrays produced by the seeded generator (or hand-made ones) and returns fp64
+results.  See dsa_oracle.c for the definitions and the passages of the pages each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16, F8E4M3 = 0, 1, 2
+_DT = {"f32": F32, "bf16": BF16, "f8": F8E4M3}
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.dsa_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.dsa_oracle_e4m3_value.restype = D
+        L.dsa_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.dsa_oracle_bf16_value.restype = D
+        L.dsa_oracle_decode.argtypes = [P, I32, I64, P]
+        L.dsa_oracle_decode.restype = None
+        L.dsa_oracle_indexer_scores.argtypes = [I32, I32, I32, I32, P, P, P, P, P, P, P, P, I32, I32, P, I64]
+        L.dsa_oracle_indexer_scores.restype = ctypes.c_int
+        L.dsa_oracle_topk.argtypes = [I32, I32, P, P, I64, P, P]
+        L.dsa_oracle_topk.restype = ctypes.c_int
+        L.dsa_oracle_sparse_attn.argtypes = [I32, I32, I32, I32, P, P, P, I32, P, P, I32, I32, D, P, P]
+        L.dsa_oracle_sparse_attn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def decode(codes: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of every stored element ("f8" codes, "bf16" bit patterns or "f32")."""
+    src = np.ascontiguousarray(codes)
+    out = np.empty(src.shape, np.float64)
+    lib().dsa_oracle_decode(_p(src), _DT[dtype], src.size, _p(out))
+    return out
+
+
+def indexer_scores(q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, row_seq, row_len, page_table,
+                   page_size: int, idx_dtype: str, ld: int | None = None) -> np.ndarray:
+    """I[r, s] for s < row_len[r] (fp64); entries at s >= row_len[r] are NaN."""
+    R, H_I, d_I = q_idx.shape
+    row_len = _c(row_len, np.int32)
+    ld = int(ld if ld is not None else (row_len.max() if R else 0))
+    out = np.full((R, max(ld, 1)), np.nan)
+    code_t = np.uint8 if idx_dtype == "f8" else np.float32
+    q_idx, k_idx_pool = _c(q_idx, code_t), _c(k_idx_pool, code_t)
+    q_idx_scale, k_idx_scale = _c(q_idx_scale, np.float32), _c(k_idx_scale, np.float32)
+    head_w, row_seq, page_table = _c(head_w, np.float32), _c(row_seq, np.int32), _c(page_table, np.int32)
+    rc = lib().dsa_oracle_indexer_scores(
+        R, H_I, d_I, _DT[idx_dtype], _p(q_idx), _p(q_idx_scale), _p(head_w), _p(k_idx_pool), _p(k_idx_scale),
+        _p(row_seq), _p(row_len), _p(page_table), page_table.shape[1], page_size, _p(out), out.shape[1])
+    if rc:
+        raise ValueError(f"oracle indexer rejected its arguments (code {rc})")
+    return out[:, :ld]
+
+
+def topk(scores: np.ndarray, row_len, k: int):
+    """(idx [R, k] int32 with -1 padding, k_eff-th score [R]); order: score desc, position asc."""
+    scores = np.ascontiguousarray(scores, np.float64)
+    R = scores.shape[0]
+    row_len = _c(row_len, np.int32)
+    idx = np.empty((R, k), np.int32)
+    kth = np.empty(R, np.float64)
+    rc = lib().dsa_oracle_topk(R, k, _p(row_len), _p(scores), scores.shape[1] if scores.ndim == 2 else 0,
+                               _p(idx), _p(kth))
+    if rc:
+        raise ValueError(f"oracle top-k rejected its arguments (code {rc})")
+    return idx, kth
+
+
+def sparse_attn(q, kv_pool, topk_idx, row_seq, page_table, page_size: int, kv_dtype: str, scale: float):
+    """(o [R, H, d_c] fp64, lse [R, H] fp64) over the selected rows (entries < 0 are ignored)."""
+    R, H, d_c = q.shape
+    code_t = np.uint16 if kv_dtype == "bf16" else np.float32
+    q, kv_pool = _c(q, code_t), _c(kv_pool, code_t)
+    topk_idx, row_seq, page_table = _c(topk_idx, np.int32), _c(row_seq, np.int32), _c(page_table, np.int32)
+    k = topk_idx.shape[1]
+    out = np.empty((R, H, d_c), np.float64)
+    lse = np.empty((R, H), np.float64)
+    rc = lib().dsa_oracle_sparse_attn(R, H, d_c, _DT[kv_dtype], _p(q), _p(kv_pool), _p(topk_idx), k, _p(row_seq),
+                                      _p(page_table), page_table.shape[1], page_size, float(scale), _p(out), _p(lse))
+    if rc:
+        raise ValueError(f"oracle attention rejected its arguments (code {rc})")
+    return out, lse
+
+
+def decode_step(prob):
+    """The whole step on a synth.Problem: (scores, idx, kth, o, lse)."""
+    scores = indexer_scores(prob.q_idx, prob.q_idx_scale, prob.head_w, prob.k_idx_pool, prob.k_idx_scale,
+                            prob.row_seq, prob.row_len, prob.page_table, prob.page_size, prob.idx_dtype)
+    idx, kth = topk(scores, prob.row_len, prob.k)
+    o, lse = sparse_attn(prob.q, prob.kv_pool, idx, prob.row_seq, prob.page_table, prob.page_size, prob.kv_dtype,
+                         prob.softmax_scale)
+    return scores, idx, kth, o, lse

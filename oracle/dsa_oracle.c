@@ -1,0 +1,175 @@
+/*
+ * dsa_oracle.c -- plain fp64 CPU reference of the DeepSeek Sparse Attention (DSA) decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * load this library.  It shares no source, header, table or helper with the GPU library and includes
+ * nothing from it.  It is deliberately slow: every value is decoded to fp64 and every sum is a plain loop.
+ *
+ * What it computes, and where the pages define it:
+ *   1. Element decoding.  The indexer operands are FP8 ("the whole scorer runs in FP8", DeepSeek Sparse
+ *      Attention explained, "How Does the Lightning Indexer Score a Token?"; "float8_e4m3" in "What Does
+ *      the GPU Actually Run?") with one fp32 scale per stored 64-vector ("128 FP8 numbers and one scale per
+ *      token", same section).  The format is OCP E4M3FN: bias 7, no infinities, S.1111.111 is NaN.
+ *      The latent cache and attention queries are BF16 ("attended over, in full BF16 precision",
+ *      "What Does the Whole Block Look Like?").  fp32 inputs are taken as they are.
+ *   2. Indexer score (same pages, "How Does the Lightning Indexer Score a Token?"; milos-mitrovic,
+ *      "How Does the Lightning Indexer Pick Which Tokens Matter?"; lizeman DSA page section 2, stage 1):
+ *      for every visible position s, each indexer head j takes the dot product of its query q_I[j] with
+ *      the position's single shared key k_I[s]; the result goes through a ReLU; the H_I results are summed
+ *      with the head weights w[j], which carry no sign constraint:
+ *          I[s] = sum_j w[j] * max(0, <q_I[j], k_I[s]>),   q_I = sq * decode(q8), k_I = sk * decode(k8).
+ *   3. Selection ("How Does the Selector Pick 1,024?"): sort the scores, keep the highest
+ *      k_eff = min(k, n) positions (a short context is read in full).  Equal scores are ordered by
+ *      position, lowest first.
+ *   4. Sparse attention in MQA mode (lizeman section 2, stage 2; kiadev "How DSA works"; "What Does the
+ *      Whole Block Look Like?"): every query head attends with an ordinary softmax over only the selected
+ *      latent rows, which serve as both key and value:
+ *          l_i = scale * <q[h], c[T_i]>,  p = softmax(l),  o[h] = sum_i p_i c[T_i],  lse[h] = log sum exp l.
+ *      An empty selection gives o = 0 and lse = -inf.
+ *   Cached positions are addressed through a page table: physical row = table[seq][pos / P] * P + pos % P
+ *   (the selected positions are "an address list into the paged KV cache", "How Does the Selector Pick").
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F8E4M3 = 2 };
+
+/* ---- 1. element decoding ------------------------------------------------------------------------- */
+
+double dsa_oracle_e4m3_value(uint8_t code) {
+  int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return sign ? -mag : mag;
+}
+
+double dsa_oracle_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double elem(const void *base, int dtype, int64_t i) {
+  switch (dtype) {
+    case ORACLE_F32: return (double)((const float *)base)[i];
+    case ORACLE_BF16: return dsa_oracle_bf16_value(((const uint16_t *)base)[i]);
+    default: return dsa_oracle_e4m3_value(((const uint8_t *)base)[i]);
+  }
+}
+
+void dsa_oracle_decode(const void *src, int32_t dtype, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = elem(src, dtype, i);
+}
+
+static int64_t phys_row(const int32_t *page_table, int32_t max_pages, int32_t page_size, int32_t seq, int64_t pos) {
+  return (int64_t)page_table[(int64_t)seq * max_pages + pos / page_size] * page_size + pos % page_size;
+}
+
+/* ---- 2. indexer score ---------------------------------------------------------------------------- */
+
+int dsa_oracle_indexer_scores(int32_t R, int32_t H_I, int32_t d_I, int32_t idx_dtype,
+                              const void *q_idx, const float *q_idx_scale, const float *head_w,
+                              const void *k_idx_pool, const float *k_idx_scale,
+                              const int32_t *row_seq, const int32_t *row_len, const int32_t *page_table,
+                              int32_t max_pages, int32_t page_size, double *scores, int64_t ld) {
+  if (R < 0 || H_I <= 0 || d_I <= 0 || d_I > 1024 || page_size <= 0) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    const int64_t n = row_len[r];
+    /* dequantised indexer queries of this row */
+    double *q = (double *)malloc(sizeof(double) * (size_t)H_I * d_I);
+    if (!q) return 2;
+    for (int32_t j = 0; j < H_I; ++j) {
+      double sq = q_idx_scale ? (double)q_idx_scale[(int64_t)r * H_I + j] : 1.0;
+      for (int32_t d = 0; d < d_I; ++d) q[j * d_I + d] = sq * elem(q_idx, idx_dtype, ((int64_t)r * H_I + j) * d_I + d);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < n; ++s) {
+      const int64_t p = phys_row(page_table, max_pages, page_size, row_seq[r], s);
+      const double sk = k_idx_scale ? (double)k_idx_scale[p] : 1.0;
+      double kv[1024];
+      for (int32_t d = 0; d < d_I; ++d) kv[d] = sk * elem(k_idx_pool, idx_dtype, p * d_I + d);
+      double score = 0.0;
+      for (int32_t j = 0; j < H_I; ++j) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < d_I; ++d) dot += q[j * d_I + d] * kv[d];
+        score += (double)head_w[(int64_t)r * H_I + j] * (dot > 0.0 ? dot : 0.0);
+      }
+      scores[(int64_t)r * ld + s] = score;
+    }
+    free(q);
+  }
+  return 0;
+}
+
+/* ---- 3. selection -------------------------------------------------------------------------------- */
+
+typedef struct { double score; int64_t pos; } scored_pos;
+
+static int by_score_then_position(const void *a, const void *b) {
+  const scored_pos *x = (const scored_pos *)a, *y = (const scored_pos *)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+int dsa_oracle_topk(int32_t R, int32_t k, const int32_t *row_len, const double *scores, int64_t ld,
+                    int32_t *topk_idx, double *kth_score) {
+  if (R < 0 || k <= 0) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    const int64_t n = row_len[r];
+    const int64_t keff = n < k ? n : k;
+    scored_pos *all = (scored_pos *)malloc(sizeof(scored_pos) * (size_t)(n > 0 ? n : 1));
+    if (!all) return 2;
+    for (int64_t s = 0; s < n; ++s) { all[s].score = scores[(int64_t)r * ld + s]; all[s].pos = s; }
+    qsort(all, (size_t)n, sizeof(scored_pos), by_score_then_position);
+    for (int64_t i = 0; i < k; ++i) topk_idx[(int64_t)r * k + i] = i < keff ? (int32_t)all[i].pos : -1;
+    if (kth_score) kth_score[r] = keff > 0 ? all[keff - 1].score : NAN;
+    free(all);
+  }
+  return 0;
+}
+
+/* ---- 4. sparse attention over the selected latent rows ------------------------------------------ */
+
+int dsa_oracle_sparse_attn(int32_t R, int32_t H, int32_t d_c, int32_t kv_dtype, const void *q, const void *kv_pool,
+                           const int32_t *topk_idx, int32_t k, const int32_t *row_seq, const int32_t *page_table,
+                           int32_t max_pages, int32_t page_size, double scale, double *out, double *lse) {
+  if (R < 0 || H <= 0 || d_c <= 0 || k <= 0 || page_size <= 0) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)k);
+    if (!rows) return 2;
+    int32_t m = 0;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t pos = topk_idx[(int64_t)r * k + i];
+      if (pos >= 0) rows[m++] = phys_row(page_table, max_pages, page_size, row_seq[r], pos);
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t h = 0; h < H; ++h) {
+      double *o = out + ((int64_t)r * H + h) * d_c;
+      for (int32_t d = 0; d < d_c; ++d) o[d] = 0.0;
+      if (m == 0) { lse[(int64_t)r * H + h] = -INFINITY; continue; }
+      double *logit = (double *)malloc(sizeof(double) * (size_t)m);
+      double mx = -INFINITY;
+      for (int32_t i = 0; i < m; ++i) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < d_c; ++d)
+          dot += elem(q, kv_dtype, ((int64_t)r * H + h) * d_c + d) * elem(kv_pool, kv_dtype, rows[i] * d_c + d);
+        logit[i] = scale * dot;
+        if (logit[i] > mx) mx = logit[i];
+      }
+      double z = 0.0;
+      for (int32_t i = 0; i < m; ++i) { logit[i] = exp(logit[i] - mx); z += logit[i]; }
+      for (int32_t i = 0; i < m; ++i) {
+        double p = logit[i] / z;
+        for (int32_t d = 0; d < d_c; ++d) o[d] += p * elem(kv_pool, kv_dtype, rows[i] * d_c + d);
+      }
+      lse[(int64_t)r * H + h] = mx + log(z);
+      free(logit);
+    }
+    free(rows);
+  }
+  return 0;
+}

@@ -1,0 +1,6 @@
+"""Seeded synthetic workloads shared by the oracle tests, the GPU tests and the benchmark.
+
+Holds random draws and storage-format casts only; none of the step's arithmetic.
+"""
+from .configs import CONFIGS, ORDER, get  # noqa: F401
+from .gen import Problem, make_problem  # noqa: F401

@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for the DSA decode step.
+
+This module only draws random numbers and stores them in the byte formats the step consumes: bf16 for the
+latent cache and queries, OCP e4m3fn codes plus one fp32 scale per 64-vector for the indexer operands.  It
+computes none of the method's steps (no scoring, no selection, no attention); both the CPU oracle and the
+GPU path receive the arrays it returns.
+
+Recipe (per sequence, fp32 masters, "N(0, v)" means variance v):
+  latent c[s] ~ N(0, 1) over d_c = 512 dims, stored rounded to the latent dtype;
+  W_KI ~ N(0, 1/d_c) shared by every sequence of a workload; indexer keys k_I = c_stored @ W_KI, as the
+    indexer key projection of the lizeman DSA page (section 3 sketch) writes it;
+  indexer queries q_I[j] ~ N(0, 1/d_I) for each of the H_I heads; head weights w[j] ~ U(0, 1);
+  attention queries q[h] ~ N(0, 1/d_c) for each of the H heads (already in latent space);
+  boosted positions (random anchors drawn without replacement outside the most recent window, plus that
+    window) get k_I[s] += 0.5 * mean_j q_I[j], which makes the score spiky at planted positions;
+  fp8 operands: scale = amax / 448 per 64-vector (1 for an all-zero vector), code = e4m3fn(RNE(x / scale)).
+Pages are 64 positions; a paged workload places every logical page of every sequence at a random physical
+page of one shared pool, the others place them in order.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass
+class Problem:
+    cfg: dict
+    R: int
+    S: int
+    H_I: int
+    d_I: int
+    H: int
+    d_c: int
+    k: int
+    page_size: int
+    max_pages: int
+    num_pages: int
+    idx_dtype: str
+    kv_dtype: str
+    softmax_scale: float
+    q_idx: np.ndarray            # [R, H_I, d_I] uint8 e4m3fn codes | float32
+    q_idx_scale: np.ndarray | None  # [R, H_I] float32 (fp8 only)
+    head_w: np.ndarray           # [R, H_I] float32
+    k_idx_pool: np.ndarray       # [num_pages * page_size, d_I] uint8 | float32
+    k_idx_scale: np.ndarray | None  # [num_pages * page_size] float32 (fp8 only)
+    q: np.ndarray                # [R, H, d_c] uint16 bf16 bits | float32
+    kv_pool: np.ndarray          # [num_pages * page_size, d_c] uint16 | float32
+    row_seq: np.ndarray          # [R] int32
+    row_len: np.ndarray          # [R] int32
+    page_table: np.ndarray       # [S, max_pages] int32
+    boosted: list                # per sequence: int64 positions that were boosted
+
+    @property
+    def max_row_len(self) -> int:
+        return int(self.row_len.max()) if self.R else 0
+
+
+def _child(seed: int, *key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=tuple(key)))
+
+
+def _round_kv(x: np.ndarray, kv_dtype: str):
+    """(stored bits or values, fp32 value of what is stored)."""
+    if kv_dtype == "f32":
+        return x, x
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy(), t.to(torch.float32).numpy()
+
+
+def _quant_rows(x: np.ndarray):
+    """Per-64-vector e4m3fn quantisation of the last axis: (codes uint8, scale float32)."""
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = np.clip(x / scale[..., None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, scale
+
+
+def _draw_sequence(rng: np.random.Generator, n: int, cfg: dict, W_KI: np.ndarray):
+    d_c, d_I, H_I, H = cfg["d_c"], cfg["d_I"], cfg["H_I"], cfg["H"]
+    c = rng.standard_normal((n, d_c), dtype=np.float32)
+    q_I = rng.standard_normal((H_I, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_I))
+    w = rng.random(H_I, dtype=np.float32)
+    q = rng.standard_normal((H, d_c), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
+    W = min(cfg["recent"], n)
+    A = min(cfg["anchors"], n - W)
+    anchors = rng.choice(n - W, size=A, replace=False) if A > 0 else np.zeros(0, np.int64)
+    boosted = np.sort(np.concatenate([anchors.astype(np.int64), np.arange(n - W, n, dtype=np.int64)]))
+    c_bits, c_val = _round_kv(c, cfg["kv_dtype"])
+    del c
+    k_I = c_val @ W_KI
+    k_I[boosted] += np.float32(0.5) * q_I.mean(axis=0)
+    return dict(c_bits=c_bits, k_I=k_I, q_I=q_I, w=w, q=q, boosted=boosted)
+
+
+def _extra_row(rng: np.random.Generator, cfg: dict):
+    d_c, d_I, H_I, H = cfg["d_c"], cfg["d_I"], cfg["H_I"], cfg["H"]
+    q_I = rng.standard_normal((H_I, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_I))
+    w = rng.random(H_I, dtype=np.float32)
+    q = rng.standard_normal((H, d_c), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
+    return q_I, w, q
+
+
+def make_problem(cfg: dict) -> Problem:
+    """Generate every input of one workload (see synth.configs)."""
+    seed, ps = cfg["seed"], cfg["page_size"]
+    d_c, d_I, H_I, H = cfg["d_c"], cfg["d_I"], cfg["H_I"], cfg["H"]
+    W_KI = _child(seed, 0).standard_normal((d_c, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
+
+    if cfg["kind"] == "prefill":
+        lengths = [cfg["cache_len"]]
+    elif "lengths" in cfg:
+        lengths = list(cfg["lengths"])
+    else:
+        lo, hi = cfg["length_range"]
+        lengths = _child(seed, 1).integers(lo, hi, endpoint=True, size=cfg["batch"]).tolist()
+    S = len(lengths)
+    pages_per = [-(-n // ps) for n in lengths]
+    num_pages = max(1, sum(pages_per))
+    max_pages = max(1, max(pages_per))
+    if cfg.get("paged"):
+        perm = _child(seed, 2).permutation(num_pages).astype(np.int32)
+    else:
+        perm = np.arange(num_pages, dtype=np.int32)
+    page_table = np.zeros((S, max_pages), np.int32)
+    off = 0
+    for b, npg in enumerate(pages_per):
+        page_table[b, :npg] = perm[off:off + npg]
+        off += npg
+
+    f8 = cfg["idx_dtype"] == "f8"
+    kv_np = np.uint16 if cfg["kv_dtype"] == "bf16" else np.float32
+    k_pool = np.zeros((num_pages * ps, d_I), np.uint8 if f8 else np.float32)
+    k_scale = np.ones(num_pages * ps, np.float32) if f8 else None
+    kv_pool = np.zeros((num_pages * ps, d_c), kv_np)
+
+    q_I_rows, w_rows, q_rows, row_seq, row_len, boosted = [], [], [], [], [], []
+    for b, n in enumerate(lengths):
+        seq = _draw_sequence(_child(seed, 3, b), n, cfg, W_KI)
+        phys = (page_table[b, np.arange(n) // ps].astype(np.int64) * ps + np.arange(n) % ps)
+        kv_pool[phys] = seq["c_bits"]
+        if f8:
+            codes, sc = _quant_rows(seq["k_I"])
+            k_pool[phys] = codes
+            k_scale[phys] = sc
+        else:
+            k_pool[phys] = seq["k_I"]
+        boosted.append(seq["boosted"])
+        if cfg["kind"] == "decode":
+            q_I_rows.append(seq["q_I"]); w_rows.append(seq["w"]); q_rows.append(seq["q"])
+            row_seq.append(b); row_len.append(n)
+        else:
+            # causal chunk: the row at 1-based position p sees positions 0..p-1; the last row is the
+            # sequence's own query, the others are fresh draws
+            rows, first = cfg["rows"], cfg["cache_len"] - cfg["rows"] + 1
+            rng = _child(seed, 4)
+            for r in range(rows - 1):
+                a, bw, c = _extra_row(rng, cfg)
+                q_I_rows.append(a); w_rows.append(bw); q_rows.append(c)
+            q_I_rows.append(seq["q_I"]); w_rows.append(seq["w"]); q_rows.append(seq["q"])
+            row_seq.extend([b] * rows)
+            row_len.extend(range(first, first + rows))
+        del seq
+
+    R = len(row_seq)
+    q_I = np.stack(q_I_rows) if R else np.zeros((0, H_I, d_I), np.float32)
+    if f8:
+        q_idx, q_idx_scale = _quant_rows(q_I)
+    else:
+        q_idx, q_idx_scale = q_I.astype(np.float32), None
+    q_all = np.stack(q_rows) if R else np.zeros((0, H, d_c), np.float32)
+    q_bits, _ = _round_kv(q_all, cfg["kv_dtype"])
+    return Problem(
+        cfg=cfg, R=R, S=S, H_I=H_I, d_I=d_I, H=H, d_c=d_c, k=cfg["k"], page_size=ps, max_pages=max_pages,
+        num_pages=num_pages, idx_dtype=cfg["idx_dtype"], kv_dtype=cfg["kv_dtype"],
+        softmax_scale=float(cfg["softmax_scale"]),
+        q_idx=np.ascontiguousarray(q_idx), q_idx_scale=q_idx_scale,
+        head_w=np.ascontiguousarray(np.stack(w_rows).astype(np.float32)) if R else np.zeros((0, H_I), np.float32),
+        k_idx_pool=k_pool, k_idx_scale=k_scale, q=np.ascontiguousarray(q_bits), kv_pool=kv_pool,
+        row_seq=np.asarray(row_seq, np.int32), row_len=np.asarray(row_len, np.int32),
+        page_table=page_table, boosted=boosted)

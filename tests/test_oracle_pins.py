@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check reduces an oracle function to a library routine, a closed form, a brute-force definition, a value
+printed on the pages, or an invariant the method's definition implies, so that a dropped term, a wrong sign,
+a wrong head/position index or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------------------------- codecs
+
+def test_e4m3_all_codes_match_torch_cast():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode(codes, "f8")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def test_e4m3_closed_forms():
+    v = oracle.decode(np.array([0x7E, 0x01, 0x08, 0x38, 0xB8, 0x00, 0x80, 0x07], np.uint8), "f8")
+    # largest finite 448, smallest subnormal 2^-9, smallest normal 2^-6, 1.0, -1.0, +0, -0, largest subnormal 7*2^-9
+    assert list(v[:5]) == [448.0, 2.0 ** -9, 2.0 ** -6, 1.0, -1.0]
+    assert v[5] == 0.0 and v[6] == 0.0 and math.copysign(1, v[6]) == -1
+    assert v[7] == 7 * 2.0 ** -9
+
+
+def test_bf16_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2 ** 16, size=20000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # drop inf/NaN patterns
+    mine = oracle.decode(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref)
+
+
+# --------------------------------------------------------------------------------------------- indexer
+
+def _contig_layout(n, S=1):
+    """Identity page table for S sequences of n positions (page size 64)."""
+    pages = -(-n // 64)
+    return np.arange(S * pages, dtype=np.int32).reshape(S, pages)
+
+
+def _rand_f8_problem(rng, R=2, H_I=8, d_I=64, n=300):
+    q8 = rng.integers(0, 256, size=(R, H_I, d_I), dtype=np.uint8)
+    k8 = rng.integers(0, 256, size=(-(-n // 64) * 64, d_I), dtype=np.uint8)
+    q8[(q8 & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    k8[(k8 & 0x7F) == 0x7F] = 0x38
+    sq = rng.uniform(0.5, 2.0, size=(R, H_I)).astype(np.float32)
+    sk = rng.uniform(0.5, 2.0, size=k8.shape[0]).astype(np.float32)
+    w = rng.uniform(-1.0, 1.0, size=(R, H_I)).astype(np.float32)
+    return q8, sq, w, k8, sk
+
+
+def _scores(q, sq, w, k, sk, n, dtype, pt=None, row_seq=None):
+    R = q.shape[0]
+    pt = _contig_layout(n) if pt is None else pt
+    row_seq = np.zeros(R, np.int32) if row_seq is None else row_seq
+    return oracle.indexer_scores(q, sq, w, k, sk, row_seq, np.full(R, n, np.int32), pt, 64, dtype)
+
+
+def test_indexer_worked_example_from_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "indexer_worked_example.json")))
+    keys = np.array(g["keys_1based_tokens"], np.float32)
+    n = keys.shape[0]
+    pool = np.zeros((64, g["d_I"]), np.float32)
+    pool[:n] = keys
+    q = np.array(g["q_idx"], np.float32)[None]
+    w = np.array(g["head_w"], np.float32)[None]
+    sc = _scores(q, None, w, pool, None, n, "f32")
+    assert np.allclose(sc[0], g["expected_scores"], atol=g["tolerance_abs"], rtol=0)
+    for tok, val in g["printed_values"].items():
+        assert abs(sc[0, int(tok) - 1] - val) < g["tolerance_abs"]
+    assert (sc[0] < 0).any()  # signed head weights give negative scores
+    idx, kth = oracle.topk(sc, [n], g["budget"])
+    assert [i + 1 for i in idx[0]] == g["expected_kept_tokens_1based_in_order"]
+    assert abs(kth[0] - 6.4) < g["tolerance_abs"]
+
+
+def test_indexer_single_head_unit_weight_is_relu_of_matmul_f8_exact():
+    """H_I = 1, w = 1, unit scales: I = max(0, q.k); with fp8 operands every dot is exact in fp64, so it must
+    equal float64 numpy matmul of the torch-decoded codes bit for bit."""
+    rng = np.random.default_rng(1)
+    q8, _, _, k8, _ = _rand_f8_problem(rng, R=3, H_I=1, n=256)
+    ones_q, ones_k = np.ones((3, 1), np.float32), np.ones(k8.shape[0], np.float32)
+    sc = _scores(q8, ones_q, np.ones((3, 1), np.float32), k8, ones_k, 256, "f8")
+    dq = torch.from_numpy(q8).view(torch.float8_e4m3fn).to(torch.float64).numpy()[:, 0, :]
+    dk = torch.from_numpy(k8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = np.maximum(dq @ dk[:256].T, 0.0)
+    assert np.array_equal(sc, ref)
+
+
+def test_indexer_single_head_f32_is_relu_of_matmul():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((2, 1, 64)).astype(np.float32)
+    k = rng.standard_normal((128, 64)).astype(np.float32)
+    sc = _scores(q, None, np.ones((2, 1), np.float32), k, None, 128, "f32")
+    ref = np.maximum(q[:, 0, :].astype(np.float64) @ k.astype(np.float64).T, 0.0)
+    assert np.allclose(sc, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_is_sum_over_heads_of_single_head_scores():
+    rng = np.random.default_rng(3)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng)
+    full = _scores(q8, sq, w, k8, sk, 300, "f8")
+    parts = sum(_scores(q8[:, j:j + 1], sq[:, j:j + 1], w[:, j:j + 1], k8, sk, 300, "f8") for j in range(q8.shape[1]))
+    assert np.allclose(full, parts, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_single_head_scales_and_weight_factor_out():
+    """Positive scales and the head weight multiply the single-head score: w*sq*sk*max(0, dot of codes)."""
+    rng = np.random.default_rng(4)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng, R=2, H_I=1)
+    unit = _scores(q8, np.ones_like(sq), np.ones_like(w), k8, np.ones_like(sk), 300, "f8")
+    scaled = _scores(q8, sq, w, k8, sk, 300, "f8")
+    expect = unit * (w.astype(np.float64) * sq.astype(np.float64)) * sk[:300].astype(np.float64)[None, :]
+    assert np.allclose(scaled, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_per_head_relu_nonnegative_and_zero_on_negative_dots():
+    rng = np.random.default_rng(5)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng, R=1, H_I=4)
+    for j in range(4):
+        onehot = np.zeros((1, 4), np.float32)
+        onehot[0, j] = 1.0
+        sc = _scores(q8, sq, onehot, k8, sk, 300, "f8")
+        dq = torch.from_numpy(q8[0, j]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        dk = torch.from_numpy(k8[:300]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        dots = dk @ dq
+        assert (sc >= 0).all()
+        assert (sc[0][dots <= 0] == 0).all() and (sc[0][dots > 0] > 0).all()
+
+
+def test_indexer_weight_linearity_and_sign():
+    rng = np.random.default_rng(6)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng)
+    base = _scores(q8, sq, w, k8, sk, 300, "f8")
+    assert np.array_equal(_scores(q8, sq, 2 * w, k8, sk, 300, "f8"), 2 * base)
+    assert np.array_equal(_scores(q8, sq, -w, k8, sk, 300, "f8"), -base)
+
+
+def test_indexer_paging_and_position_permutation():
+    """A random page table over a permuted pool gives the same scores; permuting the cache permutes them."""
+    rng = np.random.default_rng(7)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng, n=320)
+    base = _scores(q8, sq, w, k8, sk, 320, "f8")
+    perm = rng.permutation(5).astype(np.int32)
+    pk8, psk = np.empty_like(k8), np.empty_like(sk)
+    for lp in range(5):
+        pk8[perm[lp] * 64:(perm[lp] + 1) * 64] = k8[lp * 64:(lp + 1) * 64]
+        psk[perm[lp] * 64:(perm[lp] + 1) * 64] = sk[lp * 64:(lp + 1) * 64]
+    paged = _scores(q8, sq, w, pk8, psk, 320, "f8", pt=perm[None, :])
+    assert np.array_equal(base, paged)
+    sperm = rng.permutation(320)
+    moved = _scores(q8, sq, w, k8[sperm], sk[sperm], 320, "f8")
+    assert np.array_equal(moved, base[:, sperm])
+
+
+def test_indexer_rows_see_only_their_prefix_and_their_sequence():
+    rng = np.random.default_rng(8)
+    q8, sq, w, k8, sk = _rand_f8_problem(rng, R=2, n=256)
+    # two sequences of 128 positions each in one pool; row 0 -> seq 1 with 100 visible, row 1 -> seq 0 with 128
+    pt = np.array([[0, 1], [2, 3]], np.int32)
+    sc = oracle.indexer_scores(q8, sq, w, k8, sk, np.array([1, 0], np.int32), np.array([100, 128], np.int32),
+                               pt, 64, "f8", ld=128)
+    alone1 = oracle.indexer_scores(q8[:1], sq[:1], w[:1], k8[128:], sk[128:], np.zeros(1, np.int32),
+                                   np.array([100], np.int32), _contig_layout(128), 64, "f8", ld=128)
+    assert np.array_equal(sc[0, :100], alone1[0, :100]) and np.isnan(sc[0, 100:]).all()
+    alone0 = _scores(q8[1:], sq[1:], w[1:], k8[:128], sk[:128], 128, "f8")
+    assert np.array_equal(sc[1], alone0[0])
+
+
+def test_p1_sketch_special_case_same_selection():
+    """The lizeman sketch scores one head as (k_I @ q_I)/sqrt(d_I) with no ReLU.  With one head, unit weight and
+    every dot positive, the ReLU is inactive and a positive factor cannot change the order, so the selected set
+    must equal torch.topk of the sketch's scores."""
+    rng = np.random.default_rng(9)
+    d_I, n, k = 64, 500, 37
+    q = np.abs(rng.standard_normal((1, 1, d_I))).astype(np.float32)
+    kk = np.abs(rng.standard_normal((-(-n // 64) * 64, d_I))).astype(np.float32)
+    sc = _scores(q, None, np.ones((1, 1), np.float32), kk, None, n, "f32")
+    idx, _ = oracle.topk(sc, [n], k)
+    sketch = (torch.from_numpy(kk[:n]).double() @ torch.from_numpy(q[0, 0]).double()) / d_I ** 0.5
+    assert set(idx[0].tolist()) == set(sketch.topk(k).indices.tolist())
+
+
+# ----------------------------------------------------------------------------------------------- top-k
+
+def _brute_force_selection(scores, k):
+    """Definition by rank: position p is kept iff fewer than min(k, n) positions precede it in the order
+    (higher score first, then lower position)."""
+    n = len(scores)
+    keff = min(k, n)
+    rank = [sum(1 for s in range(n) if scores[s] > scores[p] or (scores[s] == scores[p] and s < p)) for p in range(n)]
+    return [p for r in range(keff) for p in range(n) if rank[p] == r]
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.sampled_from([-2.0, -0.5, 0.0, 0.25, 1.0, 3.0, 7.5]), min_size=1, max_size=64),
+       st.integers(min_value=1, max_value=66))
+def test_topk_matches_rank_definition_with_ties(vals, k):
+    sc = np.array([vals], np.float64)
+    idx, kth = oracle.topk(sc, [len(vals)], k)
+    expect = _brute_force_selection(vals, k)
+    keff = min(k, len(vals))
+    assert idx[0, :keff].tolist() == expect
+    assert (idx[0, keff:] == -1).all()
+    assert kth[0] == vals[expect[-1]]
+
+
+def test_topk_matches_torch_topk_on_distinct_scores():
+    rng = np.random.default_rng(10)
+    sc = rng.standard_normal((3, 5000))
+    for k in (1, 17, 2048, 4999, 5000, 6000):
+        idx, kth = oracle.topk(sc, [5000, 5000, 5000], k)
+        keff = min(k, 5000)
+        for r in range(3):
+            ref = torch.from_numpy(sc[r]).topk(keff)
+            assert idx[r, :keff].tolist() == ref.indices.tolist()
+            assert kth[r] == ref.values[-1].item()
+
+
+def test_topk_short_row_reads_everything():
+    sc = np.array([[3.0, 1.0, 2.0, np.nan, np.nan]])
+    idx, kth = oracle.topk(sc, [3], 8)
+    assert idx[0].tolist() == [0, 2, 1, -1, -1, -1, -1, -1] and kth[0] == 1.0
+
+
+def test_topk_empty_row():
+    idx, kth = oracle.topk(np.zeros((1, 4)), [0], 4)
+    assert (idx == -1).all() and np.isnan(kth[0])
+
+
+# ------------------------------------------------------------------------------------------- attention
+
+def _attn_case(rng, n=200, H=4, d_c=64, dtype="f32"):
+    c = rng.standard_normal((-(-n // 64) * 64, d_c)).astype(np.float32)
+    q = (rng.standard_normal((1, H, d_c)) / math.sqrt(d_c)).astype(np.float32)
+    if dtype == "bf16":
+        c = torch.from_numpy(c).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        q = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return q, c
+
+
+def _as_f64(x, dtype):
+    return oracle.decode(x, dtype)
+
+
+def _attn(q, c, idx, n, dtype, scale, pt=None):
+    pt = _contig_layout(n) if pt is None else pt
+    return oracle.sparse_attn(q, c, np.asarray(idx, np.int32)[None], np.zeros(1, np.int32), pt, 64, dtype, scale)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 1 / math.sqrt(64)])
+def test_attention_full_selection_equals_dense_sdpa(dtype, scale):
+    """k >= n selects every position, so the step must equal dense softmax attention (torch SDPA, fp64)."""
+    rng = np.random.default_rng(11)
+    n, H, d_c = 200, 4, 64
+    q, c = _attn_case(rng, n, H, d_c, dtype)
+    o, lse = _attn(q, c, np.arange(n), n, dtype, scale)
+    Q = torch.from_numpy(_as_f64(q, dtype))[:, :, None, :]              # [1, H, 1, d]
+    K = torch.from_numpy(_as_f64(c, dtype)[:n])[None, None].expand(1, H, n, d_c)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, K, scale=scale)
+    assert np.allclose(o, ref[:, :, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+    logits = (Q @ K.transpose(-1, -2))[:, :, 0, :] * scale
+    assert np.allclose(lse, torch.logsumexp(logits, -1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_mask_form_equals_gather_form():
+    """The selector's reference form: top-k then -inf outside the list, softmax over the whole row."""
+    rng = np.random.default_rng(12)
+    n, H, d_c = 300, 3, 32
+    q, c = _attn_case(rng, n, H, d_c)
+    sel = rng.choice(n, size=40, replace=False)
+    o, lse = _attn(q, c, sel, n, "f32", 0.7)
+    Q, K = torch.from_numpy(q.astype(np.float64))[0], torch.from_numpy(c[:n].astype(np.float64))
+    logits = 0.7 * (Q @ K.T)
+    mask = torch.full((n,), float("-inf"), dtype=torch.float64)
+    mask[torch.from_numpy(sel)] = 0.0
+    p = torch.softmax(logits + mask, dim=-1)
+    assert np.allclose(o[0], (p @ K).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(13)
+    n, H, d_c = 100, 2, 16
+    q, c = _attn_case(rng, n, H, d_c)
+    # one selected row: output is that row, lse is its logit
+    o, lse = _attn(q, c, [37, -1, -1], n, "f32", 1.0)
+    assert np.array_equal(o[0, 0], c[37].astype(np.float64))
+    assert np.isclose(lse[0, 0], float(q[0, 0].astype(np.float64) @ c[37].astype(np.float64)), rtol=1e-14)
+    # zero query: uniform weights, output is the mean of the selected rows, lse = log(count)
+    sel = np.array([3, 9, 50, 77])
+    o, lse = _attn(np.zeros_like(q), c, sel, n, "f32", 1.0)
+    assert np.allclose(o[0, 1], c[sel].astype(np.float64).mean(0), rtol=1e-14, atol=1e-15)
+    assert np.isclose(lse[0, 1], math.log(4))
+    # empty selection
+    o, lse = _attn(q, c, [-1, -1], n, "f32", 1.0)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+def test_attention_order_invariant_and_paged():
+    rng = np.random.default_rng(14)
+    n, H, d_c = 256, 3, 32
+    q, c = _attn_case(rng, n, H, d_c)
+    sel = rng.choice(n, size=50, replace=False)
+    o1, l1 = _attn(q, c, sel, n, "f32", 1.0)
+    o2, l2 = _attn(q, c, sel[::-1], n, "f32", 1.0)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-14) and np.allclose(l1, l2, rtol=1e-14)
+    perm = rng.permutation(4).astype(np.int32)
+    pc = np.empty_like(c)
+    for lp in range(4):
+        pc[perm[lp] * 64:(perm[lp] + 1) * 64] = c[lp * 64:(lp + 1) * 64]
+    o3, l3 = _attn(q, pc, sel, n, "f32", 1.0, pt=perm[None])
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+def test_attention_heads_share_one_latent_row():
+    """MQA: each head's output depends only on its own query and the shared rows."""
+    rng = np.random.default_rng(15)
+    n, H, d_c = 128, 4, 32
+    q, c = _attn_case(rng, n, H, d_c)
+    sel = rng.choice(n, size=20, replace=False)
+    o_all, _ = _attn(q, c, sel, n, "f32", 1.0)
+    for h in range(H):
+        o_h, _ = _attn(q[:, h:h + 1], c, sel, n, "f32", 1.0)
+        assert np.array_equal(o_all[0, h], o_h[0, 0])
