@@ -1,0 +1,153 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) DeepSeek Sparse Attention decode-step library.
+ *
+ * For each query row the step
+ *   1. scores every visible cached position with the lightning indexer: H_I narrow heads each take the
+ *      dot product of their query with the position's single shared key, pass it through a ReLU, and the
+ *      H_I results are summed with per-head weights that carry no sign constraint (DeepSeek Sparse Attention
+ *      explained, "How Does the Lightning Indexer Score a Token?"; milos-mitrovic, "How Does the Lightning
+ *      Indexer Pick Which Tokens Matter?"; lizeman DSA page, section 2 stage 1);
+ *   2. keeps the min(k, n) highest-scoring positions ("How Does the Selector Pick 1,024?");
+ *   3. runs softmax attention in MQA mode over only the selected 512-wide latent rows, which every query
+ *      head shares and which serve as both key and value (lizeman section 2 stage 2; kiadev "How DSA works";
+ *      "What Does the Whole Block Look Like?").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never allocates, frees or
+ *     retains caller memory and keeps no state between calls; scratch space comes from the caller's
+ *     workspace (size from dsa_workspace_bytes).
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream) and the call
+ *     returns after the enqueue.  The caller synchronises.
+ *   - Every argument that the host can check is checked BEFORE anything is enqueued: a non-OK return means
+ *     no work was queued.  DSA_EHIP reports a failed launch.  Nothing throws or aborts across the ABI.
+ *     dsa_last_error() gives a thread-local message for the last non-OK return.
+ *   - Device-side metadata (row_seq, row_len, page_table) cannot be checked by the host.  Kernels clamp a
+ *     row length to [0, max_row_len] and a page id to [0, num_pages) so that a bad value never reads or
+ *     writes out of bounds; results for such rows are unspecified.
+ *   - Positions are 0-based logical positions within a row's sequence; row r sees positions 0..n_r-1.
+ *     Position s of sequence q lives at physical row page_table[q][s / page_size] * page_size +
+ *     s % page_size of each pool (the selected positions are "an address list into the paged KV cache").
+ *   - Calls on one stream are ordered; concurrent calls on different streams must use different
+ *     workspaces.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_EINVAL = 1,        /* a NULL pointer, a bad size or an inconsistent argument */
+  DSA_EUNSUPPORTED = 2,  /* a valid combination this build has no kernel for */
+  DSA_EWORKSPACE = 3,    /* workspace NULL or smaller than dsa_workspace_bytes() */
+  DSA_EHIP = 4           /* the HIP runtime reported an error at launch */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,     /* IEEE binary32 */
+  DSA_BF16 = 1,    /* bfloat16 */
+  DSA_F8E4M3 = 2   /* OCP FP8 E4M3FN codes (bias 7, max 448, no inf) with one fp32 scale per stored vector */
+} dsa_dtype_t;
+
+typedef enum { DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_STEP = 3 } dsa_op_t;
+
+/* Shapes, dtypes and bounds of one call.  Host memory, read during the call only. */
+typedef struct {
+  int32_t num_rows;      /* R: query rows in the call (one per sequence in decode, one per position in prefill) */
+  int32_t num_seqs;      /* S: rows of page_table */
+  int32_t idx_heads;     /* H_I: indexer heads.  F8E4M3: 32 or 64.  F32: 1..64 */
+  int32_t idx_dim;       /* d_I: indexer head width.  F8E4M3: 64.  F32: 1..128 */
+  int32_t attn_heads;    /* H: attention heads sharing one latent row.  BF16: multiple of 16, <= 256.  F32: <= 256 */
+  int32_t latent_dim;    /* d_c: latent width.  BF16: 512.  F32: 1..1024 */
+  int32_t topk;          /* k: positions kept per row, 1..16384 */
+  int32_t page_size;     /* positions per page: power of two, 32..4096 */
+  int32_t max_pages;     /* row stride of page_table */
+  int32_t num_pages;     /* physical pages in each pool (both pools have num_pages * page_size rows) */
+  int32_t max_row_len;   /* host-side bound: 0 <= row_len[r] <= max_row_len <= max_pages * page_size */
+  int32_t rows_per_seq;  /* >= 1.  Consecutive groups of this many rows share one sequence (a chunked prefill);
+                            the caller guarantees row_seq is constant within each group.  1 for plain decode */
+  int32_t idx_dtype;     /* dsa_dtype_t of q_idx / k_idx_pool: DSA_F8E4M3 (scales required) or DSA_F32 (scales NULL) */
+  int32_t kv_dtype;      /* dsa_dtype_t of q / kv_pool / out: DSA_BF16 or DSA_F32 */
+  float softmax_scale;   /* logits = softmax_scale * <q[h], c[s]> */
+} dsa_problem_t;
+
+/* Device-resident int32 metadata.  The struct itself is host memory. */
+typedef struct {
+  const int32_t *row_seq;     /* [R] sequence (page_table row) of each query row */
+  const int32_t *row_len;     /* [R] visible positions n_r of each row */
+  const int32_t *page_table;  /* [S, max_pages] physical page of each logical page, shared by both pools */
+} dsa_layout_t;
+
+/*
+ * Lightning-indexer scores (step 1).
+ *   q_idx       [R, H_I, d_I]   fp8 codes or fp32 indexer queries
+ *   q_idx_scale [R, H_I]        fp32 dequantisation scale of each query vector (F8E4M3; NULL for F32)
+ *   head_w      [R, H_I]        fp32 head weights, any sign
+ *   k_idx_pool  [num_pages*page_size, d_I]  fp8 codes or fp32 keys, one per cached position
+ *   k_idx_scale [num_pages*page_size]       fp32 scale of each key (F8E4M3; NULL for F32)
+ *   scores      [R, scores_ld]  fp32 out: scores[r][s] = sum_j w[r][j] * max(0, <q_I[r][j], k_I[s]>) for
+ *                               s < n_r, with q_I = scale * code; entries s >= n_r are not written.
+ *   scores_ld   >= max_row_len
+ * The fp8 path computes the per-head dot products exactly (fp8 x fp8 products, fp32 accumulation of 64
+ * terms) and applies the positive scales outside the ReLU, max(0, a*b*x) = a*b*max(0, x).
+ */
+dsa_status_t dsa_indexer_scores(const dsa_problem_t *problem, const dsa_layout_t *layout,
+                                 const void *q_idx, const float *q_idx_scale, const float *head_w,
+                                 const void *k_idx_pool, const float *k_idx_scale,
+                                 float *scores, int64_t scores_ld, void *stream);
+
+/*
+ * Top-k selection (step 2): for each row, the k_eff = min(k, n_r) positions with the largest scores,
+ * ties broken by lower position ("keeps the highest index_topk"; "the smaller of the budget and the number
+ * of tokens").
+ *   scores    [R, scores_ld] fp32, read for s < n_r
+ *   topk_idx  [R, k] int32 out: the selected positions in increasing position order, then -1 padding
+ *   workspace >= dsa_workspace_bytes(problem, DSA_OP_TOPK) bytes of device memory, 256-byte aligned
+ * Scores are ranked by an order-preserving integer key of their fp32 value (+0 and -0 are equal).
+ */
+dsa_status_t dsa_topk(const dsa_problem_t *problem, const dsa_layout_t *layout, const float *scores,
+                      int64_t scores_ld, int32_t *topk_idx, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse MLA attention in MQA mode (step 3) over the selected latent rows.
+ *   q         [R, H, d_c]  bf16 or fp32 queries, already in latent space
+ *   kv_pool   [num_pages*page_size, d_c]  bf16 or fp32 latent rows (key = value = the latent row)
+ *   topk_idx  [R, k] int32 positions; entries < 0 are skipped; order does not matter
+ *   out       [R, H, d_c]  bf16 or fp32 out: softmax-weighted sum of the selected rows
+ *   lse       [R, H] fp32 out (may be NULL): natural-log sum of exp(logits); -inf for an empty selection,
+ *             whose output is 0
+ * The bf16 path runs QK^T and PV on bf16 MFMA with fp32 accumulation and an fp32 online softmax.
+ */
+dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t *problem, const dsa_layout_t *layout, const void *q,
+                                 const void *kv_pool, const int32_t *topk_idx, void *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The whole step on one stream: indexer scores -> top-k -> sparse attention (the four-stage decode pipeline
+ * of "What Does the GPU Actually Run?", with the head weights applied in the scoring kernel).
+ * Arguments as above; topk_idx may be NULL (the selection then stays in the workspace), lse may be NULL.
+ * workspace >= dsa_workspace_bytes(problem, DSA_OP_STEP).
+ */
+dsa_status_t dsa_decode_step(const dsa_problem_t *problem, const dsa_layout_t *layout,
+                             const void *q_idx, const float *q_idx_scale, const float *head_w,
+                             const void *k_idx_pool, const float *k_idx_scale,
+                             const void *q, const void *kv_pool, int32_t *topk_idx,
+                             void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes an operation needs for this problem (0 on an invalid problem; see dsa_last_error). */
+size_t dsa_workspace_bytes(const dsa_problem_t *problem, int32_t op);
+
+const char *dsa_status_str(dsa_status_t status);
+const char *dsa_last_error(void);
+int32_t dsa_abi_version(void);  /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,263 @@
+// C-ABI entry points of libdsa (declared in include/dsa.h): argument validation on the host, workspace
+// layout, and dispatch to the gfx950 kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define DSA_CHECK(cond, st, ...) \
+  do {                           \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+// Checks the problem description (no device pointers) and fills the derived geometry.
+dsa_status_t check_problem(const dsa_problem_t* p, const dsa_layout_t* lay, bool need_idx, bool need_attn,
+                           dsa::Geo* g) {
+  DSA_CHECK(p != nullptr, DSA_EINVAL, "problem is NULL");
+  DSA_CHECK(p->num_rows >= 0, DSA_EINVAL, "num_rows = %d < 0", p->num_rows);
+  DSA_CHECK(p->num_seqs >= 1, DSA_EINVAL, "num_seqs = %d < 1", p->num_seqs);
+  DSA_CHECK(p->topk >= 1 && p->topk <= 16384, DSA_EINVAL, "topk = %d outside 1..16384", p->topk);
+  const int lg = ilog2_exact(p->page_size);
+  DSA_CHECK(p->page_size >= 32 && p->page_size <= 4096 && lg >= 0, DSA_EINVAL,
+            "page_size = %d is not a power of two in 32..4096", p->page_size);
+  DSA_CHECK(p->max_pages >= 1 && p->num_pages >= 1, DSA_EINVAL, "max_pages = %d, num_pages = %d must be >= 1",
+            p->max_pages, p->num_pages);
+  DSA_CHECK((int64_t)p->num_pages * p->page_size <= (int64_t)1 << 40, DSA_EINVAL, "pool too large");
+  DSA_CHECK(p->max_row_len >= 0 && (int64_t)p->max_row_len <= (int64_t)p->max_pages * p->page_size, DSA_EINVAL,
+            "max_row_len = %d outside 0..max_pages*page_size = %lld", p->max_row_len,
+            (long long)p->max_pages * p->page_size);
+  DSA_CHECK((int64_t)p->max_row_len <= (int64_t)dsa::kTopkMaxBlocksPerRow * dsa::kTopkChunk, DSA_EUNSUPPORTED,
+            "max_row_len = %d above the supported %d", p->max_row_len,
+            dsa::kTopkMaxBlocksPerRow * dsa::kTopkChunk);
+  DSA_CHECK(p->rows_per_seq >= 1, DSA_EINVAL, "rows_per_seq = %d < 1", p->rows_per_seq);
+  DSA_CHECK(p->num_rows <= 65535, DSA_EUNSUPPORTED, "num_rows = %d above 65535", p->num_rows);
+  DSA_CHECK(lay != nullptr, DSA_EINVAL, "layout is NULL");
+  DSA_CHECK(lay->row_seq && lay->row_len && lay->page_table, DSA_EINVAL, "layout has a NULL pointer");
+  if (need_idx) {
+    DSA_CHECK(p->idx_dtype == DSA_F8E4M3 || p->idx_dtype == DSA_F32, DSA_EINVAL, "idx_dtype = %d invalid",
+              p->idx_dtype);
+    if (p->idx_dtype == DSA_F8E4M3) {
+      DSA_CHECK(p->idx_dim == 64, DSA_EUNSUPPORTED, "fp8 indexer needs idx_dim = 64 (got %d)", p->idx_dim);
+      DSA_CHECK(p->idx_heads == 32 || p->idx_heads == 64, DSA_EUNSUPPORTED,
+                "fp8 indexer needs idx_heads of 32 or 64 (got %d)", p->idx_heads);
+    } else {
+      DSA_CHECK(p->idx_heads >= 1 && p->idx_heads <= 64, DSA_EUNSUPPORTED, "fp32 indexer: idx_heads = %d not in 1..64",
+                p->idx_heads);
+      DSA_CHECK(p->idx_dim >= 1 && p->idx_dim <= 128, DSA_EUNSUPPORTED, "fp32 indexer: idx_dim = %d not in 1..128",
+                p->idx_dim);
+    }
+  }
+  if (need_attn) {
+    DSA_CHECK(p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_F32, DSA_EINVAL, "kv_dtype = %d invalid", p->kv_dtype);
+    DSA_CHECK(p->attn_heads >= 1 && p->attn_heads <= 256, DSA_EUNSUPPORTED, "attn_heads = %d not in 1..256",
+              p->attn_heads);
+    DSA_CHECK(p->softmax_scale == p->softmax_scale, DSA_EINVAL, "softmax_scale is NaN");
+    if (p->kv_dtype == DSA_BF16) {
+      DSA_CHECK(p->latent_dim == 512, DSA_EUNSUPPORTED, "bf16 attention needs latent_dim = 512 (got %d)",
+                p->latent_dim);
+      DSA_CHECK(p->attn_heads % 16 == 0, DSA_EUNSUPPORTED, "bf16 attention needs attn_heads %% 16 == 0 (got %d)",
+                p->attn_heads);
+    } else {
+      DSA_CHECK(p->latent_dim >= 1 && p->latent_dim <= 1024, DSA_EUNSUPPORTED, "fp32 attention: latent_dim = %d",
+                p->latent_dim);
+      DSA_CHECK(p->topk <= 4096, DSA_EUNSUPPORTED, "fp32 attention supports topk <= 4096 (got %d)", p->topk);
+    }
+  }
+  g->R = p->num_rows;
+  g->S = p->num_seqs;
+  g->H_I = p->idx_heads;
+  g->d_I = p->idx_dim;
+  g->H = p->attn_heads;
+  g->d_c = p->latent_dim;
+  g->k = p->topk;
+  g->page_size = p->page_size;
+  g->log2ps = lg;
+  g->max_pages = p->max_pages;
+  g->num_pages = p->num_pages;
+  g->max_row_len = p->max_row_len;
+  g->rows_per_seq = p->rows_per_seq;
+  g->idx_dtype = p->idx_dtype;
+  g->kv_dtype = p->kv_dtype;
+  g->softmax_scale = p->softmax_scale;
+  g->row_seq = lay->row_seq;
+  g->row_len = lay->row_len;
+  g->page_table = lay->page_table;
+  return DSA_OK;
+}
+
+dsa_status_t check_indexer_args(const dsa::Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                                const void* k_idx_pool, const float* k_idx_scale) {
+  DSA_CHECK(q_idx && head_w && k_idx_pool, DSA_EINVAL, "q_idx, head_w and k_idx_pool must be non-NULL");
+  DSA_CHECK(aligned16(q_idx) && aligned16(k_idx_pool), DSA_EINVAL, "q_idx and k_idx_pool must be 16-byte aligned");
+  if (g.idx_dtype == DSA_F8E4M3)
+    DSA_CHECK(q_idx_scale && k_idx_scale, DSA_EINVAL, "fp8 indexer needs q_idx_scale and k_idx_scale");
+  else
+    DSA_CHECK(!q_idx_scale && !k_idx_scale, DSA_EINVAL, "fp32 indexer takes no scales (pass NULL)");
+  return DSA_OK;
+}
+
+dsa_status_t check_attn_args(const dsa::Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx,
+                             const void* out) {
+  DSA_CHECK(q && kv_pool && topk_idx && out, DSA_EINVAL, "q, kv_pool, topk_idx and out must be non-NULL");
+  DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
+            "q, kv_pool and out must be 16-byte aligned");
+  (void)g;
+  return DSA_OK;
+}
+
+dsa_status_t check_scores(const dsa::Geo& g, const float* scores, int64_t ld) {
+  DSA_CHECK(scores != nullptr, DSA_EINVAL, "scores is NULL");
+  DSA_CHECK(aligned16(scores), DSA_EINVAL, "scores must be 16-byte aligned");
+  DSA_CHECK(ld >= g.max_row_len && ld % 4 == 0, DSA_EINVAL, "scores_ld = %lld must be >= max_row_len = %d and a multiple of 4",
+            (long long)ld, g.max_row_len);
+  return DSA_OK;
+}
+
+dsa_status_t check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return DSA_OK;
+  DSA_CHECK(ws != nullptr, DSA_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  DSA_CHECK((reinterpret_cast<uintptr_t>(ws) & (dsa::kAlign - 1)) == 0, DSA_EWORKSPACE,
+            "workspace must be %zu-byte aligned", dsa::kAlign);
+  DSA_CHECK(have >= need, DSA_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t step_ld(const dsa::Geo& g) { return ((int64_t)std::max(g.max_row_len, 1) + 63) / 64 * 64; }
+
+size_t step_bytes(const dsa::Geo& g) {
+  return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) + dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
+         std::max(dsa::topk_workspace_bytes(g), dsa::attn_workspace_bytes(g));
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_indexer_scores(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,
+                                const float* q_idx_scale, const float* head_w, const void* k_idx_pool,
+                                const float* k_idx_scale, float* scores, int64_t scores_ld, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, true, false, &g);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_args(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale)) != DSA_OK) return st;
+  if ((st = check_scores(g, scores, scores_ld)) != DSA_OK) return st;
+  return hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, scores_ld,
+                                        static_cast<hipStream_t>(stream)),
+                    "indexer launch");
+}
+
+dsa_status_t dsa_topk(const dsa_problem_t* problem, const dsa_layout_t* layout, const float* scores,
+                      int64_t scores_ld, int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, false, false, &g);
+  if (st != DSA_OK) return st;
+  if ((st = check_scores(g, scores, scores_ld)) != DSA_OK) return st;
+  DSA_CHECK(topk_idx != nullptr, DSA_EINVAL, "topk_idx is NULL");
+  if ((st = check_ws(workspace, workspace_bytes, dsa::topk_workspace_bytes(g))) != DSA_OK) return st;
+  return hip_status(dsa::launch_topk(g, scores, scores_ld, topk_idx, workspace, static_cast<hipStream_t>(stream)),
+                    "top-k launch");
+}
+
+dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q,
+                                 const void* kv_pool, const int32_t* topk_idx, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, false, true, &g);
+  if (st != DSA_OK) return st;
+  if ((st = check_attn_args(g, q, kv_pool, topk_idx, out)) != DSA_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, dsa::attn_workspace_bytes(g))) != DSA_OK) return st;
+  return hip_status(dsa::launch_attn(g, q, kv_pool, topk_idx, out, lse, workspace, static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,
+                             const float* q_idx_scale, const float* head_w, const void* k_idx_pool,
+                             const float* k_idx_scale, const void* q, const void* kv_pool, int32_t* topk_idx,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, true, true, &g);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_args(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale)) != DSA_OK) return st;
+  DSA_CHECK(q && kv_pool && out, DSA_EINVAL, "q, kv_pool and out must be non-NULL");
+  DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
+            "q, kv_pool and out must be 16-byte aligned");
+  if ((st = check_ws(workspace, workspace_bytes, step_bytes(g))) != DSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t ld = step_ld(g);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += dsa::align_up(sizeof(float) * (size_t)g.R * ld);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws);
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  if (topk_idx) idx = topk_idx;
+  if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld, s),
+                       "indexer launch")) != DSA_OK)
+    return st;
+  if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, s), "top-k launch")) != DSA_OK) return st;
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, s), "attention launch");
+}
+
+size_t dsa_workspace_bytes(const dsa_problem_t* problem, int32_t op) {
+  g_last_error.clear();  // a 0 return with an empty message means "no workspace needed"
+  if (!problem) { fail(DSA_EINVAL, "problem is NULL"); return 0; }
+  dsa_layout_t dummy{reinterpret_cast<const int32_t*>(16), reinterpret_cast<const int32_t*>(16),
+                     reinterpret_cast<const int32_t*>(16)};
+  dsa::Geo g;
+  const bool idx = op == DSA_OP_STEP, attn = op == DSA_OP_ATTN || op == DSA_OP_STEP;
+  if (check_problem(problem, &dummy, idx, attn, &g) != DSA_OK) return 0;
+  switch (op) {
+    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(g);
+    case DSA_OP_ATTN: return dsa::attn_workspace_bytes(g);
+    case DSA_OP_STEP: return step_bytes(g);
+    default: fail(DSA_EINVAL, "unknown op %d", op); return 0;
+  }
+}
+
+const char* dsa_status_str(dsa_status_t s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_EINVAL: return "DSA_EINVAL: invalid argument";
+    case DSA_EUNSUPPORTED: return "DSA_EUNSUPPORTED: no kernel for this combination";
+    case DSA_EWORKSPACE: return "DSA_EWORKSPACE: workspace missing or too small";
+    case DSA_EHIP: return "DSA_EHIP: HIP runtime error";
+  }
+  return "unknown dsa_status_t";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dsa_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 kernels of libdsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned short v8us __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Physical pool row of logical position `pos` (>= 0) of sequence `seq`.  The logical page is clamped to
+// [0, max_pages) and the page id to [0, num_pages), so corrupt metadata never addresses memory outside the
+// table or the pools.
+__device__ __forceinline__ int64_t phys_row(const int32_t* __restrict__ page_table, int max_pages, int num_pages,
+                                            int log2ps, int seq, int64_t pos) {
+  const int lp = (int)min(pos >> log2ps, (int64_t)max_pages - 1);
+  int page = page_table[(int64_t)seq * max_pages + lp];
+  page = min(max(page, 0), num_pages - 1);
+  return ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
+}
+
+__device__ __forceinline__ int clamp_len(int n, int max_len) { return min(max(n, 0), max_len); }
+__device__ __forceinline__ int clamp_seq(int seq, int num_seqs) { return min(max(seq, 0), num_seqs - 1); }
+
+// Order-preserving unsigned key of an fp32 score: a > b  <=>  key(a) > key(b); +0 and -0 share one key.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (the gfx950 conversion instruction).
+__device__ __forceinline__ unsigned short float_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(unsigned short, h);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Exclusive prefix of `v` over the lanes of a wave (and the wave total).
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
+// Block-wide exclusive scan of one value per thread.  `scratch` holds blockDim.x / 64 + 1 words of LDS.
+// Must be called by every thread of the block.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
+  uint32_t wt;
+  uint32_t x = wave_exclusive_scan(v, wt);
+  if (lane == 0) scratch[wave] = wt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < nwaves; ++w) { uint32_t t = scratch[w]; scratch[w] = run; run += t; }
+    scratch[nwaves] = run;
+  }
+  __syncthreads();
+  x += scratch[wave];
+  total = scratch[nwaves];
+  __syncthreads();
+  return x;
+}
+
+}  // namespace dsa

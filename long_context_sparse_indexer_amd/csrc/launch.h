@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI entry points (api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// A validated problem with its device metadata.
+struct Geo {
+  int R, S, H_I, d_I, H, d_c, k;
+  int page_size, log2ps, max_pages, num_pages, max_row_len, rows_per_seq;
+  int idx_dtype, kv_dtype;
+  float softmax_scale;
+  const int32_t* row_seq;
+  const int32_t* row_len;
+  const int32_t* page_table;
+};
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// indexer.hip
+hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                          const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
+                          hipStream_t stream);
+
+// topk.hip
+constexpr int kTopkMaxBlocksPerRow = 1024;
+constexpr int kTopkChunk = 4096;
+size_t topk_workspace_bytes(const Geo& g);
+hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
+                       hipStream_t stream);
+
+// attn.hip
+size_t attn_workspace_bytes(const Geo& g);
+hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
+                       float* lse, void* workspace, hipStream_t stream);
+
+}  // namespace dsa

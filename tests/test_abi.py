@@ -1,0 +1,149 @@
+"""The C-ABI library loads, exports every symbol include/dsa.h declares, and rejects bad arguments on the host
+before anything is enqueued.  No call here reaches a kernel launch (each one fails validation first), so the
+file runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_indexer_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a 256-byte-aligned non-NULL address that validation never dereferences
+MISALIGNED = FAKE + 4
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_workspace_bytes",
+            "dsa_status_str", "dsa_last_error", "dsa_abi_version"} <= set(names)
+    L = dsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert dsa.dsa_abi_version() == 1
+
+
+def _problem(**kw):
+    base = dict(num_rows=2, num_seqs=1, idx_heads=64, idx_dim=64, attn_heads=128, latent_dim=512, topk=2048,
+                page_size=64, max_pages=64, num_pages=64, max_row_len=4096, idx_dtype="f8", kv_dtype="bf16")
+    base.update(kw)
+    return dsa.make_problem(**base)
+
+
+LAYOUT = dsa.dsa_layout_t(FAKE, FAKE, FAKE)
+
+
+def _idx(p, layout=LAYOUT, q=FAKE, qs=FAKE, w=FAKE, k=FAKE, ks=FAKE, scores=FAKE, ld=4096):
+    L = dsa.lib()
+    return L.dsa_indexer_scores(ctypes.byref(p) if p is not None else None,
+                                ctypes.byref(layout) if layout is not None else None, q, qs, w, k, ks, scores, ld, None)
+
+
+def test_null_problem_and_layout():
+    assert _idx(None) == dsa.DSA_EINVAL
+    assert "problem is NULL" in dsa.dsa_last_error()
+    assert _idx(_problem(), layout=None) == dsa.DSA_EINVAL
+    assert _idx(_problem(), layout=dsa.dsa_layout_t(FAKE, None, FAKE)) == dsa.DSA_EINVAL
+
+
+@pytest.mark.parametrize("kw, status, text", [
+    (dict(num_rows=-1), dsa.DSA_EINVAL, "num_rows"),
+    (dict(topk=0), dsa.DSA_EINVAL, "topk"),
+    (dict(topk=20000), dsa.DSA_EINVAL, "topk"),
+    (dict(page_size=48), dsa.DSA_EINVAL, "page_size"),
+    (dict(page_size=16), dsa.DSA_EINVAL, "page_size"),
+    (dict(max_row_len=4097), dsa.DSA_EINVAL, "max_row_len"),
+    (dict(max_row_len=-5), dsa.DSA_EINVAL, "max_row_len"),
+    (dict(rows_per_seq=0), dsa.DSA_EINVAL, "rows_per_seq"),
+    (dict(idx_dim=128), dsa.DSA_EUNSUPPORTED, "idx_dim"),
+    (dict(idx_heads=48), dsa.DSA_EUNSUPPORTED, "idx_heads"),
+    (dict(idx_dtype=7), dsa.DSA_EINVAL, "idx_dtype"),
+    (dict(num_pages=0), dsa.DSA_EINVAL, "num_pages"),
+    (dict(num_rows=70000), dsa.DSA_EUNSUPPORTED, "num_rows"),
+])
+def test_indexer_problem_validation(kw, status, text):
+    assert _idx(_problem(**kw)) == status
+    assert text in dsa.dsa_last_error()
+
+
+def test_indexer_pointer_validation():
+    p = _problem()
+    assert _idx(p, q=None) == dsa.DSA_EINVAL
+    assert _idx(p, qs=None) == dsa.DSA_EINVAL and "scale" in dsa.dsa_last_error()
+    assert _idx(p, k=MISALIGNED) == dsa.DSA_EINVAL and "aligned" in dsa.dsa_last_error()
+    assert _idx(p, scores=None) == dsa.DSA_EINVAL
+    assert _idx(p, ld=4000) == dsa.DSA_EINVAL and "scores_ld" in dsa.dsa_last_error()
+    assert _idx(p, ld=4098) == dsa.DSA_EINVAL
+    pf = _problem(idx_dtype="f32")
+    assert _idx(pf) == dsa.DSA_EINVAL and "no scales" in dsa.dsa_last_error()
+
+
+def test_topk_workspace_validation():
+    p = _problem()
+    L = dsa.lib()
+    need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_TOPK)
+    assert need > 0
+    st = L.dsa_topk(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, 4096, FAKE, None, need, None)
+    assert st == dsa.DSA_EWORKSPACE
+    st = L.dsa_topk(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, 4096, FAKE, FAKE, need - 1, None)
+    assert st == dsa.DSA_EWORKSPACE and "bytes" in dsa.dsa_last_error()
+    st = L.dsa_topk(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, 4096, FAKE, FAKE + 16, need, None)
+    assert st == dsa.DSA_EWORKSPACE and "aligned" in dsa.dsa_last_error()
+    st = L.dsa_topk(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, 4096, None, FAKE, need, None)
+    assert st == dsa.DSA_EINVAL
+
+
+def test_attention_validation():
+    L = dsa.lib()
+    for kw, status in [(dict(latent_dim=576), dsa.DSA_EUNSUPPORTED), (dict(attn_heads=24), dsa.DSA_EUNSUPPORTED),
+                       (dict(kv_dtype=9), dsa.DSA_EINVAL), (dict(kv_dtype="f32", topk=8192), dsa.DSA_EUNSUPPORTED),
+                       (dict(softmax_scale=float("nan")), dsa.DSA_EINVAL)]:
+        p = _problem(**kw)
+        st = L.dsa_sparse_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   1 << 30, None)
+        assert st == status, (kw, dsa.dsa_last_error())
+    p = _problem(num_rows=1)
+    need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_ATTN)
+    assert need > 0  # one row splits its selection over several blocks
+    st = L.dsa_sparse_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert st == dsa.DSA_EWORKSPACE
+    st = L.dsa_sparse_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, None, FAKE, None, FAKE, need, None)
+    assert st == dsa.DSA_EINVAL
+
+
+def test_decode_step_validation():
+    L = dsa.lib()
+    p = _problem()
+    need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_STEP)
+    assert need >= dsa.dsa_workspace_bytes(p, dsa.DSA_OP_TOPK)
+    args = [FAKE] * 5 + [FAKE, FAKE, None, FAKE, None]
+    assert L.dsa_decode_step(ctypes.byref(p), ctypes.byref(LAYOUT), *args, FAKE, need - 256, None) == dsa.DSA_EWORKSPACE
+    bad = list(args)
+    bad[6] = MISALIGNED  # kv_pool
+    assert L.dsa_decode_step(ctypes.byref(p), ctypes.byref(LAYOUT), *bad, FAKE, need, None) == dsa.DSA_EINVAL
+
+
+def test_workspace_query_errors_and_strings():
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_workspace_bytes(_problem(topk=0), dsa.DSA_OP_TOPK)
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_workspace_bytes(_problem(), 99)
+    # attention of many rows needs no split buffers: 0 bytes with no error
+    assert dsa.dsa_workspace_bytes(_problem(num_rows=64), dsa.DSA_OP_ATTN) == 0
+    for s in range(5):
+        assert dsa.dsa_status_str(s).startswith("DSA_")
+    assert "unknown" in dsa.dsa_status_str(42)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    p = _problem()
+    lay = dsa.dsa_layout_t(FAKE, FAKE, FAKE)
+    with pytest.raises(ValueError):
+        dsa.dsa_indexer_scores(p, lay, torch.zeros(4), None, None, None, None, torch.zeros(4), 4096, stream=0)

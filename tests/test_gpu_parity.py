@@ -1,0 +1,154 @@
+"""GPU parity: every kernel of the HIP path, called through the C ABI, against the CPU oracle.
+
+Run on an MI355X (gfx950).  Sizes span several indexer tiles (512 positions), several top-k chunks (4096
+scores) and attention chunks (64 slots), each with a ragged tail; the decode_128k case runs at full size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_indexer_amd as dsa
+import oracle
+import synth
+from harness import full_check, gpu_step, say, check_topk_exact
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()
+
+
+def _run(cfg, fields=None, mutate=None):
+    say(f"case {cfg.get('name')} {({k: v for k, v in cfg.items() if k not in ('name',)})}")
+    prob = synth.make_problem(cfg)
+    if mutate:
+        mutate(prob)
+    res, err = full_check(prob, fields)
+    say(f"  ok: score err {err['score_ratio']:.3f} of bound, attention err {err['attn_err']:.2e}, "
+        f"end-to-end err {err['e2e_err']:.2e}")
+    return prob, res
+
+
+def test_tiny_fp32_full():
+    _run(synth.get("tiny_fp32"))
+
+
+def test_tiny_fp32_short_and_ragged():
+    _run(synth.get("tiny_fp32", lengths=[1000], k=256, H=3, H_I=3, d_I=40, anchors=4))
+    _run(synth.get("tiny_fp32", lengths=[200], k=256, H=5, anchors=4))  # k > n: read in full
+
+
+def test_decode_fp8_bf16_ragged():
+    _run(synth.get("decode_128k", lengths=[20000], anchors=64, recent=96))
+
+
+def test_decode_128k_full_size():
+    _run(synth.get("decode_128k"))
+
+
+def test_batched_paged_mixed_lengths():
+    _run(synth.get("batched_paged", batch=6, length_range=(3000, 9000)))
+
+
+def test_batched_short_empty_and_tiny_rows():
+    # one empty row, one single-position row, one row shorter than k, one longer
+    _run(synth.get("batched_paged", batch=4, lengths=[0, 1, 1500, 6000], anchors=8, recent=8))
+
+
+def test_index_heads_32_and_small_budgets():
+    _run(synth.get("decode_128k", lengths=[9000], H_I=32, k=100, anchors=16, recent=32))
+    _run(synth.get("decode_128k", lengths=[5000], k=1, H=16, anchors=16, recent=32))
+
+
+def test_softmax_scale_and_signed_weights():
+    def signed(prob):
+        rng = np.random.default_rng(123)
+        prob.head_w[:] = rng.uniform(-1, 1, size=prob.head_w.shape).astype(np.float32)
+    prob, res = _run(synth.get("decode_128k", lengths=[7000], softmax_scale=1 / math.sqrt(512), H=32,
+                               anchors=16, recent=32), mutate=signed)
+    assert (res.scores[0, :7000] < 0).any()
+
+
+def test_prefill_chunk_rows_share_the_cache():
+    prob, res = _run(synth.get("prefill_chunk", cache_len=9000, rows=40, H=32))
+    assert prob.row_len.tolist() == list(range(8961, 9001))
+
+
+def test_paged_equals_contiguous_bit_for_bit():
+    cfg = synth.get("batched_paged", batch=3, length_range=(2500, 7000), H=32)
+    a = gpu_step(synth.make_problem(cfg))
+    b = gpu_step(synth.make_problem(dict(cfg, paged=False)))
+    assert np.array_equal(a.idx, b.idx) and np.array_equal(a.out, b.out) and np.array_equal(a.lse, b.lse)
+
+
+def test_rerun_is_bit_identical():
+    prob = synth.make_problem(synth.get("decode_128k", lengths=[12000], H=64))
+    a, b = gpu_step(prob), gpu_step(prob)
+    assert np.array_equal(a.scores[:, :12000], b.scores[:, :12000])
+    assert np.array_equal(a.idx, b.idx) and np.array_equal(a.out, b.out)
+
+
+# ------------------------------------------------------------------------------- top-k on crafted scores
+
+def _topk_only(scores_np, row_len, k):
+    R, n = scores_np.shape
+    ld = max(4, -(-n // 4) * 4)
+    dev = "cuda"
+    s = torch.zeros((R, ld), dtype=torch.float32, device=dev)
+    s[:, :n] = torch.from_numpy(scores_np.astype(np.float32)).to(dev)
+    pages = max(1, -(-max(max(row_len), 1) // 64))
+    P = dsa.make_problem(num_rows=R, num_seqs=1, topk=k, page_size=64, max_pages=pages, num_pages=pages,
+                         max_row_len=max(row_len))
+    rl = torch.tensor(row_len, dtype=torch.int32, device=dev)
+    rs = torch.zeros(R, dtype=torch.int32, device=dev)
+    pt = torch.zeros((1, pages), dtype=torch.int32, device=dev)
+    L = dsa.make_layout(rs, rl, pt)
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_TOPK), dtype=torch.uint8, device=dev)
+    dsa.dsa_topk(P, L, s, idx, ws, ld)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def _expect_exact(scores_np, row_len, k):
+    got = _topk_only(scores_np, row_len, k)
+    ref, _ = oracle.topk(scores_np.astype(np.float32).astype(np.float64), row_len, k)
+    for r in range(len(row_len)):
+        keff = min(k, row_len[r])
+        assert np.array_equal(got[r, :keff], np.sort(ref[r, :keff])), f"row {r}"
+        assert (got[r, keff:] == -1).all()
+
+
+def test_topk_heavy_ties_in_lds_path():
+    rng = np.random.default_rng(5)
+    sc = rng.integers(0, 4, size=(3, 9000)).astype(np.float32)
+    _expect_exact(sc, [9000, 8191, 4097], 2048)
+
+
+def test_topk_all_equal_uses_the_row_rescan():
+    sc = np.full((2, 20000), 0.5, np.float32)   # every score ties: candidates overflow the LDS list
+    sc[1, 123] = 0.75
+    _expect_exact(sc, [20000, 19999], 2048)
+
+
+def test_topk_negative_zero_and_signs():
+    rng = np.random.default_rng(6)
+    sc = rng.standard_normal((2, 6000)).astype(np.float32)
+    sc[0, ::7] = 0.0
+    sc[0, 3::7] = -0.0
+    sc[1] = -np.abs(sc[1])
+    _expect_exact(sc, [6000, 6000], 3000)
+    _expect_exact(sc, [6000, 6000], 5999)
+
+
+def test_topk_long_row_1m():
+    rng = np.random.default_rng(7)
+    n = 1 << 20
+    sc = rng.standard_normal((1, n)).astype(np.float32) * 3 + 10
+    _expect_exact(sc, [n], 2048)
