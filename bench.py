@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA decode step (indexer + top-k + sparse MLA attention) on one MI355X.
+
+Workload (default): decode_128k, one query row over a 131072-position cache, 64 fp8 indexer heads of width
+64, top-k 2048, 128 bf16 attention heads over a 512-wide latent.  Inputs are seeded synthetic data already
+resident in HBM; the timed loop rotates through enough distinct input copies that the 256 MiB Infinity
+Cache cannot serve one step's bytes to a later step.
+
+Prints one JSON line.  `value` = query rows completed per second of wall time (torch.cuda.synchronize()
+on both sides of exactly --steps steps).  `roofline` = the indexer kernel (the dominant one) against the
+8 TB/s HBM peak: algorithmic bytes per launch over its mean launch time, from HIP events on its stream.
+`cpu_baseline` = the fp64 CPU oracle timed on this host over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "DSA decode queries/s @T=128K, k=2048 (indexer+topk+attn); % HBM roofline"
+PMC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_128k_pmc.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "common.h"):
+        with open(os.path.join(ROOT, "long_context_sparse_indexer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per indexer launch from the committed counter run, if it was taken on the current kernel."""
+    try:
+        with open(PMC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode_128k", choices=["decode_128k", "batched_paged", "decode_1m"])
+    ap.add_argument("--copies", type=int, default=0, help="distinct input copies to rotate (0 = auto)")
+    ap.add_argument("--phase-iters", type=int, default=400)
+    ap.add_argument("--graph", action="store_true", help="replay the step loop from a captured HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding design); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import long_context_sparse_indexer_amd as dsa
+    from long_context_sparse_indexer_amd import cost
+    import synth
+    from synth.device import upload
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    cfg = synth.get(args.workload)
+    t0 = time.perf_counter()
+    prob = synth.make_problem(cfg)
+    base = upload(prob, dev)
+    gen_s = time.perf_counter() - t0
+    P = dsa.make_problem(**base.fields)
+    L = dsa.make_layout(base.row_seq, base.row_len, base.page_table)
+
+    # distinct copies of every per-step input, enough to exceed the 256 MiB Infinity Cache several times
+    touched = sum(cost.decode_row_bytes(int(n), prob.k, prob.H_I, prob.d_I, prob.H, prob.d_c) for n in prob.row_len)
+    copies = args.copies or max(2, min(64, int(np.ceil(3 * 256e6 / touched))))
+    names = ["q_idx", "q_idx_scale", "head_w", "k_idx_pool", "k_idx_scale", "q", "kv_pool"]
+    sets = [{n: getattr(base, n) for n in names}]
+    for _ in range(copies - 1):
+        sets.append({n: getattr(base, n).clone() for n in names})
+    R = prob.R
+    ws = torch.empty(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_STEP), dtype=torch.uint8, device=dev)
+    idx = torch.empty((R, prob.k), dtype=torch.int32, device=dev)
+    out = torch.empty((R, prob.H, prob.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, prob.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(i):
+        s = sets[i % copies]
+        dsa.dsa_decode_step(P, L, s["q_idx"], s["q_idx_scale"], s["head_w"], s["k_idx_pool"], s["k_idx_scale"],
+                            s["q"], s["kv_pool"], idx, out, lse, ws, sptr)
+
+    graph = None
+    if args.graph:
+        # one graph walks every copy once; replays continue the rotation
+        for i in range(copies):
+            step(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                s = sets[i]
+                dsa.dsa_decode_step(P, L, s["q_idx"], s["q_idx_scale"], s["head_w"], s["k_idx_pool"],
+                                    s["k_idx_scale"], s["q"], s["kv_pool"], idx, out, lse, ws,
+                                    torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+
+    def run(n_steps, offset=0):
+        if graph is None:
+            for i in range(n_steps):
+                step(offset + i)
+        else:
+            for _ in range(n_steps // copies):
+                graph.replay()
+            for i in range(n_steps % copies):
+                step(offset + i)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run(args.steps, args.warmup)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    qps = args.steps * R / wall
+
+    # per-phase mean launch times: each phase alone, back to back over the rotated copies, HIP events on the
+    # stream the kernels run on
+    ld = ((max(prob.max_row_len, 1) + 63) // 64) * 64
+    scores = torch.empty((R, ld), dtype=torch.float32, device=dev)
+
+    def timed(fn, iters):
+        for i in range(min(iters, 20)):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters  # microseconds per launch
+
+    def ph_indexer(i):
+        s = sets[i % copies]
+        dsa.dsa_indexer_scores(P, L, s["q_idx"], s["q_idx_scale"], s["head_w"], s["k_idx_pool"], s["k_idx_scale"],
+                               scores, ld, sptr)
+
+    topk_ws = torch.empty(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_TOPK), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(256, dsa.dsa_workspace_bytes(P, dsa.DSA_OP_ATTN)), dtype=torch.uint8, device=dev)
+
+    def ph_topk(i):
+        dsa.dsa_topk(P, L, scores, idx, topk_ws, ld, sptr)
+
+    def ph_attn(i):
+        s = sets[i % copies]
+        dsa.dsa_sparse_mla_attn(P, L, s["q"], s["kv_pool"], idx, out, lse, attn_ws, sptr)
+
+    us_idx = timed(ph_indexer, args.phase_iters)
+    us_topk = timed(ph_topk, args.phase_iters)
+    us_attn = timed(ph_attn, args.phase_iters)
+
+    idx_bytes = sum(cost.indexer_row_bytes(int(n), prob.H_I, prob.d_I) for n in prob.row_len)
+    achieved = idx_bytes / (us_idx * 1e-6) / 1e9
+    traffic = measured_traffic()
+    step_bytes = touched
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-indexer/bf16-attention",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": R, "context": int(prob.max_row_len), "k": prob.k,
+                   "H_I": prob.H_I, "d_I": prob.d_I, "H": prob.H, "d_c": prob.d_c, "page_size": prob.page_size,
+                   "input_copies": copies, "graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "indexer_f8_kernel", "bytes_per_launch": idx_bytes, "us_per_launch": round(us_idx, 3)},
+        "end_to_end": {"algorithmic_bytes_per_step": step_bytes,
+                       "hbm_frac": round(step_bytes / (wall / args.steps) / (HBM_PEAK_GBS * 1e9), 4),
+                       "gpu_event_ms_per_step": round(gpu_s / args.steps * 1e3, 5)},
+        "phases_us": {"indexer": round(us_idx, 3), "topk": round(us_topk, 3), "attention": round(us_attn, 3)},
+        "gen_seconds": round(gen_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        reps, t_c = 0, time.perf_counter()
+        while True:
+            oracle.decode_step(prob)
+            reps += 1
+            el = time.perf_counter() - t_c
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {"value": round(reps * R / el, 3), "unit": "queries/s", "cores": oracle.threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{reps} full {args.workload} steps ({R} row(s) each), fp64 oracle, "
+                                            f"{el:.1f} s"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -174,7 +174,7 @@ dsa_status_t dsa_indexer_scores(const dsa_problem_t* problem, const dsa_layout_t
   if ((st = check_indexer_args(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale)) != DSA_OK) return st;
   if ((st = check_scores(g, scores, scores_ld)) != DSA_OK) return st;
   return hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, scores_ld,
-                                        static_cast<hipStream_t>(stream)),
+                                        nullptr, static_cast<hipStream_t>(stream)),
                     "indexer launch");
 }
 
@@ -222,10 +222,20 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
   int32_t* idx = reinterpret_cast<int32_t*>(ws);
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
   if (topk_idx) idx = topk_idx;
-  if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld, s),
+  // fp8 indexer: its epilogue starts the selection (digit-1 histogram), so the top-k state is zeroed first
+  const bool fuse = g.idx_dtype == DSA_F8E4M3;
+  const dsa::TopkState tstate = dsa::topk_state(g, ws);
+  if (fuse && (st = hip_status(dsa::launch_topk_zero(g, ws, s), "top-k launch")) != DSA_OK) return st;
+  if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,
+                                           fuse ? &tstate : nullptr, s),
                        "indexer launch")) != DSA_OK)
     return st;
-  if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, s), "top-k launch")) != DSA_OK) return st;
+  if (fuse) {
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, true, s), "top-k launch")) != DSA_OK)
+      return st;
+  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, s), "top-k launch")) != DSA_OK) {
+    return st;
+  }
   return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, s), "attention launch");
 }
 

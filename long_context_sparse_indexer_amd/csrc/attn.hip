@@ -82,17 +82,24 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const int slot = c0 + lane;
     const int pos = slot < end ? idx[slot] : -1;
     const int64_t prow = pos >= 0 ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
-    // gather this wave's 16 rows: lane loads 16 bytes of each
-#pragma unroll 4
+    // gather this wave's 16 rows straight into LDS (global_load_lds_dwordx4: the 64 lanes' 16-byte pieces
+    // land contiguously, one 1 KiB latent row per instruction); slots without a position get zeros
+#pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int rr = wave * 16 + t;
       const int lo = __shfl((int)(prow & 0xffffffff), rr, 64);
       const int hi = __shfl((int)(prow >> 32), rr, 64);
       const int64_t pr = ((int64_t)hi << 32) | (uint32_t)lo;
-      v4i val = {0, 0, 0, 0};
-      if (pr >= 0) val = *reinterpret_cast<const v4i*>(kv + pr * kDC + lane * 8);
-      *reinterpret_cast<v4i*>(kv_lds + rr * kRowB + lane * 16) = val;
+      char* dst = kv_lds + rr * kRowB;
+      if (pr >= 0)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(kv + pr * kDC + lane * 8),
+                                         (__attribute__((address_space(3))) void*)(
+                                             (__attribute__((address_space(3))) char*)dst),
+                                         16, 0, 0);
+      else
+        *reinterpret_cast<v4i*>(dst + lane * 16) = v4i{0, 0, 0, 0};
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
@@ -189,33 +196,43 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s.
+// Block (row*H + head, column slice): the split weights are computed once by the first wave.
+constexpr int kMaxSplit = 64;
 template <bool kBf16Out>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse, int H, int d_c,
                                                            int nsplit, void* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float wts[kMaxSplit];
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[((int64_t)r * nsplit + s) * H + h]);
-  float wsum = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ls = part_lse[((int64_t)r * nsplit + s) * H + h];
-    wsum += ls == -INFINITY ? 0.f : expf(ls - mx);
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float ls = s < nsplit ? part_lse[((int64_t)r * nsplit + s) * H + h] : -INFINITY;
+    const float mx = wave_max(ls);
+    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
+    const float wsum = wave_sum(w);
+    wts[s] = wsum > 0.f ? w / wsum : 0.f;
+    if (s == 0 && lse && blockIdx.y == 0) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
-  for (int d = threadIdx.x; d < d_c; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ls = part_lse[((int64_t)r * nsplit + s) * H + h];
-      if (ls == -INFINITY) continue;
-      acc = fmaf(expf(ls - mx), part_o[(((int64_t)r * nsplit + s) * H + h) * d_c + d], acc);
-    }
-    const float val = wsum > 0.f ? acc / wsum : 0.f;
-    if (kBf16Out)
-      static_cast<unsigned short*>(out)[((int64_t)r * H + h) * d_c + d] = float_to_bf16_bits(val);
-    else
-      static_cast<float*>(out)[((int64_t)r * H + h) * d_c + d] = val;
+  __syncthreads();
+  const int d = blockIdx.y * blockDim.x + threadIdx.x;
+  if (d >= d_c) return;
+  const float* src = part_o + ((int64_t)r * nsplit * H + h) * d_c + d;
+  const int64_t stride = (int64_t)H * d_c;
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + j], v[j], acc);
   }
-  if (threadIdx.x == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  for (; s < nsplit; ++s) acc = fmaf(wts[s], src[s * stride], acc);
+  if (kBf16Out)
+    static_cast<unsigned short*>(out)[((int64_t)r * H + h) * d_c + d] = float_to_bf16_bits(acc);
+  else
+    static_cast<float*>(out)[((int64_t)r * H + h) * d_c + d] = acc;
 }
 
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
@@ -294,7 +311,7 @@ AttnPlan plan(const Geo& g) {
   const int64_t target = 512;  // about two blocks per CU
   if (blocks < target) {
     int want = (int)((target + blocks - 1) / blocks);
-    want = std::min(want, chunks);
+    want = std::min(std::min(want, chunks), kMaxSplit);
     const int per = (chunks + want - 1) / want;  // chunks per split
     p.nsplit = (chunks + per - 1) / per;
     p.split_len = per * kNC;
@@ -331,7 +348,8 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
                                                           g.S, g.max_pages, g.num_pages, g.log2ps, g.H, p.nsplit,
                                                           p.split_len, scale_log2, nullptr, nullptr, part_o, part_lse);
-      attn_combine_kernel<true><<<g.R * g.H, 128, 0, stream>>>(part_o, part_lse, g.H, g.d_c, p.nsplit, out, lse);
+      attn_combine_kernel<true><<<dim3(g.R * g.H, (g.d_c + 255) / 256), 256, 0, stream>>>(part_o, part_lse, g.H, g.d_c,
+                                                                                       p.nsplit, out, lse);
     }
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;

@@ -16,8 +16,13 @@
 //
 // Every key row is read once, as 32-byte pieces: one wave covers 32 consecutive positions = 2 KiB of
 // contiguous pool memory (a 32-aligned run never crosses a page of >= 32 positions).
+//
+// In the fused step the epilogue also starts the top-k selection: each block histograms the first 12 bits
+// of its scores' order-preserving keys in LDS and merges the non-empty bins into the row's histogram; the
+// block that finishes a row last finds the threshold bin (see topk.hip).
 #include "common.h"
 #include "launch.h"
+#include "topk_common.h"
 
 namespace dsa {
 namespace {
@@ -25,17 +30,26 @@ namespace {
 constexpr int kIdxSub = 4;                          // 32-position subtiles per wave
 constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread block
 
-template <int HB>  // number of 32-head blocks: H_I = 32 * HB
+template <int HB, bool kHist>  // HB = number of 32-head blocks (H_I = 32 * HB); kHist = fused top-k histogram
 __global__ __launch_bounds__(256) void indexer_f8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
-    int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld) {
+    int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, int k,
+    uint32_t* __restrict__ hist1, uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr) {
   constexpr int H_I = 32 * HB;
+  __shared__ uint32_t h[kHist ? kTopkBins : 1];
+  __shared__ uint32_t scan[256 / 64 + 1];
+  __shared__ int flag;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int64_t tile0 = (int64_t)blockIdx.x * kIdxTile;
   if (tile0 >= n) return;
+  const bool do_hist = kHist && k < n;  // uniform over the block; a row with k >= n keeps every position
+  if (do_hist) {
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) h[i] = 0u;
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
@@ -79,7 +93,16 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     }
     part += __shfl_xor(part, 32, 64);
     const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
-    if (half == 0 && pos < n) scores[(int64_t)r * ld + pos] = sk[s] * part;
+    if (half == 0 && pos < n) {
+      const float v = sk[s] * part;
+      scores[(int64_t)r * ld + pos] = v;
+      if (do_hist) atomicAdd(&h[order_key(v) >> 20], 1u);
+    }
+  }
+  if (do_hist) {
+    __syncthreads();
+    hist_merge_and_threshold<256>(h, hist1 + (int64_t)r * kTopkBins, &cnt[4 * r + 0], (n + kIdxTile - 1) / kIdxTile,
+                             (uint32_t)k, 0u, &thr[4 * r + 0], &thr[4 * r + 1], scan, &flag);
   }
 }
 
@@ -113,22 +136,31 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 }  // namespace
 
+template <int HB, bool kHist>
+void launch_f8(const Geo& g, dim3 grid, const uint8_t* qp, const float* q_idx_scale, const float* head_w,
+               const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse,
+               hipStream_t stream) {
+  indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
+      qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
+      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->cnt : nullptr,
+      fuse ? fuse->thr : nullptr);
+}
+
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
-                          hipStream_t stream) {
+                          const TopkState* fuse, hipStream_t stream) {
   if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
   if (g.idx_dtype == 2 /* F8E4M3 */) {
     dim3 grid((g.max_row_len + kIdxTile - 1) / kIdxTile, g.R);
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
-    if (g.H_I == 64)
-      indexer_f8_kernel<2><<<grid, 256, 0, stream>>>(qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len,
-                                                     g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps,
-                                                     g.max_row_len, scores, ld);
-    else
-      indexer_f8_kernel<1><<<grid, 256, 0, stream>>>(qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len,
-                                                     g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps,
-                                                     g.max_row_len, scores, ld);
+    if (g.H_I == 64) {
+      if (fuse) launch_f8<2, true>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      else launch_f8<2, false>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    } else {
+      if (fuse) launch_f8<1, true>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      else launch_f8<1, false>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    }
   } else {
     dim3 grid((g.max_row_len + 255) / 256, g.R);
     size_t lds = sizeof(float) * (size_t)(g.H_I * g.d_I + g.H_I);

@@ -21,15 +21,28 @@ struct Geo {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// indexer.hip
+// Digit-1 radix-select state the indexer can fill in its epilogue (see topk.hip).
+struct TopkState {
+  uint32_t* hist1;
+  uint32_t* cnt;
+  uint32_t* thr;
+};
+
+// indexer.hip.  With `fuse` non-NULL the indexer also builds the top-k digit-1 histogram and threshold; the
+// state must have been zeroed (launch_topk_zero) earlier on the stream.
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
-                          hipStream_t stream);
+                          const TopkState* fuse, hipStream_t stream);
 
 // topk.hip
 constexpr int kTopkMaxBlocksPerRow = 1024;
 constexpr int kTopkChunk = 4096;
 size_t topk_workspace_bytes(const Geo& g);
+TopkState topk_state(const Geo& g, void* workspace);
+hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream);
+// hist_done: the digit-1 histogram and threshold were already produced (by the indexer)
+hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
+                              bool hist_done, hipStream_t stream);
 hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
                        hipStream_t stream);
 

@@ -31,6 +31,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_oracle_e4m3_value.restype = D
         L.dsa_oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.dsa_oracle_bf16_value.restype = D
+        L.dsa_oracle_threads.argtypes = []
+        L.dsa_oracle_threads.restype = ctypes.c_int
         L.dsa_oracle_decode.argtypes = [P, I32, I64, P]
         L.dsa_oracle_decode.restype = None
         L.dsa_oracle_indexer_scores.argtypes = [I32, I32, I32, I32, P, P, P, P, P, P, P, P, I32, I32, P, I64]
@@ -49,6 +51,11 @@ def _p(a):
 
 def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(lib().dsa_oracle_threads())
 
 
 def decode(codes: np.ndarray, dtype: str) -> np.ndarray:

@@ -30,11 +30,15 @@
  *   (the selected positions are "an address list into the paged KV cache", "How Does the Selector Pick").
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F8E4M3 = 2 };
+
+/* Threads an OpenMP parallel region of this library uses (reported beside its timings). */
+int dsa_oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---- 1. element decoding ------------------------------------------------------------------------- */
 
