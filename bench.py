@@ -56,7 +56,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_128k", choices=["decode_128k", "batched_paged", "decode_1m"])
     ap.add_argument("--copies", type=int, default=0, help="distinct input copies to rotate (0 = auto)")
     ap.add_argument("--phase-iters", type=int, default=400)
-    ap.add_argument("--graph", action="store_true", help="replay the step loop from a captured HIP graph")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=True,
+                    help="replay the step loop from a captured HIP graph (default)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch every step from the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -84,6 +84,9 @@ dsa_status_t check_problem(const dsa_problem_t* p, const dsa_layout_t* lay, bool
                 p->latent_dim);
       DSA_CHECK(p->attn_heads % 16 == 0, DSA_EUNSUPPORTED, "bf16 attention needs attn_heads %% 16 == 0 (got %d)",
                 p->attn_heads);
+      DSA_CHECK((int64_t)p->num_pages * p->page_size < ((int64_t)1 << 31), DSA_EUNSUPPORTED,
+                "bf16 attention addresses latent rows with 31 bits (num_pages * page_size = %lld)",
+                (long long)p->num_pages * p->page_size);
     } else {
       DSA_CHECK(p->latent_dim >= 1 && p->latent_dim <= 1024, DSA_EUNSUPPORTED, "fp32 attention: latent_dim = %d",
                 p->latent_dim);

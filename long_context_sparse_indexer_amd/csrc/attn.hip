@@ -25,6 +25,8 @@ constexpr int kDC = 512;                 // latent width of the bf16 path
 constexpr int kRowB = kDC * 2 + 16;      // LDS row stride (bytes)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplitLen = 4096;       // selection slots one block handles
+constexpr int kChunksPerSplitSmallBatch = 1;  // gathers spread over as many CUs as possible
 
 typedef __attribute__((address_space(3))) v4bf lds_v4bf;
 
@@ -42,14 +44,53 @@ __device__ __forceinline__ v8bf pack8(const float (&p)[8]) {
   return r;
 }
 
+// Gathers the 16 latent rows of this wave for chunk c straight into LDS: global_load_lds_dwordx4 lands the 64
+// lanes' 16-byte pieces contiguously at the LDS address in M0, one 1 KiB row per instruction.  Every wave
+// issues exactly 16 such loads per chunk (a slot without a position reads `dummy`, a selected row of the split,
+// and is masked later), so "this chunk has arrived" is a fixed vmcnt once the next chunk has been issued.
+// The loads are written as asm so that the compiler's wait insertion, which cannot tell which LDS buffer a
+// pending DMA targets across the chunk loop, does not add a full vmcnt(0) before every LDS read; the waits
+// on them are explicit (kWaitVm16 / s_waitcnt 0).  No output register is involved: the data goes to LDS and
+// the address operands are read when the instruction issues.
+__device__ __forceinline__ void gather_chunk(const unsigned short* __restrict__ kv, const int32_t* prow, int dummy,
+                                             char* buf, int wave, int lane) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int rr = wave * 16 + t;
+    int pr = prow[rr];
+    if (pr < 0) pr = dummy;
+    const unsigned short* src = kv + (int64_t)pr * kDC + lane * 8;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(buf + rr * kRowB)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int kWaitVm16 = (16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8);  // vmcnt <= 16 only
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
+
+// Workgroup barrier for data this wave wrote with ds_* instructions.  Unlike __syncthreads() it does not wait
+// for vector-memory operations, so the next chunk's LDS-DMA gather stays in flight across it; the empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <bool kSplit>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
     int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int split_len, float scale_log2, unsigned short* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char kv_lds[kNC * kRowB];
+  __shared__ __attribute__((aligned(16))) char kv_lds0[kNC * kRowB];
+  __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowB];
   __shared__ __attribute__((aligned(16))) float s_lds[kHG][kNC + 4];
+  __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
+  __shared__ int first_valid;
 
   const int ngroups = H / kHG;
   const int split = blockIdx.x % nsplit;
@@ -75,98 +116,106 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   const int seq = clamp_seq(row_seq[r], num_seqs);
   const int begin = split * split_len;
   const int end = min(k, begin + split_len);
-  const int32_t* idx = topk_idx + (int64_t)r * k;
+  const int len = max(end - begin, 0);
+  const int nch = (len + kNC - 1) / kNC;
+  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
 
-  for (int c0 = begin; c0 < end; c0 += kNC) {
-    // slot c0 + lane -> physical row (every wave computes all 64)
-    const int slot = c0 + lane;
-    const int pos = slot < end ? idx[slot] : -1;
-    const int64_t prow = pos >= 0 ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
-    // gather this wave's 16 rows straight into LDS (global_load_lds_dwordx4: the 64 lanes' 16-byte pieces
-    // land contiguously, one 1 KiB latent row per instruction); slots without a position get zeros
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int rr = wave * 16 + t;
-      const int lo = __shfl((int)(prow & 0xffffffff), rr, 64);
-      const int hi = __shfl((int)(prow >> 32), rr, 64);
-      const int64_t pr = ((int64_t)hi << 32) | (uint32_t)lo;
-      char* dst = kv_lds + rr * kRowB;
-      if (pr >= 0)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(kv + pr * kDC + lane * 8),
-                                         (__attribute__((address_space(3))) void*)(
-                                             (__attribute__((address_space(3))) char*)dst),
-                                         16, 0, 0);
-      else
-        *reinterpret_cast<v4i*>(dst + lane * 16) = v4i{0, 0, 0, 0};
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
-    v4f sacc = {0.f, 0.f, 0.f, 0.f};
-    {
-      const char* brow = kv_lds + (wave * 16 + i) * kRowB + g * 16;
-#pragma unroll
-      for (int kd = 0; kd < kDC / 32; ++kd) {
-        const v8bf b = *reinterpret_cast<const v8bf*>(brow + kd * 64);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kd], b, sacc, 0, 0, 0);
+  // every slot of the split -> physical row before any gather (so gathers are the only loads in flight)
+  if (threadIdx.x == 0) first_valid = 0x7fffffff;
+  __syncthreads();
+  for (int s = threadIdx.x; s < nch * kNC; s += blockDim.x) {
+    const int pos = s < len ? idx[s] : -1;
+    const int pr = pos >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
+    prow_lds[s] = pr;
+    if (pr >= 0) atomicMin(&first_valid, s);
+  }
+  __syncthreads();
+  // a split with no selected row contributes nothing; otherwise slots without a position read a selected row
+  // of this split instead (their logits are -inf, so they carry zero weight)
+  if (first_valid != 0x7fffffff) {
+    const int dummy = prow_lds[first_valid];
+    // one chunk: wait for its rows (the next chunk's gather stays in flight), then QK^T, softmax, PV.
+    // `cur` and `nxt` are fixed per call site, so the compiler can tell the DMA target from the buffer read.
+    auto chunk = [&](const int c, const char* cur, char* nxt) __attribute__((always_inline)) {
+      if (c + 1 < nch) {
+        gather_chunk(kv, prow_lds + (c + 1) * kNC, dummy, nxt, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitVm16);  // chunk c has landed; chunk c+1 stays in flight
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
       }
-    }
-    const int my_pos = __shfl(pos, wave * 16 + i, 64);
+      lds_barrier();
+      // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
+      v4f sacc = {0.f, 0.f, 0.f, 0.f};
+      {
+        const char* brow = cur + (wave * 16 + i) * kRowB + g * 16;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s_lds[g * 4 + v][wave * 16 + i] = my_pos >= 0 ? sacc[v] * scale_log2 : -INFINITY;
-    __syncthreads();
-
-    // online softmax for head i over slots kk*32 + 8g + (0..7), kk = 0, 1
-    float sv[16];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const v4f x0 = *reinterpret_cast<const v4f*>(&s_lds[i][kk * 32 + 8 * g]);
-      const v4f x1 = *reinterpret_cast<const v4f*>(&s_lds[i][kk * 32 + 8 * g + 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { sv[kk * 8 + e] = x0[e]; sv[kk * 8 + 4 + e] = x1[e]; }
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { sv[e] = exp2f(sv[e] - m_use); rs += sv[e]; }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    l = l * alpha + rs;
-    m = m_new;
-
-    // rescale O rows (head g*4 + v) by that head's alpha, held by lane g*4 + v
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float av = __shfl(alpha, g * 4 + v, 64);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][v] *= av;
-    }
-
-    // O += P V.  A operand element e of K-step kk is slot kk*32 + 8g + perm[e], perm = {0,2,4,6,1,3,5,7}.
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const float pe[8] = {sv[kk * 8 + 0], sv[kk * 8 + 2], sv[kk * 8 + 4], sv[kk * 8 + 6],
-                           sv[kk * 8 + 1], sv[kk * 8 + 3], sv[kk * 8 + 5], sv[kk * 8 + 7]};
-      const v8bf pa = pack8(pe);
-      const int row1 = kk * 32 + 8 * g + 2 * (i >> 2);
-      const char* p1 = kv_lds + row1 * kRowB + (wave * 128 + 4 * (i & 3)) * 2;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const v4bf lo4 = lds_tr_read(p1 + dt * 32);
-        const v4bf hi4 = lds_tr_read(p1 + kRowB + dt * 32);
-        const v8bf b = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[dt], 0, 0, 0);
+        for (int kd = 0; kd < kDC / 32; ++kd) {
+          const v8bf b = *reinterpret_cast<const v8bf*>(brow + kd * 64);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kd], b, sacc, 0, 0, 0);
+        }
       }
+      const bool valid = prow_lds[c * kNC + wave * 16 + i] >= 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_lds[g * 4 + v][wave * 16 + i] = valid ? sacc[v] * scale_log2 : -INFINITY;
+      lds_barrier();
+
+      // online softmax for head i over slots kk*32 + 8g + (0..7), kk = 0, 1
+      float sv[16];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const v4f x0 = *reinterpret_cast<const v4f*>(&s_lds[i][kk * 32 + 8 * g]);
+        const v4f x1 = *reinterpret_cast<const v4f*>(&s_lds[i][kk * 32 + 8 * g + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { sv[kk * 8 + e] = x0[e]; sv[kk * 8 + 4 + e] = x1[e]; }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { sv[e] = exp2f(sv[e] - m_use); rs += sv[e]; }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l = l * alpha + rs;
+      m = m_new;
+
+      // rescale O rows (head g*4 + v) by that head's alpha, held by lane g*4 + v
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, g * 4 + v, 64);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt][v] *= av;
+      }
+
+      // O += P V.  A operand element e of K-step kk is slot kk*32 + 8g + perm[e], perm = {0,2,4,6,1,3,5,7}.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const float pe[8] = {sv[kk * 8 + 0], sv[kk * 8 + 2], sv[kk * 8 + 4], sv[kk * 8 + 6],
+                             sv[kk * 8 + 1], sv[kk * 8 + 3], sv[kk * 8 + 5], sv[kk * 8 + 7]};
+        const v8bf pa = pack8(pe);
+        const int row1 = kk * 32 + 8 * g + 2 * (i >> 2);
+        const char* p1 = cur + row1 * kRowB + (wave * 128 + 4 * (i & 3)) * 2;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4bf lo4 = lds_tr_read(p1 + dt * 32);
+          const v4bf hi4 = lds_tr_read(p1 + kRowB + dt * 32);
+          const v8bf b = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[dt], 0, 0, 0);
+        }
+      }
+      lds_barrier();  // every wave is done with `cur` and s_lds before they are overwritten
+    };
+    __builtin_amdgcn_s_waitcnt(0);  // Q operands and slot rows are in; from here the gathers are the only loads
+    gather_chunk(kv, prow_lds, dummy, kv_lds0, wave, lane);
+    for (int c = 0; c < nch; c += 2) {
+      chunk(c, kv_lds0, kv_lds1);
+      if (c + 1 < nch) chunk(c + 1, kv_lds1, kv_lds0);
     }
-    __syncthreads();
   }
 
   // finish: O rows are heads g*4 + v, columns wave*128 + dt*16 + i
@@ -304,18 +353,21 @@ struct AttnPlan {
 };
 
 AttnPlan plan(const Geo& g) {
-  AttnPlan p{1, ((g.k + kNC - 1) / kNC) * kNC};
+  const int chunks = std::max(1, (g.k + kNC - 1) / kNC);
+  AttnPlan p{1, chunks * kNC};
   if (g.kv_dtype != 1 /* BF16 */) return p;
-  const int chunks = (g.k + kNC - 1) / kNC;
-  const int64_t blocks = (int64_t)g.R * (g.H / kHG);
-  const int64_t target = 512;  // about two blocks per CU
-  if (blocks < target) {
-    int want = (int)((target + blocks - 1) / blocks);
-    want = std::min(std::min(want, chunks), kMaxSplit);
-    const int per = (chunks + want - 1) / want;  // chunks per split
-    p.nsplit = (chunks + per - 1) / per;
-    p.split_len = per * kNC;
+  // a block handles at most kMaxSplitLen slots; below ~2 blocks per CU the selection is split further into
+  // pieces of about kChunksPerSplitSmallBatch chunks (double buffering needs a few), at most kMaxSplit of them
+  const int64_t groups = (int64_t)g.R * (g.H / kHG);
+  int per = std::min(chunks, kMaxSplitLen / kNC);
+  if (groups * ((chunks + per - 1) / per) < 256) per = std::min(per, kChunksPerSplitSmallBatch);
+  int nsplit = (chunks + per - 1) / per;
+  if (nsplit > kMaxSplit) {
+    per = (chunks + kMaxSplit - 1) / kMaxSplit;
+    nsplit = (chunks + per - 1) / per;
   }
+  p.nsplit = nsplit;
+  p.split_len = per * kNC;
   return p;
 }
 

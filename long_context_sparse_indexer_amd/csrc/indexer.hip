@@ -18,8 +18,8 @@
 // contiguous pool memory (a 32-aligned run never crosses a page of >= 32 positions).
 //
 // In the fused step the epilogue also starts the top-k selection: each block histograms the first 12 bits
-// of its scores' order-preserving keys in LDS and merges the non-empty bins into the row's histogram; the
-// block that finishes a row last finds the threshold bin (see topk.hip).
+// of its scores' order-preserving keys in LDS and merges the non-empty bins into the row's histogram (see
+// topk.hip).  The key loads are issued before the query operands so that both are in flight together.
 #include "common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -36,11 +36,9 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, int k,
-    uint32_t* __restrict__ hist1, uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr) {
+    uint32_t* __restrict__ hist1) {
   constexpr int H_I = 32 * HB;
   __shared__ uint32_t h[kHist ? kTopkBins : 1];
-  __shared__ uint32_t scan[256 / 64 + 1];
-  __shared__ int flag;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int64_t tile0 = (int64_t)blockIdx.x * kIdxTile;
@@ -54,6 +52,25 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
 
+  int64_t prow[kIdxSub];
+#pragma unroll
+  for (int s = 0; s < kIdxSub; ++s) {
+    const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
+    prow[s] = pos < n ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
+  }
+  v8i b[kIdxSub];
+  float sk[kIdxSub];
+#pragma unroll
+  for (int s = 0; s < kIdxSub; ++s) {
+    if (prow[s] >= 0) {
+      b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
+      sk[s] = k_scale[prow[s]];
+    } else {
+      b[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      sk[s] = 0.f;
+    }
+  }
+
   v8i a[HB];
   float wq[HB][16];
 #pragma unroll
@@ -63,21 +80,6 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     for (int i = 0; i < 16; ++i) {
       const int head = hb * 32 + half * 4 + (i & 3) + 8 * (i >> 2);
       wq[hb][i] = head_w[(int64_t)r * H_I + head] * q_scale[(int64_t)r * H_I + head];
-    }
-  }
-
-  v8i b[kIdxSub];
-  float sk[kIdxSub];
-#pragma unroll
-  for (int s = 0; s < kIdxSub; ++s) {
-    const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
-    if (pos < n) {
-      const int64_t p = phys_row(page_table, max_pages, num_pages, log2ps, seq, pos);
-      b[s] = *reinterpret_cast<const v8i*>(k_pool + p * 64 + half * 32);
-      sk[s] = k_scale[p];
-    } else {
-      b[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      sk[s] = 0.f;
     }
   }
 
@@ -101,8 +103,7 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
   }
   if (do_hist) {
     __syncthreads();
-    hist_merge_and_threshold<256>(h, hist1 + (int64_t)r * kTopkBins, &cnt[4 * r + 0], (n + kIdxTile - 1) / kIdxTile,
-                             (uint32_t)k, 0u, &thr[4 * r + 0], &thr[4 * r + 1], scan, &flag);
+    hist_merge<256>(h, hist1 + ((int64_t)r * kHistCopies + blockIdx.x % kHistCopies) * kTopkBins);
   }
 }
 
@@ -142,8 +143,7 @@ void launch_f8(const Geo& g, dim3 grid, const uint8_t* qp, const float* q_idx_sc
                hipStream_t stream) {
   indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->cnt : nullptr,
-      fuse ? fuse->thr : nullptr);
+      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr);
 }
 
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,

@@ -24,12 +24,10 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Digit-1 radix-select state the indexer can fill in its epilogue (see topk.hip).
 struct TopkState {
   uint32_t* hist1;
-  uint32_t* cnt;
-  uint32_t* thr;
 };
 
-// indexer.hip.  With `fuse` non-NULL the indexer also builds the top-k digit-1 histogram and threshold; the
-// state must have been zeroed (launch_topk_zero) earlier on the stream.
+// indexer.hip.  With `fuse` non-NULL the indexer also builds the top-k digit-1 histogram; the state must have
+// been zeroed (launch_topk_zero) earlier on the stream.
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
                           const TopkState* fuse, hipStream_t stream);

@@ -4,23 +4,21 @@
 // is written in increasing position order, padded with -1.
 //
 // Scores become order-preserving 32-bit keys, selected by a radix select over three digits
-// (bits 31..20, 19..8, 7..0):
+// (bits 31..20, 19..8, 7..0).  Every hand-over between blocks happens at a kernel boundary:
 //   digit 1  a per-row histogram of the first digit, accumulated in LDS per block and merged with one global
 //            atomic per non-empty bin -- in the indexer's epilogue (fused step) or in a histogram pass over
-//            stored scores (standalone call); the last block of a row finds the bin b1 holding the k_eff-th
-//            largest key and the count A1 of keys above it.
-//   filter   grid (4096-score chunks, rows): keys with digit 1 >= b1 go, in position order, into a segment of
-//            the row's candidate list; keys inside bin b1 also feed a histogram of digit 2, whose last block
-//            finds b2 and the count A2 of keys above (b1, b2).
-//   resolve  one block per row: loads the candidates (k + one bin's worth) into LDS in position order,
-//            settles digit 3 among the few keys left in (b1, b2), and writes the selection in position order
-//            with a two-pass wave-ballot compaction.  A row whose candidates overflow the LDS list (heavily
-//            tied scores) is resolved over the whole stored score row instead.
+//            stored scores (standalone call).
+//   filter   grid (4096-score chunks, rows): every block finds the threshold bin b1 (the bin holding the
+//            k_eff-th largest key) from the row histogram, writes the keys with digit 1 >= b1 in position
+//            order into a segment of the row's candidate list, and histograms digit 2 of the keys in bin b1.
+//   resolve  one 1024-thread block per row: finds b2 from the digit-2 histogram, places the candidates
+//            (k + one bin's worth) in position order in LDS, settles digit 3 among the few keys of (b1, b2),
+//            and writes the selection with a two-pass wave-ballot compaction.  A row whose candidates overflow
+//            the list (heavily tied scores) is resolved over its whole stored score row instead.
 #include "common.h"
 #include "launch.h"
 #include "topk_common.h"
 
-#include <type_traits>
 
 namespace dsa {
 namespace {
@@ -28,17 +26,14 @@ namespace {
 constexpr int kCh = kTopkChunk;    // scores per filter / histogram block
 constexpr int kTpb = 1024;         // threads of histogram / filter blocks
 constexpr int kEpt = kCh / kTpb;   // scores per thread (consecutive)
-constexpr int kRes = 512;          // threads of the resolve block
-constexpr int kResWaves = kRes / 64;
 constexpr int kCap = 12288;        // candidate entries a row keeps for the resolve step
-constexpr int kTopkFusedResolveRows = 64;
 
 Ws carve(const Geo& g, void* base) {
   Ws w;
   char* p = static_cast<char*>(base);
   w.nblk = std::max(1, (g.max_row_len + kCh - 1) / kCh);
   auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes); return q; };
-  w.hist1 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
+  w.hist1 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kHistCopies * kTopkBins));
   w.hist2 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
   w.cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.thr = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
@@ -48,14 +43,15 @@ Ws carve(const Geo& g, void* base) {
   return w;
 }
 
-// Zeroes both histograms and the counters of every row (one block per row).
+// Zeroes the histograms and the counters of every row (one block per row).
 __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2,
                                                         uint32_t* __restrict__ cnt) {
   const int r = blockIdx.x;
   const v4i z = {0, 0, 0, 0};
-  v4i* h1 = reinterpret_cast<v4i*>(hist1 + (int64_t)r * kTopkBins);
+  v4i* h1 = reinterpret_cast<v4i*>(hist1 + (int64_t)r * kHistCopies * kTopkBins);
   v4i* h2 = reinterpret_cast<v4i*>(hist2 + (int64_t)r * kTopkBins);
-  for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) { h1[i] = z; h2[i] = z; }
+  for (int i = threadIdx.x; i < kHistCopies * kTopkBins / 4; i += blockDim.x) h1[i] = z;
+  for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h2[i] = z;
   if (threadIdx.x == 0) reinterpret_cast<v4i*>(cnt)[r] = z;
 }
 
@@ -81,16 +77,12 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
 // First-digit histogram of stored scores (standalone top-k): one block per 4096-score chunk.
 __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                          const int32_t* __restrict__ row_len, int max_row_len, int k,
-                                                         uint32_t* __restrict__ hist1, uint32_t* __restrict__ cnt,
-                                                         uint32_t* __restrict__ thr) {
+                                                         uint32_t* __restrict__ hist1) {
   __shared__ uint32_t h[kTopkBins];
-  __shared__ uint32_t scan[kTpb / 64 + 1];
-  __shared__ int flag;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
-  const int keff = min(k, n);
   const int nblk = (n + kCh - 1) / kCh;
-  if (keff >= n || (int)blockIdx.x >= nblk) return;  // nothing to choose, or a chunk past the row's end
+  if (min(k, n) >= n || (int)blockIdx.x >= nblk) return;  // nothing to choose, or a chunk past the row's end
   for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h[i] = 0u;
   __syncthreads();
   uint32_t key[kEpt];
@@ -100,22 +92,7 @@ __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict
   for (int e = 0; e < kEpt; ++e)
     if (valid[e]) atomicAdd(&h[key[e] >> 20], 1u);
   __syncthreads();
-  hist_merge_and_threshold<kTpb>(h, hist1 + (int64_t)r * kTopkBins, &cnt[4 * r + 0], nblk, (uint32_t)keff, 0u,
-                           &thr[4 * r + 0], &thr[4 * r + 1], scan, &flag);
-}
-
-// Device-coherent accesses for data one block hands to another within a kernel (no cache flush needed).
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  hist_merge<kTpb>(h, hist1 + ((int64_t)r * kHistCopies + blockIdx.x % kHistCopies) * kTopkBins);
 }
 
 // Candidate access for the resolve step: entries of the LDS list, or every position of the stored row.
@@ -228,114 +205,61 @@ struct ResolveLds {
   uint32_t scan[1024 / 64 + 1];  // one word per wave of the largest block, plus the total
 };
 
-// Final selection of row r by one block of NT threads: b1 / b2 are the digit-1 / digit-2 threshold bins,
-// A2 the number of keys above (b1, b2), len the row's candidate count.  The candidate data must be visible
-// to ordinary loads (written by an earlier kernel, or acquired after the row's completion counter).
-template <int NT>
-__device__ void resolve_row(int r, int n, int keff, int k, const float* __restrict__ row, uint32_t b1, uint32_t b2,
-                            uint32_t A2, uint32_t len, const uint32_t* seg_cnt, const uint32_t* seg_off,
-                            const uint64_t* cand, int nblk_max, int32_t* __restrict__ out, ResolveLds& S) {
-  if (len <= (uint32_t)kCap) {
-    const int nblk = (n + kCh - 1) / kCh;
-    {  // segment starts in chunk (= position) order; thread t owns chunks [t*CPT, (t+1)*CPT)
-      constexpr int CPT = (kTopkMaxBlocksPerRow + NT - 1) / NT;
-      const int c0 = threadIdx.x * CPT;
-      uint32_t cc[CPT];
-      uint32_t sum = 0;
+// Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of COPIES
+// consecutive 4096-bin replicas, top bin first), and the number of keys in bins above b.  Called by all NT
+// threads; the result lands in *b, *above.
+template <int NT, int COPIES>
+__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, uint32_t need, uint32_t* scan,
+                                              uint32_t* b, uint32_t* above_out) {
+  constexpr int kPer = kTopkBins / NT;
+  const int grp = NT - 1 - threadIdx.x;  // thread 0 owns the top bins
+  uint32_t c[kPer];
+  uint32_t local = 0;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int b = c0 + j;
-        cc[j] = 0;
-        if (b < nblk) {
-          cc[j] = seg_cnt[(int64_t)r * nblk_max + b];
-          S.seg_src[b] = seg_off[(int64_t)r * nblk_max + b];
-        }
-        sum += cc[j];
-      }
-      uint32_t total;
-      uint32_t start = block_exclusive_scan(sum, S.scan, total);
+  for (int j = 0; j < kPer; ++j) c[j] = 0u;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        if (c0 + j < nblk) S.seg_start[c0 + j] = start;
-        start += cc[j];
+  for (int cp = 0; cp < COPIES; ++cp)
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c[j] += gh[cp * kTopkBins + grp * kPer + j];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) local += c[j];
+  uint32_t total;
+  uint32_t above = block_exclusive_scan(local, scan, total);
+  if (above < need && above + local >= need) {
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (above + c[j] >= need) {
+        *b = (uint32_t)(grp * kPer + j);
+        *above_out = above;
+        break;
       }
-      if (threadIdx.x == 0) S.seg_start[nblk] = total;
-      __syncthreads();
+      above += c[j];
     }
-    // copy the segments into the LDS list: list entry i lives in the last segment starting at or before i;
-    // each thread issues 8 independent loads before it stores any, so the copy costs a few round trips
-    constexpr int kBatch = 8;
-    for (int base = 0; base < (int)len; base += NT * kBatch) {
-      uint64_t e[kBatch];
-      int dst[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * NT + threadIdx.x;
-        dst[j] = -1;
-        if (i < (int)len) {
-          int lo = 0, hi = nblk - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (S.seg_start[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
-          }
-          dst[j] = i;
-          e[j] = cand[(int64_t)r * kCap + S.seg_src[lo] + (i - S.seg_start[lo])];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (dst[j] >= 0) {
-          S.key[dst[j]] = (uint32_t)e[j];
-          S.pos[dst[j]] = (int32_t)(e[j] >> 32);
-        }
-      }
-    }
-    __syncthreads();
-    uint32_t need = (uint32_t)keff - A2;  // keys of (b1, b2) still to take
-    const LdsList L{S.key, S.pos};
-    const uint32_t d3 = refine_digit<NT>(L, (int)len, (b1 << 12) | b2, 0, 8, need, S.h, S.scan);
-    write_selection<NT>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out);
-  } else {
-    const RowList L{row};
-    uint32_t need = (uint32_t)keff;
-    const uint32_t d1 = refine_digit<NT>(L, n, 0u, 20, 12, need, S.h, S.scan);
-    const uint32_t d2 = refine_digit<NT>(L, n, d1, 8, 12, need, S.h, S.scan);
-    const uint32_t d3 = refine_digit<NT>(L, n, (d1 << 12) | d2, 0, 8, need, S.h, S.scan);
-    write_selection<NT>(L, n, (d1 << 20) | (d2 << 8) | d3, need, keff, out);
   }
-  for (int i = keff + threadIdx.x; i < k; i += NT) out[i] = -1;
+  __syncthreads();
 }
 
-// kFused: the block that completes a row also resolves it (small batches); otherwise a resolve kernel follows.
-template <bool kFused>
 __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
                                                            const int32_t* __restrict__ row_len, int max_row_len,
-                                                           int k, uint32_t* __restrict__ thr,
+                                                           int k, const uint32_t* __restrict__ hist1,
                                                            uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
-                                                           uint32_t* __restrict__ seg_cnt,
+                                                           uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
-                                                           int nblk_max, int32_t* __restrict__ topk_idx) {
+                                                           int nblk_max) {
   __shared__ uint32_t scan[kTpb / 64 + 1];
-  __shared__ uint32_t seg_base, s_b2, s_A2;
-  __shared__ int flag;
-  __shared__ typename std::conditional<kFused, ResolveLds, int>::type R;
+  __shared__ uint32_t seg_base, s_b1, s_A1;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
   const int nblk = (n + kCh - 1) / kCh;
-  if (keff >= n || (int)blockIdx.x >= nblk) {
-    if (kFused && blockIdx.x == 0) {  // nothing to choose: the row keeps every position
-      int32_t* out = topk_idx + (int64_t)r * k;
-      for (int i = threadIdx.x; i < k; i += kTpb) out[i] = i < n ? i : -1;
-    }
-    return;
-  }
-  const uint32_t b1 = thr[4 * r + 0], A1 = thr[4 * r + 1];
+  if (keff >= n || (int)blockIdx.x >= nblk) return;
   const int64_t first = (int64_t)blockIdx.x * kCh + threadIdx.x * kEpt;
   uint32_t key[kEpt];
   bool valid[kEpt];
-  const float* row = scores + (int64_t)r * ld;
-  load_keys(row, first, n, key, valid);
+  load_keys(scores + (int64_t)r * ld, first, n, key, valid);
+  // every block finds b1 itself (a 16 KiB read) instead of waiting for one block to publish it
+  threshold_bin<kTpb, kHistCopies>(hist1 + (int64_t)r * kHistCopies * kTopkBins, (uint32_t)keff, scan, &s_b1, &s_A1);
+  const uint32_t b1 = s_b1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
   uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
   uint32_t c = 0;
 #pragma unroll
@@ -350,45 +274,88 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const uint32_t off = block_exclusive_scan(c, scan, total);
   if (threadIdx.x == 0) {
     seg_base = atomicAdd(&cnt[4 * r + 2], total);
-    st_dev(&seg_cnt[(int64_t)r * nblk_max + blockIdx.x], total);
-    st_dev(&seg_off[(int64_t)r * nblk_max + blockIdx.x], seg_base);
+    seg_cnt[(int64_t)r * nblk_max + blockIdx.x] = total;
+    seg_off[(int64_t)r * nblk_max + blockIdx.x] = seg_base;
   }
   __syncthreads();
-  if (seg_base + total <= (uint32_t)kCap) {  // on overflow the resolve step rescans the row
+  if (seg_base + total <= (uint32_t)kCap) {  // on overflow the resolve kernel rescans the row
     uint64_t* dst = cand + (int64_t)r * kCap + seg_base + off;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e)
-      if (valid[e] && (key[e] >> 20) >= b1) st_dev(dst++, ((uint64_t)(first + e) << 32) | key[e]);
-  }
-  // second digit: the last chunk of the row finds b2 among keys of bin b1 (need = k_eff - A1 of them)
-  if (!hist_threshold_last<kTpb>(h2, &cnt[4 * r + 1], nblk, (uint32_t)keff - A1, A1, &s_b2, &s_A2, scan, &flag)) return;
-  if constexpr (kFused) {
-    resolve_row<kTpb>(r, n, keff, k, row, b1, s_b2, s_A2, cnt[4 * r + 2], seg_cnt, seg_off, cand, nblk_max,
-                      topk_idx + (int64_t)r * k, R);
-  } else {
-    if (threadIdx.x == 0) { thr[4 * r + 2] = s_b2; thr[4 * r + 3] = s_A2; }
+      if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
   }
 }
 
-__global__ __launch_bounds__(512) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
-                                                           const int32_t* __restrict__ row_len, int max_row_len,
-                                                           int k, const uint32_t* __restrict__ thr,
-                                                           const uint32_t* __restrict__ cnt,
-                                                           const uint32_t* __restrict__ seg_cnt,
-                                                           const uint32_t* __restrict__ seg_off,
-                                                           const uint64_t* __restrict__ cand, int nblk_max,
-                                                           int32_t* __restrict__ topk_idx) {
+constexpr int kRes = 1024;  // threads of the resolve block
+
+__global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
+                                                            const int32_t* __restrict__ row_len, int max_row_len,
+                                                            int k, const uint32_t* __restrict__ thr,
+                                                            const uint32_t* __restrict__ hist2,
+                                                            const uint32_t* __restrict__ cnt,
+                                                            const uint32_t* __restrict__ seg_cnt,
+                                                            const uint32_t* __restrict__ seg_off,
+                                                            const uint64_t* __restrict__ cand, int nblk_max,
+                                                            int32_t* __restrict__ topk_idx) {
+  static_assert(kRes >= kTopkMaxBlocksPerRow, "one chunk per thread");
   __shared__ ResolveLds S;
+  __shared__ uint32_t s_b2, s_A2;
   const int r = blockIdx.x;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
   int32_t* out = topk_idx + (int64_t)r * k;
   if (keff >= n) {
-    for (int i = threadIdx.x; i < k; i += 512) out[i] = i < n ? i : -1;
+    for (int i = threadIdx.x; i < k; i += kRes) out[i] = i < n ? i : -1;
     return;
   }
-  resolve_row<512>(r, n, keff, k, scores + (int64_t)r * ld, thr[4 * r + 0], thr[4 * r + 2], thr[4 * r + 3],
-                   cnt[4 * r + 2], seg_cnt, seg_off, cand, nblk_max, out, S);
+  const float* row = scores + (int64_t)r * ld;
+  const uint32_t b1 = thr[4 * r + 0], A1 = thr[4 * r + 1];
+  const uint32_t len = cnt[4 * r + 2];
+  if (len <= (uint32_t)kCap) {
+    const int nblk = (n + kCh - 1) / kCh;
+    const int t = threadIdx.x;
+    const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
+    if (t < nblk) S.seg_src[t] = seg_off[(int64_t)r * nblk_max + t];
+    // b2: the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key
+    threshold_bin<kRes, 1>(hist2 + (int64_t)r * kTopkBins, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
+    uint32_t total;
+    const uint32_t start = block_exclusive_scan(c, S.scan, total);  // segment starts in position order
+    if (t < nblk) S.seg_start[t] = start;
+    __syncthreads();
+    const uint32_t b2 = s_b2, A2 = A1 + s_A2;
+    // every candidate goes to its chunk's segment start + its offset within the segment
+    constexpr int kPer = (kCap + kRes - 1) / kRes;
+    uint64_t e[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kRes + t;
+      e[j] = i < (int)len ? cand[(int64_t)r * kCap + i] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kRes + t;
+      if (i < (int)len) {
+        const uint32_t pos = (uint32_t)(e[j] >> 32);
+        const int chunk = (int)(pos / kCh);
+        const uint32_t dst = S.seg_start[chunk] + ((uint32_t)i - S.seg_src[chunk]);
+        S.key[dst] = (uint32_t)e[j];
+        S.pos[dst] = (int32_t)pos;
+      }
+    }
+    __syncthreads();
+    uint32_t need = (uint32_t)keff - A2;  // keys of (b1, b2) still to take
+    const LdsList L{S.key, S.pos};
+    const uint32_t d3 = refine_digit<kRes>(L, (int)len, (b1 << 12) | b2, 0, 8, need, S.h, S.scan);
+    write_selection<kRes>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out);
+  } else {
+    const RowList L{row};
+    uint32_t need = (uint32_t)keff;
+    const uint32_t d1 = refine_digit<kRes>(L, n, 0u, 20, 12, need, S.h, S.scan);
+    const uint32_t d2 = refine_digit<kRes>(L, n, d1, 8, 12, need, S.h, S.scan);
+    const uint32_t d3 = refine_digit<kRes>(L, n, (d1 << 12) | d2, 0, 8, need, S.h, S.scan);
+    write_selection<kRes>(L, n, (d1 << 20) | (d2 << 8) | d3, need, keff, out);
+  }
+  for (int i = keff + threadIdx.x; i < k; i += kRes) out[i] = -1;
 }
 
 }  // namespace
@@ -396,12 +363,13 @@ __global__ __launch_bounds__(512) void topk_resolve_kernel(const float* __restri
 size_t topk_workspace_bytes(const Geo& g) {
   const size_t nblk = (size_t)std::max(1, (g.max_row_len + kCh - 1) / kCh);
   const size_t R = (size_t)g.R;
-  return 2 * align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) + 2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
+  return align_up(4 * R * kHistCopies * kTopkBins) + align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) +
+         2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
 }
 
 TopkState topk_state(const Geo& g, void* workspace) {
   const Ws w = carve(g, workspace);
-  return TopkState{w.hist1, w.cnt, w.thr};
+  return TopkState{w.hist1};
 }
 
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
@@ -417,17 +385,11 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const Ws w = carve(g, workspace);
   dim3 grid(w.nblk, g.R);
   if (!hist_done)
-    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.cnt, w.thr);
-  // few rows: the chunk that completes a row resolves it; many rows: a resolve kernel with a block per row
-  if (g.R <= kTopkFusedResolveRows) {
-    topk_filter_kernel<true><<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2,
-                                                        w.cnt, w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
-  } else {
-    topk_filter_kernel<false><<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2,
-                                                         w.cnt, w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
-    topk_resolve_kernel<<<g.R, 512, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt, w.seg_cnt,
-                                                 w.seg_off, w.cand, w.nblk, topk_idx);
-  }
+    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1);
+  topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
+                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk);
+  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,
+                                                w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
   return hipGetLastError();
 }
 
