@@ -61,6 +61,8 @@ def main() -> int:
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch every step from the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 4 times (reference dispatches for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding design); "
@@ -207,6 +209,16 @@ def main() -> int:
         "phases_us": {"indexer": round(us_idx, 3), "topk": round(us_topk, 3), "attention": round(us_attn, 3)},
         "gen_seconds": round(gen_s, 2),
     }
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n
+        del src, dst
 
     if not args.no_cpu_baseline:
         import oracle
