@@ -24,7 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense OCP fp8 MFMA, MI355X
 METRIC = "DSA decode queries/s @T=128K, k=2048 (indexer+topk+attn); % HBM roofline"
+METRIC_PREFILL = "DSA chunked-prefill query rows/s (indexer+topk+attn); indexer % fp8 MFMA peak"
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_128k_pmc.json")
 
 
@@ -53,7 +55,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode_128k", choices=["decode_128k", "batched_paged", "decode_1m"])
+    ap.add_argument("--workload", default="decode_128k",
+                    choices=["decode_128k", "batched_paged", "decode_1m", "prefill_chunk"])
     ap.add_argument("--copies", type=int, default=0, help="distinct input copies to rotate (0 = auto)")
     ap.add_argument("--phase-iters", type=int, default=400)
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,
@@ -88,8 +91,9 @@ def main() -> int:
     L = dsa.make_layout(base.row_seq, base.row_len, base.page_table)
 
     # distinct copies of every per-step input, enough to exceed the 256 MiB Infinity Cache several times
+    prefill = prob.rows_per_seq > 1
     touched = sum(cost.decode_row_bytes(int(n), prob.k, prob.H_I, prob.d_I, prob.H, prob.d_c) for n in prob.row_len)
-    copies = args.copies or max(2, min(64, int(np.ceil(3 * 256e6 / touched))))
+    copies = args.copies or (2 if prefill else max(2, min(64, int(np.ceil(3 * 256e6 / touched)))))
     names = ["q_idx", "q_idx_scale", "head_w", "k_idx_pool", "k_idx_scale", "q", "kv_pool"]
     sets = [{n: getattr(base, n) for n in names}]
     for _ in range(copies - 1):
@@ -181,11 +185,23 @@ def main() -> int:
     us_attn = timed(ph_attn, args.phase_iters)
 
     idx_bytes = sum(cost.indexer_row_bytes(int(n), prob.H_I, prob.d_I) for n in prob.row_len)
-    achieved = idx_bytes / (us_idx * 1e-6) / 1e9
-    traffic = measured_traffic()
+    idx_flops = sum(cost.indexer_row_flops(int(n), prob.H_I, prob.d_I) for n in prob.row_len)
+    if prefill:
+        # rows of one sequence share their keys: the tiled indexer is a GEMM, priced against the fp8 MFMA peak
+        achieved = idx_flops / (us_idx * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "indexer_f8_tiled_kernel", "flops_per_launch": idx_flops,
+                    "us_per_launch": round(us_idx, 3)}
+    else:
+        achieved = idx_bytes / (us_idx * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic() if args.workload == "decode_128k" else None,
+                    "kernel": "indexer_f8_kernel", "bytes_per_launch": idx_bytes, "us_per_launch": round(us_idx, 3)}
     step_bytes = touched
     result = {
-        "metric": METRIC,
+        "metric": METRIC_PREFILL if prefill else METRIC,
         "value": round(qps, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -200,9 +216,7 @@ def main() -> int:
         "config": {"workload": args.workload, "rows": R, "context": int(prob.max_row_len), "k": prob.k,
                    "H_I": prob.H_I, "d_I": prob.d_I, "H": prob.H, "d_c": prob.d_c, "page_size": prob.page_size,
                    "input_copies": copies, "graph": bool(args.graph)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "indexer_f8_kernel", "bytes_per_launch": idx_bytes, "us_per_launch": round(us_idx, 3)},
+        "roofline": roofline,
         "end_to_end": {"algorithmic_bytes_per_step": step_bytes,
                        "hbm_frac": round(step_bytes / (wall / args.steps) / (HBM_PEAK_GBS * 1e9), 4),
                        "gpu_event_ms_per_step": round(gpu_s / args.steps * 1e3, 5)},
@@ -221,18 +235,28 @@ def main() -> int:
         del src, dst
 
     if not args.no_cpu_baseline:
+        import copy
         import oracle
-        reps, t_c = 0, time.perf_counter()
+        # bounded sample: consecutive groups of up to 8 rows of the same workload, until the time is spent
+        chunk = min(R, 8)
+        rows_done, reps, t_c = 0, 0, time.perf_counter()
         while True:
-            oracle.decode_step(prob)
+            rows = (np.arange(chunk) + reps * chunk) % R
+            sub = copy.copy(prob)
+            sub.R = chunk
+            for name in ("q_idx", "q_idx_scale", "head_w", "q", "row_seq", "row_len"):
+                a = getattr(prob, name)
+                setattr(sub, name, None if a is None else np.ascontiguousarray(a[rows]))
+            oracle.decode_step(sub)
             reps += 1
+            rows_done += chunk
             el = time.perf_counter() - t_c
             if el >= args.cpu_seconds or reps >= 1000:
                 break
-        result["cpu_baseline"] = {"value": round(reps * R / el, 3), "unit": "queries/s", "cores": oracle.threads(),
+        result["cpu_baseline"] = {"value": round(rows_done / el, 3), "unit": "queries/s", "cores": oracle.threads(),
                                   "kind": "oracle",
-                                  "sample": f"{reps} full {args.workload} steps ({R} row(s) each), fp64 oracle, "
-                                            f"{el:.1f} s"}
+                                  "sample": f"{rows_done} query rows of {args.workload} in {reps} call(s) of "
+                                            f"{chunk} row(s), fp64 oracle, {el:.1f} s"}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -226,7 +226,7 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
   if (topk_idx) idx = topk_idx;
   // fp8 indexer: its epilogue starts the selection (digit-1 histogram), so the top-k state is zeroed first
-  const bool fuse = g.idx_dtype == DSA_F8E4M3;
+  const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
   const dsa::TopkState tstate = dsa::topk_state(g, ws);
   if (fuse && (st = hip_status(dsa::launch_topk_zero(g, ws, s), "top-k launch")) != DSA_OK) return st;
   if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,

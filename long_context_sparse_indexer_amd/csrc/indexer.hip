@@ -12,7 +12,7 @@
 // are OCP e4m3fn (the format gfx950's f8f6f4 MFMA reads with format code 0), products are exact and the 64
 // terms accumulate in fp32.  Because the per-vector scales are positive they move outside the ReLU:
 // max(0, sq*sk*x) = sq*sk*max(0, x), so the epilogue weight of head j is w[j]*sq[j] and sk multiplies
-// the finished sum.
+// the finished sum.  The ReLU-weighted sum is formed as (sum_j wq_j x_j + sum_j wq_j |x_j|) / 2.
 //
 // Every key row is read once, as 32-byte pieces: one wave covers 32 consecutive positions = 2 KiB of
 // contiguous pool memory (a 32-aligned run never crosses a page of >= 32 positions).
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, int k,
-    uint32_t* __restrict__ hist1) {
+    uint32_t* __restrict__ hist1, int copies) {
   constexpr int H_I = 32 * HB;
   __shared__ uint32_t h[kHist ? kTopkBins : 1];
   const int r = blockIdx.y;
@@ -85,25 +85,216 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
 
 #pragma unroll
   for (int s = 0; s < kIdxSub; ++s) {
-    float part = 0.f;
+    // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
+    // fmaxf would also need a NaN-quieting max
+    float lin = 0.f, ab = 0.f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       v16f acc = {};
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s], acc, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(wq[hb][i], fmaxf(acc[i], 0.f), part);
+      for (int i = 0; i < 16; ++i) {
+        lin = fmaf(wq[hb][i], acc[i], lin);
+        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+      }
     }
+    float part = lin + ab;
     part += __shfl_xor(part, 32, 64);
     const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
     if (half == 0 && pos < n) {
-      const float v = sk[s] * part;
+      const float v = sk[s] * (0.5f * part);
       scores[(int64_t)r * ld + pos] = v;
       if (do_hist) atomicAdd(&h[order_key(v) >> 20], 1u);
     }
   }
   if (do_hist) {
     __syncthreads();
-    hist_merge<256>(h, hist1 + ((int64_t)r * kHistCopies + blockIdx.x % kHistCopies) * kTopkBins);
+    hist_merge<256>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
+  }
+}
+
+// Chunked prefill: consecutive rows of one sequence score the same keys, so the contraction is a real GEMM
+// [rows * H_I x d_I] x [d_I x n] (DeepSeek Sparse Attention explained: over a prefill the indexer's cost stays
+// quadratic in the context).  A block owns kPfRows rows of one sequence and kPfPasses * kPfTile positions.
+//
+// The fp8 MFMAs are cheap next to a two-instruction ReLU epilogue (64 cycles per 32x32x64 MFMA against
+// 16 elements x 2 VALU ops x 4 cycles), so the epilogue is rewritten with max(0, x) = (x + |x|) / 2:
+//     sum_j wq_j max(0, x_j) = ( sum_j wq_j x_j + sum_j wq_j |x_j| ) / 2,
+// where x_j = <q8_j, k8> and wq_j = w_j * sq_j.  The |x| term is one v_fma_f32 with an abs source modifier
+// per element.  The linear term is <u, k8> with u = sum_j wq_j q8_j, a 64-vector per row: it runs on a
+// bf16 MFMA with u split into four bf16 pieces (u = p0 + p1 + p2 + p3 to 2^-32 relative, each piece the
+// RNE rounding of what the previous ones leave) and the fp8 keys widened to bf16 exactly, so every product is
+// exact and only fp32 accumulation rounds.  A row group of 8 rows x 4 pieces fills the 32 rows of
+// v_mfma_f32_32x32x16_bf16: A row 8c + r holds piece c of row r; output register 4c + e of lane half h then
+// holds piece c of row 4h + e, and the four pieces are summed in-lane.
+//
+// Layout per wave: 128 positions = four 32-position subtiles whose fp8 keys stay in registers as MFMA B
+// operands (lane l: position l % 32, key bytes 32 (l / 32) .. +32); the same bytes, widened, feed the linear
+// MFMA with K index d = 32 (l / 32) + 8 m + e for K-step m, slot e, and u is laid out to match.  Queries,
+// epilogue weights and the u pieces sit in LDS, shared by the four waves.
+constexpr int kPfRows = 16;               // query rows per block: two groups of 8 for the linear MFMA
+constexpr int kPfSub = 4;                 // 32-position subtiles per wave
+constexpr int kPfTile = 4 * kPfSub * 32;  // positions per pass of a 256-thread block
+constexpr int kPfPasses = 4;              // passes per block: the row staging is paid once per 2048 positions
+
+template <int HB>
+__global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int num_pages, int log2ps, int max_row_len, int R, int rows_per_seq, int tiles_per_group,
+    float* __restrict__ scores, int64_t ld) {
+  constexpr int H_I = 32 * HB;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32];    // lane l's fp8 A operand
+  __shared__ __attribute__((aligned(16))) float w_lds[kPfRows][HB][2][16];       // wq of each lane half's heads
+  __shared__ __attribute__((aligned(16))) __bf16 u_lds[kPfRows / 8][4][64][8];   // linear-MFMA A operands
+  __shared__ int n_lds[kPfRows];
+  const int group = (int)blockIdx.y / tiles_per_group;
+  const int r0 = group * rows_per_seq + ((int)blockIdx.y % tiles_per_group) * kPfRows;
+  const int rows = min(min(kPfRows, (group + 1) * rows_per_seq - r0), R - r0);
+  if (rows <= 0) return;  // a tile past the end of a short last group (uniform)
+  const int64_t span0 = (int64_t)blockIdx.x * (kPfPasses * kPfTile);
+  if ((int)threadIdx.x < kPfRows)
+    n_lds[threadIdx.x] = (int)threadIdx.x < rows ? clamp_len(row_len[r0 + threadIdx.x], max_row_len) : 0;
+  __syncthreads();
+  int nmax = 0;
+  for (int q = 0; q < rows; ++q) nmax = max(nmax, n_lds[q]);
+  if (span0 >= nmax) return;  // uniform: no row of the tile sees these positions
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int seq = clamp_seq(row_seq[r0], num_seqs);  // shared by the group's rows
+
+  // stage the rows' A operands (16-byte pieces: c = (q * HB + hb) * 128 + l * 2 + piece) and epilogue weights
+  for (int c = threadIdx.x; c < rows * HB * 128; c += 256) {
+    const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
+    const v4i v = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)(r0 + q) * H_I + hb * 32 + (l & 31)) * 64 +
+                                                (l >> 5) * 32 + piece * 16);
+    *reinterpret_cast<v4i*>(&a_lds[q][hb][l][piece * 16]) = v;
+  }
+  for (int c = threadIdx.x; c < rows * H_I; c += 256) {
+    const int q = c / H_I, head = c % H_I, hh = head & 31;
+    const int64_t gi = (int64_t)(r0 + q) * H_I + head;
+    // lane half (hh >> 2) & 1 holds head hh as accumulator entry (hh & 3) + 4 * (hh >> 3)
+    w_lds[q][head >> 5][(hh >> 2) & 1][(hh & 3) + 4 * (hh >> 3)] = head_w[gi] * q_scale[gi];
+  }
+  __syncthreads();
+
+  // u[q][d] = sum_j wq_j q8[q][j][d] in fp32, split into bf16 pieces placed as linear-MFMA A operands
+  {
+    const int q = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 4;  // 16 rows x 16 threads x 4 dims
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    if (q < rows) {
+      for (int j = 0; j < H_I; ++j) {
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(&a_lds[q][j >> 5][(d0 >> 5) * 32 + (j & 31)][d0 & 31]);
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.f, true);
+        const float w = w_lds[q][j >> 5][(j >> 2) & 1][(j & 3) + 4 * ((j >> 3) & 3)];
+        u[0] = fmaf(w, lo.x, u[0]);
+        u[1] = fmaf(w, lo.y, u[1]);
+        u[2] = fmaf(w, hi.x, u[2]);
+        u[3] = fmaf(w, hi.y, u[3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d = d0 + t;
+      float rest = u[t];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const __bf16 p = (__bf16)rest;  // round to nearest even; rest - p is exact
+        rest -= (float)p;
+        u_lds[q >> 3][(d >> 3) & 3][(d >> 5) * 32 + 8 * c + (q & 7)][d & 7] = p;
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int pass = 0; pass < kPfPasses; ++pass) {
+    const int64_t tile0 = span0 + (int64_t)pass * kPfTile;
+    if (tile0 >= nmax) break;  // uniform
+    int64_t prow[kPfSub];
+#pragma unroll
+    for (int s = 0; s < kPfSub; ++s) {
+      const int64_t pos = tile0 + wave * (kPfSub * 32) + s * 32 + col;
+      prow[s] = pos < nmax ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
+    }
+    v8i b[kPfSub];
+    float sk[kPfSub];
+#pragma unroll
+    for (int s = 0; s < kPfSub; ++s) {
+      if (prow[s] >= 0) {
+        b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
+        sk[s] = k_scale[prow[s]];
+      } else {
+        b[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        sk[s] = 0.f;
+      }
+    }
+
+#pragma unroll 1
+    for (int g = 0; g < kPfRows / 8; ++g) {
+      if (8 * g >= rows) break;  // uniform
+      // linear term: lin[s][e] = <u of row 8 g + 4 half + e, k8 of this lane's position in subtile s>
+      float lin[kPfSub][4];
+#pragma unroll
+      for (int s = 0; s < kPfSub; ++s) {
+        v16f acc = {};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, false);
+          const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, true);
+          const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, false);
+          const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, true);
+          const v8bf kb = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(&u_lds[g][m][lane][0]), kb,
+                                                        acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lin[s][e] = ((acc[12 + e] + acc[8 + e]) + acc[4 + e]) + acc[e];
+      }
+
+#pragma unroll 1
+      for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qq = 4 * hq + e, q = 8 * g + qq;
+        const int n = q < rows ? n_lds[q] : 0;
+        if (tile0 >= n) continue;  // uniform; also skips rows past the tile's end
+        v8i a[HB];
+        float wq[HB][16];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          a[hb] = *reinterpret_cast<const v8i*>(&a_lds[q][hb][lane][0]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
+        }
+        float* out = scores + (int64_t)(r0 + q) * ld;
+        const bool owner = hq == half;  // this lane half holds row q's linear term
+#pragma unroll
+        for (int s = 0; s < kPfSub; s += 2) {
+          float ab0 = 0.f, ab1 = 0.f;  // sum_j wq_j |x_j| over this lane half's heads, subtiles s and s + 1
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            v16f acc0 = {}, acc1 = {};
+            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s], acc0, 0, 0, 0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s + 1], acc1, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              ab0 = fmaf(wq[hb][i], fabsf(acc0[i]), ab0);
+              ab1 = fmaf(wq[hb][i], fabsf(acc1[i]), ab1);
+            }
+          }
+          // half 0 finishes subtile s and half 1 subtile s + 1; the owner half adds the linear term of both
+          const float l0 = lin[s][e], l1 = lin[s + 1][e];
+          const float keep = owner ? (half ? ab1 + l1 : ab0 + l0) : (half ? ab1 : ab0);
+          const float send = owner ? (half ? ab0 + l0 : ab1 + l1) : (half ? ab0 : ab1);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
+          const float total = keep + __uint_as_float(half ? sw[0] : sw[1]);
+          const int64_t pos = tile0 + wave * (kPfSub * 32) + (s + half) * 32 + col;
+          if (pos < n) out[pos] = (half ? sk[s + 1] : sk[s]) * (0.5f * total);
+        }
+      }
+    }
   }
 }
 
@@ -143,13 +334,34 @@ void launch_f8(const Geo& g, dim3 grid, const uint8_t* qp, const float* q_idx_sc
                hipStream_t stream) {
   indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr);
+      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->copies : 1);
 }
+
+template <int HB>
+void launch_f8_tiled(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w,
+                     const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, hipStream_t stream) {
+  const int tiles_per_group = (g.rows_per_seq + kPfRows - 1) / kPfRows;
+  const int groups = (g.R + g.rows_per_seq - 1) / g.rows_per_seq;
+  dim3 grid((g.max_row_len + kPfPasses * kPfTile - 1) / (kPfPasses * kPfTile), groups * tiles_per_group);
+  indexer_f8_tiled_kernel<HB><<<grid, 256, 0, stream>>>(
+      qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
+      g.log2ps, g.max_row_len, g.R, g.rows_per_seq, tiles_per_group, scores, ld);
+}
+
+bool indexer_tiled(const Geo& g) { return g.idx_dtype == 2 /* F8E4M3 */ && g.rows_per_seq >= kTiledMinRows; }
 
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
                           const TopkState* fuse, hipStream_t stream) {
   if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
+  if (indexer_tiled(g)) {
+    if (fuse) return hipErrorInvalidValue;  // the tiled kernel has no histogram epilogue
+    auto* qp = static_cast<const uint8_t*>(q_idx);
+    auto* kp = static_cast<const uint8_t*>(k_idx_pool);
+    if (g.H_I == 64) launch_f8_tiled<2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    else launch_f8_tiled<1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    return hipGetLastError();
+  }
   if (g.idx_dtype == 2 /* F8E4M3 */) {
     dim3 grid((g.max_row_len + kIdxTile - 1) / kIdxTile, g.R);
     auto* qp = static_cast<const uint8_t*>(q_idx);

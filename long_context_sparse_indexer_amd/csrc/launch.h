@@ -23,11 +23,15 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Digit-1 radix-select state the indexer can fill in its epilogue (see topk.hip).
 struct TopkState {
-  uint32_t* hist1;
+  uint32_t* hist1;  // [R, copies, 4096]
+  int copies;
 };
 
-// indexer.hip.  With `fuse` non-NULL the indexer also builds the top-k digit-1 histogram; the state must have
+// indexer.hip.  fp8 problems whose rows come in groups of at least kTiledMinRows per sequence (chunked prefill)
+// run the tiled GEMM kernel, which takes no `fuse`.  Otherwise, with `fuse` non-NULL the indexer also builds the top-k digit-1 histogram; the state must have
 // been zeroed (launch_topk_zero) earlier on the stream.
+constexpr int kTiledMinRows = 8;
+bool indexer_tiled(const Geo& g);
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
                           const TopkState* fuse, hipStream_t stream);

@@ -32,8 +32,9 @@ Ws carve(const Geo& g, void* base) {
   Ws w;
   char* p = static_cast<char*>(base);
   w.nblk = std::max(1, (g.max_row_len + kCh - 1) / kCh);
+  w.copies = hist_copies(g.R);
   auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes); return q; };
-  w.hist1 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kHistCopies * kTopkBins));
+  w.hist1 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * w.copies * kTopkBins));
   w.hist2 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
   w.cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.thr = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
@@ -45,12 +46,12 @@ Ws carve(const Geo& g, void* base) {
 
 // Zeroes the histograms and the counters of every row (one block per row).
 __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2,
-                                                        uint32_t* __restrict__ cnt) {
+                                                        uint32_t* __restrict__ cnt, int copies) {
   const int r = blockIdx.x;
   const v4i z = {0, 0, 0, 0};
-  v4i* h1 = reinterpret_cast<v4i*>(hist1 + (int64_t)r * kHistCopies * kTopkBins);
+  v4i* h1 = reinterpret_cast<v4i*>(hist1 + (int64_t)r * copies * kTopkBins);
   v4i* h2 = reinterpret_cast<v4i*>(hist2 + (int64_t)r * kTopkBins);
-  for (int i = threadIdx.x; i < kHistCopies * kTopkBins / 4; i += blockDim.x) h1[i] = z;
+  for (int i = threadIdx.x; i < copies * kTopkBins / 4; i += blockDim.x) h1[i] = z;
   for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h2[i] = z;
   if (threadIdx.x == 0) reinterpret_cast<v4i*>(cnt)[r] = z;
 }
@@ -77,7 +78,7 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
 // First-digit histogram of stored scores (standalone top-k): one block per 4096-score chunk.
 __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                          const int32_t* __restrict__ row_len, int max_row_len, int k,
-                                                         uint32_t* __restrict__ hist1) {
+                                                         uint32_t* __restrict__ hist1, int copies) {
   __shared__ uint32_t h[kTopkBins];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict
   for (int e = 0; e < kEpt; ++e)
     if (valid[e]) atomicAdd(&h[key[e] >> 20], 1u);
   __syncthreads();
-  hist_merge<kTpb>(h, hist1 + ((int64_t)r * kHistCopies + blockIdx.x % kHistCopies) * kTopkBins);
+  hist_merge<kTpb>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
 }
 
 // Candidate access for the resolve step: entries of the LDS list, or every position of the stored row.
@@ -205,20 +206,19 @@ struct ResolveLds {
   uint32_t scan[1024 / 64 + 1];  // one word per wave of the largest block, plus the total
 };
 
-// Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of COPIES
+// Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of `copies`
 // consecutive 4096-bin replicas, top bin first), and the number of keys in bins above b.  Called by all NT
 // threads; the result lands in *b, *above.
-template <int NT, int COPIES>
-__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, uint32_t need, uint32_t* scan,
-                                              uint32_t* b, uint32_t* above_out) {
+template <int NT>
+__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, int copies, uint32_t need,
+                                              uint32_t* scan, uint32_t* b, uint32_t* above_out) {
   constexpr int kPer = kTopkBins / NT;
   const int grp = NT - 1 - threadIdx.x;  // thread 0 owns the top bins
   uint32_t c[kPer];
   uint32_t local = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) c[j] = 0u;
-#pragma unroll
-  for (int cp = 0; cp < COPIES; ++cp)
+  for (int cp = 0; cp < copies; ++cp)
 #pragma unroll
     for (int j = 0; j < kPer; ++j) c[j] += gh[cp * kTopkBins + grp * kPer + j];
 #pragma unroll
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
                                                            uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
                                                            uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
-                                                           int nblk_max) {
+                                                           int nblk_max, int copies) {
   __shared__ uint32_t scan[kTpb / 64 + 1];
   __shared__ uint32_t seg_base, s_b1, s_A1;
   const int r = blockIdx.y;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   bool valid[kEpt];
   load_keys(scores + (int64_t)r * ld, first, n, key, valid);
   // every block finds b1 itself (a 16 KiB read) instead of waiting for one block to publish it
-  threshold_bin<kTpb, kHistCopies>(hist1 + (int64_t)r * kHistCopies * kTopkBins, (uint32_t)keff, scan, &s_b1, &s_A1);
+  threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
   const uint32_t b1 = s_b1;
   if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
   uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
     if (t < nblk) S.seg_src[t] = seg_off[(int64_t)r * nblk_max + t];
     // b2: the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key
-    threshold_bin<kRes, 1>(hist2 + (int64_t)r * kTopkBins, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
+    threshold_bin<kRes>(hist2 + (int64_t)r * kTopkBins, 1, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
     uint32_t total;
     const uint32_t start = block_exclusive_scan(c, S.scan, total);  // segment starts in position order
     if (t < nblk) S.seg_start[t] = start;
@@ -363,19 +363,19 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
 size_t topk_workspace_bytes(const Geo& g) {
   const size_t nblk = (size_t)std::max(1, (g.max_row_len + kCh - 1) / kCh);
   const size_t R = (size_t)g.R;
-  return align_up(4 * R * kHistCopies * kTopkBins) + align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) +
+  return align_up(4 * R * hist_copies(g.R) * kTopkBins) + align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) +
          2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
 }
 
 TopkState topk_state(const Geo& g, void* workspace) {
   const Ws w = carve(g, workspace);
-  return TopkState{w.hist1};
+  return TopkState{w.hist1, w.copies};
 }
 
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
-  topk_zero_kernel<<<g.R, 256, 0, stream>>>(w.hist1, w.hist2, w.cnt);
+  topk_zero_kernel<<<g.R, 256, 0, stream>>>(w.hist1, w.hist2, w.cnt, w.copies);
   return hipGetLastError();
 }
 
@@ -385,9 +385,9 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const Ws w = carve(g, workspace);
   dim3 grid(w.nblk, g.R);
   if (!hist_done)
-    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1);
+    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.copies);
   topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
-                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk);
+                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies);
   topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,
                                                 w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
   return hipGetLastError();

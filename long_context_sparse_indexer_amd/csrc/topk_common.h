@@ -6,11 +6,14 @@
 namespace dsa {
 
 constexpr int kTopkBins = 4096;  // bins of one 12-bit key digit
-constexpr int kHistCopies = 8;   // digit-1 histogram replicas: block b merges into copy b % 8, which keeps the
-                                 // atomics on a popular bin to a few dozen per copy
+
+// Digit-1 histogram replicas per row: block b merges into copy b % copies.  With few rows, hundreds of blocks
+// of one row hit the same popular bins, and replicas keep those atomics to a few dozen per address; with many
+// rows the atomics spread over the rows' own histograms and one copy avoids clearing megabytes of replicas.
+__host__ __device__ constexpr int hist_copies(int R) { return R <= 8 ? 8 : R <= 16 ? 4 : R <= 32 ? 2 : 1; }
 
 struct Ws {
-  uint32_t* hist1;    // [R, 8, 4096]  digit-1 histogram replicas
+  uint32_t* hist1;    // [R, copies, 4096]  digit-1 histogram replicas
   uint32_t* hist2;    // [R, 4096]  digit-2 histogram of keys inside bin b1
   uint32_t* cnt;      // [R, 4]     unused, unused, candidates reserved, unused
   uint32_t* thr;      // [R, 4]     b1, keys above b1 (written by the filter's first block)
@@ -18,6 +21,7 @@ struct Ws {
   uint32_t* seg_off;  // [R, nblk]  where each chunk's candidates start in the row's list
   uint64_t* cand;     // [R, cap]   candidates: position << 32 | key
   int nblk;
+  int copies;
 };
 
 // Merges a block's LDS histogram `h` (complete: a barrier after its last update) into a global histogram

@@ -36,6 +36,11 @@ CONFIGS = {
         kind="prefill", cache_len=131072, rows=4096, H_I=64, d_I=64, k=2048, H=128, d_c=512,
         idx_dtype="f8", kv_dtype="bf16", anchors=256, recent=512, paged=False, seed=1, page_size=64,
         softmax_scale=1.0),
+    # chunked prefill of several paged sequences at once (rows consecutive rows per sequence)
+    "prefill_paged": dict(
+        kind="prefill", batch=3, length_range=(3000, 9000), rows=37, H_I=64, d_I=64, k=2048, H=32, d_c=512,
+        idx_dtype="f8", kv_dtype="bf16", anchors=64, recent=128, paged=True, seed=5, page_size=64,
+        softmax_scale=1.0),
     # 8 sequences of 2^20 tokens
     "decode_1m": dict(
         kind="decode", batch=8, lengths=[1048576] * 8, H_I=64, d_I=64, k=2048, H=128, d_c=512,
@@ -43,7 +48,7 @@ CONFIGS = {
         softmax_scale=1.0),
 }
 
-ORDER = ["tiny_fp32", "decode_128k", "batched_paged", "prefill_chunk", "decode_1m"]
+ORDER = ["tiny_fp32", "decode_128k", "batched_paged", "prefill_chunk", "decode_1m", "prefill_paged"]
 
 
 def get(name: str, **overrides) -> dict:

@@ -35,9 +35,7 @@ def upload(p: Problem, device="cuda") -> types.SimpleNamespace:
     d.page_table = _t(p.page_table, device)
     d.fields = dict(num_rows=p.R, num_seqs=p.S, idx_heads=p.H_I, idx_dim=p.d_I, attn_heads=p.H, latent_dim=p.d_c,
                     topk=p.k, page_size=p.page_size, max_pages=p.max_pages, num_pages=p.num_pages,
-                    max_row_len=p.max_row_len, rows_per_seq=1, idx_dtype=p.idx_dtype, kv_dtype=p.kv_dtype,
-                    softmax_scale=p.softmax_scale)
-    if p.cfg.get("kind") == "prefill":
-        d.fields["rows_per_seq"] = p.R
+                    max_row_len=p.max_row_len, rows_per_seq=p.rows_per_seq, idx_dtype=p.idx_dtype,
+                    kv_dtype=p.kv_dtype, softmax_scale=p.softmax_scale)
     d.f8 = f8
     return d

@@ -55,6 +55,7 @@ class Problem:
     row_len: np.ndarray          # [R] int32
     page_table: np.ndarray       # [S, max_pages] int32
     boosted: list                # per sequence: int64 positions that were boosted
+    rows_per_seq: int = 1        # consecutive rows sharing one sequence (a chunked prefill: rows per sequence)
 
     @property
     def max_row_len(self) -> int:
@@ -113,7 +114,7 @@ def make_problem(cfg: dict) -> Problem:
     d_c, d_I, H_I, H = cfg["d_c"], cfg["d_I"], cfg["H_I"], cfg["H"]
     W_KI = _child(seed, 0).standard_normal((d_c, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
 
-    if cfg["kind"] == "prefill":
+    if cfg["kind"] == "prefill" and "cache_len" in cfg:
         lengths = [cfg["cache_len"]]
     elif "lengths" in cfg:
         lengths = list(cfg["lengths"])
@@ -158,8 +159,10 @@ def make_problem(cfg: dict) -> Problem:
         else:
             # causal chunk: the row at 1-based position p sees positions 0..p-1; the last row is the
             # sequence's own query, the others are fresh draws
-            rows, first = cfg["rows"], cfg["cache_len"] - cfg["rows"] + 1
-            rng = _child(seed, 4)
+            rows = cfg["rows"]
+            assert 1 <= rows <= n, "a prefill chunk needs at least `rows` cached positions per sequence"
+            first = n - rows + 1
+            rng = _child(seed, 4, b)
             for r in range(rows - 1):
                 a, bw, c = _extra_row(rng, cfg)
                 q_I_rows.append(a); w_rows.append(bw); q_rows.append(c)
@@ -184,4 +187,5 @@ def make_problem(cfg: dict) -> Problem:
         head_w=np.ascontiguousarray(np.stack(w_rows).astype(np.float32)) if R else np.zeros((0, H_I), np.float32),
         k_idx_pool=k_pool, k_idx_scale=k_scale, q=np.ascontiguousarray(q_bits), kv_pool=kv_pool,
         row_seq=np.asarray(row_seq, np.int32), row_len=np.asarray(row_len, np.int32),
-        page_table=page_table, boosted=boosted)
+        page_table=page_table, boosted=boosted,
+        rows_per_seq=cfg["rows"] if cfg["kind"] == "prefill" else 1)

@@ -8,7 +8,10 @@ Acceptance (from the step's definition and the stated tolerances):
     with the oracle's set has an oracle score within 1e-3 relative of the oracle's k_eff-th score; given the
     same scores, the selection is bit-exact against the oracle's selection rule;
   * attention: max abs error <= 2e-2 for bf16 latents and <= 1e-4 for fp32, on the GPU's own index set
-    against the oracle's attention over that same set, and end to end against the oracle's own set.
+    against the oracle's attention over that same set, and end to end against the oracle's own set for every
+    row whose selection equals the oracle's.  A row whose selection legitimately differs inside the tie band
+    attends over a different set: one swapped position can move an output by more than the tolerance, so that
+    row's output is held to the attention check on its own set alone (the tie-band rule covers the set).
 """
 from __future__ import annotations
 
@@ -32,8 +35,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_step(prob, stream=None, fields=None):
-    """Run the indexer, top-k and attention as separate calls and as the fused step; returns host arrays."""
+def gpu_step(prob, stream=None, fields=None, rows=None):
+    """Run the indexer, top-k and attention as separate calls and as the fused step; returns host arrays
+    (scores, outputs and lse for `rows` only when given; the selections for every row)."""
     d = upload(prob)
     f = dict(d.fields)
     if fields:
@@ -58,12 +62,25 @@ def gpu_step(prob, stream=None, fields=None):
     dsa.dsa_decode_step(P, L, d.q_idx, d.q_idx_scale, d.head_w, d.k_idx_pool, d.k_idx_scale, d.q, d.kv_pool, idx2,
                         out2, lse2, ws, stream)
     torch.cuda.synchronize()
+    sel = slice(None) if rows is None else torch.as_tensor(rows, device=dev)
     res = types.SimpleNamespace(
-        scores=scores.cpu().numpy().astype(np.float64), idx=idx.cpu().numpy(), out=out.float().cpu().numpy(),
-        lse=lse.cpu().numpy(), idx_step=idx2.cpu().numpy(), out_step=out2.float().cpu().numpy(),
-        lse_step=lse2.cpu().numpy())
+        scores=scores[sel].cpu().numpy().astype(np.float64), idx=idx.cpu().numpy(),
+        out=out[sel].float().cpu().numpy(), lse=lse[sel].cpu().numpy(), idx_step=idx2.cpu().numpy(),
+        out_step=out2[sel].float().cpu().numpy(), lse_step=lse2[sel].cpu().numpy())
     del d, scores, ws
     return res
+
+
+def subproblem(prob, rows):
+    """The same workload restricted to some query rows (shares the caches and page table)."""
+    import copy
+    sub = copy.copy(prob)
+    rows = np.asarray(rows)
+    sub.R = len(rows)
+    for name in ("q_idx", "q_idx_scale", "head_w", "q", "row_seq", "row_len"):
+        a = getattr(prob, name)
+        setattr(sub, name, None if a is None else np.ascontiguousarray(a[rows]))
+    return sub
 
 
 def score_bound(prob, r):
@@ -137,6 +154,52 @@ def check_attention(prob, out, lse, idx):
     return err
 
 
+def check_selection_valid(prob, gpu_idx):
+    """Properties every row's selection must have (checked for all rows at any size)."""
+    for r in range(prob.R):
+        n = int(prob.row_len[r])
+        keff = min(prob.k, n)
+        g = gpu_idx[r]
+        assert (g[keff:] == -1).all(), f"row {r}: padding"
+        sel = g[:keff]
+        assert ((sel >= 0) & (sel < n)).all(), f"row {r}: out-of-range index"
+        assert (np.diff(sel) > 0).all(), f"row {r}: not strictly increasing"
+
+
+def check_end_to_end(prob, out, gpu_idx, ref_o, ref_idx):
+    """Max abs error against the oracle's own output over the rows whose selection equals the oracle's;
+    returns (error, number of rows with a tie-band swap)."""
+    tol = ATOL[prob.kv_dtype]
+    worst, swapped = 0.0, 0
+    for r in range(prob.R):
+        keff = min(prob.k, int(prob.row_len[r]))
+        if not np.array_equal(np.sort(ref_idx[r, :keff]), gpu_idx[r, :keff]):
+            swapped += 1
+            continue
+        e = float(np.abs(out[r] - ref_o[r]).max()) if out[r].size else 0.0
+        assert e <= tol, f"row {r}: end-to-end error {e:.3e} against the oracle's own selection"
+        worst = max(worst, e)
+    return worst, swapped
+
+
+def sampled_check(prob, rows, fields=None):
+    """Full-size workload: every row's selection is checked for validity; the sampled rows are checked
+    element by element against the oracle (scores, selection band, attention on both selections)."""
+    res = gpu_step(prob, fields=fields, rows=rows)
+    check_selection_valid(prob, res.idx)
+    assert np.array_equal(res.idx_step, res.idx)
+    sub = subproblem(prob, rows)
+    ref_scores, ref_idx, ref_kth, ref_o, _ = oracle.decode_step(sub)
+    score_ratio = check_scores(sub, res.scores, ref_scores)
+    sub_idx = res.idx[np.asarray(rows)]
+    check_topk_exact(sub, res.scores, sub_idx)
+    check_topk_set(sub, sub_idx, ref_scores, ref_idx, ref_kth)
+    e_own = check_attention(sub, res.out, res.lse, sub_idx)
+    e2e, swapped = check_end_to_end(sub, res.out, sub_idx, ref_o, ref_idx)
+    assert np.array_equal(res.out_step, res.out)
+    return res, dict(attn_err=e_own, e2e_err=e2e, score_ratio=score_ratio, swapped=swapped)
+
+
 def full_check(prob, fields=None):
     res = gpu_step(prob, fields=fields)
     ref_scores, ref_idx, ref_kth, ref_o, _ = oracle.decode_step(prob)
@@ -144,10 +207,8 @@ def full_check(prob, fields=None):
     check_topk_exact(prob, res.scores, res.idx)
     check_topk_set(prob, res.idx, ref_scores, ref_idx, ref_kth)
     e_own = check_attention(prob, res.out, res.lse, res.idx)
-    tol = ATOL[prob.kv_dtype]
-    e2e = float(np.abs(res.out - ref_o).max())
-    assert e2e <= tol, f"end-to-end error {e2e:.3e} against the oracle's own selection"
+    e2e, swapped = check_end_to_end(prob, res.out, res.idx, ref_o, ref_idx)
     # the fused step equals the separate calls bit for bit
     assert np.array_equal(res.idx_step, res.idx)
     assert np.array_equal(res.out_step, res.out) and np.array_equal(res.lse_step, res.lse, equal_nan=True)
-    return res, dict(attn_err=e_own, e2e_err=e2e, score_ratio=score_ratio)
+    return res, dict(attn_err=e_own, e2e_err=e2e, score_ratio=score_ratio, swapped=swapped)

@@ -12,7 +12,7 @@ import torch
 import long_context_sparse_indexer_amd as dsa
 import oracle
 import synth
-from harness import full_check, gpu_step, say, check_topk_exact
+from harness import full_check, gpu_step, say, check_topk_exact, sampled_check
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _run(cfg, fields=None, mutate=None):
         mutate(prob)
     res, err = full_check(prob, fields)
     say(f"  ok: score err {err['score_ratio']:.3f} of bound, attention err {err['attn_err']:.2e}, "
-        f"end-to-end err {err['e2e_err']:.2e}")
+        f"end-to-end err {err['e2e_err']:.2e} ({err['swapped']} of {prob.R} rows with a tie-band swap)")
     return prob, res
 
 
@@ -80,6 +80,23 @@ def test_prefill_chunk_rows_share_the_cache():
     assert prob.row_len.tolist() == list(range(8961, 9001))
 
 
+def test_prefill_several_paged_sequences():
+    # 3 paged sequences x 37 causal rows: tiles of 16 rows never straddle two sequences, the last is ragged
+    prob, res = _run(synth.get("prefill_paged"))
+    assert prob.rows_per_seq == 37 and prob.R == 111
+
+
+@pytest.mark.parametrize("rows,H_I", [(8, 64), (9, 64), (16, 32), (23, 32)])
+def test_prefill_tiled_row_groups(rows, H_I):
+    # row tiles of 16 made of two 8-row groups: exactly one group, a group plus one row, 32 heads, ragged
+    _run(synth.get("prefill_paged", rows=rows, H_I=H_I, batch=2, k=700, H=16))
+
+
+def test_prefill_rows_through_the_per_row_kernel():
+    # the same prefill chunk declared as independent rows runs the per-row kernel and must agree as well
+    _run(synth.get("prefill_paged", rows=20, H=16), fields=dict(rows_per_seq=1))
+
+
 def test_paged_equals_contiguous_bit_for_bit():
     cfg = synth.get("batched_paged", batch=3, length_range=(2500, 7000), H=32)
     a = gpu_step(synth.make_problem(cfg))
@@ -92,6 +109,38 @@ def test_rerun_is_bit_identical():
     a, b = gpu_step(prob), gpu_step(prob)
     assert np.array_equal(a.scores[:, :12000], b.scores[:, :12000])
     assert np.array_equal(a.idx, b.idx) and np.array_equal(a.out, b.out)
+
+
+# ---------------------------------------------------------------------------- full-size workloads, sampled
+
+def _sampled(name, rows_fn, **overrides):
+    cfg = synth.get(name, **overrides)
+    say(f"case {name} full size {overrides or ''}")
+    prob = synth.make_problem(cfg)
+    rows = rows_fn(prob)
+    res, err = sampled_check(prob, rows)
+    say(f"  ok: rows {list(rows)}: score err {err['score_ratio']:.3f} of bound, attention err {err['attn_err']:.2e}, "
+        f"end-to-end err {err['e2e_err']:.2e} ({err['swapped']} rows with a tie-band swap)")
+    return prob, res
+
+
+def test_batched_paged_full_size():
+    # the shortest and longest sequences plus a few others, out of 64 paged sequences
+    def rows(p):
+        order = np.argsort(p.row_len)
+        return sorted({int(order[0]), int(order[-1]), 5, 31, 62})
+    _sampled("batched_paged", rows)
+
+
+def test_prefill_chunk_full_size():
+    # first, last (= the decode_128k query) and interior rows of the 4096-row causal chunk
+    prob, res = _sampled("prefill_chunk", lambda p: [0, 1, 1000, 2047, 4094, 4095])
+
+
+@pytest.mark.slow
+def test_decode_1m_full_size():
+    # 8 sequences of 2^20 positions; two rows checked against the oracle
+    _sampled("decode_1m", lambda p: [0, 7])
 
 
 # ------------------------------------------------------------------------------- top-k on crafted scores

@@ -65,3 +65,13 @@ def test_prefill_reuses_the_decode_cache_and_query():
     assert pf.row_len.tolist() == [4995, 4996, 4997, 4998, 4999, 5000]
     assert np.array_equal(pf.q_idx[-1], d.q_idx[0]) and np.array_equal(pf.q[-1], d.q[0])
     assert not np.array_equal(pf.q_idx[0], d.q_idx[0])
+
+
+def test_prefill_of_several_sequences_groups_rows():
+    p = synth.make_problem(synth.get("prefill_paged", rows=5, length_range=(300, 700), H=4))
+    assert p.R == 15 and p.rows_per_seq == 5
+    for b in range(3):
+        rows = slice(5 * b, 5 * b + 5)
+        assert (p.row_seq[rows] == b).all()
+        n = int(p.row_len[5 * b + 4])
+        assert p.row_len[rows].tolist() == list(range(n - 4, n + 1))
