@@ -132,13 +132,22 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
 // operands (lane l: position l % 32, key bytes 32 (l / 32) .. +32); the same bytes, widened, feed the linear
 // MFMA with K index d = 32 (l / 32) + 8 m + e for K-step m, slot e, and u is laid out to match.  Queries,
 // epilogue weights and the u pieces sit in LDS, shared by the four waves.
-constexpr int kPfRows = 16;               // query rows per block: two groups of 8 for the linear MFMA
+//
+// Scheduling: each row is a software pipeline over (head block, subtile pair, subtile) units, the MFMA of the
+// next unit issued before the epilogue of the current one (sched_barrier keeps that order), so one wave keeps
+// the matrix core and the VALU busy together; 8-row blocks need 38 KiB of LDS and 168 VGPRs, which leaves room
+// for three waves per SIMD.  The finish of a subtile pair is branch-free: lane halves exchange partial sums
+// with v_permlane32_swap, the half that holds a row's linear term adds it through a 0/1 factor, and scores go
+// out through a raw buffer whose size is the row's visible length, so stores past it are dropped by the
+// hardware.  Staging loads are all issued before the first LDS write.
+constexpr int kPfRows = 8;                // query rows per block: one group of 8 for the linear MFMA
 constexpr int kPfSub = 4;                 // 32-position subtiles per wave
 constexpr int kPfTile = 4 * kPfSub * 32;  // positions per pass of a 256-thread block
-constexpr int kPfPasses = 4;              // passes per block: the row staging is paid once per 2048 positions
+constexpr int kPfPasses = 8;              // passes per block: the row staging is paid once per 4096 positions
+constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource word 3 on gfx9: 32-bit, range-checked
 
 template <int HB>
-__global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
+__global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
@@ -164,39 +173,65 @@ __global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r0], num_seqs);  // shared by the group's rows
 
-  // stage the rows' A operands (16-byte pieces: c = (q * HB + hb) * 128 + l * 2 + piece) and epilogue weights
-  for (int c = threadIdx.x; c < rows * HB * 128; c += 256) {
-    const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
-    const v4i v = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)(r0 + q) * H_I + hb * 32 + (l & 31)) * 64 +
-                                                (l >> 5) * 32 + piece * 16);
-    *reinterpret_cast<v4i*>(&a_lds[q][hb][l][piece * 16]) = v;
-  }
-  for (int c = threadIdx.x; c < rows * H_I; c += 256) {
-    const int q = c / H_I, head = c % H_I, hh = head & 31;
-    const int64_t gi = (int64_t)(r0 + q) * H_I + head;
-    // lane half (hh >> 2) & 1 holds head hh as accumulator entry (hh & 3) + 4 * (hh >> 3)
-    w_lds[q][head >> 5][(hh >> 2) & 1][(hh & 3) + 4 * (hh >> 3)] = head_w[gi] * q_scale[gi];
+  // stage the rows' A operands (16-byte pieces: c = (q * HB + hb) * 128 + l * 2 + piece) and epilogue weights;
+  // every load is issued before the first LDS write so the block pays one memory round trip, not one per piece
+  {
+    constexpr int kA = kPfRows * HB * 128 / 256;  // A pieces per thread
+    constexpr int kW = kPfRows * H_I / 256;       // weights per thread
+    v4i av[kA];
+    float wv[kW], sv[kW];
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
+      if (q < rows)
+        av[i] = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)(r0 + q) * H_I + hb * 32 + (l & 31)) * 64 +
+                                              (l >> 5) * 32 + piece * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+      const int c = threadIdx.x + 256 * i, q = c / H_I;
+      if (q < rows) {
+        wv[i] = head_w[(int64_t)r0 * H_I + c];
+        sv[i] = q_scale[(int64_t)r0 * H_I + c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
+      if (q < rows) *reinterpret_cast<v4i*>(&a_lds[q][hb][l][piece * 16]) = av[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+      const int c = threadIdx.x + 256 * i, q = c / H_I, head = c % H_I, hh = head & 31;
+      // lane half (hh >> 2) & 1 holds head hh as accumulator entry (hh & 3) + 4 * (hh >> 3)
+      if (q < rows) w_lds[q][head >> 5][(hh >> 2) & 1][(hh & 3) + 4 * (hh >> 3)] = wv[i] * sv[i];
+    }
   }
   __syncthreads();
 
   // u[q][d] = sum_j wq_j q8[q][j][d] in fp32, split into bf16 pieces placed as linear-MFMA A operands
   {
-    const int q = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 4;  // 16 rows x 16 threads x 4 dims
-    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kTpr = 256 / kPfRows, kDpt = 64 / kTpr;  // threads per row, dims per thread
+    const int q = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * kDpt;
+    float u[kDpt];
+#pragma unroll
+    for (int t = 0; t < kDpt; ++t) u[t] = 0.f;
     if (q < rows) {
       for (int j = 0; j < H_I; ++j) {
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(&a_lds[q][j >> 5][(d0 >> 5) * 32 + (j & 31)][d0 & 31]);
-        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.f, false);
-        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.f, true);
         const float w = w_lds[q][j >> 5][(j >> 2) & 1][(j & 3) + 4 * ((j >> 3) & 3)];
-        u[0] = fmaf(w, lo.x, u[0]);
-        u[1] = fmaf(w, lo.y, u[1]);
-        u[2] = fmaf(w, hi.x, u[2]);
-        u[3] = fmaf(w, hi.y, u[3]);
+#pragma unroll
+        for (int t = 0; t < kDpt; t += 2) {
+          const uint16_t codes = *reinterpret_cast<const uint16_t*>(&a_lds[q][j >> 5][((d0 + t) >> 5) * 32 + (j & 31)][(d0 + t) & 31]);
+          const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)codes, 1.f, false);
+          u[t] = fmaf(w, x.x, u[t]);
+          u[t + 1] = fmaf(w, x.y, u[t + 1]);
+        }
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kDpt; ++t) {
       const int d = d0 + t;
       float rest = u[t];
 #pragma unroll
@@ -209,6 +244,8 @@ __global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
   }
   __syncthreads();
 
+  v8i b[kPfSub];
+  float sk[kPfSub];
   for (int pass = 0; pass < kPfPasses; ++pass) {
     const int64_t tile0 = span0 + (int64_t)pass * kPfTile;
     if (tile0 >= nmax) break;  // uniform
@@ -218,8 +255,6 @@ __global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
       const int64_t pos = tile0 + wave * (kPfSub * 32) + s * 32 + col;
       prow[s] = pos < nmax ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
     }
-    v8i b[kPfSub];
-    float sk[kPfSub];
 #pragma unroll
     for (int s = 0; s < kPfSub; ++s) {
       if (prow[s] >= 0) {
@@ -231,67 +266,108 @@ __global__ __launch_bounds__(256, 2) void indexer_f8_tiled_kernel(
       }
     }
 
+    // per pass, per lane: half 0 stores subtile 2p and half 1 subtile 2p + 1 of each pair p; 0.5 sk of that
+    // position (the 1/2 of (lin + abs) folded in, exact) and its byte offset within the row
+    float skm[kPfSub / 2];
+    int voff[kPfSub / 2];
+#pragma unroll
+    for (int p = 0; p < kPfSub / 2; ++p) {
+      const int rel = wave * (kPfSub * 32) + (2 * p + half) * 32 + col;
+      const int64_t pos = tile0 + rel;
+      // the scale of the position this lane stores, loaded directly (a select between subtiles would index
+      // the register array with the lane's half)
+      skm[p] = pos < nmax ? 0.5f * k_scale[phys_row(page_table, max_pages, num_pages, log2ps, seq, pos)] : 0.f;
+      voff[p] = rel * 4;
+    }
+    const int soff = (int)tile0 * 4;
+
 #pragma unroll 1
     for (int g = 0; g < kPfRows / 8; ++g) {
       if (8 * g >= rows) break;  // uniform
-      // linear term: lin[s][e] = <u of row 8 g + 4 half + e, k8 of this lane's position in subtile s>
-      float lin[kPfSub][4];
+      // linear term of rows 8 g + 4 half + e, arranged per pair p for the lane half that keeps it (linK: the
+      // subtile this half stores) and the half it is sent to (linS)
+      float linK[kPfSub / 2][4], linS[kPfSub / 2][4];
 #pragma unroll
-      for (int s = 0; s < kPfSub; ++s) {
-        v16f acc = {};
+      for (int p = 0; p < kPfSub / 2; ++p) {
+        float lin[2][4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, false);
-          const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, true);
-          const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, false);
-          const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, true);
-          const v8bf kb = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(&u_lds[g][m][lane][0]), kb,
-                                                        acc, 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+          const int s = 2 * p + t;
+          v16f acc = {};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, false);
+            const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, true);
+            const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, false);
+            const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, true);
+            const v8bf kb = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(&u_lds[g][m][lane][0]), kb,
+                                                          acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lin[t][e] = ((acc[12 + e] + acc[8 + e]) + acc[4 + e]) + acc[e];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lin[s][e] = ((acc[12 + e] + acc[8 + e]) + acc[4 + e]) + acc[e];
+        for (int e = 0; e < 4; ++e) {
+          linK[p][e] = half ? lin[1][e] : lin[0][e];
+          linS[p][e] = half ? lin[0][e] : lin[1][e];
+        }
       }
 
 #pragma unroll 1
-      for (int hq = 0; hq < 2; ++hq)
+      for (int hq = 0; hq < 2; ++hq) {
+        const float ownf = hq == half ? 1.f : 0.f;  // this lane half holds the linear term of rows 8 g + 4 hq + e
+        int nq[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qq = 4 * hq + e, q = 8 * g + qq;
-        const int n = q < rows ? n_lds[q] : 0;
-        if (tile0 >= n) continue;  // uniform; also skips rows past the tile's end
-        v8i a[HB];
-        float wq[HB][16];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          a[hb] = *reinterpret_cast<const v8i*>(&a_lds[q][hb][lane][0]);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
+        for (int e = 0; e < 4; ++e) {
+          const int q = 8 * g + 4 * hq + e;
+          nq[e] = q < rows ? __builtin_amdgcn_readfirstlane(n_lds[q]) : 0;
         }
-        float* out = scores + (int64_t)(r0 + q) * ld;
-        const bool owner = hq == half;  // this lane half holds row q's linear term
 #pragma unroll
-        for (int s = 0; s < kPfSub; s += 2) {
-          float ab0 = 0.f, ab1 = 0.f;  // sum_j wq_j |x_j| over this lane half's heads, subtiles s and s + 1
+        for (int e = 0; e < 4; ++e) {
+          const int q = 8 * g + 4 * hq + e;
+          if (tile0 >= nq[e]) continue;  // uniform; also rows past the tile's end
+          v8i a[HB];
+          float wq[HB][16];
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
-            v16f acc0 = {}, acc1 = {};
-            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s], acc0, 0, 0, 0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s + 1], acc1, 0, 0, 0, 0, 0, 0);
+            a[hb] = *reinterpret_cast<const v8i*>(&a_lds[q][hb][lane][0]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              ab0 = fmaf(wq[hb][i], fabsf(acc0[i]), ab0);
-              ab1 = fmaf(wq[hb][i], fabsf(acc1[i]), ab1);
-            }
+            for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
           }
-          // half 0 finishes subtile s and half 1 subtile s + 1; the owner half adds the linear term of both
-          const float l0 = lin[s][e], l1 = lin[s + 1][e];
-          const float keep = owner ? (half ? ab1 + l1 : ab0 + l0) : (half ? ab1 : ab0);
-          const float send = owner ? (half ? ab0 + l0 : ab1 + l1) : (half ? ab0 : ab1);
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
-          const float total = keep + __uint_as_float(half ? sw[0] : sw[1]);
-          const int64_t pos = tile0 + wave * (kPfSub * 32) + (s + half) * 32 + col;
-          if (pos < n) out[pos] = (half ? sk[s + 1] : sk[s]) * (0.5f * total);
+          // stores past the row's visible length fall outside the buffer and are dropped
+          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(r0 + q) * ld, (short)0, nq[e] * 4,
+                                                              kBufferWord3);
+          constexpr int U = 2 * HB;             // units per subtile pair
+          constexpr int K = (kPfSub / 2) * U;   // units per row
+          float ab[2] = {0.f, 0.f};
+          v16f prev = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], b[0], v16f{}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int k = 1; k <= K; ++k) {
+            v16f next;
+            if (k < K) {
+              const int p = k / U, hb = (k % U) >> 1, t = k & 1;
+              next = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[2 * p + t], v16f{}, 0, 0, 0, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+              const int kp = k - 1, p = kp / U, hb = (kp % U) >> 1, t = kp & 1;
+              float acc_ab = hb == 0 ? 0.f : ab[t];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc_ab = fmaf(wq[hb][i], fabsf(prev[i]), acc_ab);
+              ab[t] = acc_ab;
+              if (kp % U == U - 1) {  // pair p complete: half 0 finishes subtile 2p, half 1 subtile 2p + 1
+                const float mine = half ? ab[1] : ab[0], other = half ? ab[0] : ab[1];
+                const float keep = fmaf(ownf, linK[p][e], mine);
+                const float send = fmaf(ownf, linS[p][e], other);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
+                const float total = keep + __uint_as_float(half ? sw[0] : sw[1]);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], soff, 0);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (k < K) prev = next;
+          }
         }
       }
     }
