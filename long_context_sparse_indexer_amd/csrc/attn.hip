@@ -244,6 +244,263 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// bf16 path, all heads of a row per block.  Every head of a row reads the same latent rows (MQA), so a block
+// that owns up to 128 heads gathers each selected row once instead of once per 16-head group.  Wave w owns
+// 32 heads and computes, per 64-slot chunk:
+//   S^T = C Q^T on v_mfma_f32_32x32x16_bf16 with the gathered rows as the A operand (row-contiguous 16-byte
+//       LDS reads) and Q^T held in registers (32 K-steps x 8 bf16).  Lane (half h, column n) then holds 16
+//       slots 8 (i >> 2) + 4 h + (i & 3) of each 32-slot tile for head n, so the online softmax of a head
+//       is an in-lane reduction plus one v_permlane32_swap with the other half.
+//   O += P C with P as the A operand: K-step ks takes slots 16 ks + 4 h + (j & 3) + 8 (j >> 2) for K
+//       position 8 h + j, which is exactly the lane's own probabilities i = 8 (ks & 1) + j of tile ks >> 1,
+//       so P needs no exchange; the B operand is read with ds_read_b64_tr_b16 (four consecutive slots of
+//       one latent column per lane, two reads per K-step).
+// O (32 heads x 512 columns, fp32) is 256 accumulator registers per wave, so one wave runs per SIMD and the
+// next chunk's LDS-DMA gather is kept in flight behind the current chunk's MFMAs.  The 1056-byte LDS row
+// stride leaves both read patterns free of bank conflicts.
+constexpr int kRowW = kDC * 2 + 32;
+constexpr int kWideMaxSplitLen = 2048;  // selection slots one block handles
+
+template <int NW>  // waves per block: 32 * NW heads
+__device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restrict__ kv, const int32_t* prow,
+                                                  int dummy, char* buf, int wave, int lane) {
+  constexpr int kRows = kNC / NW;
+#pragma unroll
+  for (int t = 0; t < kRows; ++t) {
+    const int rr = wave * kRows + t;
+    int pr = prow[rr];
+    if (pr < 0) pr = dummy;
+    const unsigned short* src = kv + (int64_t)pr * kDC + lane * 8;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(buf + rr * kRowW)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  }
+}
+
+template <int NW, bool kSplit>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
+    int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int num_pages, int log2ps, int H, int nsplit, int split_len, float scale_log2, unsigned short* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  static_assert(kNC % NW == 0, "every wave gathers the same number of rows");
+  constexpr int kRows = kNC / NW;  // rows each wave gathers per chunk
+  // wait until only the next chunk's kRows gathers are outstanding; vmcnt counts to 63, so a single wave
+  // (64 gathers per chunk) waits for everything and does not overlap its gathers with compute
+  constexpr int kWaitGather = kRows > 63 ? 0 : (kRows & 15) | ((kRows >> 4) << 14) | (7 << 4) | (15 << 8);
+  __shared__ __attribute__((aligned(16))) char kv_lds0[kNC * kRowW];
+  __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowW];
+  __shared__ int32_t prow_lds[kWideMaxSplitLen];           // physical row of every slot, -1 = no position
+  __shared__ uint32_t valid_lds[kWideMaxSplitLen / 32];    // bit per slot: it has a position
+  __shared__ int first_valid, overflow;
+
+  const int ngroups = H / (32 * NW);
+  const int split = blockIdx.x % nsplit;
+  const int rg = blockIdx.x / nsplit;
+  const int hg = rg % ngroups;
+  const int r = rg / ngroups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int hw = hg * 32 * NW + wave * 32;  // first head of this wave
+
+  // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
+  v8bf qb[kDC / 16];
+  {
+    const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kDC + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
+  }
+  v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
+
+  const int seq = clamp_seq(row_seq[r], num_seqs);
+  const int begin = split * split_len;
+  const int end = min(k, begin + split_len);
+  const int len = max(end - begin, 0);
+  const int nch = (len + kNC - 1) / kNC;
+  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
+
+  if (threadIdx.x == 0) {
+    first_valid = 0x7fffffff;
+    overflow = 0;
+  }
+  __syncthreads();
+  // slots -> physical rows; wave w takes whole 64-slot chunks so that a ballot gives the chunk's validity bits
+  for (int c = wave; c < nch; c += NW) {
+    const int sl = c * kNC + lane;
+    const int pos = sl < len ? idx[sl] : -1;
+    const int pr = pos >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
+    prow_lds[sl] = pr;
+    const uint64_t bits = __ballot(pr >= 0);
+    if (lane == 0) {
+      valid_lds[2 * c] = (uint32_t)bits;
+      valid_lds[2 * c + 1] = (uint32_t)(bits >> 32);
+      if (bits) atomicMin(&first_valid, c * kNC + (int)__builtin_ctzll(bits));
+    }
+  }
+  __syncthreads();
+
+  // Softmax without rescaling O.  Every head accumulates p = 2^(s - m_ref) against a fixed reference: the
+  // largest logit of the first chunk in which it has one.  O and l are then plain sums, and o = O / l,
+  // lse = m_ref + log2 l are exact; probabilities of later, larger logits exceed 1, which fp32 sums and bf16
+  // MFMA operands hold without loss of relative precision.  Only a logit more than kHeadroom above the
+  // reference could overflow; then the block recomputes against the exact maximum of a QK-only pass.
+  constexpr float kHeadroom = 64.f;
+  float m_ref = -INFINITY, l = 0.f;  // of head hw + col (the same in both lane halves)
+  if (first_valid != 0x7fffffff) {
+    const int dummy = prow_lds[first_valid];
+    const int S16 = lane & 15, qh = (lane >> 4) & 1;  // transpose-read lane roles
+    // qk_only: only track the per-head maximum (into m_ref); otherwise accumulate O and l
+    auto chunk = [&](const int c, const char* cur, char* nxt, const bool qk_only) __attribute__((always_inline)) {
+      if (c + 1 < nch) {
+        gather_chunk_wide<NW>(kv, prow_lds + (c + 1) * kNC, dummy, nxt, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitGather);  // chunk c has landed; chunk c + 1 stays in flight
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      lds_barrier();
+      // S^T: tile t = slots 32 t .. +32 (A rows) x this wave's 32 heads (B columns).  The A operands are read
+      // kQkDepth K-steps ahead of their MFMAs; sched_barrier keeps the compiler from hoisting further.
+      v16f st[2] = {v16f{}, v16f{}};
+      {
+        constexpr int kQkDepth = 4;
+        const char* arow = cur + col * kRowW + 16 * half;
+        v8bf abuf[kQkDepth][2];
+#pragma unroll
+        for (int ks = 0; ks < kQkDepth; ++ks)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) abuf[ks][t] = *reinterpret_cast<const v8bf*>(arow + 32 * t * kRowW + 32 * ks);
+#pragma unroll
+        for (int ks = 0; ks < kDC / 16; ++ks) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kQkDepth][t], qb[ks], st[t], 0, 0, 0);
+            if (ks + kQkDepth < kDC / 16)
+              abuf[ks % kQkDepth][t] =
+                  *reinterpret_cast<const v8bf*>(arow + 32 * t * kRowW + 32 * (ks + kQkDepth));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // logits in the log2 domain; slots without a position get -inf
+      const uint32_t vw0 = valid_lds[2 * c], vw1 = valid_lds[2 * c + 1];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[t][i] *= scale_log2;
+      if ((vw0 & vw1) != ~0u) {  // uniform: a chunk with slots that hold no position
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t w = (t ? vw1 : vw0) >> (4 * half);  // bit 8 (i >> 2) + (i & 3) is register i's slot
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            st[t][i] = (w >> (8 * (i >> 2) + (i & 3))) & 1u ? st[t][i] : -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][i]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
+      }
+      if (qk_only) {
+        m_ref = fmaxf(m_ref, mx);
+      } else {
+        if (m_ref == -INFINITY) m_ref = mx;
+        if (mx > m_ref + kHeadroom) overflow = 1;  // any wave; read after the loop
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float rs = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            st[t][i] = exp2f(st[t][i] - m_use);
+            rs += st[t][i];
+          }
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+          rs += __uint_as_float(half ? sw[0] : sw[1]);
+        }
+        l += rs;
+        // O += P C over K-steps of 16 slots; the transposed B reads run kPvDepth MFMAs ahead
+        constexpr int kPvDepth = 4;
+        constexpr int kSteps = (kNC / 16) * (kDC / 32);  // (K-step, column tile) pairs
+        const char* pbase = cur + (4 * half + (S16 >> 2)) * kRowW + (16 * qh + 4 * (S16 & 3)) * 2;
+        auto bread = [&](int u) __attribute__((always_inline)) {
+          const int ks = u / (kDC / 32), dt = u % (kDC / 32);
+          const char* p = pbase + 16 * ks * kRowW + dt * 64;
+          const v4bf lo4 = lds_tr_read(p);
+          const v4bf hi4 = lds_tr_read(p + 8 * kRowW);
+          return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        v8bf bbuf[kPvDepth];
+#pragma unroll
+        for (int u = 0; u < kPvDepth; ++u) bbuf[u] = bread(u);
+        v8bf pa[kNC / 16];
+#pragma unroll
+        for (int ks = 0; ks < kNC / 16; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pa[ks][j] = (__bf16)st[ks >> 1][8 * (ks & 1) + j];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+          const int ks = u / (kDC / 32), dt = u % (kDC / 32);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bbuf[u % kPvDepth], o[dt], 0, 0, 0);
+          if (u + kPvDepth < kSteps) bbuf[u % kPvDepth] = bread(u + kPvDepth);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      lds_barrier();  // every wave is done with `cur` before the next gather overwrites it
+    };
+    // one chunk loop per pass; the gathers are opaque to the compiler's wait insertion (their waits are
+    // explicit), so alternating the buffers at run time costs no extra waits
+    auto run = [&](const bool qk_only) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
+      gather_chunk_wide<NW>(kv, prow_lds, dummy, kv_lds0, wave, lane);
+      for (int c = 0; c < nch; ++c) chunk(c, (c & 1) ? kv_lds1 : kv_lds0, (c & 1) ? kv_lds0 : kv_lds1, qk_only);
+      __syncthreads();
+    };
+#pragma unroll
+    for (int dt = 0; dt < kDC / 32; ++dt) o[dt] = v16f{};
+    run(false);       // reference = each head's first-chunk maximum
+    if (overflow) {  // uniform and rare: exact maxima first, then accumulate against them
+#pragma unroll
+      for (int dt = 0; dt < kDC / 32; ++dt) o[dt] = v16f{};
+      l = 0.f;
+      m_ref = -INFINITY;
+      run(true);
+      run(false);
+    }
+  }
+
+  // finish: normalise O rows by their head's sum (held in lane (0, head))
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int hh = 8 * (i >> 2) + 4 * half + (i & 3);
+    const float inv = __shfl(inv_l, hh, 64);
+    const int64_t orow = (int64_t)r * H + hw + hh;
+#pragma unroll
+    for (int dt = 0; dt < kDC / 32; ++dt) {
+      const int d = 32 * dt + col;
+      const float val = first_valid != 0x7fffffff ? o[dt][i] * inv : 0.f;
+      if (kSplit)
+        part_o[(((int64_t)r * nsplit + split) * H + hw + hh) * kDC + d] = val;
+      else
+        out[orow * kDC + d] = float_to_bf16_bits(val);
+    }
+  }
+  if (half == 0) {
+    const float lz = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+    if (kSplit)
+      part_lse[((int64_t)r * nsplit + split) * H + hw + col] = lz;
+    else if (lse)
+      lse[(int64_t)r * H + hw + col] = lz;
+  }
+}
+
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s.
 // Block (row*H + head, column slice): the split weights are computed once by the first wave.
 constexpr int kMaxSplit = 64;
@@ -350,12 +607,28 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
 struct AttnPlan {
   int nsplit;
   int split_len;
+  int nw;  // > 0: all-heads kernel with nw waves (32 nw heads per block); 0: 16-head kernel
 };
 
 AttnPlan plan(const Geo& g) {
   const int chunks = std::max(1, (g.k + kNC - 1) / kNC);
-  AttnPlan p{1, chunks * kNC};
+  AttnPlan p{1, chunks * kNC, 0};
   if (g.kv_dtype != 1 /* BF16 */) return p;
+  const int nw = g.H % 128 == 0 ? 4 : g.H % 64 == 0 ? 2 : 1;  // waves per block divide the 64 gathers of a chunk
+  if (g.H % 32 == 0 && (int64_t)g.R * (g.H / (32 * nw)) * chunks >= 128) {
+    // all-heads kernel: one block per (row, head group of <= 128, split), one block per CU at a time; split
+    // the selection only as far as needed to give every CU a block.  With fewer than 128 (row, group, chunk)
+    // units it could not spread over the chip, and the 16-head kernel below runs instead.
+    p.nw = nw;
+    const int64_t groups = (int64_t)g.R * (g.H / (32 * p.nw));
+    const int min_split = (chunks * kNC + kWideMaxSplitLen - 1) / kWideMaxSplitLen;
+    int64_t want = (256 + groups - 1) / groups;
+    int nsplit = (int)std::max<int64_t>(min_split, std::min<int64_t>(want, std::min(chunks, kMaxSplit)));
+    const int per = (chunks + nsplit - 1) / nsplit;
+    p.nsplit = (chunks + per - 1) / per;
+    p.split_len = per * kNC;
+    return p;
+  }
   // a block handles at most kMaxSplitLen slots; below ~2 blocks per CU the selection is split further into
   // pieces of about kChunksPerSplitSmallBatch chunks (double buffering needs a few), at most kMaxSplit of them
   const int64_t groups = (int64_t)g.R * (g.H / kHG);
@@ -369,6 +642,21 @@ AttnPlan plan(const Geo& g) {
   p.nsplit = nsplit;
   p.split_len = per * kNC;
   return p;
+}
+
+template <int NW>
+void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const unsigned short* kp,
+                const int32_t* topk_idx, void* out, float* lse, float* part_o, float* part_lse, float scale_log2,
+                hipStream_t stream) {
+  const int nblocks = g.R * (g.H / (32 * NW)) * p.nsplit;
+  if (p.nsplit == 1)
+    attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
+        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
+        p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr);
+  else
+    attn_bf16_mqa_kernel<NW, true><<<nblocks, NW * 64, 0, stream>>>(
+        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, p.nsplit,
+        p.split_len, scale_log2, nullptr, nullptr, part_o, part_lse);
 }
 
 }  // namespace
@@ -385,24 +673,35 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
   if (g.kv_dtype == 1 /* BF16 */) {
     const AttnPlan p = plan(g);
     const float scale_log2 = g.softmax_scale * kLog2e;
-    const int nblocks = g.R * (g.H / kHG) * p.nsplit;
     auto* qp = static_cast<const unsigned short*>(q);
     auto* kp = static_cast<const unsigned short*>(kv_pool);
-    if (p.nsplit == 1) {
-      attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
-                                                           g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1, p.split_len,
-                                                           scale_log2, static_cast<unsigned short*>(out), lse,
-                                                           nullptr, nullptr);
+    float* part_o = static_cast<float*>(workspace);
+    float* part_lse = p.nsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                             align_up(sizeof(float) * (size_t)g.R * p.nsplit * g.H * g.d_c))
+                                   : nullptr;
+    if (p.nw > 0) {
+      switch (p.nw) {
+        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
+        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
+        default: launch_mqa<4>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
+      }
     } else {
-      float* part_o = static_cast<float*>(workspace);
-      float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                 align_up(sizeof(float) * (size_t)g.R * p.nsplit * g.H * g.d_c));
-      attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
-                                                          g.S, g.max_pages, g.num_pages, g.log2ps, g.H, p.nsplit,
-                                                          p.split_len, scale_log2, nullptr, nullptr, part_o, part_lse);
-      attn_combine_kernel<true><<<dim3(g.R * g.H, (g.d_c + 255) / 256), 256, 0, stream>>>(part_o, part_lse, g.H, g.d_c,
-                                                                                       p.nsplit, out, lse);
+      const int nblocks = g.R * (g.H / kHG) * p.nsplit;
+      if (p.nsplit == 1)
+        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
+                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
+                                                             p.split_len, scale_log2,
+                                                             static_cast<unsigned short*>(out), lse, nullptr,
+                                                             nullptr);
+      else
+        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
+                                                            g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
+                                                            p.nsplit, p.split_len, scale_log2, nullptr, nullptr,
+                                                            part_o, part_lse);
     }
+    if (p.nsplit > 1)
+      attn_combine_kernel<true><<<dim3(g.R * g.H, (g.d_c + 255) / 256), 256, 0, stream>>>(part_o, part_lse, g.H,
+                                                                                       g.d_c, p.nsplit, out, lse);
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
     attn_f32_kernel<<<g.R * g.H, 256, lds, stream>>>(static_cast<const float*>(q), static_cast<const float*>(kv_pool),

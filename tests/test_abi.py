@@ -134,8 +134,9 @@ def test_workspace_query_errors_and_strings():
         dsa.dsa_workspace_bytes(_problem(topk=0), dsa.DSA_OP_TOPK)
     with pytest.raises(dsa.DsaError):
         dsa.dsa_workspace_bytes(_problem(), 99)
-    # attention of many rows needs no split buffers: 0 bytes with no error
-    assert dsa.dsa_workspace_bytes(_problem(num_rows=64), dsa.DSA_OP_ATTN) == 0
+    # attention of enough rows to give every CU a block needs no split buffers: 0 bytes with no error
+    assert dsa.dsa_workspace_bytes(_problem(num_rows=256), dsa.DSA_OP_ATTN) == 0
+    assert dsa.dsa_workspace_bytes(_problem(num_rows=1), dsa.DSA_OP_ATTN) > 0
     for s in range(5):
         assert dsa.dsa_status_str(s).startswith("DSA_")
     assert "unknown" in dsa.dsa_status_str(42)

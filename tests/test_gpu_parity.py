@@ -97,6 +97,21 @@ def test_prefill_rows_through_the_per_row_kernel():
     _run(synth.get("prefill_paged", rows=20, H=16), fields=dict(rows_per_seq=1))
 
 
+@pytest.mark.parametrize("H", [96, 256])
+def test_attention_head_counts(H):
+    # 96 heads: three 32-head waves per block; 256 heads: two head groups of 128 per row
+    _run(synth.get("batched_paged", batch=2, length_range=(2500, 5000), H=H, anchors=16, recent=32))
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_attention_wide_logit_range(batch):
+    # logits spanning hundreds of units.  One row runs the 16-head kernel (online rescaling); four rows run
+    # the all-heads kernel, where a later chunk's maximum far above the first chunk's forces the recompute
+    # against exact per-head maxima
+    _run(synth.get("batched_paged", batch=batch, length_range=(6000, 9000), softmax_scale=60.0, anchors=16,
+                   recent=32))
+
+
 def test_paged_equals_contiguous_bit_for_bit():
     cfg = synth.get("batched_paged", batch=3, length_range=(2500, 7000), H=32)
     a = gpu_step(synth.make_problem(cfg))
