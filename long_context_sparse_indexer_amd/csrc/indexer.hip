@@ -20,6 +20,8 @@
 // In the fused step the epilogue also starts the top-k selection: each block histograms the first 12 bits
 // of its scores' order-preserving keys in LDS and merges the non-empty bins into the row's histogram (see
 // topk.hip).  The key loads are issued before the query operands so that both are in flight together.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -27,6 +29,11 @@
 namespace dsa {
 namespace {
 
+constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource word 3 on gfx9: 32-bit, range-checked
+
+// An empty use of a loaded value: the compiler waits for the load here, once, instead of at a later use whose
+// wait it would place inside a loop.
+__device__ __forceinline__ void require_loaded(const v8i& x) { asm volatile("" ::"v"(x)); }
 constexpr int kIdxSub = 4;                          // 32-position subtiles per wave
 constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread block
 
@@ -36,13 +43,14 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, int k,
-    uint32_t* __restrict__ hist1, int copies) {
+    uint32_t* __restrict__ hist1, int copies, int tiles_per_block) {
   constexpr int H_I = 32 * HB;
   __shared__ uint32_t h[kHist ? kTopkBins : 1];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
-  const int64_t tile0 = (int64_t)blockIdx.x * kIdxTile;
-  if (tile0 >= n) return;
+  const int64_t first = (int64_t)blockIdx.x * tiles_per_block * kIdxTile;
+  if (first >= n) return;
+  const int ntile = (int)min((int64_t)tiles_per_block, (n - first + kIdxTile - 1) / kIdxTile);
   const bool do_hist = kHist && k < n;  // uniform over the block; a row with k >= n keeps every position
   if (do_hist) {
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) h[i] = 0u;
@@ -52,25 +60,45 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
 
-  int64_t prow[kIdxSub];
+  // Tile t of the block covers positions first + 512 t .. +512; wave w owns 128 of them as four 32-position
+  // subtiles s.  A 32-aligned subtile lies in one page (pages hold >= 32 positions), so its page id is one
+  // scalar load; lanes past the row's end use the last position instead (their scores are never stored), so
+  // every key load is unconditional and stays in flight instead of waiting in a divergent branch.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto position = [&](int t, int s) { return first + (int64_t)t * kIdxTile + wave * (kIdxSub * 32) + s * 32 + col; };
+  // pool row of lane `col` in subtile s of tile t: one scalar page lookup per subtile; a lane past the row's
+  // end takes the row's last position (same 32-aligned block, so the same page)
+  auto subtile_rows = [&](int t, int s) -> int64_t {
+    const int64_t base = first + (int64_t)t * kIdxTile + wave_u * (kIdxSub * 32) + s * 32;  // uniform
+    const int64_t b = base < n ? base : n - 1;
+    const int lp = (int)min(b >> log2ps, (int64_t)max_pages - 1);
+    int page = page_table[(int64_t)seq * max_pages + lp];
+    page = min(max(page, 0), num_pages - 1);
+    const int64_t row0 = ((int64_t)page << log2ps) | (b & ((1 << log2ps) - 1));
+    return row0 + (base < n ? min((int64_t)col, n - 1 - base) : 0);
+  };
+  // per tile and lane: the key rows of the four subtiles (MFMA B operands) and the scales of the two positions
+  // the lane stores (subtile 2 p + half of each pair p)
+  struct TileLoad {
+    v8i b[kIdxSub];
+    float skm[kIdxSub / 2];
+  };
+  auto issue = [&](int t, TileLoad& L) __attribute__((always_inline)) {
+    int64_t prow[kIdxSub];
 #pragma unroll
-  for (int s = 0; s < kIdxSub; ++s) {
-    const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
-    prow[s] = pos < n ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
-  }
-  v8i b[kIdxSub];
-  float sk[kIdxSub];
+    for (int s = 0; s < kIdxSub; ++s) prow[s] = subtile_rows(t, s);
 #pragma unroll
-  for (int s = 0; s < kIdxSub; ++s) {
-    if (prow[s] >= 0) {
-      b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
-      sk[s] = k_scale[prow[s]];
-    } else {
-      b[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      sk[s] = 0.f;
+    for (int s = 0; s < kIdxSub; ++s) L.b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
+#pragma unroll
+    for (int p = 0; p < kIdxSub / 2; ++p) {
+      // the store subtile's row, picked arithmetically (an indexed pick would put prow in scratch)
+      const int64_t srow = prow[2 * p] + (prow[2 * p + 1] - prow[2 * p]) * half;
+      L.skm[p] = k_scale[srow];
     }
-  }
+  };
 
+  TileLoad cur;
+  issue(0, cur);
   v8i a[HB];
   float wq[HB][16];
 #pragma unroll
@@ -82,30 +110,55 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
       wq[hb][i] = head_w[(int64_t)r * H_I + head] * q_scale[(int64_t)r * H_I + head];
     }
   }
+  // the row's query operands are complete before the loop (an asm use makes the compiler wait here once
+  // instead of inside every iteration)
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) require_loaded(a[hb]);
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)r * ld, (short)0, n * 4, kBufferWord3);
 
+  auto compute = [&](int t, const TileLoad& cur) __attribute__((always_inline)) {
 #pragma unroll
-  for (int s = 0; s < kIdxSub; ++s) {
-    // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
-    // fmaxf would also need a NaN-quieting max
-    float lin = 0.f, ab = 0.f;
+    for (int p = 0; p < kIdxSub / 2; ++p) {
+      // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
+      // fmaxf would also need a NaN-quieting max
+      float part[2];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      v16f acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[s], acc, 0, 0, 0, 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        float lin = 0.f, ab = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        lin = fmaf(wq[hb][i], acc[i], lin);
-        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+        for (int hb = 0; hb < HB; ++hb) {
+          v16f acc = {};
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], cur.b[2 * p + u], acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            lin = fmaf(wq[hb][i], acc[i], lin);
+            ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+          }
+        }
+        part[u] = lin + ab;
       }
+      // half 0 finishes subtile 2 p and half 1 subtile 2 p + 1: one exchange per pair
+      const float keep = half ? part[1] : part[0];
+      const float send = half ? part[0] : part[1];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
+      const float v = cur.skm[p] * (0.5f * (keep + __uint_as_float(half ? sw[0] : sw[1])));
+      const int64_t pos = position(t, 2 * p + half);
+      // the buffer ends at the row's visible length: stores past it are dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)pos * 4, 0, 0);
+      if (do_hist && pos < n) atomicAdd(&h[order_key(v) >> 20], 1u);
     }
-    float part = lin + ab;
-    part += __shfl_xor(part, 32, 64);
-    const int64_t pos = tile0 + (s * 4 + wave) * 32 + col;
-    if (half == 0 && pos < n) {
-      const float v = sk[s] * (0.5f * part);
-      scores[(int64_t)r * ld + pos] = v;
-      if (do_hist) atomicAdd(&h[order_key(v) >> 20], 1u);
-    }
+  };
+
+  // Two tile buffers in turn: the keys of tile t + 1 are requested before tile t is computed, so a block keeps
+  // a tile in flight, and a buffer is reloaded only after its tile is done (no copies between them).
+  TileLoad other;
+#pragma unroll 1
+  for (int t = 0; t < ntile; t += 2) {
+    if (t + 1 < ntile) issue(t + 1, other);
+    compute(t, cur);
+    if (t + 1 >= ntile) break;
+    if (t + 2 < ntile) issue(t + 2, cur);
+    compute(t + 1, other);
   }
   if (do_hist) {
     __syncthreads();
@@ -144,7 +197,6 @@ constexpr int kPfRows = 8;                // query rows per block: one group of 
 constexpr int kPfSub = 4;                 // 32-position subtiles per wave
 constexpr int kPfTile = 4 * kPfSub * 32;  // positions per pass of a 256-thread block
 constexpr int kPfPasses = 8;              // passes per block: the row staging is paid once per 4096 positions
-constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource word 3 on gfx9: 32-bit, range-checked
 
 template <int HB>
 __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
@@ -405,12 +457,18 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 }  // namespace
 
 template <int HB, bool kHist>
-void launch_f8(const Geo& g, dim3 grid, const uint8_t* qp, const float* q_idx_scale, const float* head_w,
-               const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse,
-               hipStream_t stream) {
+void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w, const uint8_t* kp,
+               const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse, hipStream_t stream) {
+  // one 512-position tile per block while that gives fewer than ~2 blocks per CU (latency-bound small
+  // problems spread as wide as they can); beyond that a block streams several tiles so that each keeps a tile
+  // of keys in flight
+  const int tiles_row = (g.max_row_len + kIdxTile - 1) / kIdxTile;
+  const int64_t tiles = (int64_t)tiles_row * g.R;
+  const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / 1024));
+  dim3 grid((tiles_row + per - 1) / per, g.R);
   indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->copies : 1);
+      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->copies : 1, per);
 }
 
 template <int HB>
@@ -439,15 +497,14 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
     return hipGetLastError();
   }
   if (g.idx_dtype == 2 /* F8E4M3 */) {
-    dim3 grid((g.max_row_len + kIdxTile - 1) / kIdxTile, g.R);
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
     if (g.H_I == 64) {
-      if (fuse) launch_f8<2, true>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-      else launch_f8<2, false>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      if (fuse) launch_f8<2, true>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      else launch_f8<2, false>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
     } else {
-      if (fuse) launch_f8<1, true>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-      else launch_f8<1, false>(g, grid, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      if (fuse) launch_f8<1, true>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      else launch_f8<1, false>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
     }
   } else {
     dim3 grid((g.max_row_len + 255) / 256, g.R);
