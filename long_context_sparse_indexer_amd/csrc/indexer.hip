@@ -459,12 +459,13 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 template <int HB, bool kHist>
 void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w, const uint8_t* kp,
                const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse, hipStream_t stream) {
-  // one 512-position tile per block while that gives fewer than ~2 blocks per CU (latency-bound small
-  // problems spread as wide as they can); beyond that a block streams several tiles so that each keeps a tile
-  // of keys in flight
+  // one 512-position tile per block up to kIdxTargetBlocks blocks (small, latency-bound problems spread as
+  // wide as they can); beyond that a block streams several tiles so that each keeps a tile of keys in flight.
+  // 4096 blocks (about 5 rounds of 3 blocks per CU) measured best on 8 x 1M and 64 x 40K rows.
+  constexpr int kIdxTargetBlocks = 4096;
   const int tiles_row = (g.max_row_len + kIdxTile - 1) / kIdxTile;
   const int64_t tiles = (int64_t)tiles_row * g.R;
-  const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / 1024));
+  const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / kIdxTargetBlocks));
   dim3 grid((tiles_row + per - 1) / per, g.R);
   indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,

@@ -15,6 +15,8 @@
 //            (k + one bin's worth) in position order in LDS, settles digit 3 among the few keys of (b1, b2),
 //            and writes the selection with a two-pass wave-ballot compaction.  A row whose candidates overflow
 //            the list (heavily tied scores) is resolved over its whole stored score row instead.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -75,23 +77,28 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
   }
 }
 
-// First-digit histogram of stored scores (standalone top-k): one block per 4096-score chunk.
+// First-digit histogram of stored scores (standalone top-k): a block covers `cpb` consecutive 4096-score
+// chunks of one row, accumulates them in LDS and merges once.
 __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                          const int32_t* __restrict__ row_len, int max_row_len, int k,
-                                                         uint32_t* __restrict__ hist1, int copies) {
+                                                         uint32_t* __restrict__ hist1, int copies, int cpb) {
   __shared__ uint32_t h[kTopkBins];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
-  const int nblk = (n + kCh - 1) / kCh;
-  if (min(k, n) >= n || (int)blockIdx.x >= nblk) return;  // nothing to choose, or a chunk past the row's end
+  const int nchunk = (n + kCh - 1) / kCh;
+  const int c0 = (int)blockIdx.x * cpb;
+  if (min(k, n) >= n || c0 >= nchunk) return;  // nothing to choose, or chunks past the row's end
   for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h[i] = 0u;
   __syncthreads();
-  uint32_t key[kEpt];
-  bool valid[kEpt];
-  load_keys(scores + (int64_t)r * ld, (int64_t)blockIdx.x * kCh + threadIdx.x * kEpt, n, key, valid);
+  const int c1 = min(nchunk, c0 + cpb);
+  for (int c = c0; c < c1; ++c) {
+    uint32_t key[kEpt];
+    bool valid[kEpt];
+    load_keys(scores + (int64_t)r * ld, (int64_t)c * kCh + threadIdx.x * kEpt, n, key, valid);
 #pragma unroll
-  for (int e = 0; e < kEpt; ++e)
-    if (valid[e]) atomicAdd(&h[key[e] >> 20], 1u);
+    for (int e = 0; e < kEpt; ++e)
+      if (valid[e]) atomicAdd(&h[key[e] >> 20], 1u);
+  }
   __syncthreads();
   hist_merge<kTpb>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
 }
@@ -244,45 +251,52 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
                                                            uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
                                                            uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
-                                                           int nblk_max, int copies) {
+                                                           int nblk_max, int copies, int cpb) {
   __shared__ uint32_t scan[kTpb / 64 + 1];
   __shared__ uint32_t seg_base, s_b1, s_A1;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
-  const int nblk = (n + kCh - 1) / kCh;
-  if (keff >= n || (int)blockIdx.x >= nblk) return;
-  const int64_t first = (int64_t)blockIdx.x * kCh + threadIdx.x * kEpt;
-  uint32_t key[kEpt];
-  bool valid[kEpt];
-  load_keys(scores + (int64_t)r * ld, first, n, key, valid);
-  // every block finds b1 itself (a 16 KiB read) instead of waiting for one block to publish it
+  const int nchunk = (n + kCh - 1) / kCh;
+  const int c0 = (int)blockIdx.x * cpb;
+  if (keff >= n || c0 >= nchunk) return;
+  // every block finds b1 itself (a read of the row's histogram replicas) instead of waiting for one block to
+  // publish it; a block covers several chunks when the row has many
   threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
   const uint32_t b1 = s_b1;
   if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
   uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
-  uint32_t c = 0;
+  const int c1 = min(nchunk, c0 + cpb);
+  for (int ch = c0; ch < c1; ++ch) {
+    const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
+    uint32_t key[kEpt];
+    bool valid[kEpt];
+    load_keys(scores + (int64_t)r * ld, first, n, key, valid);
+    uint32_t c = 0;
 #pragma unroll
-  for (int e = 0; e < kEpt; ++e) {
-    const uint32_t d1 = key[e] >> 20;
-    if (valid[e] && d1 >= b1) {
-      ++c;
-      if (d1 == b1) atomicAdd(&h2[(key[e] >> 8) & 0xfffu], 1u);
+    for (int e = 0; e < kEpt; ++e) {
+      const uint32_t d1 = key[e] >> 20;
+      if (valid[e] && d1 >= b1) {
+        ++c;
+        if (d1 == b1) atomicAdd(&h2[(key[e] >> 8) & 0xfffu], 1u);
+      }
     }
-  }
-  uint32_t total;
-  const uint32_t off = block_exclusive_scan(c, scan, total);
-  if (threadIdx.x == 0) {
-    seg_base = atomicAdd(&cnt[4 * r + 2], total);
-    seg_cnt[(int64_t)r * nblk_max + blockIdx.x] = total;
-    seg_off[(int64_t)r * nblk_max + blockIdx.x] = seg_base;
-  }
-  __syncthreads();
-  if (seg_base + total <= (uint32_t)kCap) {  // on overflow the resolve kernel rescans the row
-    uint64_t* dst = cand + (int64_t)r * kCap + seg_base + off;
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(c, scan, total);
+    if (threadIdx.x == 0) {
+      seg_base = atomicAdd(&cnt[4 * r + 2], total);
+      seg_cnt[(int64_t)r * nblk_max + ch] = total;
+      seg_off[(int64_t)r * nblk_max + ch] = seg_base;
+    }
+    __syncthreads();
+    const uint32_t base = seg_base;
+    if (base + total <= (uint32_t)kCap) {  // on overflow the resolve kernel rescans the row
+      uint64_t* dst = cand + (int64_t)r * kCap + base + off;
 #pragma unroll
-    for (int e = 0; e < kEpt; ++e)
-      if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
+      for (int e = 0; e < kEpt; ++e)
+        if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
+    }
+    __syncthreads();  // seg_base and the scan words are reused by the next chunk
   }
 }
 
@@ -379,15 +393,23 @@ hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Chunks per histogram / filter block: at most 32 blocks per row (each filter block re-reads the row's
+// histogram replicas to find the threshold) and about 2048 blocks overall for large batches.
+int chunks_per_block(const Geo& g, int nblk) {
+  const int64_t total = (int64_t)nblk * g.R;
+  return (int)std::min<int64_t>(nblk, std::max<int64_t>({1, (nblk + 31) / 32, total / 2048}));
+}
+
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
                               bool hist_done, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
-  dim3 grid(w.nblk, g.R);
+  const int cpb = chunks_per_block(g, w.nblk);
+  dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
   if (!hist_done)
-    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.copies);
+    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.copies, cpb);
   topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
-                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies);
+                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies, cpb);
   topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,
                                                 w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
   return hipGetLastError();
