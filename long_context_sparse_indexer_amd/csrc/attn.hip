@@ -250,16 +250,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 // 32 heads and computes, per 64-slot chunk:
 //   S^T = C Q^T on v_mfma_f32_32x32x16_bf16 with the gathered rows as the A operand (row-contiguous 16-byte
 //       LDS reads) and Q^T held in registers (32 K-steps x 8 bf16).  Lane (half h, column n) then holds 16
-//       slots 8 (i >> 2) + 4 h + (i & 3) of each 32-slot tile for head n, so the online softmax of a head
-//       is an in-lane reduction plus one v_permlane32_swap with the other half.
-//   O += P C with P as the A operand: K-step ks takes slots 16 ks + 4 h + (j & 3) + 8 (j >> 2) for K
-//       position 8 h + j, which is exactly the lane's own probabilities i = 8 (ks & 1) + j of tile ks >> 1,
-//       so P needs no exchange; the B operand is read with ds_read_b64_tr_b16 (four consecutive slots of
-//       one latent column per lane, two reads per K-step).
+//       S^T rows 8 (i >> 2) + 4 h + (i & 3) of each 32-slot tile for head n, so the softmax of a head is an
+//       in-lane reduction plus one v_permlane32_swap with the other half.
+//   O += P C with P as the A operand: K position 8 h + j of K-step ks is S^T row 16 ks + 4 h + (j & 3) +
+//       8 (j >> 2), which is exactly the lane's own probability i = 8 (ks & 1) + j of tile ks >> 1, so P
+//       needs no exchange; the B operand is read with ds_read_b64_tr_b16 (four slots of one latent column
+//       per lane, two reads per K-step).
 // O (32 heads x 512 columns, fp32) is 256 accumulator registers per wave, so one wave runs per SIMD and the
-// next chunk's LDS-DMA gather is kept in flight behind the current chunk's MFMAs.  The 1056-byte LDS row
-// stride leaves both read patterns free of bank conflicts.
-constexpr int kRowW = kDC * 2 + 32;
+// next chunk's LDS-DMA gather is kept in flight behind the current chunk's MFMAs.
+//
+// LDS bank conflicts (32 four-byte banks): the LDS row stride is 1040 bytes (260 dwords, 4 mod 32), and the
+// QK A operand of lane m reads row 8 (m >> 3) + tau(m & 7), tau = {0,2,4,6,1,3,5,7}.  Eight consecutive
+// lanes then read rows whose 16-byte pieces start 4 tau(x) banks apart, and the four rows behind one
+// transpose read (slots 4 h + e of a K-step become rows 2 e + h) start 8 banks apart; both patterns are
+// conflict-free.  The permutation is only a relabelling of which slot each S^T row holds.
+constexpr int kRowW = kDC * 2 + 16;
 constexpr int kWideMaxSplitLen = 2048;  // selection slots one block handles
 
 template <int NW>  // waves per block: 32 * NW heads
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
       v16f st[2] = {v16f{}, v16f{}};
       {
         constexpr int kQkDepth = 4;
-        const char* arow = cur + col * kRowW + 16 * half;
+        const char* arow = cur + (8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1)) * kRowW + 16 * half;
         v8bf abuf[kQkDepth][2];
 #pragma unroll
         for (int ks = 0; ks < kQkDepth; ++ks)
@@ -391,10 +396,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
       if ((vw0 & vw1) != ~0u) {  // uniform: a chunk with slots that hold no position
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const uint32_t w = (t ? vw1 : vw0) >> (4 * half);  // bit 8 (i >> 2) + (i & 3) is register i's slot
+          const uint32_t w = (t ? vw1 : vw0) >> half;  // register i holds row 8 (i >> 2) + 2 (i & 3) + half
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            st[t][i] = (w >> (8 * (i >> 2) + (i & 3))) & 1u ? st[t][i] : -INFINITY;
+            st[t][i] = (w >> (8 * (i >> 2) + 2 * (i & 3))) & 1u ? st[t][i] : -INFINITY;
         }
       }
       float mx = -INFINITY;
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         // O += P C over K-steps of 16 slots; the transposed B reads run kPvDepth MFMAs ahead
         constexpr int kPvDepth = 4;
         constexpr int kSteps = (kNC / 16) * (kDC / 32);  // (K-step, column tile) pairs
-        const char* pbase = cur + (4 * half + (S16 >> 2)) * kRowW + (16 * qh + 4 * (S16 & 3)) * 2;
+        const char* pbase = cur + (2 * (S16 >> 2) + half) * kRowW + (16 * qh + 4 * (S16 & 3)) * 2;
         auto bread = [&](int u) __attribute__((always_inline)) {
           const int ks = u / (kDC / 32), dt = u % (kDC / 32);
           const char* p = pbase + 16 * ks * kRowW + dt * 64;
@@ -502,10 +507,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s.
-// Block (row*H + head, column slice): the split weights are computed once by the first wave.
+// One 128-thread block per (row, head); the first wave computes the normalised split weights, then every
+// thread combines four adjacent columns with 16-byte loads, all splits' loads in flight together.
 constexpr int kMaxSplit = 64;
 template <bool kBf16Out>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse, int H, int d_c,
                                                            int nsplit, void* __restrict__ out, float* __restrict__ lse) {
   __shared__ float wts[kMaxSplit];
@@ -518,27 +524,38 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
     const float wsum = wave_sum(w);
     wts[s] = wsum > 0.f ? w / wsum : 0.f;
-    if (s == 0 && lse && blockIdx.y == 0) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+    if (s == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
   __syncthreads();
-  const int d = blockIdx.y * blockDim.x + threadIdx.x;
-  if (d >= d_c) return;
-  const float* src = part_o + ((int64_t)r * nsplit * H + h) * d_c + d;
   const int64_t stride = (int64_t)H * d_c;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= nsplit; s += 8) {
-    float v[8];
+  const float* src = part_o + ((int64_t)r * nsplit * H + h) * d_c;
+  for (int d = 4 * threadIdx.x; d < d_c; d += 4 * 128) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      v4f v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = src[(s + j) * stride];
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const v4f*>(src + (s + j) * stride + d);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + j], v[j], acc);
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[s + j], v[j][e], acc[e]);
+    }
+    for (; s < nsplit; ++s) {
+      const v4f v = *reinterpret_cast<const v4f*>(src + s * stride + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[s], v[e], acc[e]);
+    }
+    const int64_t o = ((int64_t)r * H + h) * d_c + d;
+    if (kBf16Out) {
+      v4s b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = (short)float_to_bf16_bits(acc[e]);
+      *reinterpret_cast<v4s*>(static_cast<unsigned short*>(out) + o) = b;  // 8-byte aligned: d is a multiple of 4
+    } else {
+      *reinterpret_cast<v4f*>(static_cast<float*>(out) + o) = acc;
+    }
   }
-  for (; s < nsplit; ++s) acc = fmaf(wts[s], src[s * stride], acc);
-  if (kBf16Out)
-    static_cast<unsigned short*>(out)[((int64_t)r * H + h) * d_c + d] = float_to_bf16_bits(acc);
-  else
-    static_cast<float*>(out)[((int64_t)r * H + h) * d_c + d] = acc;
 }
 
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
@@ -700,8 +717,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                             part_o, part_lse);
     }
     if (p.nsplit > 1)
-      attn_combine_kernel<true><<<dim3(g.R * g.H, (g.d_c + 255) / 256), 256, 0, stream>>>(part_o, part_lse, g.H,
-                                                                                       g.d_c, p.nsplit, out, lse);
+      attn_combine_kernel<true><<<g.R * g.H, 128, 0, stream>>>(part_o, part_lse, g.H, g.d_c, p.nsplit, out, lse);
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
     attn_f32_kernel<<<g.R * g.H, 256, lds, stream>>>(static_cast<const float*>(q), static_cast<const float*>(kv_pool),
