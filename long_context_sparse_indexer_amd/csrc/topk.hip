@@ -58,23 +58,14 @@ __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ h
   if (threadIdx.x == 0) reinterpret_cast<v4i*>(cnt)[r] = z;
 }
 
-// Loads the kEpt consecutive scores of this thread as keys; positions >= n give valid = false.
-__device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t first, int n, uint32_t (&key)[kEpt],
-                                          bool (&valid)[kEpt]) {
-  if (first + kEpt <= n) {
-#pragma unroll
-    for (int v = 0; v < kEpt / 4; ++v) {
-      const v4f x = *reinterpret_cast<const v4f*>(row + first + 4 * v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { key[4 * v + e] = order_key(x[e]); valid[4 * v + e] = true; }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) {
-      valid[e] = first + e < n;
-      key[e] = valid[e] ? order_key(row[first + e]) : 0u;
-    }
-  }
+// The kEpt = 4 consecutive scores of this thread in chunk c, as one 16-byte load with no branch: the row's
+// stride is a multiple of 4 and at least n, so a 4-aligned offset below n can always be read whole; past the
+// row's end offset 0 is read instead and the values are marked invalid where they are used.  Keeping the raw
+// load apart from the key conversion lets a chunk's load stay in flight while the previous one is processed.
+static_assert(kEpt == 4, "one 16-byte load per thread and chunk");
+__device__ __forceinline__ v4f load_raw(const float* __restrict__ row, int c, int n) {
+  const int64_t f = (int64_t)c * kCh + threadIdx.x * kEpt;
+  return *reinterpret_cast<const v4f*>(row + (f < n ? f : 0));
 }
 
 // First-digit histogram of stored scores (standalone top-k): a block covers `cpb` consecutive 4096-score
@@ -91,13 +82,21 @@ __global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict
   for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h[i] = 0u;
   __syncthreads();
   const int c1 = min(nchunk, c0 + cpb);
-  for (int c = c0; c < c1; ++c) {
-    uint32_t key[kEpt];
-    bool valid[kEpt];
-    load_keys(scores + (int64_t)r * ld, (int64_t)c * kCh + threadIdx.x * kEpt, n, key, valid);
+  const float* row = scores + (int64_t)r * ld;
+  auto count = [&](int c, const v4f& x) __attribute__((always_inline)) {
+    const int64_t f = (int64_t)c * kCh + threadIdx.x * kEpt;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e)
-      if (valid[e]) atomicAdd(&h[key[e] >> 20], 1u);
+      if (f + e < n) atomicAdd(&h[order_key(x[e]) >> 20], 1u);
+  };
+  // two buffers in turn: chunk c + 1 is loading while chunk c is counted
+  v4f xa = load_raw(row, c0, n), xb;
+  for (int c = c0; c < c1; c += 2) {
+    if (c + 1 < c1) xb = load_raw(row, c + 1, n);
+    count(c, xa);
+    if (c + 1 >= c1) break;
+    if (c + 2 < c1) xa = load_raw(row, c + 2, n);
+    count(c + 1, xb);
   }
   __syncthreads();
   hist_merge<kTpb>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
@@ -267,14 +266,16 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
   uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
   const int c1 = min(nchunk, c0 + cpb);
-  for (int ch = c0; ch < c1; ++ch) {
+  const float* row = scores + (int64_t)r * ld;
+  auto filter = [&](int ch, const v4f& x) __attribute__((always_inline)) {
     const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
     uint32_t key[kEpt];
     bool valid[kEpt];
-    load_keys(scores + (int64_t)r * ld, first, n, key, valid);
     uint32_t c = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
+      valid[e] = first + e < n;
+      key[e] = order_key(x[e]);
       const uint32_t d1 = key[e] >> 20;
       if (valid[e] && d1 >= b1) {
         ++c;
@@ -297,6 +298,15 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
         if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
     }
     __syncthreads();  // seg_base and the scan words are reused by the next chunk
+  };
+  // two buffers in turn: chunk c + 1 is loading while chunk c is filtered
+  v4f xa = load_raw(row, c0, n), xb;
+  for (int ch = c0; ch < c1; ch += 2) {
+    if (ch + 1 < c1) xb = load_raw(row, ch + 1, n);
+    filter(ch, xa);
+    if (ch + 1 >= c1) break;
+    if (ch + 2 < c1) xa = load_raw(row, ch + 2, n);
+    filter(ch + 1, xb);
   }
 }
 
