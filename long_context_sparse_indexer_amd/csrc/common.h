@@ -81,10 +81,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   uint32_t x = wave_exclusive_scan(v, wt);
   if (lane == 0) scratch[wave] = wt;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nwaves; ++w) { uint32_t t = scratch[w]; scratch[w] = run; run += t; }
-    scratch[nwaves] = run;
+  if (wave == 0) {  // the wave totals, scanned by one wave (at most 64 waves per block)
+    const uint32_t t = lane < nwaves ? scratch[lane] : 0u;
+    uint32_t run;
+    const uint32_t ex = wave_exclusive_scan(t, run);
+    if (lane < nwaves) scratch[lane] = ex;
+    if (lane == 0) scratch[nwaves] = run;
   }
   __syncthreads();
   x += scratch[wave];

@@ -160,6 +160,7 @@ __device__ uint32_t refine_digit(const List& L, int len, uint32_t prefix, int lo
 template <int NT, class List>
 __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out) {
   constexpr int NW = NT / 64;
+  static_assert(NW <= 64, "one wave scans the per-wave counts");
   __shared__ uint32_t w_gt[NW], w_eq[NW], w_eqbase[NW], w_slot[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int span = ((len + NW * 64 - 1) / (NW * 64)) * 64;
@@ -174,15 +175,13 @@ __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_
   }
   if (lane == 0) { w_gt[wave] = gt; w_eq[wave] = eq; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t eq_run = 0, slot_run = 0;
-    for (int w = 0; w < NW; ++w) {
-      w_eqbase[w] = eq_run;
-      w_slot[w] = slot_run;
-      const uint32_t take_eq = eq_run >= eq_need ? 0u : min(w_eq[w], eq_need - eq_run);
-      slot_run += w_gt[w] + take_eq;
-      eq_run += w_eq[w];
-    }
+  if (wave == 0) {  // per-wave starting ranks and slots: two scans by one wave
+    const uint32_t weq = lane < NW ? w_eq[lane] : 0u, wgt = lane < NW ? w_gt[lane] : 0u;
+    uint32_t tot;
+    const uint32_t eqbase = wave_exclusive_scan(weq, tot);
+    const uint32_t take_eq = eqbase >= eq_need ? 0u : min(weq, eq_need - eqbase);
+    const uint32_t slot = wave_exclusive_scan(wgt + take_eq, tot);
+    if (lane < NW) { w_eqbase[lane] = eqbase; w_slot[lane] = slot; }
   }
   __syncthreads();
   uint32_t eq_run = w_eqbase[wave], slot_run = w_slot[wave];
@@ -199,7 +198,8 @@ __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_
     eq_run += (uint32_t)__popcll(eqm);
     slot_run += (uint32_t)__popcll(selm);
   }
-  __syncthreads();
+  // no trailing barrier: every caller calls this once, as its last use of the LDS (a barrier would also wait
+  // for the stores above to complete)
 }
 
 // LDS of the resolve step.
@@ -215,6 +215,31 @@ struct ResolveLds {
 // Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of `copies`
 // consecutive 4096-bin replicas, top bin first), and the number of keys in bins above b.  Called by all NT
 // threads; the result lands in *b, *above.
+// The same search over one histogram whose kTopkBins / NT bins of this thread (bins (NT - 1 - t) * kPer ..
+// +kPer) are already in registers.
+template <int NT>
+__device__ __forceinline__ void threshold_bin_vals(const uint32_t (&c)[kTopkBins / NT], uint32_t need,
+                                                   uint32_t* scan, uint32_t* b, uint32_t* above_out) {
+  constexpr int kPer = kTopkBins / NT;
+  const int grp = NT - 1 - threadIdx.x;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) local += c[j];
+  uint32_t total;
+  uint32_t above = block_exclusive_scan(local, scan, total);
+  if (above < need && above + local >= need) {
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (above + c[j] >= need) {
+        *b = (uint32_t)(grp * kPer + j);
+        *above_out = above;
+        break;
+      }
+      above += c[j];
+    }
+  }
+  __syncthreads();
+}
+
 template <int NT>
 __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, int copies, uint32_t need,
                                               uint32_t* scan, uint32_t* b, uint32_t* above_out) {
@@ -259,6 +284,8 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const int nchunk = (n + kCh - 1) / kCh;
   const int c0 = (int)blockIdx.x * cpb;
   if (keff >= n || c0 >= nchunk) return;
+  const float* row = scores + (int64_t)r * ld;
+  v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads while the threshold is found
   // every block finds b1 itself (a read of the row's histogram replicas) instead of waiting for one block to
   // publish it; a block covers several chunks when the row has many
   threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
@@ -266,7 +293,6 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
   uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
   const int c1 = min(nchunk, c0 + cpb);
-  const float* row = scores + (int64_t)r * ld;
   auto filter = [&](int ch, const v4f& x) __attribute__((always_inline)) {
     const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
     uint32_t key[kEpt];
@@ -300,7 +326,6 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
     __syncthreads();  // seg_base and the scan words are reused by the next chunk
   };
   // two buffers in turn: chunk c + 1 is loading while chunk c is filtered
-  v4f xa = load_raw(row, c0, n), xb;
   for (int ch = c0; ch < c1; ch += 2) {
     if (ch + 1 < c1) xb = load_raw(row, ch + 1, n);
     filter(ch, xa);
@@ -333,21 +358,23 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     return;
   }
   const float* row = scores + (int64_t)r * ld;
+  // every read that does not depend on another is issued here, together: the thresholds, the candidate count,
+  // the segment tables and the digit-2 histogram; the candidates follow as soon as their count arrives and stay
+  // in flight through the two block scans
+  const int nblk = (n + kCh - 1) / kCh;
+  const int t = threadIdx.x;
   const uint32_t b1 = thr[4 * r + 0], A1 = thr[4 * r + 1];
   const uint32_t len = cnt[4 * r + 2];
+  const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
+  const uint32_t src = t < nblk ? seg_off[(int64_t)r * nblk_max + t] : 0u;
+  constexpr int kPerBin = kTopkBins / kRes;
+  uint32_t h2v[kPerBin];
+  {
+    const uint32_t* gh = hist2 + (int64_t)r * kTopkBins + (kRes - 1 - t) * kPerBin;  // top bins first
+#pragma unroll
+    for (int j = 0; j < kPerBin; ++j) h2v[j] = gh[j];
+  }
   if (len <= (uint32_t)kCap) {
-    const int nblk = (n + kCh - 1) / kCh;
-    const int t = threadIdx.x;
-    const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
-    if (t < nblk) S.seg_src[t] = seg_off[(int64_t)r * nblk_max + t];
-    // b2: the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key
-    threshold_bin<kRes>(hist2 + (int64_t)r * kTopkBins, 1, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
-    uint32_t total;
-    const uint32_t start = block_exclusive_scan(c, S.scan, total);  // segment starts in position order
-    if (t < nblk) S.seg_start[t] = start;
-    __syncthreads();
-    const uint32_t b2 = s_b2, A2 = A1 + s_A2;
-    // every candidate goes to its chunk's segment start + its offset within the segment
     constexpr int kPer = (kCap + kRes - 1) / kRes;
     uint64_t e[kPer];
 #pragma unroll
@@ -355,6 +382,15 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       const int i = j * kRes + t;
       e[j] = i < (int)len ? cand[(int64_t)r * kCap + i] : 0ull;
     }
+    if (t < nblk) S.seg_src[t] = src;
+    // b2: the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key
+    threshold_bin_vals<kRes>(h2v, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
+    uint32_t total;
+    const uint32_t start = block_exclusive_scan(c, S.scan, total);  // segment starts in position order
+    if (t < nblk) S.seg_start[t] = start;
+    __syncthreads();
+    const uint32_t b2 = s_b2, A2 = A1 + s_A2;
+    // every candidate goes to its chunk's segment start + its offset within the segment
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = j * kRes + t;
