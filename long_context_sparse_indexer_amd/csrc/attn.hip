@@ -67,7 +67,8 @@ __device__ __forceinline__ void gather_chunk(const unsigned short* __restrict__ 
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-constexpr int kWaitVm16 = (16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8);  // vmcnt <= 16 only
+constexpr int kWaitVmOnly(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }  // vmcnt <= n only
+constexpr int kWaitVm16 = kWaitVmOnly(16);
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
 
 // Workgroup barrier for data this wave wrote with ds_* instructions.  Unlike __syncthreads() it does not wait
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowB];
   __shared__ __attribute__((aligned(16))) float s_lds[kHG][kNC + 4];
   __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
-  __shared__ int first_valid;
+  __shared__ int wave_first[4];               // first slot with a position among each wave's slots
 
   const int ngroups = H / kHG;
   const int split = blockIdx.x % nsplit;
@@ -100,6 +101,23 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
 
+  const int seq = clamp_seq(row_seq[r], num_seqs);
+  const int begin = split * split_len;
+  const int end = min(k, begin + split_len);
+  const int len = max(end - begin, 0);
+  const int nch = (len + kNC - 1) / kNC;
+  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
+
+  // Every slot of the split -> physical row before any gather, so that the gathers are the only loads in
+  // flight later: all position loads are issued together, then all page-table loads (two round trips).
+  constexpr int kSlotsPerThread = kMaxSplitLen / 256;
+  int pr[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int s = j * 256 + threadIdx.x;
+    pr[j] = s < len ? idx[s] : -1;
+  }
+
   // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8
   v8bf qa[kDC / 32];
   {
@@ -108,28 +126,28 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 32);
   }
 
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j)
+    pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+  {
+    // slot j * 256 + 64 wave + lane; the wave's first slot with a position comes from the ballots
+    int first = 0x7fffffff;
+#pragma unroll
+    for (int j = kSlotsPerThread - 1; j >= 0; --j) {
+      const int s = j * 256 + threadIdx.x;
+      if (s < nch * kNC) prow_lds[s] = pr[j];
+      const uint64_t bits = __ballot(pr[j] >= 0);
+      if (bits) first = j * 256 + wave * 64 + (int)__builtin_ctzll(bits);
+    }
+    if (lane == 0) wave_first[wave] = first;
+  }
+
   v4f o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // running max (log2 domain) and sum for head i
-
-  const int seq = clamp_seq(row_seq[r], num_seqs);
-  const int begin = split * split_len;
-  const int end = min(k, begin + split_len);
-  const int len = max(end - begin, 0);
-  const int nch = (len + kNC - 1) / kNC;
-  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
-
-  // every slot of the split -> physical row before any gather (so gathers are the only loads in flight)
-  if (threadIdx.x == 0) first_valid = 0x7fffffff;
   __syncthreads();
-  for (int s = threadIdx.x; s < nch * kNC; s += blockDim.x) {
-    const int pos = s < len ? idx[s] : -1;
-    const int pr = pos >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
-    prow_lds[s] = pr;
-    if (pr >= 0) atomicMin(&first_valid, s);
-  }
-  __syncthreads();
+  const int first_valid = min(min(wave_first[0], wave_first[1]), min(wave_first[2], wave_first[3]));
   // a split with no selected row contributes nothing; otherwise slots without a position read a selected row
   // of this split instead (their logits are -inf, so they carry zero weight)
   if (first_valid != 0x7fffffff) {
@@ -247,17 +265,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 // ---------------------------------------------------------------------------------------------------------
 // bf16 path, all heads of a row per block.  Every head of a row reads the same latent rows (MQA), so a block
 // that owns up to 128 heads gathers each selected row once instead of once per 16-head group.  Wave w owns
-// 32 heads and computes, per 64-slot chunk:
+// 32 heads and computes, per 32-slot chunk:
 //   S^T = C Q^T on v_mfma_f32_32x32x16_bf16 with the gathered rows as the A operand (row-contiguous 16-byte
-//       LDS reads) and Q^T held in registers (32 K-steps x 8 bf16).  Lane (half h, column n) then holds 16
-//       S^T rows 8 (i >> 2) + 4 h + (i & 3) of each 32-slot tile for head n, so the softmax of a head is an
-//       in-lane reduction plus one v_permlane32_swap with the other half.
+//       LDS reads) and Q^T held in registers (32 K-steps x 8 bf16).  Lane (half h, column n) then holds the 16
+//       S^T rows 8 (i >> 2) + 4 h + (i & 3) of the chunk for head n, so the softmax of a head is an in-lane
+//       reduction plus one v_permlane32_swap with the other half.
 //   O += P C with P as the A operand: K position 8 h + j of K-step ks is S^T row 16 ks + 4 h + (j & 3) +
-//       8 (j >> 2), which is exactly the lane's own probability i = 8 (ks & 1) + j of tile ks >> 1, so P
-//       needs no exchange; the B operand is read with ds_read_b64_tr_b16 (four slots of one latent column
-//       per lane, two reads per K-step).
-// O (32 heads x 512 columns, fp32) is 256 accumulator registers per wave, so one wave runs per SIMD and the
-// next chunk's LDS-DMA gather is kept in flight behind the current chunk's MFMAs.
+//       8 (j >> 2), which is exactly the lane's own probability i = 8 ks + j, so P needs no exchange; the B
+//       operand is read with ds_read_b64_tr_b16 (four slots of one latent column per lane, two reads per
+//       K-step).
+// O (32 heads x 512 columns, fp32) is 256 accumulator registers per wave, so one wave runs per SIMD.  The
+// gathers are LDS-DMA loads, whose throughput per CU is bounded by the loads it keeps in flight; a ring of
+// four chunk buffers keeps the next three chunks' gathers in flight behind the current chunk's MFMAs.
 //
 // LDS bank conflicts (32 four-byte banks): the LDS row stride is 1040 bytes (260 dwords, 4 mod 32), and the
 // QK A operand of lane m reads row 8 (m >> 3) + tau(m & 7), tau = {0,2,4,6,1,3,5,7}.  Eight consecutive
@@ -267,10 +286,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 constexpr int kRowW = kDC * 2 + 16;
 constexpr int kWideMaxSplitLen = 2048;  // selection slots one block handles
 
+constexpr int kCW = 32;    // slots per chunk: one S^T tile
+constexpr int kBufW = 4;   // LDS ring of gathered chunks
+
 template <int NW>  // waves per block: 32 * NW heads
 __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restrict__ kv, const int32_t* prow,
                                                   int dummy, char* buf, int wave, int lane) {
-  constexpr int kRows = kNC / NW;
+  constexpr int kRows = kCW / NW;
 #pragma unroll
   for (int t = 0; t < kRows; ++t) {
     const int rr = wave * kRows + t;
@@ -289,16 +311,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int split_len, float scale_log2, unsigned short* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  static_assert(kNC % NW == 0, "every wave gathers the same number of rows");
-  constexpr int kRows = kNC / NW;  // rows each wave gathers per chunk
-  // wait until only the next chunk's kRows gathers are outstanding; vmcnt counts to 63, so a single wave
-  // (64 gathers per chunk) waits for everything and does not overlap its gathers with compute
-  constexpr int kWaitGather = kRows > 63 ? 0 : (kRows & 15) | ((kRows >> 4) << 14) | (7 << 4) | (15 << 8);
-  __shared__ __attribute__((aligned(16))) char kv_lds0[kNC * kRowW];
-  __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowW];
+  static_assert(kCW % NW == 0, "every wave gathers the same number of rows");
+  constexpr int kRows = kCW / NW;  // rows each wave gathers per chunk
+  // chunks gathered ahead: at the wait for chunk c, the kDepth - 1 chunks after it may still be in flight,
+  // which must fit vmcnt (at most 63 outstanding loads per wave)
+  constexpr int kDepth = kBufW < 63 / kRows + 1 ? kBufW : 63 / kRows + 1;
+  static_assert(kDepth >= 2 && (kDepth - 1) * kRows <= 63, "gathers in flight fit vmcnt");
+  __shared__ __attribute__((aligned(16))) char kv_lds[kBufW][kCW * kRowW];
   __shared__ int32_t prow_lds[kWideMaxSplitLen];           // physical row of every slot, -1 = no position
   __shared__ uint32_t valid_lds[kWideMaxSplitLen / 32];    // bit per slot: it has a position
-  __shared__ int first_valid, overflow;
+  __shared__ int wave_first[NW], overflow;  // first slot with a position among each wave's slots
 
   const int ngroups = H / (32 * NW);
   const int split = blockIdx.x % nsplit;
@@ -309,6 +331,46 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int hw = hg * 32 * NW + wave * 32;  // first head of this wave
 
+  const int seq = clamp_seq(row_seq[r], num_seqs);
+  const int begin = split * split_len;
+  const int end = min(k, begin + split_len);
+  const int len = max(end - begin, 0);
+  const int nch = (len + kCW - 1) / kCW;  // chunks of kCW slots
+  const int n64 = (len + 63) / 64;
+  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
+
+  // Slots -> physical rows: all position loads are issued together, then all page-table loads.  Slot
+  // j * 64 NW + 64 wave + lane belongs to 64-slot group j NW + wave, so a ballot gives the validity bits of
+  // two chunks.
+  constexpr int kSlotsPerThread = kWideMaxSplitLen / (64 * NW);
+  int pr[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int sl = (j * NW + wave) * 64 + lane;
+    pr[j] = sl < len ? idx[sl] : -1;
+  }
+
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j)
+    pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+  {
+    int first = 0x7fffffff;
+#pragma unroll
+    for (int j = kSlotsPerThread - 1; j >= 0; --j) {
+      const int c = j * NW + wave;
+      if (c < n64) {
+        prow_lds[c * 64 + lane] = pr[j];
+        const uint64_t bits = __ballot(pr[j] >= 0);
+        if (lane == 0) {
+          valid_lds[2 * c] = (uint32_t)bits;
+          valid_lds[2 * c + 1] = (uint32_t)(bits >> 32);
+        }
+        if (bits) first = c * 64 + (int)__builtin_ctzll(bits);
+      }
+    }
+    if (lane == 0) wave_first[wave] = first;
+    if (threadIdx.x == 0) overflow = 0;
+  }
   // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
   v8bf qb[kDC / 16];
   {
@@ -317,33 +379,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
   }
   v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
-
-  const int seq = clamp_seq(row_seq[r], num_seqs);
-  const int begin = split * split_len;
-  const int end = min(k, begin + split_len);
-  const int len = max(end - begin, 0);
-  const int nch = (len + kNC - 1) / kNC;
-  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
-
-  if (threadIdx.x == 0) {
-    first_valid = 0x7fffffff;
-    overflow = 0;
-  }
   __syncthreads();
-  // slots -> physical rows; wave w takes whole 64-slot chunks so that a ballot gives the chunk's validity bits
-  for (int c = wave; c < nch; c += NW) {
-    const int sl = c * kNC + lane;
-    const int pos = sl < len ? idx[sl] : -1;
-    const int pr = pos >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
-    prow_lds[sl] = pr;
-    const uint64_t bits = __ballot(pr >= 0);
-    if (lane == 0) {
-      valid_lds[2 * c] = (uint32_t)bits;
-      valid_lds[2 * c + 1] = (uint32_t)(bits >> 32);
-      if (bits) atomicMin(&first_valid, c * kNC + (int)__builtin_ctzll(bits));
-    }
-  }
-  __syncthreads();
+  int first_valid = wave_first[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) first_valid = min(first_valid, wave_first[w]);
 
   // Softmax without rescaling O.  Every head accumulates p = 2^(s - m_ref) against a fixed reference: the
   // largest logit of the first chunk in which it has one.  O and l are then plain sums, and o = O / l,
@@ -355,58 +394,38 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   if (first_valid != 0x7fffffff) {
     const int dummy = prow_lds[first_valid];
     const int S16 = lane & 15, qh = (lane >> 4) & 1;  // transpose-read lane roles
-    // qk_only: only track the per-head maximum (into m_ref); otherwise accumulate O and l
-    auto chunk = [&](const int c, const char* cur, char* nxt, const bool qk_only) __attribute__((always_inline)) {
-      if (c + 1 < nch) {
-        gather_chunk_wide<NW>(kv, prow_lds + (c + 1) * kNC, dummy, nxt, wave, lane);
-        __builtin_amdgcn_s_waitcnt(kWaitGather);  // chunk c has landed; chunk c + 1 stays in flight
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      lds_barrier();
-      // S^T: tile t = slots 32 t .. +32 (A rows) x this wave's 32 heads (B columns).  The A operands are read
+    // One chunk: S^T tile, softmax, O += P C.  qk_only: only track the per-head maximum (into m_ref);
+    // otherwise accumulate O and l.
+    auto chunk = [&](const int c, const char* cur, const bool qk_only) __attribute__((always_inline)) {
+      // S^T: slots 0..31 of the chunk (A rows) x this wave's 32 heads (B columns).  The A operands are read
       // kQkDepth K-steps ahead of their MFMAs; sched_barrier keeps the compiler from hoisting further.
-      v16f st[2] = {v16f{}, v16f{}};
+      v16f st = {};
       {
-        constexpr int kQkDepth = 4;
+        constexpr int kQkDepth = 8;
         const char* arow = cur + (8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1)) * kRowW + 16 * half;
-        v8bf abuf[kQkDepth][2];
+        v8bf abuf[kQkDepth];
 #pragma unroll
-        for (int ks = 0; ks < kQkDepth; ++ks)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) abuf[ks][t] = *reinterpret_cast<const v8bf*>(arow + 32 * t * kRowW + 32 * ks);
+        for (int ks = 0; ks < kQkDepth; ++ks) abuf[ks] = *reinterpret_cast<const v8bf*>(arow + 32 * ks);
 #pragma unroll
         for (int ks = 0; ks < kDC / 16; ++ks) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kQkDepth][t], qb[ks], st[t], 0, 0, 0);
-            if (ks + kQkDepth < kDC / 16)
-              abuf[ks % kQkDepth][t] =
-                  *reinterpret_cast<const v8bf*>(arow + 32 * t * kRowW + 32 * (ks + kQkDepth));
-          }
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kQkDepth], qb[ks], st, 0, 0, 0);
+          if (ks + kQkDepth < kDC / 16)
+            abuf[ks % kQkDepth] = *reinterpret_cast<const v8bf*>(arow + 32 * (ks + kQkDepth));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       // logits in the log2 domain; slots without a position get -inf
-      const uint32_t vw0 = valid_lds[2 * c], vw1 = valid_lds[2 * c + 1];
+      const uint32_t vw = valid_lds[c];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 16; ++i) st[i] *= scale_log2;
+      if (vw != ~0u) {  // uniform: a chunk with slots that hold no position
+        const uint32_t w = vw >> half;  // register i holds row 8 (i >> 2) + 2 (i & 3) + half
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[t][i] *= scale_log2;
-      if ((vw0 & vw1) != ~0u) {  // uniform: a chunk with slots that hold no position
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t w = (t ? vw1 : vw0) >> half;  // register i holds row 8 (i >> 2) + 2 (i & 3) + half
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            st[t][i] = (w >> (8 * (i >> 2) + 2 * (i & 3))) & 1u ? st[t][i] : -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) st[i] = (w >> (8 * (i >> 2) + 2 * (i & 3))) & 1u ? st[i] : -INFINITY;
       }
-      float mx = -INFINITY;
+      float mx = st[0];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
@@ -419,20 +438,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
         float rs = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            st[t][i] = exp2f(st[t][i] - m_use);
-            rs += st[t][i];
-          }
+        for (int i = 0; i < 16; ++i) {
+          st[i] = exp2f(st[i] - m_use);
+          rs += st[i];
+        }
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
           rs += __uint_as_float(half ? sw[0] : sw[1]);
         }
         l += rs;
-        // O += P C over K-steps of 16 slots; the transposed B reads run kPvDepth MFMAs ahead
+        // O += P C over the chunk's two K-steps of 16 slots; the transposed B reads run kPvDepth MFMAs ahead
         constexpr int kPvDepth = 4;
-        constexpr int kSteps = (kNC / 16) * (kDC / 32);  // (K-step, column tile) pairs
+        constexpr int kSteps = (kCW / 16) * (kDC / 32);  // (K-step, column tile) pairs
         const char* pbase = cur + (2 * (S16 >> 2) + half) * kRowW + (16 * qh + 4 * (S16 & 3)) * 2;
         auto bread = [&](int u) __attribute__((always_inline)) {
           const int ks = u / (kDC / 32), dt = u % (kDC / 32);
@@ -444,11 +461,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         v8bf bbuf[kPvDepth];
 #pragma unroll
         for (int u = 0; u < kPvDepth; ++u) bbuf[u] = bread(u);
-        v8bf pa[kNC / 16];
+        v8bf pa[kCW / 16];
 #pragma unroll
-        for (int ks = 0; ks < kNC / 16; ++ks)
+        for (int ks = 0; ks < kCW / 16; ++ks)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pa[ks][j] = (__bf16)st[ks >> 1][8 * (ks & 1) + j];
+          for (int j = 0; j < 8; ++j) pa[ks][j] = (__bf16)st[8 * ks + j];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
           const int ks = u / (kDC / 32), dt = u % (kDC / 32);
@@ -457,14 +474,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      lds_barrier();  // every wave is done with `cur` before the next gather overwrites it
     };
-    // one chunk loop per pass; the gathers are opaque to the compiler's wait insertion (their waits are
-    // explicit), so alternating the buffers at run time costs no extra waits
+    // Wait until chunk c has landed while the `ahead` chunks gathered after it stay in flight.  The gathers
+    // are opaque to the compiler's wait insertion, so these waits are the only ones on them.
+    auto wait_chunk = [&](const int ahead) __attribute__((always_inline)) {
+      switch (ahead) {
+        case 0: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kRows)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * kRows < 63 ? 2 * kRows : 63)); break;
+        default: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(3 * kRows < 63 ? 3 * kRows : 63)); break;
+      }
+    };
+    // One pass over the chunks: kDepth chunks are gathered ahead into a ring of kBufW LDS buffers; after the
+    // barrier that ends chunk c, chunk c + kDepth is gathered into a buffer no wave still reads.
     auto run = [&](const bool qk_only) __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
-      gather_chunk_wide<NW>(kv, prow_lds, dummy, kv_lds0, wave, lane);
-      for (int c = 0; c < nch; ++c) chunk(c, (c & 1) ? kv_lds1 : kv_lds0, (c & 1) ? kv_lds0 : kv_lds1, qk_only);
+      for (int c = 0; c < kDepth && c < nch; ++c)
+        gather_chunk_wide<NW>(kv, prow_lds + c * kCW, dummy, kv_lds[c % kBufW], wave, lane);
+      for (int c = 0; c < nch; ++c) {
+        wait_chunk(min(nch - 1 - c, kDepth - 1));
+        lds_barrier();
+        chunk(c, kv_lds[c % kBufW], qk_only);
+        lds_barrier();  // every wave is done with this buffer before a gather overwrites it
+        if (c + kDepth < nch)
+          gather_chunk_wide<NW>(kv, prow_lds + (c + kDepth) * kCW, dummy, kv_lds[(c + kDepth) % kBufW], wave, lane);
+      }
       __syncthreads();
     };
 #pragma unroll
@@ -507,55 +541,49 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s.
-// One 128-thread block per (row, head); the first wave computes the normalised split weights, then every
-// thread combines four adjacent columns with 16-byte loads, all splits' loads in flight together.
+// One 128-thread block per (row, head), thread t owning latent columns 4t .. 4t+3 (d_c = 512).  Every load --
+// the first wave's split lse values and each thread's 16-byte pieces of up to kCombineBatch partial rows -- is
+// issued before any is used, so the weights and the rows arrive in one round trip.
 constexpr int kMaxSplit = 64;
-template <bool kBf16Out>
+constexpr int kCombineBatch = 32;
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse, int H, int d_c,
-                                                           int nsplit, void* __restrict__ out, float* __restrict__ lse) {
+                                                           const float* __restrict__ part_lse, int H, int nsplit,
+                                                           unsigned short* __restrict__ out, float* __restrict__ lse) {
+  static_assert(kDC == 4 * 128, "four latent columns per thread");
   __shared__ float wts[kMaxSplit];
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
+  const int d = 4 * threadIdx.x;
+  const int64_t stride = (int64_t)H * kDC;
+  const float* src = part_o + ((int64_t)r * nsplit * H + h) * kDC + d;
+  float ls = -INFINITY;
+  if (threadIdx.x < 64 && threadIdx.x < nsplit) ls = part_lse[((int64_t)r * nsplit + threadIdx.x) * H + h];
+  v4f v[kCombineBatch];
+#pragma unroll
+  for (int j = 0; j < kCombineBatch; ++j)
+    v[j] = j < nsplit ? *reinterpret_cast<const v4f*>(src + j * stride) : v4f{0.f, 0.f, 0.f, 0.f};
   if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    const float ls = s < nsplit ? part_lse[((int64_t)r * nsplit + s) * H + h] : -INFINITY;
     const float mx = wave_max(ls);
     const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
     const float wsum = wave_sum(w);
-    wts[s] = wsum > 0.f ? w / wsum : 0.f;
-    if (s == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+    wts[threadIdx.x] = wsum > 0.f ? w / wsum : 0.f;
+    if (threadIdx.x == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
   __syncthreads();
-  const int64_t stride = (int64_t)H * d_c;
-  const float* src = part_o + ((int64_t)r * nsplit * H + h) * d_c;
-  for (int d = 4 * threadIdx.x; d < d_c; d += 4 * 128) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
-      v4f v[8];
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const v4f*>(src + (s + j) * stride + d);
+  for (int j = 0; j < kCombineBatch; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[j], v[j][e], acc[e]);  // wts[j] = 0 past nsplit
+  for (int j = kCombineBatch; j < nsplit; ++j) {
+    const v4f x = *reinterpret_cast<const v4f*>(src + j * stride);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[s + j], v[j][e], acc[e]);
-    }
-    for (; s < nsplit; ++s) {
-      const v4f v = *reinterpret_cast<const v4f*>(src + s * stride + d);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[s], v[e], acc[e]);
-    }
-    const int64_t o = ((int64_t)r * H + h) * d_c + d;
-    if (kBf16Out) {
-      v4s b;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = (short)float_to_bf16_bits(acc[e]);
-      *reinterpret_cast<v4s*>(static_cast<unsigned short*>(out) + o) = b;  // 8-byte aligned: d is a multiple of 4
-    } else {
-      *reinterpret_cast<v4f*>(static_cast<float*>(out) + o) = acc;
-    }
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[j], x[e], acc[e]);
   }
+  v4s b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b[e] = (short)float_to_bf16_bits(acc[e]);
+  *reinterpret_cast<v4s*>(out + ((int64_t)r * H + h) * kDC + d) = b;  // 8-byte aligned: d is a multiple of 4
 }
 
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
@@ -717,7 +745,8 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                             part_o, part_lse);
     }
     if (p.nsplit > 1)
-      attn_combine_kernel<true><<<g.R * g.H, 128, 0, stream>>>(part_o, part_lse, g.H, g.d_c, p.nsplit, out, lse);
+      attn_combine_kernel<<<g.R * g.H, 128, 0, stream>>>(part_o, part_lse, g.H, p.nsplit,
+                                                       static_cast<unsigned short*>(out), lse);
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
     attn_f32_kernel<<<g.R * g.H, 256, lds, stream>>>(static_cast<const float*>(q), static_cast<const float*>(kv_pool),
