@@ -81,12 +81,43 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Split partials.  A split's o_s is a convex combination of its rows; it is stored as fp16 scaled by 2^-e per
+// (row, split, head), e being the frexp exponent of the head's largest magnitude, so every stored value lies in
+// (-1, 1) and its rounding is below 2^-12 of that maximum.  e is kept beside it.
+__device__ __forceinline__ int part_exponent(float maxabs) {
+  int e;
+  frexpf(maxabs, &e);
+  return maxabs > 0.f ? e : 0;
+}
+__device__ __forceinline__ unsigned short part_bits(float v, int e) {
+  return __builtin_bit_cast(unsigned short, (_Float16)ldexpf(v, -e));
+}
+__device__ __forceinline__ float max_over_lanes(float v, int width) {  // width = 16 or 32 aligned lanes
+  for (int m = 1; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Work unit (row, head group) and split of this block.  Workgroups are handed to the eight XCDs in turn
+// (block b runs on XCD b % 8), so the splits of one unit get block ids 8 apart: they share an XCD, whose L2
+// then serves the unit's queries, read by every split, after one HBM read.  The grid has
+// ceil(units / 8) * 8 * nsplit blocks; a block past the last unit has no work.
+struct BlockWork {
+  int unit, split;
+};
+__device__ __forceinline__ BlockWork block_work(int nsplit) {
+  const int b = blockIdx.x, slot = b >> 3;
+  return BlockWork{(slot / nsplit) * 8 + (b & 7), slot % nsplit};
+}
+__host__ __forceinline__ int work_blocks(int64_t units, int nsplit) { return (int)((units + 7) / 8 * 8 * nsplit); }
+
 template <bool kSplit>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
     int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
-    int num_pages, int log2ps, int H, int nsplit, int split_len, float scale_log2, unsigned short* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
+    unsigned short* __restrict__ out,
+    float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
+    float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) char kv_lds0[kNC * kRowB];
   __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowB];
   __shared__ __attribute__((aligned(16))) float s_lds[kHG][kNC + 4];
@@ -94,10 +125,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   __shared__ int wave_first[4];               // first slot with a position among each wave's slots
 
   const int ngroups = H / kHG;
-  const int split = blockIdx.x % nsplit;
-  const int rg = blockIdx.x / nsplit;
-  const int grp16 = rg % ngroups;
-  const int r = rg / ngroups;
+  const BlockWork bw = block_work(nsplit);
+  if (bw.unit >= units) return;
+  const int split = bw.split;
+  const int grp16 = bw.unit % ngroups;
+  const int r = bw.unit / ngroups;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
 
@@ -238,19 +270,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 
   // finish: O rows are heads g*4 + v, columns wave*128 + dt*16 + i
   const int64_t head0 = (int64_t)r * H + grp16 * kHG;
+  if (kSplit) {
+    // each head's largest |o| over the block's four waves (128 columns each), for its partial exponent
+    float* wmax = &s_lds[0][0];  // [4 waves][16 heads]; s_lds is free after the last chunk
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mx = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) mx = fmaxf(mx, fabsf(o[dt][v]));
+      mx = max_over_lanes(mx, 16);
+      if (i == 0) wmax[wave * kHG + g * 4 + v] = mx;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int hh = g * 4 + v;
     const float lv = __shfl(l, hh, 64);
     const float inv = lv > 0.f ? 1.f / lv : 0.f;
+    if (kSplit) {
+      const float* wmax = &s_lds[0][0];
+      const float mx = fmaxf(fmaxf(wmax[hh], wmax[kHG + hh]), fmaxf(wmax[2 * kHG + hh], wmax[3 * kHG + hh]));
+      const int e = part_exponent(mx * inv);
+      const int64_t prow = ((int64_t)r * nsplit + split) * H + grp16 * kHG + hh;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = wave * 128 + dt * 16 + i;
-      const float val = o[dt][v] * inv;
-      if (kSplit)
-        part_o[(((int64_t)r * nsplit + split) * H + grp16 * kHG + hh) * kDC + d] = val;
-      else
-        out[(head0 + hh) * kDC + d] = float_to_bf16_bits(val);
+      for (int dt = 0; dt < 8; ++dt) part_o[prow * kDC + wave * 128 + dt * 16 + i] = part_bits(o[dt][v] * inv, e);
+      if (wave == 0 && i == 0) part_exp[prow] = e;
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        out[(head0 + hh) * kDC + wave * 128 + dt * 16 + i] = float_to_bf16_bits(o[dt][v] * inv);
     }
   }
   if (wave == 0 && g == 0) {
@@ -309,8 +358,10 @@ template <int NW, bool kSplit>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
     int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
-    int num_pages, int log2ps, int H, int nsplit, int split_len, float scale_log2, unsigned short* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
+    unsigned short* __restrict__ out,
+    float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
+    float* __restrict__ part_lse) {
   static_assert(kCW % NW == 0, "every wave gathers the same number of rows");
   constexpr int kRows = kCW / NW;  // rows each wave gathers per chunk
   // chunks gathered ahead: at the wait for chunk c, the kDepth - 1 chunks after it may still be in flight,
@@ -323,10 +374,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   __shared__ int wave_first[NW], overflow;  // first slot with a position among each wave's slots
 
   const int ngroups = H / (32 * NW);
-  const int split = blockIdx.x % nsplit;
-  const int rg = blockIdx.x / nsplit;
-  const int hg = rg % ngroups;
-  const int r = rg / ngroups;
+  const BlockWork bw = block_work(nsplit);
+  if (bw.unit >= units) return;
+  const int split = bw.split;
+  const int hg = bw.unit % ngroups;
+  const int r = bw.unit / ngroups;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int hw = hg * 32 * NW + wave * 32;  // first head of this wave
@@ -349,6 +401,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const int sl = (j * NW + wave) * 64 + lane;
     pr[j] = sl < len ? idx[sl] : -1;
   }
+  // the queries load while the positions and then the page-table entries arrive
+  // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
+  v8bf qb[kDC / 16];
+  {
+    const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kDC + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
+  }
+  v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
 
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j)
@@ -371,14 +432,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     if (lane == 0) wave_first[wave] = first;
     if (threadIdx.x == 0) overflow = 0;
   }
-  // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
-  v8bf qb[kDC / 16];
-  {
-    const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kDC + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
-  }
-  v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
   __syncthreads();
   int first_valid = wave_first[0];
 #pragma unroll
@@ -516,19 +569,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 
   // finish: normalise O rows by their head's sum (held in lane (0, head))
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const bool any = first_valid != 0x7fffffff;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int hh = 8 * (i >> 2) + 4 * half + (i & 3);
     const float inv = __shfl(inv_l, hh, 64);
-    const int64_t orow = (int64_t)r * H + hw + hh;
+    if (kSplit) {  // head hh's 512 columns: tiles dt = 0..15 across the 32 lanes of this half
+      // O is only initialised when the split has a selected row (`any`, uniform); otherwise store zeros
+      float mx = 0.f;
+      if (any)
 #pragma unroll
-    for (int dt = 0; dt < kDC / 32; ++dt) {
-      const int d = 32 * dt + col;
-      const float val = first_valid != 0x7fffffff ? o[dt][i] * inv : 0.f;
-      if (kSplit)
-        part_o[(((int64_t)r * nsplit + split) * H + hw + hh) * kDC + d] = val;
-      else
-        out[orow * kDC + d] = float_to_bf16_bits(val);
+        for (int dt = 0; dt < kDC / 32; ++dt) mx = fmaxf(mx, fabsf(o[dt][i]));
+      const int ex = part_exponent(max_over_lanes(mx, 32) * inv);
+      const int64_t prow = ((int64_t)r * nsplit + split) * H + hw + hh;
+#pragma unroll
+      for (int dt = 0; dt < kDC / 32; ++dt)
+        part_o[prow * kDC + 32 * dt + col] = part_bits(any ? o[dt][i] * inv : 0.f, ex);
+      if (col == 0) part_exp[prow] = ex;
+    } else {
+      const int64_t orow = (int64_t)r * H + hw + hh;
+#pragma unroll
+      for (int dt = 0; dt < kDC / 32; ++dt)
+        out[orow * kDC + 32 * dt + col] = float_to_bf16_bits(any ? o[dt][i] * inv : 0.f);
     }
   }
   if (half == 0) {
@@ -540,13 +602,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   }
 }
 
-// Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s.
-// One 128-thread block per (row, head), thread t owning latent columns 4t .. 4t+3 (d_c = 512).  Every load --
-// the first wave's split lse values and each thread's 16-byte pieces of up to kCombineBatch partial rows -- is
-// issued before any is used, so the weights and the rows arrive in one round trip.
+// Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s,
+// in fp32.  One 128-thread block per (row, head), thread t owning latent columns 4t .. 4t+3 (d_c = 512).  Every
+// load -- the first wave's split lse values, each thread's 8-byte pieces of up to kCombineBatch partial rows
+// and their exponents -- is issued before any is used, so the weights and the rows arrive in one round trip.
 constexpr int kMaxSplit = 64;
 constexpr int kCombineBatch = 32;
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
+                                                           const int32_t* __restrict__ part_exp,
                                                            const float* __restrict__ part_lse, int H, int nsplit,
                                                            unsigned short* __restrict__ out, float* __restrict__ lse) {
   static_assert(kDC == 4 * 128, "four latent columns per thread");
@@ -554,14 +617,18 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
   const int d = 4 * threadIdx.x;
-  const int64_t stride = (int64_t)H * kDC;
-  const float* src = part_o + ((int64_t)r * nsplit * H + h) * kDC + d;
+  const int64_t row0 = (int64_t)r * nsplit * H + h;  // partial row of split 0; split j is j * H further
   float ls = -INFINITY;
-  if (threadIdx.x < 64 && threadIdx.x < nsplit) ls = part_lse[((int64_t)r * nsplit + threadIdx.x) * H + h];
-  v4f v[kCombineBatch];
+  if (threadIdx.x < 64 && threadIdx.x < nsplit) ls = part_lse[row0 + (int64_t)threadIdx.x * H];
+  auto piece = [&](int j) { return *reinterpret_cast<const v4s*>(part_o + (row0 + (int64_t)j * H) * kDC + d); };
+  auto expo = [&](int j) { return part_exp[row0 + (int64_t)j * H]; };
+  v4s v[kCombineBatch];
+  int ex[kCombineBatch];
 #pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j)
-    v[j] = j < nsplit ? *reinterpret_cast<const v4f*>(src + j * stride) : v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kCombineBatch; ++j) {
+    v[j] = j < nsplit ? piece(j) : v4s{0, 0, 0, 0};
+    ex[j] = j < nsplit ? expo(j) : 0;
+  }
   if (threadIdx.x < 64) {
     const float mx = wave_max(ls);
     const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
@@ -570,15 +637,19 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     if (threadIdx.x == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
   __syncthreads();
+  auto half_f = [](short b) { return (float)__builtin_bit_cast(_Float16, (unsigned short)b); };
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j)
+  for (int j = 0; j < kCombineBatch; ++j) {
+    const float w = ldexpf(wts[j], ex[j]);  // wts[j] = 0 past nsplit
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[j], v[j][e], acc[e]);  // wts[j] = 0 past nsplit
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, half_f(v[j][e]), acc[e]);
+  }
   for (int j = kCombineBatch; j < nsplit; ++j) {
-    const v4f x = *reinterpret_cast<const v4f*>(src + j * stride);
+    const v4s x = piece(j);
+    const float w = ldexpf(wts[j], expo(j));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wts[j], x[e], acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, half_f(x[e]), acc[e]);
   }
   v4s b;
 #pragma unroll
@@ -689,19 +760,40 @@ AttnPlan plan(const Geo& g) {
   return p;
 }
 
+// Split partials in the workspace: o [R, nsplit, H, d_c] fp16, lse [R, nsplit, H] fp32, exponents
+// [R, nsplit, H] int32.
+struct Partials {
+  unsigned short* o;
+  float* lse;
+  int32_t* ex;
+};
+Partials carve_partials(const Geo& g, int nsplit, void* workspace) {
+  if (nsplit <= 1) return Partials{nullptr, nullptr, nullptr};
+  const size_t rows = (size_t)g.R * nsplit * g.H;
+  char* p = static_cast<char*>(workspace);
+  Partials w;
+  w.o = reinterpret_cast<unsigned short*>(p);
+  p += align_up(sizeof(uint16_t) * rows * g.d_c);
+  w.lse = reinterpret_cast<float*>(p);
+  p += align_up(sizeof(float) * rows);
+  w.ex = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
 template <int NW>
 void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const unsigned short* kp,
-                const int32_t* topk_idx, void* out, float* lse, float* part_o, float* part_lse, float scale_log2,
+                const int32_t* topk_idx, void* out, float* lse, const Partials& pt, float scale_log2,
                 hipStream_t stream) {
-  const int nblocks = g.R * (g.H / (32 * NW)) * p.nsplit;
+  const int64_t units = (int64_t)g.R * (g.H / (32 * NW));
+  const int nblocks = work_blocks(units, p.nsplit);
   if (p.nsplit == 1)
     attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
-        p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr);
+        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1, (int)units,
+        p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr, nullptr);
   else
     attn_bf16_mqa_kernel<NW, true><<<nblocks, NW * 64, 0, stream>>>(
         qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, p.nsplit,
-        p.split_len, scale_log2, nullptr, nullptr, part_o, part_lse);
+        (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex, pt.lse);
 }
 
 }  // namespace
@@ -709,7 +801,9 @@ void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const
 size_t attn_workspace_bytes(const Geo& g) {
   const AttnPlan p = plan(g);
   if (p.nsplit <= 1) return 0;
-  return align_up(sizeof(float) * (size_t)g.R * p.nsplit * g.H * g.d_c) + align_up(sizeof(float) * (size_t)g.R * p.nsplit * g.H);
+  const size_t rows = (size_t)g.R * p.nsplit * g.H;
+  return align_up(sizeof(uint16_t) * rows * g.d_c) + align_up(sizeof(float) * rows) +
+         align_up(sizeof(int32_t) * rows);
 }
 
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
@@ -720,32 +814,30 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
     const float scale_log2 = g.softmax_scale * kLog2e;
     auto* qp = static_cast<const unsigned short*>(q);
     auto* kp = static_cast<const unsigned short*>(kv_pool);
-    float* part_o = static_cast<float*>(workspace);
-    float* part_lse = p.nsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                             align_up(sizeof(float) * (size_t)g.R * p.nsplit * g.H * g.d_c))
-                                   : nullptr;
+    const Partials pt = carve_partials(g, p.nsplit, workspace);
     if (p.nw > 0) {
       switch (p.nw) {
-        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
-        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
-        default: launch_mqa<4>(g, p, qp, kp, topk_idx, out, lse, part_o, part_lse, scale_log2, stream); break;
+        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
+        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
+        default: launch_mqa<4>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
       }
     } else {
-      const int nblocks = g.R * (g.H / kHG) * p.nsplit;
+      const int64_t units = (int64_t)g.R * (g.H / kHG);
+      const int nblocks = work_blocks(units, p.nsplit);
       if (p.nsplit == 1)
         attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
                                                              g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
-                                                             p.split_len, scale_log2,
+                                                             (int)units, p.split_len, scale_log2,
                                                              static_cast<unsigned short*>(out), lse, nullptr,
-                                                             nullptr);
+                                                             nullptr, nullptr);
       else
         attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
-                                                            p.nsplit, p.split_len, scale_log2, nullptr, nullptr,
-                                                            part_o, part_lse);
+                                                            p.nsplit, (int)units, p.split_len, scale_log2, nullptr,
+                                                            nullptr, pt.o, pt.ex, pt.lse);
     }
     if (p.nsplit > 1)
-      attn_combine_kernel<<<g.R * g.H, 128, 0, stream>>>(part_o, part_lse, g.H, p.nsplit,
+      attn_combine_kernel<<<g.R * g.H, 128, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit,
                                                        static_cast<unsigned short*>(out), lse);
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
