@@ -156,50 +156,117 @@ __device__ uint32_t refine_digit(const List& L, int len, uint32_t prefix, int lo
 }
 
 // Writes, in list (= position) order, every entry with key > T and the first eq_need entries with key == T.
-// Each wave owns a contiguous stretch of the list; one pass counts, one block-level prefix, one pass writes.
+// Each wave owns a contiguous stretch of the list; one pass counts, one barrier publishes the per-wave counts,
+// every wave adds up those of the waves before it, and a second pass writes.
 template <int NT, class List>
 __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out) {
   constexpr int NW = NT / 64;
-  static_assert(NW <= 64, "one wave scans the per-wave counts");
-  __shared__ uint32_t w_gt[NW], w_eq[NW], w_eqbase[NW], w_slot[NW];
+  __shared__ uint32_t w_gt[NW], w_eq[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int span = ((len + NW * 64 - 1) / (NW * 64)) * 64;
   const int lo = wave * span, hi = min(len, lo + span);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int U = 4;  // 64-entry steps per iteration, their LDS reads issued together
   uint32_t gt = 0, eq = 0;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t key = i < hi ? L.k(i) : 0u;
-    gt += __popcll(__ballot(i < hi && key > T));
-    eq += __popcll(__ballot(i < hi && key == T));
+  for (int base = lo; base < hi; base += 64 * U) {
+    uint32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + 64 * u + lane;
+      key[u] = i < hi ? L.k(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = base + 64 * u + lane < hi;
+      gt += __popcll(__ballot(in && key[u] > T));
+      eq += __popcll(__ballot(in && key[u] == T));
+    }
   }
   if (lane == 0) { w_gt[wave] = gt; w_eq[wave] = eq; }
   __syncthreads();
-  if (wave == 0) {  // per-wave starting ranks and slots: two scans by one wave
-    const uint32_t weq = lane < NW ? w_eq[lane] : 0u, wgt = lane < NW ? w_gt[lane] : 0u;
-    uint32_t tot;
-    const uint32_t eqbase = wave_exclusive_scan(weq, tot);
-    const uint32_t take_eq = eqbase >= eq_need ? 0u : min(weq, eq_need - eqbase);
-    const uint32_t slot = wave_exclusive_scan(wgt + take_eq, tot);
-    if (lane < NW) { w_eqbase[lane] = eqbase; w_slot[lane] = slot; }
+  // this wave's first slot and its rank among the keys equal to T: the waves before it take all their keys
+  // above T and their share of the equal ones, in list order
+  uint32_t eq_run = 0, slot_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    const uint32_t we = w_eq[w];
+    slot_run += w_gt[w] + (eq_run >= eq_need ? 0u : min(we, eq_need - eq_run));
+    eq_run += we;
   }
-  __syncthreads();
-  uint32_t eq_run = w_eqbase[wave], slot_run = w_slot[wave];
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t key = i < hi ? L.k(i) : 0u;
-    const bool is_eq = i < hi && key == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t rank = eq_run + (uint32_t)__popcll(eqm & below);
-    const bool sel = i < hi && (key > T || (is_eq && rank < eq_need));
-    const uint64_t selm = __ballot(sel);
-    const uint32_t slot = slot_run + (uint32_t)__popcll(selm & below);
-    if (sel && slot < (uint32_t)keff) out[slot] = L.p(i);
-    eq_run += (uint32_t)__popcll(eqm);
-    slot_run += (uint32_t)__popcll(selm);
+  for (int base = lo; base < hi; base += 64 * U) {
+    uint32_t key[U];
+    int32_t pos[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + 64 * u + lane;
+      key[u] = i < hi ? L.k(i) : 0u;
+      pos[u] = i < hi ? L.p(i) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = base + 64 * u + lane < hi;
+      const bool is_eq = in && key[u] == T;
+      const uint64_t eqm = __ballot(is_eq);
+      const uint32_t rank = eq_run + (uint32_t)__popcll(eqm & below);
+      const bool sel = in && (key[u] > T || (is_eq && rank < eq_need));
+      const uint64_t selm = __ballot(sel);
+      const uint32_t slot = slot_run + (uint32_t)__popcll(selm & below);
+      if (sel && slot < (uint32_t)keff) out[slot] = pos[u];
+      eq_run += (uint32_t)__popcll(eqm);
+      slot_run += (uint32_t)__popcll(selm);
+    }
   }
   // no trailing barrier: every caller calls this once, as its last use of the LDS (a barrier would also wait
   // for the stores above to complete)
+}
+
+// Exclusive prefix over the block of one value per thread, and the block total, with one barrier: every wave
+// scans its lanes and publishes its total in wt[0 .. NW), then every thread adds the totals of the waves before
+// its own.  wt may be written again only after another barrier.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan1(uint32_t v, uint32_t* wt, uint32_t& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t tw;
+  uint32_t x = wave_exclusive_scan(v, tw);
+  if (lane == 0) wt[wave] = tw;
+  __syncthreads();
+  static_assert(NW % 4 == 0, "wave totals are read four at a time");
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < NW / 4; ++q) {  // 16-byte reads of the wave totals (wt is 16-byte aligned)
+    const v4i y = reinterpret_cast<const v4i*>(wt)[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (4 * q + e < wave) x += (uint32_t)y[e];
+      total += (uint32_t)y[e];
+    }
+  }
+  return x;
+}
+
+// Exclusive prefixes over the block of two values per thread, with one barrier: every wave scans its lanes and
+// publishes its totals in wt[0 .. 2 NW), then every thread adds the totals of the waves before its own.  wt may
+// be written again only after another barrier.
+template <int NT>
+__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* wt, uint32_t& pa, uint32_t& pb) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t ta, tb;
+  pa = wave_exclusive_scan(a, ta);
+  pb = wave_exclusive_scan(b, tb);
+  if (lane == 0) { wt[wave] = ta; wt[NW + wave] = tb; }
+  __syncthreads();
+  static_assert(NW % 4 == 0, "wave totals are read four at a time");
+#pragma unroll
+  for (int q = 0; q < NW / 4; ++q) {  // 16-byte reads of the wave totals (wt is 16-byte aligned)
+    const v4i ya = reinterpret_cast<const v4i*>(wt)[q], yb = reinterpret_cast<const v4i*>(wt + NW)[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * q + e < wave) {
+        pa += (uint32_t)ya[e];
+        pb += (uint32_t)yb[e];
+      }
+  }
 }
 
 // LDS of the resolve step.
@@ -210,36 +277,13 @@ struct ResolveLds {
   uint32_t seg_start[kTopkMaxBlocksPerRow + 1];
   uint32_t seg_src[kTopkMaxBlocksPerRow];
   uint32_t scan[1024 / 64 + 1];  // one word per wave of the largest block, plus the total
+  alignas(16) uint32_t scan2[2 * (1024 / 64)];
+  uint32_t bin[64];               // low digits of the keys in bin (b1, b2), when there are at most 64
 };
 
 // Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of `copies`
 // consecutive 4096-bin replicas, top bin first), and the number of keys in bins above b.  Called by all NT
 // threads; the result lands in *b, *above.
-// The same search over one histogram whose kTopkBins / NT bins of this thread (bins (NT - 1 - t) * kPer ..
-// +kPer) are already in registers.
-template <int NT>
-__device__ __forceinline__ void threshold_bin_vals(const uint32_t (&c)[kTopkBins / NT], uint32_t need,
-                                                   uint32_t* scan, uint32_t* b, uint32_t* above_out) {
-  constexpr int kPer = kTopkBins / NT;
-  const int grp = NT - 1 - threadIdx.x;
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) local += c[j];
-  uint32_t total;
-  uint32_t above = block_exclusive_scan(local, scan, total);
-  if (above < need && above + local >= need) {
-    for (int j = kPer - 1; j >= 0; --j) {
-      if (above + c[j] >= need) {
-        *b = (uint32_t)(grp * kPer + j);
-        *above_out = above;
-        break;
-      }
-      above += c[j];
-    }
-  }
-  __syncthreads();
-}
-
 template <int NT>
 __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, int copies, uint32_t need,
                                               uint32_t* scan, uint32_t* b, uint32_t* above_out) {
@@ -255,7 +299,7 @@ __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, i
 #pragma unroll
   for (int j = 0; j < kPer; ++j) local += c[j];
   uint32_t total;
-  uint32_t above = block_exclusive_scan(local, scan, total);
+  uint32_t above = block_scan1<NT>(local, scan, total);
   if (above < need && above + local >= need) {
     for (int j = kPer - 1; j >= 0; --j) {
       if (above + c[j] >= need) {
@@ -276,7 +320,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
                                                            uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
                                                            int nblk_max, int copies, int cpb) {
-  __shared__ uint32_t scan[kTpb / 64 + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ uint32_t seg_base, s_b1, s_A1;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
@@ -309,7 +353,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
       }
     }
     uint32_t total;
-    const uint32_t off = block_exclusive_scan(c, scan, total);
+    const uint32_t off = block_exclusive_scan(c, scan, total);  // per chunk: cheaper than block_scan1 under load
     if (threadIdx.x == 0) {
       seg_base = atomicAdd(&cnt[4 * r + 2], total);
       seg_cnt[(int64_t)r * nblk_max + ch] = total;
@@ -323,7 +367,8 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
       for (int e = 0; e < kEpt; ++e)
         if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
     }
-    __syncthreads();  // seg_base and the scan words are reused by the next chunk
+    // no barrier here: the next chunk writes the scan words and seg_base only after barriers that every thread
+    // reaches after reading this chunk's
   };
   // two buffers in turn: chunk c + 1 is loading while chunk c is filtered
   for (int ch = c0; ch < c1; ch += 2) {
@@ -348,7 +393,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
                                                             int32_t* __restrict__ topk_idx) {
   static_assert(kRes >= kTopkMaxBlocksPerRow, "one chunk per thread");
   __shared__ ResolveLds S;
-  __shared__ uint32_t s_b2, s_A2;
+  __shared__ uint32_t s_b2, s_A2, s_nb, s_nbin;
   const int r = blockIdx.x;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
@@ -374,22 +419,49 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
 #pragma unroll
     for (int j = 0; j < kPerBin; ++j) h2v[j] = gh[j];
   }
-  if (len <= (uint32_t)kCap) {
-    constexpr int kPer = (kCap + kRes - 1) / kRes;
-    uint64_t e[kPer];
+  // the first candidates load before their count is known (entries past it are ignored)
+  constexpr int kPer = (kCap + kRes - 1) / kRes;
+  constexpr int kFirst = 4;
+  uint64_t e[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < kFirst; ++j) e[j] = cand[(int64_t)r * kCap + j * kRes + t];
+  if (len <= (uint32_t)kCap) {
+#pragma unroll
+    for (int j = kFirst; j < kPer; ++j) {
       const int i = j * kRes + t;
       e[j] = i < (int)len ? cand[(int64_t)r * kCap + i] : 0ull;
     }
-    if (t < nblk) S.seg_src[t] = src;
-    // b2: the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key
-    threshold_bin_vals<kRes>(h2v, (uint32_t)keff - A1, S.scan, &s_b2, &s_A2);
-    uint32_t total;
-    const uint32_t start = block_exclusive_scan(c, S.scan, total);  // segment starts in position order
-    if (t < nblk) S.seg_start[t] = start;
+    // b2 -- the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key, thread t owning bins
+    // (kRes - 1 - t) * kPerBin .. top first -- and the segment starts in position order (thread t = chunk t):
+    // two scans, one barrier
+    uint32_t hl = 0;
+#pragma unroll
+    for (int j = 0; j < kPerBin; ++j) hl += h2v[j];
+    uint32_t above, start;
+    if (t == 0) s_nbin = 0;
+    block_scan2<kRes>(hl, c, S.scan2, above, start);
+    const uint32_t need2 = (uint32_t)keff - A1;
+    if (above < need2 && above + hl >= need2) {
+      uint32_t run = above;
+      for (int j = kPerBin - 1; j >= 0; --j) {
+        if (run + h2v[j] >= need2) {
+          s_b2 = (uint32_t)((kRes - 1 - t) * kPerBin + j);
+          s_A2 = run;
+          s_nb = h2v[j];
+          break;
+        }
+        run += h2v[j];
+      }
+    }
+    if (t < nblk) {
+      S.seg_start[t] = start;
+      S.seg_src[t] = src;
+    }
     __syncthreads();
-    const uint32_t b2 = s_b2, A2 = A1 + s_A2;
+    const uint32_t b2 = s_b2, A2 = A1 + s_A2, nb = s_nb;  // nb: keys in bin (b1, b2), all in the list
+    const uint32_t prefix = (b1 << 12) | b2;
+    const int lane = t & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // every candidate goes to its chunk's segment start + its offset within the segment
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -402,10 +474,43 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
         S.pos[dst] = (int32_t)pos;
       }
     }
+    // the low digits of the keys in bin (b1, b2), when they fit one wave (their order does not matter)
+    if (nb <= 64u) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = j * kRes + t;
+        const uint32_t key = (uint32_t)e[j];
+        const bool match = i < (int)len && (key >> 8) == prefix;
+        const uint64_t mm = __ballot(match);
+        if (mm) {  // uniform over the wave
+          const int leader = __builtin_ctzll(mm);
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&s_nbin, (uint32_t)__popcll(mm));
+          base = __shfl(base, leader, 64);
+          if (match) S.bin[base + (uint32_t)__popcll(mm & below)] = key & 0xffu;
+        }
+      }
+    }
     __syncthreads();
-    uint32_t need = (uint32_t)keff - A2;  // keys of (b1, b2) still to take
     const LdsList L{S.key, S.pos};
-    const uint32_t d3 = refine_digit<kRes>(L, (int)len, (b1 << 12) | b2, 0, 8, need, S.h, S.scan);
+    uint32_t need = (uint32_t)keff - A2;  // keys of (b1, b2) still to take
+    uint32_t d3;
+    if (nb <= 64u) {
+      // every wave finds digit 3 itself: lane x ranks the low digit of the x-th key of the bin among all nb
+      const uint32_t dx = lane < (int)nb ? S.bin[lane] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t y = 0; y < nb; ++y) {
+        const uint32_t dy = S.bin[y];
+        gt += dy > dx;
+        ge += dy >= dx;
+      }
+      const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);  // lanes holding the digit
+      const int src_lane = __builtin_ctzll(hit);
+      d3 = __shfl(dx, src_lane, 64);
+      need -= __shfl(gt, src_lane, 64);
+    } else {
+      d3 = refine_digit<kRes>(L, (int)len, prefix, 0, 8, need, S.h, S.scan);
+    }
     write_selection<kRes>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out);
   } else {
     const RowList L{row};
