@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32];    // lane l's fp8 A operand
   __shared__ __attribute__((aligned(16))) float w_lds[kPfRows][HB][2][16];       // wq of each lane half's heads
   __shared__ __attribute__((aligned(16))) __bf16 u_lds[kPfRows / 8][4][64][8];   // linear-MFMA A operands
-  __shared__ int n_lds[kPfRows];
+  __shared__ __attribute__((aligned(16))) int n_lds[kPfRows];
   const int group = (int)blockIdx.y / tiles_per_group;
   const int r0 = group * rows_per_seq + ((int)blockIdx.y % tiles_per_group) * kPfRows;
   const int rows = min(min(kPfRows, (group + 1) * rows_per_seq - r0), R - r0);
@@ -296,27 +296,28 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
   }
   __syncthreads();
 
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   v8i b[kPfSub];
-  float sk[kPfSub];
   for (int pass = 0; pass < kPfPasses; ++pass) {
     const int64_t tile0 = span0 + (int64_t)pass * kPfTile;
     if (tile0 >= nmax) break;  // uniform
+    // Pool rows of the wave's four 32-position subtiles: a 32-aligned subtile lies in one page (pages hold >= 32
+    // positions), so its page id is one scalar load; lanes past the tile's last position take that position
+    // (the same page, or the last one), so every load is unconditional and in range.  Scores of positions a row
+    // does not see are never stored (the row's store range ends at its length).
     int64_t prow[kPfSub];
 #pragma unroll
     for (int s = 0; s < kPfSub; ++s) {
-      const int64_t pos = tile0 + wave * (kPfSub * 32) + s * 32 + col;
-      prow[s] = pos < nmax ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
+      const int64_t base = tile0 + wave_u * (kPfSub * 32) + s * 32;  // uniform
+      const int64_t bp = base < nmax ? base : nmax - 1;
+      const int lp = (int)min(bp >> log2ps, (int64_t)max_pages - 1);
+      int page = page_table[(int64_t)seq * max_pages + lp];
+      page = min(max(page, 0), num_pages - 1);
+      const int64_t row0 = ((int64_t)page << log2ps) | (bp & ((1 << log2ps) - 1));
+      prow[s] = row0 + (base < nmax ? min((int64_t)col, nmax - 1 - base) : 0);
     }
 #pragma unroll
-    for (int s = 0; s < kPfSub; ++s) {
-      if (prow[s] >= 0) {
-        b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
-        sk[s] = k_scale[prow[s]];
-      } else {
-        b[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        sk[s] = 0.f;
-      }
-    }
+    for (int s = 0; s < kPfSub; ++s) b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
 
     // per pass, per lane: half 0 stores subtile 2p and half 1 subtile 2p + 1 of each pair p; 0.5 sk of that
     // position (the 1/2 of (lin + abs) folded in, exact) and its byte offset within the row
@@ -324,12 +325,10 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
     int voff[kPfSub / 2];
 #pragma unroll
     for (int p = 0; p < kPfSub / 2; ++p) {
-      const int rel = wave * (kPfSub * 32) + (2 * p + half) * 32 + col;
-      const int64_t pos = tile0 + rel;
-      // the scale of the position this lane stores, loaded directly (a select between subtiles would index
-      // the register array with the lane's half)
-      skm[p] = pos < nmax ? 0.5f * k_scale[phys_row(page_table, max_pages, num_pages, log2ps, seq, pos)] : 0.f;
-      voff[p] = rel * 4;
+      // the store subtile's row, picked arithmetically (an indexed pick would put prow in scratch)
+      const int64_t srow = prow[2 * p] + (prow[2 * p + 1] - prow[2 * p]) * half;
+      skm[p] = 0.5f * k_scale[srow];
+      voff[p] = (wave * (kPfSub * 32) + (2 * p + half) * 32 + col) * 4;
     }
     const int soff = (int)tile0 * 4;
 
@@ -369,11 +368,11 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
 #pragma unroll 1
       for (int hq = 0; hq < 2; ++hq) {
         const float ownf = hq == half ? 1.f : 0.f;  // this lane half holds the linear term of rows 8 g + 4 hq + e
-        int nq[4];
+        int nq[4];  // lengths of rows 8 g + 4 hq + e (0 past the tile's rows): one 16-byte LDS read
+        {
+          const v4i nv = *reinterpret_cast<const v4i*>(&n_lds[8 * g + 4 * hq]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = 8 * g + 4 * hq + e;
-          nq[e] = q < rows ? __builtin_amdgcn_readfirstlane(n_lds[q]) : 0;
+          for (int e = 0; e < 4; ++e) nq[e] = __builtin_amdgcn_readfirstlane(nv[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
