@@ -97,9 +97,9 @@ __device__ __forceinline__ float max_over_lanes(float v, int width) {  // width 
   return v;
 }
 
-// Work unit (row, head group) and split of this block.  Workgroups are handed to the eight XCDs in turn
-// (block b runs on XCD b % 8), so the splits of one unit get block ids 8 apart: they share an XCD, whose L2
-// then serves the unit's queries, read by every split, after one HBM read.  The grid has
+// Work unit (row, head group of the all-heads kernel) and split of this block.  Workgroups are handed to the
+// eight XCDs in turn (block b runs on XCD b % 8), so the splits of one unit get block ids 8 apart: they share an
+// XCD, whose L2 then serves the unit's queries, read by every split, after one HBM read.  The grid has
 // ceil(units / 8) * 8 * nsplit blocks; a block past the last unit has no work.
 struct BlockWork {
   int unit, split;
@@ -124,12 +124,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
   __shared__ int wave_first[4];               // first slot with a position among each wave's slots
 
+  // Block b runs on XCD b % 8.  The 16-head groups of one (row, split) gather the same rows, so they get block
+  // ids 8 apart and share an XCD and its L2: pair p = row * nsplit + split runs on XCD p % 8, and the grid has
+  // ceil(R nsplit / 8) * 8 * ngroups blocks (a block past the last pair has no work).
   const int ngroups = H / kHG;
-  const BlockWork bw = block_work(nsplit);
-  if (bw.unit >= units) return;
-  const int split = bw.split;
-  const int grp16 = bw.unit % ngroups;
-  const int r = bw.unit / ngroups;
+  const int slot = blockIdx.x >> 3;
+  const int grp16 = slot % ngroups;
+  const int pair = (slot / ngroups) * 8 + (blockIdx.x & 7);
+  if (pair >= units / ngroups * nsplit) return;
+  const int split = pair % nsplit;
+  const int r = pair / nsplit;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
 
@@ -823,7 +827,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       }
     } else {
       const int64_t units = (int64_t)g.R * (g.H / kHG);
-      const int nblocks = work_blocks(units, p.nsplit);
+      const int nblocks = (int)(((int64_t)g.R * p.nsplit + 7) / 8 * 8 * (g.H / kHG));
       if (p.nsplit == 1)
         attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
                                                              g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
