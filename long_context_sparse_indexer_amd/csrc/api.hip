@@ -160,7 +160,8 @@ dsa_status_t hip_status(hipError_t e, const char* what) {
 int64_t step_ld(const dsa::Geo& g) { return ((int64_t)std::max(g.max_row_len, 1) + 63) / 64 * 64; }
 
 size_t step_bytes(const dsa::Geo& g) {
-  return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) + dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
+  return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) +
+         2 * dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
          std::max(dsa::topk_workspace_bytes(g), dsa::attn_workspace_bytes(g));
 }
 
@@ -189,7 +190,7 @@ dsa_status_t dsa_topk(const dsa_problem_t* problem, const dsa_layout_t* layout, 
   if ((st = check_scores(g, scores, scores_ld)) != DSA_OK) return st;
   DSA_CHECK(topk_idx != nullptr, DSA_EINVAL, "topk_idx is NULL");
   if ((st = check_ws(workspace, workspace_bytes, dsa::topk_workspace_bytes(g))) != DSA_OK) return st;
-  return hip_status(dsa::launch_topk(g, scores, scores_ld, topk_idx, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(dsa::launch_topk(g, scores, scores_ld, topk_idx, workspace, nullptr, static_cast<hipStream_t>(stream)),
                     "top-k launch");
 }
 
@@ -201,7 +202,8 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* problem, const dsa_layout_
   if (st != DSA_OK) return st;
   if ((st = check_attn_args(g, q, kv_pool, topk_idx, out)) != DSA_OK) return st;
   if ((st = check_ws(workspace, workspace_bytes, dsa::attn_workspace_bytes(g))) != DSA_OK) return st;
-  return hip_status(dsa::launch_attn(g, q, kv_pool, topk_idx, out, lse, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(dsa::launch_attn(g, q, kv_pool, topk_idx, out, lse, workspace, nullptr,
+                                     static_cast<hipStream_t>(stream)),
                     "attention launch");
 }
 
@@ -225,6 +227,9 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
   int32_t* idx = reinterpret_cast<int32_t*>(ws);
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
   if (topk_idx) idx = topk_idx;
+  // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
+  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
   // fp8 indexer: its epilogue starts the selection (digit-1 histogram), so the top-k state is zeroed first
   const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
   const dsa::TopkState tstate = dsa::topk_state(g, ws);
@@ -234,12 +239,13 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
                        "indexer launch")) != DSA_OK)
     return st;
   if (fuse) {
-    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, true, s), "top-k launch")) != DSA_OK)
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, true, pool_rows, s), "top-k launch")) !=
+        DSA_OK)
       return st;
-  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, s), "top-k launch")) != DSA_OK) {
+  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, pool_rows, s), "top-k launch")) != DSA_OK) {
     return st;
   }
-  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, s), "attention launch");
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, pool_rows, s), "attention launch");
 }
 
 size_t dsa_workspace_bytes(const dsa_problem_t* problem, int32_t op) {

@@ -113,7 +113,8 @@ __host__ __forceinline__ int work_blocks(int64_t units, int nsplit) { return (in
 template <bool kSplit>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
-    int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
     unsigned short* __restrict__ out,
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
@@ -145,13 +146,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   const int32_t* idx = topk_idx + (int64_t)r * k + begin;
 
   // Every slot of the split -> physical row before any gather, so that the gathers are the only loads in
-  // flight later: all position loads are issued together, then all page-table loads (two round trips).
+  // flight later: all position loads are issued together, then all page-table loads (two round trips), or the
+  // pool rows the top-k wrote beside the selection are loaded directly (one).
   constexpr int kSlotsPerThread = kMaxSplitLen / 256;
+  const int32_t* slot_src = pool_rows ? pool_rows + (int64_t)r * k + begin : idx;
   int pr[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int s = j * 256 + threadIdx.x;
-    pr[j] = s < len ? idx[s] : -1;
+    pr[j] = s < len ? slot_src[s] : -1;
   }
 
   // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8
@@ -162,9 +165,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 32);
   }
 
+  if (!pool_rows)
 #pragma unroll
-  for (int j = 0; j < kSlotsPerThread; ++j)
-    pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+    for (int j = 0; j < kSlotsPerThread; ++j)
+      pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
   {
     // slot j * 256 + 64 wave + lane; the wave's first slot with a position comes from the ballots
     int first = 0x7fffffff;
@@ -361,7 +365,8 @@ __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restri
 template <int NW, bool kSplit>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
-    int k, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
     unsigned short* __restrict__ out,
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
@@ -399,11 +404,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   // j * 64 NW + 64 wave + lane belongs to 64-slot group j NW + wave, so a ballot gives the validity bits of
   // two chunks.
   constexpr int kSlotsPerThread = kWideMaxSplitLen / (64 * NW);
+  const int32_t* slot_src = pool_rows ? pool_rows + (int64_t)r * k + begin : idx;  // pool rows: no lookup
   int pr[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int sl = (j * NW + wave) * 64 + lane;
-    pr[j] = sl < len ? idx[sl] : -1;
+    pr[j] = sl < len ? slot_src[sl] : -1;
   }
   // the queries load while the positions and then the page-table entries arrive
   // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
@@ -415,9 +421,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   }
   v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
 
+  if (!pool_rows)
 #pragma unroll
-  for (int j = 0; j < kSlotsPerThread; ++j)
-    pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+    for (int j = 0; j < kSlotsPerThread; ++j)
+      pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
   {
     int first = 0x7fffffff;
 #pragma unroll
@@ -786,17 +793,19 @@ Partials carve_partials(const Geo& g, int nsplit, void* workspace) {
 
 template <int NW>
 void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const unsigned short* kp,
-                const int32_t* topk_idx, void* out, float* lse, const Partials& pt, float scale_log2,
-                hipStream_t stream) {
+                const int32_t* topk_idx, const int32_t* pool_rows, void* out, float* lse, const Partials& pt,
+                float scale_log2, hipStream_t stream) {
   const int64_t units = (int64_t)g.R * (g.H / (32 * NW));
   const int nblocks = work_blocks(units, p.nsplit);
   if (p.nsplit == 1)
     attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1, (int)units,
+        qp, kp, topk_idx, g.k, pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
+        (int)units,
         p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr, nullptr);
   else
     attn_bf16_mqa_kernel<NW, true><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, p.nsplit,
+        qp, kp, topk_idx, g.k, pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
+        p.nsplit,
         (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex, pt.lse);
 }
 
@@ -811,7 +820,7 @@ size_t attn_workspace_bytes(const Geo& g) {
 }
 
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
-                       float* lse, void* workspace, hipStream_t stream) {
+                       float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   if (g.kv_dtype == 1 /* BF16 */) {
     const AttnPlan p = plan(g);
@@ -821,21 +830,23 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
     const Partials pt = carve_partials(g, p.nsplit, workspace);
     if (p.nw > 0) {
       switch (p.nw) {
-        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
-        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
-        default: launch_mqa<4>(g, p, qp, kp, topk_idx, out, lse, pt, scale_log2, stream); break;
+        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
+        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
+        default: launch_mqa<4>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
       }
     } else {
       const int64_t units = (int64_t)g.R * (g.H / kHG);
       const int nblocks = (int)(((int64_t)g.R * p.nsplit + 7) / 8 * 8 * (g.H / kHG));
       if (p.nsplit == 1)
-        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
+        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_seq,
+                                                             g.page_table,
                                                              g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
                                                              (int)units, p.split_len, scale_log2,
                                                              static_cast<unsigned short*>(out), lse, nullptr,
                                                              nullptr, nullptr);
       else
-        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, g.row_seq, g.page_table,
+        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_seq,
+                                                            g.page_table,
                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
                                                             p.nsplit, (int)units, p.split_len, scale_log2, nullptr,
                                                             nullptr, pt.o, pt.ex, pt.lse);

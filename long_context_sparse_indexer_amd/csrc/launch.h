@@ -42,15 +42,18 @@ constexpr int kTopkChunk = 4096;
 size_t topk_workspace_bytes(const Geo& g);
 TopkState topk_state(const Geo& g, void* workspace);
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream);
-// hist_done: the digit-1 histogram and threshold were already produced (by the indexer)
+// hist_done: the digit-1 histogram and threshold were already produced (by the indexer).  pool_rows: if
+// non-NULL, [R, k] int32 receiving the pool row of every selected slot (-1 for padding), for the attention.
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              bool hist_done, hipStream_t stream);
+                              bool hist_done, int32_t* pool_rows, hipStream_t stream);
 hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                       hipStream_t stream);
+                       int32_t* pool_rows, hipStream_t stream);
 
 // attn.hip
 size_t attn_workspace_bytes(const Geo& g);
+// pool_rows: if non-NULL, the pool row of every selected slot (as written by the top-k), used instead of
+// looking the positions up in the page table (bf16 latents)
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
-                       float* lse, void* workspace, hipStream_t stream);
+                       float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream);
 
 }  // namespace dsa

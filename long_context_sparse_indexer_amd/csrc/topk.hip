@@ -115,6 +115,29 @@ struct RowList {
   __device__ int32_t p(int i) const { return i; }
 };
 
+// Where the fused step wants the pool row of every selected slot ([R, k] int32, -1 for padding); `out` NULL
+// when no pool rows are wanted.
+struct PoolRows {
+  int32_t* out;
+  const int32_t* row_seq;
+  const int32_t* page_table;
+  int num_seqs, max_pages, num_pages, log2ps;
+};
+
+// Pool rows of selected positions, written beside the selection when `out` is non-NULL (the fused step hands
+// them to the attention kernels, which then skip the page-table lookup).  The row's page table is read from
+// LDS when it was staged there (`pt`), else from global memory.
+struct RowMap {
+  int32_t* out;
+  const int32_t* pt;  // page ids of the row's sequence: LDS copy or global row of the page table
+  int max_pages, num_pages, log2ps;
+  __device__ int32_t row(int32_t pos) const {
+    const int lp = min(pos >> log2ps, max_pages - 1);
+    const int page = min(max(pt[lp], 0), num_pages - 1);
+    return (page << log2ps) | (pos & ((1 << log2ps) - 1));
+  }
+};
+
 // Among entries whose key agrees with `prefix` above bit lo+bits, find the digit (key >> lo) & (2^bits - 1)
 // holding the need-th largest key; returns it and lowers `need` by the number of entries above it.
 template <int NT, class List>
@@ -158,8 +181,9 @@ __device__ uint32_t refine_digit(const List& L, int len, uint32_t prefix, int lo
 // Writes, in list (= position) order, every entry with key > T and the first eq_need entries with key == T.
 // Each wave owns a contiguous stretch of the list; one pass counts, one barrier publishes the per-wave counts,
 // every wave adds up those of the waves before it, and a second pass writes.
-template <int NT, class List>
-__device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out) {
+template <int NT, class List, class Rows>
+__device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out,
+                                const Rows& rows) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t w_gt[NW], w_eq[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -210,7 +234,10 @@ __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_
       const bool sel = in && (key[u] > T || (is_eq && rank < eq_need));
       const uint64_t selm = __ballot(sel);
       const uint32_t slot = slot_run + (uint32_t)__popcll(selm & below);
-      if (sel && slot < (uint32_t)keff) out[slot] = pos[u];
+      if (sel && slot < (uint32_t)keff) {
+        out[slot] = pos[u];
+        if (rows.out) rows.out[slot] = rows.row(pos[u]);
+      }
       eq_run += (uint32_t)__popcll(eqm);
       slot_run += (uint32_t)__popcll(selm);
     }
@@ -269,6 +296,8 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* wt
   }
 }
 
+constexpr int kResPages = 4096;  // page-table entries a resolve block stages in LDS
+
 // LDS of the resolve step.
 struct ResolveLds {
   uint32_t key[kCap];
@@ -279,6 +308,7 @@ struct ResolveLds {
   uint32_t scan[1024 / 64 + 1];  // one word per wave of the largest block, plus the total
   alignas(16) uint32_t scan2[2 * (1024 / 64)];
   uint32_t bin[64];               // low digits of the keys in bin (b1, b2), when there are at most 64
+  int32_t pt[kResPages];          // page ids of the row's sequence, when they fit
 };
 
 // Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of `copies`
@@ -390,7 +420,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
                                                             const uint32_t* __restrict__ seg_cnt,
                                                             const uint32_t* __restrict__ seg_off,
                                                             const uint64_t* __restrict__ cand, int nblk_max,
-                                                            int32_t* __restrict__ topk_idx) {
+                                                            int32_t* __restrict__ topk_idx, PoolRows pr) {
   static_assert(kRes >= kTopkMaxBlocksPerRow, "one chunk per thread");
   __shared__ ResolveLds S;
   __shared__ uint32_t s_b2, s_A2, s_nb, s_nbin;
@@ -398,10 +428,20 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
   int32_t* out = topk_idx + (int64_t)r * k;
+  // pool rows of the selection (fused step): the sequence's page ids, staged in LDS when they fit
+  const int32_t* gpt = pr.out ? pr.page_table + (int64_t)clamp_seq(pr.row_seq[r], pr.num_seqs) * pr.max_pages : nullptr;
+  const bool pt_lds = pr.out && pr.max_pages <= kResPages;
+  RowMap rows{pr.out ? pr.out + (int64_t)r * k : nullptr, pt_lds ? S.pt : gpt, pr.max_pages, pr.num_pages, pr.log2ps};
   if (keff >= n) {
-    for (int i = threadIdx.x; i < k; i += kRes) out[i] = i < n ? i : -1;
+    const RowMap grows{rows.out, gpt, pr.max_pages, pr.num_pages, pr.log2ps};
+    for (int i = threadIdx.x; i < k; i += kRes) {
+      out[i] = i < n ? i : -1;
+      if (grows.out) grows.out[i] = i < n ? grows.row(i) : -1;
+    }
     return;
   }
+  if (pt_lds)  // read before the first barrier below, used after it
+    for (int i = threadIdx.x; i < pr.max_pages; i += kRes) S.pt[i] = gpt[i];
   const float* row = scores + (int64_t)r * ld;
   // every read that does not depend on another is issued here, together: the thresholds, the candidate count,
   // the segment tables and the digit-2 histogram; the candidates follow as soon as their count arrives and stay
@@ -511,16 +551,19 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     } else {
       d3 = refine_digit<kRes>(L, (int)len, prefix, 0, 8, need, S.h, S.scan);
     }
-    write_selection<kRes>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out);
+    write_selection<kRes>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out, rows);
   } else {
     const RowList L{row};
     uint32_t need = (uint32_t)keff;
     const uint32_t d1 = refine_digit<kRes>(L, n, 0u, 20, 12, need, S.h, S.scan);
     const uint32_t d2 = refine_digit<kRes>(L, n, d1, 8, 12, need, S.h, S.scan);
     const uint32_t d3 = refine_digit<kRes>(L, n, (d1 << 12) | d2, 0, 8, need, S.h, S.scan);
-    write_selection<kRes>(L, n, (d1 << 20) | (d2 << 8) | d3, need, keff, out);
+    write_selection<kRes>(L, n, (d1 << 20) | (d2 << 8) | d3, need, keff, out, rows);
   }
-  for (int i = keff + threadIdx.x; i < k; i += kRes) out[i] = -1;
+  for (int i = keff + threadIdx.x; i < k; i += kRes) {
+    out[i] = -1;
+    if (rows.out) rows.out[i] = -1;
+  }
 }
 
 }  // namespace
@@ -552,7 +595,7 @@ int chunks_per_block(const Geo& g, int nblk) {
 }
 
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              bool hist_done, hipStream_t stream) {
+                              bool hist_done, int32_t* pool_rows, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
   const int cpb = chunks_per_block(g, w.nblk);
@@ -562,15 +605,17 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
                                                 w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies, cpb);
   topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,
-                                                w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx);
+                                                w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx,
+                                                PoolRows{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages,
+                                                         g.num_pages, g.log2ps});
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                       hipStream_t stream) {
+                       int32_t* pool_rows, hipStream_t stream) {
   hipError_t e = launch_topk_zero(g, workspace, stream);
   if (e != hipSuccess) return e;
-  return launch_topk_select(g, scores, ld, topk_idx, workspace, false, stream);
+  return launch_topk_select(g, scores, ld, topk_idx, workspace, false, pool_rows, stream);
 }
 
 }  // namespace dsa
