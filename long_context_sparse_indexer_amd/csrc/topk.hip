@@ -410,6 +410,91 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   }
 }
 
+// Filter for blocks that cover several chunks (long rows, large batches).  The chunk loop stages each chunk's
+// candidates in LDS (position order within the chunk, chunks in order) and counts digit 2 of the keys in bin b1
+// in an LDS histogram, so its only memory traffic is the next chunk's scores, loaded while the current one is
+// filtered.  When the stage is full, and at the end, the block reserves one range of the row's candidate list
+// with one atomic, copies the stage out and writes the segment table of the chunks it holds; the histogram is
+// merged once at the end.
+constexpr int kStageCap = 6144;  // staged candidates per block (48 KiB; two 1024-thread blocks fit a CU)
+static_assert(kCh <= kStageCap, "one chunk always fits an empty stage");
+
+__global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int max_row_len, int k,
+    const uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
+    uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off,
+    uint64_t* __restrict__ cand, int nblk_max, int copies, int cpb) {
+  __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
+  __shared__ uint64_t stage[kStageCap];
+  __shared__ uint32_t h2l[kTopkBins];
+  __shared__ uint32_t chunk_n[kTopkMaxBlocksPerRow];  // candidates of each staged chunk
+  __shared__ uint32_t seg_base, s_b1, s_A1;
+  const int r = blockIdx.y;
+  const int n = clamp_len(row_len[r], max_row_len);
+  const int keff = min(k, n);
+  const int nchunk = (n + kCh - 1) / kCh;
+  const int c0 = (int)blockIdx.x * cpb;
+  if (keff >= n || c0 >= nchunk) return;
+  const float* row = scores + (int64_t)r * ld;
+  v4f x = load_raw(row, c0, n);  // the first chunk loads while the threshold is found
+  for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h2l[i] = 0u;
+  threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
+  const uint32_t b1 = s_b1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
+  const int c1 = min(nchunk, c0 + cpb);
+  // staged chunks [cs, ch) hold `staged` candidates
+  int cs = c0;
+  uint32_t staged = 0;
+  auto flush = [&](int ch) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) seg_base = atomicAdd(&cnt[4 * r + 2], staged);
+    __syncthreads();
+    const uint32_t base = seg_base;
+    uint64_t* dst = cand + (int64_t)r * kCap;
+    for (uint32_t i = threadIdx.x; i < staged; i += kTpb)
+      if (base + i < (uint32_t)kCap) dst[base + i] = stage[i];  // on overflow the resolve rescans the row
+    // segment table of the staged chunks: thread t holds chunk cs + t (at most kTopkMaxBlocksPerRow of them)
+    const int t = threadIdx.x;
+    const uint32_t cn = t < ch - cs ? chunk_n[t] : 0u;
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan(cn, scan, tot);
+    if (t < ch - cs) {
+      seg_cnt[(int64_t)r * nblk_max + cs + t] = cn;
+      seg_off[(int64_t)r * nblk_max + cs + t] = base + pre;
+    }
+    cs = ch;
+    staged = 0;
+  };
+  for (int ch = c0; ch < c1; ++ch) {
+    const v4f cur = x;
+    if (ch + 1 < c1) x = load_raw(row, ch + 1, n);  // next chunk in flight while this one is filtered
+    const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
+    uint32_t key[kEpt];
+    uint32_t c = 0, take = 0;
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) {
+      key[e] = order_key(cur[e]);
+      const uint32_t d1 = key[e] >> 20;
+      if (first + e < n && d1 >= b1) {
+        ++c;
+        take |= 1u << e;
+        if (d1 == b1) atomicAdd(&h2l[(key[e] >> 8) & 0xfffu], 1u);
+      }
+    }
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(c, scan, total);
+    if (staged + total > (uint32_t)kStageCap) flush(ch);  // uniform: total is the block's
+    uint32_t o = staged + off;
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e)
+      if (take & (1u << e)) stage[o++] = ((uint64_t)(first + e) << 32) | key[e];
+    if (threadIdx.x == 0) chunk_n[ch - cs] = total;
+    staged += total;
+  }
+  __syncthreads();  // the stage, chunk counts and histogram are complete
+  flush(c1);
+  hist_merge<kTpb>(h2l, hist2 + (int64_t)r * kTopkBins);
+}
+
 constexpr int kRes = 1024;  // threads of the resolve block
 
 __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
@@ -602,6 +687,11 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
   if (!hist_done)
     topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.copies, cpb);
+  if (cpb > 1)
+    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2,
+                                                         w.cnt, w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies,
+                                                         cpb);
+  else
   topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
                                                 w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies, cpb);
   topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,

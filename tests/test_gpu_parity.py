@@ -211,6 +211,16 @@ def test_topk_negative_zero_and_signs():
     _expect_exact(sc, [6000, 6000], 5999)
 
 
+def test_topk_staged_flush_and_ties():
+    # one filter block's chunks hold 10000 tied candidates: more than it stages at once (it reserves list space
+    # twice), fewer than the row's candidate list holds (the resolve keeps its LDS path); lowest positions win
+    rng = np.random.default_rng(8)
+    n = 1 << 20
+    sc = rng.standard_normal((1, n)).astype(np.float32)
+    sc[0, 300000:310000] = 100.0
+    _expect_exact(sc, [n], 2048)
+
+
 def test_topk_long_row_1m():
     rng = np.random.default_rng(7)
     n = 1 << 20
