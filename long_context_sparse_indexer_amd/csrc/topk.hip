@@ -673,10 +673,12 @@ hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
 }
 
 // Chunks per histogram / filter block: at most 32 blocks per row (each filter block re-reads the row's
-// histogram replicas to find the threshold) and about 2048 blocks overall for large batches.
+// histogram replicas to find the threshold) and about 512 blocks overall (two 1024-thread blocks per CU) once
+// there are enough chunks: a block that covers several chunks stages its candidates and keeps the next chunk's
+// scores in flight (64 rows of 16 chunks: 34 -> 29 us for the top-k).
 int chunks_per_block(const Geo& g, int nblk) {
   const int64_t total = (int64_t)nblk * g.R;
-  return (int)std::min<int64_t>(nblk, std::max<int64_t>({1, (nblk + 31) / 32, total / 2048}));
+  return (int)std::min<int64_t>(nblk, std::max<int64_t>({1, (nblk + 31) / 32, total / 512}));
 }
 
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
