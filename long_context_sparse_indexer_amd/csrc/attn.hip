@@ -630,7 +630,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const unsigned short*
   const int d = 4 * threadIdx.x;
   const int64_t row0 = (int64_t)r * nsplit * H + h;  // partial row of split 0; split j is j * H further
   float ls = -INFINITY;
-  if (threadIdx.x < 64 && threadIdx.x < nsplit) ls = part_lse[row0 + (int64_t)threadIdx.x * H];
+  if (threadIdx.x < 64 && (int)threadIdx.x < nsplit) ls = part_lse[row0 + (int64_t)threadIdx.x * H];
   auto piece = [&](int j) { return *reinterpret_cast<const v4s*>(part_o + (row0 + (int64_t)j * H) * kDC + d); };
   auto expo = [&](int j) { return part_exp[row0 + (int64_t)j * H]; };
   v4s v[kCombineBatch];
