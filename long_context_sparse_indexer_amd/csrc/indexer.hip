@@ -137,11 +137,10 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
         }
         part[u] = lin + ab;
       }
-      // half 0 finishes subtile 2 p and half 1 subtile 2 p + 1: one exchange per pair
-      const float keep = half ? part[1] : part[0];
-      const float send = half ? part[0] : part[1];
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
-      const float v = cur.skm[p] * (0.5f * (keep + __uint_as_float(half ? sw[0] : sw[1])));
+      // half 0 finishes subtile 2 p and half 1 subtile 2 p + 1: v_permlane32_swap of the two subtiles' partial
+      // sums hands each half the other half's sum of the subtile it stores
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+      const float v = cur.skm[p] * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1])));
       const int64_t pos = position(t, 2 * p + half);
       // the buffer ends at the row's visible length: stores past it are dropped
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)pos * 4, 0, 0);
@@ -335,9 +334,8 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
 #pragma unroll 1
     for (int g = 0; g < kPfRows / 8; ++g) {
       if (8 * g >= rows) break;  // uniform
-      // linear term of rows 8 g + 4 half + e, arranged per pair p for the lane half that keeps it (linK: the
-      // subtile this half stores) and the half it is sent to (linS)
-      float linK[kPfSub / 2][4], linS[kPfSub / 2][4];
+      // linear term of rows 8 g + 4 half + e for subtile 2 p + t of each pair p
+      float lin2[kPfSub / 2][2][4];
 #pragma unroll
       for (int p = 0; p < kPfSub / 2; ++p) {
         float lin[2][4];
@@ -359,10 +357,9 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
           for (int e = 0; e < 4; ++e) lin[t][e] = ((acc[12 + e] + acc[8 + e]) + acc[4 + e]) + acc[e];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          linK[p][e] = half ? lin[1][e] : lin[0][e];
-          linS[p][e] = half ? lin[0][e] : lin[1][e];
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lin2[p][t][e] = lin[t][e];
       }
 
 #pragma unroll 1
@@ -408,11 +405,13 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
               for (int i = 0; i < 16; ++i) acc_ab = fmaf(wq[hb][i], fabsf(prev[i]), acc_ab);
               ab[t] = acc_ab;
               if (kp % U == U - 1) {  // pair p complete: half 0 finishes subtile 2p, half 1 subtile 2p + 1
-                const float mine = half ? ab[1] : ab[0], other = half ? ab[0] : ab[1];
-                const float keep = fmaf(ownf, linK[p][e], mine);
-                const float send = fmaf(ownf, linS[p][e], other);
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
-                const float total = keep + __uint_as_float(half ? sw[0] : sw[1]);
+                // the half that holds row q's linear term adds it to both subtiles; v_permlane32_swap of the
+                // (subtile 2p, subtile 2p + 1) sums then hands each half the other half's sum of the subtile it
+                // stores, so the total is the sum of the two swapped registers
+                const float s0 = fmaf(ownf, lin2[p][0][e], ab[0]);
+                const float s1 = fmaf(ownf, lin2[p][1][e], ab[1]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+                const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], soff, 0);
               }
             }
