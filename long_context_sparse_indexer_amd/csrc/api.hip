@@ -230,16 +230,15 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
   // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
   int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? reinterpret_cast<int32_t*>(ws) : nullptr;
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
-  // fp8 indexer: its epilogue starts the selection (digit-1 histogram), so the top-k state is zeroed first
+  // the per-row fp8 indexer clears the top-k state once its scores are out, sparing the top-k its zeroing launch
   const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
   const dsa::TopkState tstate = dsa::topk_state(g, ws);
-  if (fuse && (st = hip_status(dsa::launch_topk_zero(g, ws, s), "top-k launch")) != DSA_OK) return st;
   if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,
                                            fuse ? &tstate : nullptr, s),
                        "indexer launch")) != DSA_OK)
     return st;
   if (fuse) {
-    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, true, pool_rows, s), "top-k launch")) !=
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, pool_rows, s), "top-k launch")) !=
         DSA_OK)
       return st;
   } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, pool_rows, s), "top-k launch")) != DSA_OK) {

@@ -60,17 +60,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Exclusive prefix of `v` over the lanes of a wave (and the wave total).
+// Exclusive prefix of `v` over the lanes of a wave (and the wave total), with DPP lane moves instead of LDS-routed
+// shuffles: shifts by 1, 2, 4 and 8 lanes scan each row of 16 (a lane whose source falls outside its row adds 0),
+// then row_bcast:15 adds row 0's total into row 1 and row 2's into row 3, and row_bcast:31 adds the total of rows
+// 0-1 into rows 2-3.  All 64 lanes must be active.
 __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, kWave - 1, kWave);
-  return x - v;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  total = (uint32_t)__builtin_amdgcn_readlane(x, 63);
+  return (uint32_t)x - v;
 }
 
 // Block-wide exclusive scan of one value per thread.  `scratch` holds blockDim.x / 64 + 1 words of LDS.

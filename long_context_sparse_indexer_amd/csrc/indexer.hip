@@ -17,9 +17,9 @@
 // Every key row is read once, as 32-byte pieces: one wave covers 32 consecutive positions = 2 KiB of
 // contiguous pool memory (a 32-aligned run never crosses a page of >= 32 positions).
 //
-// In the fused step the epilogue also starts the top-k selection: each block histograms the first 12 bits
-// of its scores' order-preserving keys in LDS and merges the non-empty bins into the row's histogram (see
-// topk.hip).  The key loads are issued before the query operands so that both are in flight together.
+// In the fused step block 0 of each row also clears the row's top-k state once its scores are out, so the
+// selection needs no zeroing launch of its own.  The key loads are issued before the query operands so that
+// both are in flight together.
 #include <algorithm>
 
 #include "common.h"
@@ -37,25 +37,31 @@ __device__ __forceinline__ void require_loaded(const v8i& x) { asm volatile("" :
 constexpr int kIdxSub = 4;                          // 32-position subtiles per wave
 constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread block
 
-template <int HB, bool kHist>  // HB = number of 32-head blocks (H_I = 32 * HB); kHist = fused top-k histogram
+template <int HB>  // HB = number of 32-head blocks (H_I = 32 * HB)
 __global__ __launch_bounds__(256) void indexer_f8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
-    int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, int k,
-    uint32_t* __restrict__ hist1, int copies, int tiles_per_block) {
+    int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
+    int tiles_per_block) {
   constexpr int H_I = 32 * HB;
-  __shared__ uint32_t h[kHist ? kTopkBins : 1];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int64_t first = (int64_t)blockIdx.x * tiles_per_block * kIdxTile;
-  if (first >= n) return;
-  const int ntile = (int)min((int64_t)tiles_per_block, (n - first + kIdxTile - 1) / kIdxTile);
-  const bool do_hist = kHist && k < n;  // uniform over the block; a row with k >= n keeps every position
-  if (do_hist) {
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) h[i] = 0u;
-    __syncthreads();
+  // the row's top-k state, cleared by block 0 as its last work (stores issued earlier would hold up the waits
+  // for its key loads, which count in the same in-order counter)
+  auto clear_state = [&]() __attribute__((always_inline)) {
+    if (!clear.hist || blockIdx.x != 0) return;
+    const v4i z = {0, 0, 0, 0};
+    v4i* h = reinterpret_cast<v4i*>(clear.hist + (int64_t)r * kTopkBins);
+    for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h[i] = z;
+    if (threadIdx.x == 0) reinterpret_cast<v4i*>(clear.cnt)[r] = z;
+  };
+  if (first >= n) {
+    clear_state();
+    return;
   }
+  const int ntile = (int)min((int64_t)tiles_per_block, (n - first + kIdxTile - 1) / kIdxTile);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
@@ -144,7 +150,6 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
       const int64_t pos = position(t, 2 * p + half);
       // the buffer ends at the row's visible length: stores past it are dropped
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)pos * 4, 0, 0);
-      if (do_hist && pos < n) atomicAdd(&h[order_key(v) >> 20], 1u);
     }
   };
 
@@ -159,10 +164,7 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
     if (t + 2 < ntile) issue(t + 2, cur);
     compute(t + 1, other);
   }
-  if (do_hist) {
-    __syncthreads();
-    hist_merge<256>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
-  }
+  clear_state();
 }
 
 // Chunked prefill: consecutive rows of one sequence score the same keys, so the contraction is a real GEMM
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 }  // namespace
 
-template <int HB, bool kHist>
+template <int HB>
 void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w, const uint8_t* kp,
                const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse, hipStream_t stream) {
   // one 512-position tile per block up to kIdxTargetBlocks blocks (small, latency-bound problems spread as
@@ -465,9 +467,9 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
   const int64_t tiles = (int64_t)tiles_row * g.R;
   const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / kIdxTargetBlocks));
   dim3 grid((tiles_row + per - 1) / per, g.R);
-  indexer_f8_kernel<HB, kHist><<<grid, 256, 0, stream>>>(
+  indexer_f8_kernel<HB><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, g.k, fuse ? fuse->hist1 : nullptr, fuse ? fuse->copies : 1, per);
+      g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr, nullptr}, per);
 }
 
 template <int HB>
@@ -488,7 +490,7 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
                           const TopkState* fuse, hipStream_t stream) {
   if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
   if (indexer_tiled(g)) {
-    if (fuse) return hipErrorInvalidValue;  // the tiled kernel has no histogram epilogue
+    if (fuse) return hipErrorInvalidValue;  // the tiled kernel does not clear the top-k state
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
     if (g.H_I == 64) launch_f8_tiled<2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
@@ -498,14 +500,10 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
   if (g.idx_dtype == 2 /* F8E4M3 */) {
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
-    if (g.H_I == 64) {
-      if (fuse) launch_f8<2, true>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-      else launch_f8<2, false>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-    } else {
-      if (fuse) launch_f8<1, true>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-      else launch_f8<1, false>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-    }
+    if (g.H_I == 64) launch_f8<2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    else launch_f8<1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
   } else {
+    if (fuse) return hipErrorInvalidValue;  // only the fp8 kernel clears the top-k state
     dim3 grid((g.max_row_len + 255) / 256, g.R);
     size_t lds = sizeof(float) * (size_t)(g.H_I * g.d_I + g.H_I);
     indexer_f32_kernel<<<grid, 256, lds, stream>>>(static_cast<const float*>(q_idx), head_w,

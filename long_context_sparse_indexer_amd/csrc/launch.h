@@ -21,15 +21,16 @@ struct Geo {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Digit-1 radix-select state the indexer can fill in its epilogue (see topk.hip).
+// Per-row top-k state that must start at zero: the candidate histogram and the candidate counter.  In the fused
+// step the indexer clears it (block 0 of each row, after its scores), sparing the top-k a zeroing launch.
 struct TopkState {
-  uint32_t* hist1;  // [R, copies, 4096]
-  int copies;
+  uint32_t* hist;  // [R, 4096]
+  uint32_t* cnt;   // [R, 4]
 };
 
 // indexer.hip.  fp8 problems whose rows come in groups of at least kTiledMinRows per sequence (chunked prefill)
-// run the tiled GEMM kernel, which takes no `fuse`.  Otherwise, with `fuse` non-NULL the indexer also builds the top-k digit-1 histogram; the state must have
-// been zeroed (launch_topk_zero) earlier on the stream.
+// run the tiled GEMM kernel, which takes no `fuse`.  Otherwise, with `fuse` non-NULL the indexer also clears the
+// top-k state.
 constexpr int kTiledMinRows = 8;
 bool indexer_tiled(const Geo& g);
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
@@ -42,10 +43,11 @@ constexpr int kTopkChunk = 4096;
 size_t topk_workspace_bytes(const Geo& g);
 TopkState topk_state(const Geo& g, void* workspace);
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream);
-// hist_done: the digit-1 histogram and threshold were already produced (by the indexer).  pool_rows: if
-// non-NULL, [R, k] int32 receiving the pool row of every selected slot (-1 for padding), for the attention.
+// Selection over stored scores whose top-k state is already zero (launch_topk_zero, or the fused indexer).
+// pool_rows: if non-NULL, [R, k] int32 receiving the pool row of every selected slot (-1 for padding), for the
+// attention.
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              bool hist_done, int32_t* pool_rows, hipStream_t stream);
+                              int32_t* pool_rows, hipStream_t stream);
 hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
                        int32_t* pool_rows, hipStream_t stream);
 

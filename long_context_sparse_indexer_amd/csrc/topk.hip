@@ -3,18 +3,18 @@
 // row shorter than the budget is read in full).  Equal scores are taken lowest position first; the result
 // is written in increasing position order, padded with -1.
 //
-// Scores become order-preserving 32-bit keys, selected by a radix select over three digits
-// (bits 31..20, 19..8, 7..0).  Every hand-over between blocks happens at a kernel boundary:
-//   digit 1  a per-row histogram of the first digit, accumulated in LDS per block and merged with one global
-//            atomic per non-empty bin -- in the indexer's epilogue (fused step) or in a histogram pass over
-//            stored scores (standalone call).
-//   filter   grid (4096-score chunks, rows): every block finds the threshold bin b1 (the bin holding the
-//            k_eff-th largest key) from the row histogram, writes the keys with digit 1 >= b1 in position
-//            order into a segment of the row's candidate list, and histograms digit 2 of the keys in bin b1.
-//   resolve  one 1024-thread block per row: finds b2 from the digit-2 histogram, places the candidates
-//            (k + one bin's worth) in position order in LDS, settles digit 3 among the few keys of (b1, b2),
-//            and writes the selection with a two-pass wave-ballot compaction.  A row whose candidates overflow
-//            the list (heavily tied scores) is resolved over its whole stored score row instead.
+// Scores become order-preserving 32-bit keys.  Every hand-over between blocks happens at a kernel boundary:
+//   filter   grid (4096-score chunks, rows): every block first finds the row's floor, the 20-bit key prefix of a
+//            sampled score that comfortably more than k_eff scores of the row exceed.  The sample is a fixed set
+//            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram.  The
+//            block then writes the keys whose first 20 bits reach the floor, in position order, into a segment of
+//            the row's candidate list, and counts them in a 4096-bin histogram of their 20-bit prefixes taken
+//            relative to the floor (the last bin open-ended).
+//   resolve  one 1024-thread block per row: finds the 20-bit prefix bin holding the k_eff-th largest key from
+//            that histogram, places the candidates in position order in LDS, settles the low 12 bits among the
+//            few keys of that bin, and writes the selection with a two-pass wave-ballot compaction.  A row whose
+//            sample overshot (fewer than k_eff candidates) or whose candidates overflow the list (heavily tied
+//            scores) is resolved over its whole stored score row instead, by a three-digit radix select.
 #include <algorithm>
 
 #include "common.h"
@@ -25,8 +25,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kCh = kTopkChunk;    // scores per filter / histogram block
-constexpr int kTpb = 1024;         // threads of histogram / filter blocks
+constexpr int kCh = kTopkChunk;    // scores per filter chunk
+constexpr int kTpb = 1024;         // threads of filter blocks
 constexpr int kEpt = kCh / kTpb;   // scores per thread (consecutive)
 constexpr int kCap = 12288;        // candidate entries a row keeps for the resolve step
 
@@ -34,10 +34,8 @@ Ws carve(const Geo& g, void* base) {
   Ws w;
   char* p = static_cast<char*>(base);
   w.nblk = std::max(1, (g.max_row_len + kCh - 1) / kCh);
-  w.copies = hist_copies(g.R);
   auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes); return q; };
-  w.hist1 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * w.copies * kTopkBins));
-  w.hist2 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
+  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
   w.cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.thr = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.seg_cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * w.nblk));
@@ -46,15 +44,12 @@ Ws carve(const Geo& g, void* base) {
   return w;
 }
 
-// Zeroes the histograms and the counters of every row (one block per row).
-__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2,
-                                                        uint32_t* __restrict__ cnt, int copies) {
+// Zeroes the candidate histogram and the counters of every row (one block per row).
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ cnt) {
   const int r = blockIdx.x;
   const v4i z = {0, 0, 0, 0};
-  v4i* h1 = reinterpret_cast<v4i*>(hist1 + (int64_t)r * copies * kTopkBins);
-  v4i* h2 = reinterpret_cast<v4i*>(hist2 + (int64_t)r * kTopkBins);
-  for (int i = threadIdx.x; i < copies * kTopkBins / 4; i += blockDim.x) h1[i] = z;
-  for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h2[i] = z;
+  v4i* h = reinterpret_cast<v4i*>(hist + (int64_t)r * kTopkBins);
+  for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h[i] = z;
   if (threadIdx.x == 0) reinterpret_cast<v4i*>(cnt)[r] = z;
 }
 
@@ -66,40 +61,6 @@ static_assert(kEpt == 4, "one 16-byte load per thread and chunk");
 __device__ __forceinline__ v4f load_raw(const float* __restrict__ row, int c, int n) {
   const int64_t f = (int64_t)c * kCh + threadIdx.x * kEpt;
   return *reinterpret_cast<const v4f*>(row + (f < n ? f : 0));
-}
-
-// First-digit histogram of stored scores (standalone top-k): a block covers `cpb` consecutive 4096-score
-// chunks of one row, accumulates them in LDS and merges once.
-__global__ __launch_bounds__(kTpb) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
-                                                         const int32_t* __restrict__ row_len, int max_row_len, int k,
-                                                         uint32_t* __restrict__ hist1, int copies, int cpb) {
-  __shared__ uint32_t h[kTopkBins];
-  const int r = blockIdx.y;
-  const int n = clamp_len(row_len[r], max_row_len);
-  const int nchunk = (n + kCh - 1) / kCh;
-  const int c0 = (int)blockIdx.x * cpb;
-  if (min(k, n) >= n || c0 >= nchunk) return;  // nothing to choose, or chunks past the row's end
-  for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h[i] = 0u;
-  __syncthreads();
-  const int c1 = min(nchunk, c0 + cpb);
-  const float* row = scores + (int64_t)r * ld;
-  auto count = [&](int c, const v4f& x) __attribute__((always_inline)) {
-    const int64_t f = (int64_t)c * kCh + threadIdx.x * kEpt;
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e)
-      if (f + e < n) atomicAdd(&h[order_key(x[e]) >> 20], 1u);
-  };
-  // two buffers in turn: chunk c + 1 is loading while chunk c is counted
-  v4f xa = load_raw(row, c0, n), xb;
-  for (int c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) xb = load_raw(row, c + 1, n);
-    count(c, xa);
-    if (c + 1 >= c1) break;
-    if (c + 2 < c1) xa = load_raw(row, c + 2, n);
-    count(c + 1, xb);
-  }
-  __syncthreads();
-  hist_merge<kTpb>(h, hist1 + ((int64_t)r * copies + blockIdx.x % copies) * kTopkBins);
 }
 
 // Candidate access for the resolve step: entries of the LDS list, or every position of the stored row.
@@ -311,23 +272,26 @@ struct ResolveLds {
   int32_t pt[kResPages];          // page ids of the row's sequence, when they fit
 };
 
-// Threshold bin of one digit: the bin b holding the need-th largest key of histogram `gh` (the sum of `copies`
-// consecutive 4096-bin replicas, top bin first), and the number of keys in bins above b.  Called by all NT
-// threads; the result lands in *b, *above.
+// The bin b of LDS histogram h (kTopkBins bins, complete: a barrier after its last update) holding the need-th
+// largest entry, counting from the top bin, and the number of entries in the bins above it; both stay as the
+// caller preset them when the histogram holds fewer than `need` entries.  With `clear`, every thread zeroes the
+// bins it read, so h is all zero on return.  Called by all NT threads; ends with a barrier, after which *b and
+// *above are valid.
 template <int NT>
-__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, int copies, uint32_t need,
-                                              uint32_t* scan, uint32_t* b, uint32_t* above_out) {
+__device__ __forceinline__ void lds_threshold_bin(uint32_t* h, uint32_t need, bool clear, uint32_t* scan,
+                                                  uint32_t* b, uint32_t* above_out) {
   constexpr int kPer = kTopkBins / NT;
   const int grp = NT - 1 - threadIdx.x;  // thread 0 owns the top bins
   uint32_t c[kPer];
   uint32_t local = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) c[j] = 0u;
-  for (int cp = 0; cp < copies; ++cp)
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = h[grp * kPer + j];
+    local += c[j];
+  }
+  if (clear)
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) c[j] += gh[cp * kTopkBins + grp * kPer + j];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) local += c[j];
+    for (int j = 0; j < kPer; ++j) h[grp * kPer + j] = 0u;
   uint32_t total;
   uint32_t above = block_scan1<NT>(local, scan, total);
   if (above < need && above + local >= need) {
@@ -343,15 +307,115 @@ __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ gh, i
   __syncthreads();
 }
 
+// A sampled row of n scores is sampled about n / kSampleDiv times (n / 64 measured slower: 1.7 us more per
+// 128K-position decode step, 8% more for a 4096-row prefill chunk, from the extra candidates).
+constexpr int kSampleDiv = 32;
+
+// The row's floor: the first 20 bits of the m-th largest score of a sample of the row, ranked in two rounds of an
+// LDS histogram: bits 31..20 of every sampled key, then bits 19..12 of those in the bin found (256 bins, scanned by
+// one wave).  The sample is S scores in S/4 runs of four (one 16-byte load each) spread evenly over the row, with
+// S the power of two in (n / 2d, n / d] for d = kSampleDiv, kept within [1024, 16384] (up to 65536 for rows past
+// 2^21): it reads a small part of the row and is the same in every block.  With mu = k_eff S/n the expected number
+// of sampled scores among the row's k_eff largest, m = mu + 8 sqrt(mu) + 16 puts the floor far enough below the
+// k_eff-th largest score that a row rarely has fewer than k_eff scores at or above it, while about
+// n m / S = k_eff + 8 sqrt(k_eff n / S) + 16 n / S scores reach it.  A row of at most one chunk is its own sample,
+// with m = k_eff: its floor is exactly the 20-bit prefix of the k_eff-th largest score.  h: kTopkBins words of
+// LDS, left all zero when `clear`; s: 4 words of LDS.  Called by all NT threads; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, bool clear,
+                                                 uint32_t* h, uint32_t* scan, uint32_t* s) {
+  constexpr int kGroup = 4;  // runs per thread held in registers: all of them up to S = 16384
+  int runs, m;
+  if (n <= kCh) {
+    runs = (n + 3) / 4;
+    m = keff;
+  } else {
+    const int cap = n > (1 << 21) ? 65536 : 16384;
+    const int S = min(cap, max(1024, 1 << (31 - __builtin_clz((unsigned)(n / kSampleDiv)))));
+    runs = S / 4;
+    const float mu = (float)keff * (float)S / (float)n;
+    m = min(S, (int)ceilf(mu + 8.f * sqrtf(mu) + 16.f));
+  }
+  const int ngroups = (runs + kGroup * NT - 1) / (kGroup * NT);
+  // run j starts at a multiple of 4 below n, so its 16-byte load lies inside the row's stride (a multiple of 4
+  // at least n); in a sampled row it starts at least n/runs >= 16 positions before the end, so it is whole
+  v4f x[kGroup];
+  auto load = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      const int j = threadIdx.x + (g * kGroup + q) * NT;
+      const int64_t p = n <= kCh ? 4 * (int64_t)j : ((int64_t)j * n / runs) & ~(int64_t)3;
+      if (j < runs) x[q] = *reinterpret_cast<const v4f*>(row + p);
+    }
+  };
+  // one histogram round over the sample: bin (key >> shift) & mask of every sampled key whose bits from
+  // shift + bits up equal `prefix`
+  auto round = [&](int shift, int bits, uint32_t prefix, bool reload) __attribute__((always_inline)) {
+    for (int g = 0; g < ngroups; ++g) {
+      if (g > 0 || reload) load(g);
+#pragma unroll
+      for (int q = 0; q < kGroup; ++q) {
+        const int j = threadIdx.x + (g * kGroup + q) * NT;
+        if (j < runs)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = order_key(x[q][e]);
+            if ((n > kCh || 4 * j + e < n) && (uint32_t)((uint64_t)key >> (shift + bits)) == prefix)
+              atomicAdd(&h[(key >> shift) & ((1u << bits) - 1u)], 1u);
+          }
+      }
+    }
+  };
+  load(0);  // in flight while the histogram is cleared
+  for (int i = threadIdx.x; i < kTopkBins; i += NT) h[i] = 0u;
+  if (threadIdx.x == 0) {  // a floor of 0 keeps every key, should the sample rank fail
+    s[0] = s[1] = s[2] = s[3] = 0u;
+  }
+  __syncthreads();
+  round(20, 12, 0u, false);
+  __syncthreads();
+  lds_threshold_bin<NT>(h, (uint32_t)m, true, scan, &s[0], &s[1]);
+  const uint32_t b1 = s[0];
+  round(12, 8, b1, ngroups > 1);
+  __syncthreads();
+  if (threadIdx.x < 64) {  // wave 0 ranks the 256 bins, lane l owning bins 252 - 4 l .. 255 - 4 l (top first)
+    const int lane = threadIdx.x;
+    const uint32_t need = (uint32_t)m - s[1];
+    const v4i c = reinterpret_cast<const v4i*>(h)[63 - lane];
+    if (clear) reinterpret_cast<v4i*>(h)[63 - lane] = v4i{0, 0, 0, 0};
+    const uint32_t local = (uint32_t)(c[0] + c[1] + c[2] + c[3]);
+    uint32_t tot;
+    uint32_t above = wave_exclusive_scan(local, tot);
+    if (above < need && above + local >= need) {
+      for (int j = 3; j >= 0; --j) {
+        if (above + (uint32_t)c[j] >= need) {
+          s[2] = (uint32_t)(4 * (63 - lane) + j);
+          break;
+        }
+        above += (uint32_t)c[j];
+      }
+    }
+  }
+  __syncthreads();
+  return (b1 << 8) | s[2];
+}
+
+// Bin of a candidate key in the row's candidate histogram: its 20-bit prefix relative to the floor, the last bin
+// taking everything 4095 or more 20-bit steps above the floor.
+__device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t floor20) {
+  return min((key >> 12) - floor20, (uint32_t)kTopkBins - 1u);
+}
+
 __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
                                                            const int32_t* __restrict__ row_len, int max_row_len,
-                                                           int k, const uint32_t* __restrict__ hist1,
-                                                           uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
-                                                           uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt,
+                                                           int k, uint32_t* __restrict__ hist,
+                                                           uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
+                                                           uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
-                                                           int nblk_max, int copies, int cpb) {
+                                                           int nblk_max, int cpb) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
-  __shared__ uint32_t seg_base, s_b1, s_A1;
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ uint32_t seg_base, s_f[4];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
@@ -359,27 +423,24 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const int c0 = (int)blockIdx.x * cpb;
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
-  v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads while the threshold is found
-  // every block finds b1 itself (a read of the row's histogram replicas) instead of waiting for one block to
-  // publish it; a block covers several chunks when the row has many
-  threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
-  const uint32_t b1 = s_b1;
-  if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
-  uint32_t* h2 = hist2 + (int64_t)r * kTopkBins;
+  v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
+  // every block ranks the sample itself instead of waiting for one block to publish the floor
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, false, h, scan, s_f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
+  uint32_t* hc = hist + (int64_t)r * kTopkBins;
   const int c1 = min(nchunk, c0 + cpb);
   auto filter = [&](int ch, const v4f& x) __attribute__((always_inline)) {
     const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
     uint32_t key[kEpt];
-    bool valid[kEpt];
+    bool keep[kEpt];
     uint32_t c = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
-      valid[e] = first + e < n;
       key[e] = order_key(x[e]);
-      const uint32_t d1 = key[e] >> 20;
-      if (valid[e] && d1 >= b1) {
+      keep[e] = first + e < n && (key[e] >> 12) >= fl;
+      if (keep[e]) {
         ++c;
-        if (d1 == b1) atomicAdd(&h2[(key[e] >> 8) & 0xfffu], 1u);
+        atomicAdd(&hc[cand_bin(key[e], fl)], 1u);
       }
     }
     uint32_t total;
@@ -395,7 +456,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
       uint64_t* dst = cand + (int64_t)r * kCap + base + off;
 #pragma unroll
       for (int e = 0; e < kEpt; ++e)
-        if (valid[e] && (key[e] >> 20) >= b1) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
+        if (keep[e]) *dst++ = ((uint64_t)(first + e) << 32) | key[e];
     }
     // no barrier here: the next chunk writes the scan words and seg_base only after barriers that every thread
     // reaches after reading this chunk's
@@ -411,8 +472,8 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
 }
 
 // Filter for blocks that cover several chunks (long rows, large batches).  The chunk loop stages each chunk's
-// candidates in LDS (position order within the chunk, chunks in order) and counts digit 2 of the keys in bin b1
-// in an LDS histogram, so its only memory traffic is the next chunk's scores, loaded while the current one is
+// candidates in LDS (position order within the chunk, chunks in order) and counts them in an LDS copy of the
+// candidate histogram, so its only memory traffic is the next chunk's scores, loaded while the current one is
 // filtered.  When the stage is full, and at the end, the block reserves one range of the row's candidate list
 // with one atomic, copies the stage out and writes the segment table of the chunks it holds; the histogram is
 // merged once at the end.
@@ -421,14 +482,14 @@ static_assert(kCh <= kStageCap, "one chunk always fits an empty stage");
 
 __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int max_row_len, int k,
-    const uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2, uint32_t* __restrict__ cnt,
-    uint32_t* __restrict__ thr, uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off,
-    uint64_t* __restrict__ cand, int nblk_max, int copies, int cpb) {
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
+    uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand, int nblk_max,
+    int cpb) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ uint64_t stage[kStageCap];
-  __shared__ uint32_t h2l[kTopkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histogram, then the candidates'
   __shared__ uint32_t chunk_n[kTopkMaxBlocksPerRow];  // candidates of each staged chunk
-  __shared__ uint32_t seg_base, s_b1, s_A1;
+  __shared__ uint32_t seg_base, s_f[4];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
@@ -436,11 +497,9 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   const int c0 = (int)blockIdx.x * cpb;
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
-  v4f x = load_raw(row, c0, n);  // the first chunk loads while the threshold is found
-  for (int i = threadIdx.x; i < kTopkBins; i += kTpb) h2l[i] = 0u;
-  threshold_bin<kTpb>(hist1 + (int64_t)r * copies * kTopkBins, copies, (uint32_t)keff, scan, &s_b1, &s_A1);
-  const uint32_t b1 = s_b1;
-  if (blockIdx.x == 0 && threadIdx.x == 0) { thr[4 * r + 0] = b1; thr[4 * r + 1] = s_A1; }
+  v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, true, h, scan, s_f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
   int cs = c0;
@@ -473,11 +532,10 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
       key[e] = order_key(cur[e]);
-      const uint32_t d1 = key[e] >> 20;
-      if (first + e < n && d1 >= b1) {
+      if (first + e < n && (key[e] >> 12) >= fl) {
         ++c;
         take |= 1u << e;
-        if (d1 == b1) atomicAdd(&h2l[(key[e] >> 8) & 0xfffu], 1u);
+        atomicAdd(&h[cand_bin(key[e], fl)], 1u);
       }
     }
     uint32_t total;
@@ -492,15 +550,25 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   }
   __syncthreads();  // the stage, chunk counts and histogram are complete
   flush(c1);
-  hist_merge<kTpb>(h2l, hist2 + (int64_t)r * kTopkBins);
+  hist_merge<kTpb>(h, hist + (int64_t)r * kTopkBins);
 }
 
 constexpr int kRes = 1024;  // threads of the resolve block
 
+// The key holding the need-th largest place among the list's entries, by a three-digit radix select; lowers
+// `need` to its rank among the keys equal to it.
+template <int NT, class List>
+__device__ uint32_t select_key(const List& L, int len, uint32_t& need, uint32_t* h, uint32_t* scan) {
+  const uint32_t d1 = refine_digit<NT>(L, len, 0u, 20, 12, need, h, scan);
+  const uint32_t d2 = refine_digit<NT>(L, len, d1, 8, 12, need, h, scan);
+  const uint32_t d3 = refine_digit<NT>(L, len, (d1 << 12) | d2, 0, 8, need, h, scan);
+  return (d1 << 20) | (d2 << 8) | d3;
+}
+
 __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ row_len, int max_row_len,
                                                             int k, const uint32_t* __restrict__ thr,
-                                                            const uint32_t* __restrict__ hist2,
+                                                            const uint32_t* __restrict__ hist,
                                                             const uint32_t* __restrict__ cnt,
                                                             const uint32_t* __restrict__ seg_cnt,
                                                             const uint32_t* __restrict__ seg_off,
@@ -508,7 +576,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
                                                             int32_t* __restrict__ topk_idx, PoolRows pr) {
   static_assert(kRes >= kTopkMaxBlocksPerRow, "one chunk per thread");
   __shared__ ResolveLds S;
-  __shared__ uint32_t s_b2, s_A2, s_nb, s_nbin;
+  __shared__ uint32_t s_bin, s_above, s_nb, s_nbin;
   const int r = blockIdx.x;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
@@ -528,21 +596,21 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   if (pt_lds)  // read before the first barrier below, used after it
     for (int i = threadIdx.x; i < pr.max_pages; i += kRes) S.pt[i] = gpt[i];
   const float* row = scores + (int64_t)r * ld;
-  // every read that does not depend on another is issued here, together: the thresholds, the candidate count,
-  // the segment tables and the digit-2 histogram; the candidates follow as soon as their count arrives and stay
-  // in flight through the two block scans
+  // every read that does not depend on another is issued here, together: the floor, the candidate count, the
+  // segment tables and the candidate histogram; the candidates follow as soon as their count arrives and stay in
+  // flight through the block scan
   const int nblk = (n + kCh - 1) / kCh;
   const int t = threadIdx.x;
-  const uint32_t b1 = thr[4 * r + 0], A1 = thr[4 * r + 1];
+  const uint32_t fl = thr[4 * r + 0];
   const uint32_t len = cnt[4 * r + 2];
   const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
   const uint32_t src = t < nblk ? seg_off[(int64_t)r * nblk_max + t] : 0u;
   constexpr int kPerBin = kTopkBins / kRes;
-  uint32_t h2v[kPerBin];
+  uint32_t hv[kPerBin];
   {
-    const uint32_t* gh = hist2 + (int64_t)r * kTopkBins + (kRes - 1 - t) * kPerBin;  // top bins first
+    const uint32_t* gh = hist + (int64_t)r * kTopkBins + (kRes - 1 - t) * kPerBin;  // top bins first
 #pragma unroll
-    for (int j = 0; j < kPerBin; ++j) h2v[j] = gh[j];
+    for (int j = 0; j < kPerBin; ++j) hv[j] = gh[j];
   }
   // the first candidates load before their count is known (entries past it are ignored)
   constexpr int kPer = (kCap + kRes - 1) / kRes;
@@ -550,32 +618,35 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   uint64_t e[kPer];
 #pragma unroll
   for (int j = 0; j < kFirst; ++j) e[j] = cand[(int64_t)r * kCap + j * kRes + t];
-  if (len <= (uint32_t)kCap) {
+  if (len >= (uint32_t)keff && len <= (uint32_t)kCap) {
 #pragma unroll
     for (int j = kFirst; j < kPer; ++j) {
       const int i = j * kRes + t;
       e[j] = i < (int)len ? cand[(int64_t)r * kCap + i] : 0ull;
     }
-    // b2 -- the bin of digit 2 (within b1) holding the (k_eff - A1)-th largest key, thread t owning bins
-    // (kRes - 1 - t) * kPerBin .. top first -- and the segment starts in position order (thread t = chunk t):
-    // two scans, one barrier
+    // the candidate bin holding the k_eff-th largest key -- thread t owning bins (kRes - 1 - t) * kPerBin .. top
+    // first -- and the segment starts in position order (thread t = chunk t): two scans, one barrier
     uint32_t hl = 0;
 #pragma unroll
-    for (int j = 0; j < kPerBin; ++j) hl += h2v[j];
+    for (int j = 0; j < kPerBin; ++j) hl += hv[j];
     uint32_t above, start;
-    if (t == 0) s_nbin = 0;
+    if (t == 0) {  // the open bin, unless the scan finds the threshold (it does: the bins hold len >= k_eff keys)
+      s_nbin = 0;
+      s_bin = kTopkBins - 1;
+      s_above = 0;
+      s_nb = 0;
+    }
     block_scan2<kRes>(hl, c, S.scan2, above, start);
-    const uint32_t need2 = (uint32_t)keff - A1;
-    if (above < need2 && above + hl >= need2) {
+    if (above < (uint32_t)keff && above + hl >= (uint32_t)keff) {
       uint32_t run = above;
       for (int j = kPerBin - 1; j >= 0; --j) {
-        if (run + h2v[j] >= need2) {
-          s_b2 = (uint32_t)((kRes - 1 - t) * kPerBin + j);
-          s_A2 = run;
-          s_nb = h2v[j];
+        if (run + hv[j] >= (uint32_t)keff) {
+          s_bin = (uint32_t)((kRes - 1 - t) * kPerBin + j);
+          s_above = run;
+          s_nb = hv[j];
           break;
         }
-        run += h2v[j];
+        run += hv[j];
       }
     }
     if (t < nblk) {
@@ -583,8 +654,10 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       S.seg_src[t] = src;
     }
     __syncthreads();
-    const uint32_t b2 = s_b2, A2 = A1 + s_A2, nb = s_nb;  // nb: keys in bin (b1, b2), all in the list
-    const uint32_t prefix = (b1 << 12) | b2;
+    // nb keys share the threshold's 20-bit prefix, unless the threshold lies in the open-ended top bin
+    const uint32_t bin = s_bin, nb = s_nb;
+    const bool open = bin == kTopkBins - 1;
+    const uint32_t prefix = fl + bin;
     const int lane = t & 63;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // every candidate goes to its chunk's segment start + its offset within the segment
@@ -599,29 +672,30 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
         S.pos[dst] = (int32_t)pos;
       }
     }
-    // the low digits of the keys in bin (b1, b2), when they fit one wave (their order does not matter)
-    if (nb <= 64u) {
+    // the low 12 bits of the keys of the threshold's prefix, when they fit one wave (their order does not matter)
+    const bool few = !open && nb <= 64u;
+    if (few) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int i = j * kRes + t;
         const uint32_t key = (uint32_t)e[j];
-        const bool match = i < (int)len && (key >> 8) == prefix;
+        const bool match = i < (int)len && (key >> 12) == prefix;
         const uint64_t mm = __ballot(match);
         if (mm) {  // uniform over the wave
           const int leader = __builtin_ctzll(mm);
           uint32_t base = 0;
           if (lane == leader) base = atomicAdd(&s_nbin, (uint32_t)__popcll(mm));
           base = __shfl(base, leader, 64);
-          if (match) S.bin[base + (uint32_t)__popcll(mm & below)] = key & 0xffu;
+          if (match) S.bin[base + (uint32_t)__popcll(mm & below)] = key & 0xfffu;
         }
       }
     }
     __syncthreads();
     const LdsList L{S.key, S.pos};
-    uint32_t need = (uint32_t)keff - A2;  // keys of (b1, b2) still to take
-    uint32_t d3;
-    if (nb <= 64u) {
-      // every wave finds digit 3 itself: lane x ranks the low digit of the x-th key of the bin among all nb
+    uint32_t need = (uint32_t)keff - s_above;  // keys of the threshold's bin still to take
+    uint32_t T;
+    if (few) {
+      // every wave finds the low bits itself: lane x ranks the low bits of the x-th key of the prefix among all nb
       const uint32_t dx = lane < (int)nb ? S.bin[lane] : 0u;
       uint32_t gt = 0, ge = 0;
       for (uint32_t y = 0; y < nb; ++y) {
@@ -629,21 +703,21 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
         gt += dy > dx;
         ge += dy >= dx;
       }
-      const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);  // lanes holding the digit
+      const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);  // lanes holding the low bits
       const int src_lane = __builtin_ctzll(hit);
-      d3 = __shfl(dx, src_lane, 64);
+      T = (prefix << 12) | __shfl(dx, src_lane, 64);
       need -= __shfl(gt, src_lane, 64);
+    } else if (!open) {
+      T = (prefix << 12) | refine_digit<kRes>(L, (int)len, prefix, 0, 12, need, S.h, S.scan);
     } else {
-      d3 = refine_digit<kRes>(L, (int)len, prefix, 0, 8, need, S.h, S.scan);
+      T = select_key<kRes>(L, (int)len, need, S.h, S.scan);
     }
-    write_selection<kRes>(L, (int)len, (b1 << 20) | (b2 << 8) | d3, need, keff, out, rows);
+    write_selection<kRes>(L, (int)len, T, need, keff, out, rows);
   } else {
     const RowList L{row};
     uint32_t need = (uint32_t)keff;
-    const uint32_t d1 = refine_digit<kRes>(L, n, 0u, 20, 12, need, S.h, S.scan);
-    const uint32_t d2 = refine_digit<kRes>(L, n, d1, 8, 12, need, S.h, S.scan);
-    const uint32_t d3 = refine_digit<kRes>(L, n, (d1 << 12) | d2, 0, 8, need, S.h, S.scan);
-    write_selection<kRes>(L, n, (d1 << 20) | (d2 << 8) | d3, need, keff, out, rows);
+    const uint32_t T = select_key<kRes>(L, n, need, S.h, S.scan);
+    write_selection<kRes>(L, n, T, need, keff, out, rows);
   }
   for (int i = keff + threadIdx.x; i < k; i += kRes) {
     out[i] = -1;
@@ -656,47 +730,43 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
 size_t topk_workspace_bytes(const Geo& g) {
   const size_t nblk = (size_t)std::max(1, (g.max_row_len + kCh - 1) / kCh);
   const size_t R = (size_t)g.R;
-  return align_up(4 * R * hist_copies(g.R) * kTopkBins) + align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) +
-         2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
+  return align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) + 2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
 }
 
 TopkState topk_state(const Geo& g, void* workspace) {
   const Ws w = carve(g, workspace);
-  return TopkState{w.hist1, w.copies};
+  return TopkState{w.hist, w.cnt};
 }
 
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
-  topk_zero_kernel<<<g.R, 256, 0, stream>>>(w.hist1, w.hist2, w.cnt, w.copies);
+  topk_zero_kernel<<<g.R, 256, 0, stream>>>(w.hist, w.cnt);
   return hipGetLastError();
 }
 
-// Chunks per histogram / filter block: at most 32 blocks per row (each filter block re-reads the row's
-// histogram replicas to find the threshold) and about 512 blocks overall (two 1024-thread blocks per CU) once
-// there are enough chunks: a block that covers several chunks stages its candidates and keeps the next chunk's
-// scores in flight (64 rows of 16 chunks: 34 -> 29 us for the top-k).
+// Chunks per filter block: at most 32 blocks per row (each filter block ranks the row's sample) and about 512
+// blocks overall (two 1024-thread blocks per CU) once there are enough chunks: a block that covers several chunks
+// stages its candidates and keeps the next chunk's scores in flight (64 rows of 16 chunks: 34 -> 29 us for the
+// top-k).
 int chunks_per_block(const Geo& g, int nblk) {
   const int64_t total = (int64_t)nblk * g.R;
   return (int)std::min<int64_t>(nblk, std::max<int64_t>({1, (nblk + 31) / 32, total / 512}));
 }
 
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              bool hist_done, int32_t* pool_rows, hipStream_t stream) {
+                              int32_t* pool_rows, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
   const int cpb = chunks_per_block(g, w.nblk);
   dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
-  if (!hist_done)
-    topk_hist_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.copies, cpb);
   if (cpb > 1)
-    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2,
-                                                         w.cnt, w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies,
-                                                         cpb);
+    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist, w.cnt,
+                                                         w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
   else
-  topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist1, w.hist2, w.cnt,
-                                                w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, w.copies, cpb);
-  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist2, w.cnt,
+    topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist, w.cnt, w.thr,
+                                                  w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
+  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist, w.cnt,
                                                 w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx,
                                                 PoolRows{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages,
                                                          g.num_pages, g.log2ps});
@@ -707,7 +777,7 @@ hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* t
                        int32_t* pool_rows, hipStream_t stream) {
   hipError_t e = launch_topk_zero(g, workspace, stream);
   if (e != hipSuccess) return e;
-  return launch_topk_select(g, scores, ld, topk_idx, workspace, false, pool_rows, stream);
+  return launch_topk_select(g, scores, ld, topk_idx, workspace, pool_rows, stream);
 }
 
 }  // namespace dsa

@@ -221,6 +221,31 @@ def test_topk_staged_flush_and_ties():
     _expect_exact(sc, [n], 2048)
 
 
+def test_topk_sample_overshoot_rescans_the_row():
+    # a row of 2^17 is sampled as 1024 runs of four scores, one run every 128 positions; only the first 40 runs
+    # hold high scores, so the sample's floor sits above all but 160 scores, fewer than k, and the resolve rescans
+    # the whole row
+    rng = np.random.default_rng(9)
+    n = 1 << 17
+    sc = rng.standard_normal((1, n)).astype(np.float32)
+    for j in range(40):
+        sc[0, 128 * j:128 * j + 4] = 50.0
+    _expect_exact(sc, [n], 2048)
+
+
+def test_topk_threshold_far_above_the_floor():
+    # k + 100 scores near 1000 at random positions above a standard-normal bulk: the sample's floor lies in the
+    # bulk, and the k-th largest score beyond the two octaves above it that the candidate histogram resolves (in
+    # its open-ended top bin), so the resolve radix-selects its candidate list
+    rng = np.random.default_rng(10)
+    n = 1 << 17
+    sc = rng.standard_normal((2, n)).astype(np.float32)
+    for r in range(2):
+        hi = rng.choice(n, 2148, replace=False)
+        sc[r, hi] = 1000.0 + rng.standard_normal(len(hi)).astype(np.float32)
+    _expect_exact(sc, [n, n - 77], 2048)
+
+
 def test_topk_long_row_1m():
     rng = np.random.default_rng(7)
     n = 1 << 20
