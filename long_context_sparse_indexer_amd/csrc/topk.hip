@@ -146,7 +146,8 @@ template <int NT, class List, class Rows>
 __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out,
                                 const Rows& rows) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t w_gt[NW], w_eq[NW];
+  static_assert(NW % 4 == 0, "wave counts are read four at a time");
+  __shared__ __attribute__((aligned(16))) uint32_t w_gt[NW], w_eq[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int span = ((len + NW * 64 - 1) / (NW * 64)) * 64;
   const int lo = wave * span, hi = min(len, lo + span);
@@ -325,7 +326,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, bool clear,
                                                  uint32_t* h, uint32_t* scan, uint32_t* s) {
   constexpr int kGroup = 4;  // runs per thread held in registers: all of them up to S = 16384
-  int runs, m;
+  int runs, m, step = 4;  // run j starts at position j * step (rounded down to a multiple of 4)
   if (n <= kCh) {
     runs = (n + 3) / 4;
     m = keff;
@@ -333,24 +334,25 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
     const int cap = n > (1 << 21) ? 65536 : 16384;
     const int S = min(cap, max(1024, 1 << (31 - __builtin_clz((unsigned)(n / kSampleDiv)))));
     runs = S / 4;
+    step = n / runs;
     const float mu = (float)keff * (float)S / (float)n;
     m = min(S, (int)ceilf(mu + 8.f * sqrtf(mu) + 16.f));
   }
   const int ngroups = (runs + kGroup * NT - 1) / (kGroup * NT);
   // run j starts at a multiple of 4 below n, so its 16-byte load lies inside the row's stride (a multiple of 4
-  // at least n); in a sampled row it starts at least n/runs >= 16 positions before the end, so it is whole
+  // at least n); in a sampled row step = floor(n / runs) >= 16 and j < runs, so the run ends before n
   v4f x[kGroup];
   auto load = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < kGroup; ++q) {
       const int j = threadIdx.x + (g * kGroup + q) * NT;
-      const int64_t p = n <= kCh ? 4 * (int64_t)j : ((int64_t)j * n / runs) & ~(int64_t)3;
-      if (j < runs) x[q] = *reinterpret_cast<const v4f*>(row + p);
+      if (j < runs) x[q] = *reinterpret_cast<const v4f*>(row + ((j * step) & ~3));
     }
   };
   // one histogram round over the sample: bin (key >> shift) & mask of every sampled key whose bits from
   // shift + bits up equal `prefix`
   auto round = [&](int shift, int bits, uint32_t prefix, bool reload) __attribute__((always_inline)) {
+#pragma unroll 1
     for (int g = 0; g < ngroups; ++g) {
       if (g > 0 || reload) load(g);
 #pragma unroll
@@ -565,6 +567,16 @@ __device__ uint32_t select_key(const List& L, int len, uint32_t& need, uint32_t*
   return (d1 << 20) | (d2 << 8) | d3;
 }
 
+// The rare resolve paths (a row whose sample overshot or overflowed the list, a threshold past the candidate
+// histogram's range): a three-digit radix select over the list, then the write.  Kept out of line so that the
+// common path's code stays compact.
+template <class List>
+__device__ __attribute__((noinline)) void select_and_write(List L, int len, uint32_t need, int keff, int32_t* out,
+                                                            RowMap rows, uint32_t* h, uint32_t* scan) {
+  const uint32_t T = select_key<kRes>(L, len, need, h, scan);
+  write_selection<kRes>(L, len, T, need, keff, out, rows);
+}
+
 __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ row_len, int max_row_len,
                                                             int k, const uint32_t* __restrict__ thr,
@@ -695,7 +707,9 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     uint32_t need = (uint32_t)keff - s_above;  // keys of the threshold's bin still to take
     uint32_t T;
     if (few) {
-      // every wave finds the low bits itself: lane x ranks the low bits of the x-th key of the prefix among all nb
+      // every wave finds the low bits itself, by a radix select over the nb keys held one per lane: from the top
+      // bit down, keep the lanes whose bit is set if they hold at least `need` keys, else take those keys and keep
+      // the others
       const uint32_t dx = lane < (int)nb ? S.bin[lane] : 0u;
       uint32_t gt = 0, ge = 0;
       for (uint32_t y = 0; y < nb; ++y) {
@@ -709,15 +723,11 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       need -= __shfl(gt, src_lane, 64);
     } else if (!open) {
       T = (prefix << 12) | refine_digit<kRes>(L, (int)len, prefix, 0, 12, need, S.h, S.scan);
-    } else {
-      T = select_key<kRes>(L, (int)len, need, S.h, S.scan);
     }
-    write_selection<kRes>(L, (int)len, T, need, keff, out, rows);
+    if (open) select_and_write(L, (int)len, need, keff, out, rows, S.h, S.scan);
+    else write_selection<kRes>(L, (int)len, T, need, keff, out, rows);
   } else {
-    const RowList L{row};
-    uint32_t need = (uint32_t)keff;
-    const uint32_t T = select_key<kRes>(L, n, need, S.h, S.scan);
-    write_selection<kRes>(L, n, T, need, keff, out, rows);
+    select_and_write(RowList{row}, n, (uint32_t)keff, keff, out, rows, S.h, S.scan);
   }
   for (int i = keff + threadIdx.x; i < k; i += kRes) {
     out[i] = -1;
