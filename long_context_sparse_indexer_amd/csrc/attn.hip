@@ -44,31 +44,27 @@ __device__ __forceinline__ v8bf pack8(const float (&p)[8]) {
   return r;
 }
 
-// Gathers the 16 latent rows of this wave for chunk c straight into LDS: global_load_lds_dwordx4 lands the 64
-// lanes' 16-byte pieces contiguously at the LDS address in M0, one 1 KiB row per instruction.  Every wave
-// issues exactly 16 such loads per chunk (a slot without a position reads `dummy`, a selected row of the split,
-// and is masked later), so "this chunk has arrived" is a fixed vmcnt once the next chunk has been issued.
-// The loads are written as asm so that the compiler's wait insertion, which cannot tell which LDS buffer a
-// pending DMA targets across the chunk loop, does not add a full vmcnt(0) before every LDS read; the waits
-// on them are explicit (kWaitVm16 / s_waitcnt 0).  No output register is involved: the data goes to LDS and
-// the address operands are read when the instruction issues.
-__device__ __forceinline__ void gather_chunk(const unsigned short* __restrict__ kv, const int32_t* prow, int dummy,
-                                             char* buf, int wave, int lane) {
+// 16-head kernel gathers: the 16 latent rows of this wave for one chunk, one 16-byte load per lane and row into
+// registers (a slot without a position reads `dummy`, a selected row of the split, and is masked later), then
+// written to LDS at row stride kRowB once the current chunk is computed.  The eight head groups of a (row, split)
+// read the same rows from one L2, so the LDS-DMA path's per-CU issue rate, not HBM, bounded these gathers;
+// register loads measured 0.4 us faster per batch-1 step.
+__device__ __forceinline__ void load_chunk_regs(const unsigned short* __restrict__ kv, const int32_t* prow, int dummy,
+                                                int wave, int lane, v4i (&gv)[16]) {
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int rr = wave * 16 + t;
-    int pr = prow[rr];
+    int pr = prow[wave * 16 + t];
     if (pr < 0) pr = dummy;
-    const unsigned short* src = kv + (int64_t)pr * kDC + lane * 8;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(buf + rr * kRowB)));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+    gv[t] = *reinterpret_cast<const v4i*>(kv + (int64_t)pr * kDC + lane * 8);
   }
+}
+__device__ __forceinline__ void store_chunk_regs(char* buf, int wave, int lane, const v4i (&gv)[16]) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) *reinterpret_cast<v4i*>(buf + (wave * 16 + t) * kRowB + lane * 16) = gv[t];
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
 constexpr int kWaitVmOnly(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }  // vmcnt <= n only
-constexpr int kWaitVm16 = kWaitVmOnly(16);
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
 
 // Workgroup barrier for data this wave wrote with ds_* instructions.  Unlike __syncthreads() it does not wait
@@ -92,9 +88,38 @@ __device__ __forceinline__ int part_exponent(float maxabs) {
 __device__ __forceinline__ unsigned short part_bits(float v, int e) {
   return __builtin_bit_cast(unsigned short, (_Float16)ldexpf(v, -e));
 }
-__device__ __forceinline__ float max_over_lanes(float v, int width) {  // width = 16 or 32 aligned lanes
-  for (int m = 1; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+// Cross-lane reductions in the register file (DPP and lane-swap moves; no LDS round trip).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+// Max over each aligned group of `width` (16 or 32) lanes: within a quad (quad_perm [1,0,3,2] then [2,3,0,1]),
+// then between quads by row_half_mirror and between half-rows by row_mirror, then between rows by
+// v_permlane16_swap.
+__device__ __forceinline__ float max_over_lanes(float v, int width) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
+  if (width == 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
   return v;
+}
+// Max and sum over the lanes i, i + 16, i + 32, i + 48: v_permlane16_swap pairs rows 0-1 and 2-3, then
+// v_permlane32_swap the two halves; every lane ends with the same value, summed in the same order.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Work unit (row, head group of the all-heads kernel) and split of this block.  Workgroups are handed to the
@@ -194,14 +219,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const int dummy = prow_lds[first_valid];
     // one chunk: wait for its rows (the next chunk's gather stays in flight), then QK^T, softmax, PV.
     // `cur` and `nxt` are fixed per call site, so the compiler can tell the DMA target from the buffer read.
+    v4i gv[16];
     auto chunk = [&](const int c, const char* cur, char* nxt) __attribute__((always_inline)) {
-      if (c + 1 < nch) {
-        gather_chunk(kv, prow_lds + (c + 1) * kNC, dummy, nxt, wave, lane);
-        __builtin_amdgcn_s_waitcnt(kWaitVm16);  // chunk c has landed; chunk c+1 stays in flight
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      lds_barrier();
+      if (c + 1 < nch) load_chunk_regs(kv, prow_lds + (c + 1) * kNC, dummy, wave, lane, gv);
       // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
       v4f sacc = {0.f, 0.f, 0.f, 0.f};
       {
@@ -229,26 +249,25 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       float mx = sv[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       const float m_new = fmaxf(m, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(m - m_use);
       float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sv[e] = exp2f(sv[e] - m_use); rs += sv[e]; }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
+      rs = rows_sum(rs);
       l = l * alpha + rs;
       m = m_new;
 
-      // rescale O rows (head g*4 + v) by that head's alpha, held by lane g*4 + v
+      // rescale O rows (head g*4 + v) by that head's alpha, held by lane g*4 + v (O is still zero in chunk 0)
+      if (c > 0)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float av = __shfl(alpha, g * 4 + v, 64);
+        for (int v = 0; v < 4; ++v) {
+          const float av = __shfl(alpha, g * 4 + v, 64);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt][v] *= av;
-      }
+          for (int dt = 0; dt < 8; ++dt) o[dt][v] *= av;
+        }
 
       // O += P V.  A operand element e of K-step kk is slot kk*32 + 8g + perm[e], perm = {0,2,4,6,1,3,5,7}.
 #pragma unroll
@@ -266,10 +285,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[dt], 0, 0, 0);
         }
       }
-      lds_barrier();  // every wave is done with `cur` and s_lds before they are overwritten
+      if (c + 1 < nch) store_chunk_regs(nxt, wave, lane, gv);
+      lds_barrier();  // every wave is done with `cur` and s_lds before they are overwritten; `nxt` is written
     };
-    __builtin_amdgcn_s_waitcnt(0);  // Q operands and slot rows are in; from here the gathers are the only loads
-    gather_chunk(kv, prow_lds, dummy, kv_lds0, wave, lane);
+    load_chunk_regs(kv, prow_lds, dummy, wave, lane, gv);
+    store_chunk_regs(kv_lds0, wave, lane, gv);
+    lds_barrier();
     for (int c = 0; c < nch; c += 2) {
       chunk(c, kv_lds0, kv_lds1);
       if (c + 1 < nch) chunk(c + 1, kv_lds1, kv_lds0);
