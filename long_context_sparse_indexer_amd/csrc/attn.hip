@@ -89,10 +89,6 @@ __device__ __forceinline__ unsigned short part_bits(float v, int e) {
   return __builtin_bit_cast(unsigned short, (_Float16)ldexpf(v, -e));
 }
 // Cross-lane reductions in the register file (DPP and lane-swap moves; no LDS round trip).
-template <int kCtrl>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
-}
 // Max over each aligned group of `width` (16 or 32) lanes: within a quad (quad_perm [1,0,3,2] then [2,3,0,1]),
 // then between quads by row_half_mirror and between half-rows by row_mirror, then between rows by
 // v_permlane16_swap.

@@ -48,16 +48,34 @@ __device__ __forceinline__ unsigned short float_to_bf16_bits(float f) {
   return __builtin_bit_cast(unsigned short, h);
 }
 
+// A DPP lane move of a float (every lane's source lies in its own row for the controls used here).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Reduction over the 64 lanes of a wave in the register file, every lane receiving the same value: within each
+// 16-lane row by DPP (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror), then between rows by
+// v_permlane16_swap and v_permlane32_swap.  Each step combines a lane with its partner in the same order on both
+// sides, so a sum is bit-identical in every lane.  All 64 lanes must be active.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));
+  v = op(v, dpp_move<0x4E>(v));
+  v = op(v, dpp_move<0x141>(v));
+  v = op(v, dpp_move<0x140>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 // Exclusive prefix of `v` over the lanes of a wave (and the wave total), with DPP lane moves instead of LDS-routed

@@ -697,7 +697,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
           const int leader = __builtin_ctzll(mm);
           uint32_t base = 0;
           if (lane == leader) base = atomicAdd(&s_nbin, (uint32_t)__popcll(mm));
-          base = __shfl(base, leader, 64);
+          base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
           if (match) S.bin[base + (uint32_t)__popcll(mm & below)] = key & 0xfffu;
         }
       }
@@ -719,8 +719,8 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       }
       const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);  // lanes holding the low bits
       const int src_lane = __builtin_ctzll(hit);
-      T = (prefix << 12) | __shfl(dx, src_lane, 64);
-      need -= __shfl(gt, src_lane, 64);
+      T = (prefix << 12) | (uint32_t)__builtin_amdgcn_readlane((int)dx, src_lane);
+      need -= (uint32_t)__builtin_amdgcn_readlane((int)gt, src_lane);
     } else if (!open) {
       T = (prefix << 12) | refine_digit<kRes>(L, (int)len, prefix, 0, 12, need, S.h, S.scan);
     }
