@@ -51,11 +51,7 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
   // the row's top-k state, cleared by block 0 as its last work (stores issued earlier would hold up the waits
   // for its key loads, which count in the same in-order counter)
   auto clear_state = [&]() __attribute__((always_inline)) {
-    if (!clear.hist || blockIdx.x != 0) return;
-    const v4i z = {0, 0, 0, 0};
-    v4i* h = reinterpret_cast<v4i*>(clear.hist + (int64_t)r * kTopkBins);
-    for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h[i] = z;
-    if (threadIdx.x == 0) reinterpret_cast<v4i*>(clear.cnt)[r] = z;
+    if (clear.cnt && blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<v4i*>(clear.cnt)[r] = v4i{0, 0, 0, 0};
   };
   if (first >= n) {
     clear_state();
@@ -469,7 +465,7 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
   dim3 grid((tiles_row + per - 1) / per, g.R);
   indexer_f8_kernel<HB><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr, nullptr}, per);
+      g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr}, per);
 }
 
 template <int HB>

@@ -21,11 +21,10 @@ struct Geo {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Per-row top-k state that must start at zero: the candidate histogram and the candidate counter.  In the fused
-// step the indexer clears it (block 0 of each row, after its scores), sparing the top-k a zeroing launch.
+// Per-row top-k state that must start at zero: the candidate counters.  In the fused step the indexer clears
+// them (block 0 of each row, after its scores), sparing the top-k a zeroing launch.
 struct TopkState {
-  uint32_t* hist;  // [R, 4096]
-  uint32_t* cnt;   // [R, 4]
+  uint32_t* cnt;  // [R, 4]
 };
 
 // indexer.hip.  fp8 problems whose rows come in groups of at least kTiledMinRows per sequence (chunked prefill)

@@ -8,11 +8,11 @@
 //            sampled score that comfortably more than k_eff scores of the row exceed.  The sample is a fixed set
 //            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram.  The
 //            block then writes the keys whose first 20 bits reach the floor, in position order, into a segment of
-//            the row's candidate list, and counts them in a 4096-bin histogram of their 20-bit prefixes taken
-//            relative to the floor (the last bin open-ended).
-//   resolve  one 1024-thread block per row: finds the 20-bit prefix bin holding the k_eff-th largest key from
-//            that histogram, places the candidates in position order in LDS, settles the low 12 bits among the
-//            few keys of that bin, and writes the selection with a two-pass wave-ballot compaction.  A row whose
+//            the row's candidate list.
+//   resolve  one 1024-thread block per row: counts the candidates in an LDS histogram of their 20-bit prefixes
+//            taken relative to the floor (4096 bins, the last open-ended), finds the bin holding the k_eff-th
+//            largest key, places the candidates in position order in LDS, settles the low 12 bits among the few
+//            keys of that bin, and writes the selection with a two-pass wave-ballot compaction.  A row whose
 //            sample overshot (fewer than k_eff candidates) or whose candidates overflow the list (heavily tied
 //            scores) is resolved over its whole stored score row instead, by a three-digit radix select.
 #include <algorithm>
@@ -35,7 +35,6 @@ Ws carve(const Geo& g, void* base) {
   char* p = static_cast<char*>(base);
   w.nblk = std::max(1, (g.max_row_len + kCh - 1) / kCh);
   auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes); return q; };
-  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * kTopkBins));
   w.cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.thr = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 4 * (size_t)g.R));
   w.seg_cnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)g.R * w.nblk));
@@ -44,13 +43,10 @@ Ws carve(const Geo& g, void* base) {
   return w;
 }
 
-// Zeroes the candidate histogram and the counters of every row (one block per row).
-__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ cnt) {
-  const int r = blockIdx.x;
-  const v4i z = {0, 0, 0, 0};
-  v4i* h = reinterpret_cast<v4i*>(hist + (int64_t)r * kTopkBins);
-  for (int i = threadIdx.x; i < kTopkBins / 4; i += blockDim.x) h[i] = z;
-  if (threadIdx.x == 0) reinterpret_cast<v4i*>(cnt)[r] = z;
+// Zeroes the counters of every row (one thread per row).
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ cnt, int R) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < R) reinterpret_cast<v4i*>(cnt)[r] = v4i{0, 0, 0, 0};
 }
 
 // The kEpt = 4 consecutive scores of this thread in chunk c, as one 16-byte load with no branch: the row's
@@ -233,43 +229,18 @@ __device__ __forceinline__ uint32_t block_scan1(uint32_t v, uint32_t* wt, uint32
   return x;
 }
 
-// Exclusive prefixes over the block of two values per thread, with one barrier: every wave scans its lanes and
-// publishes its totals in wt[0 .. 2 NW), then every thread adds the totals of the waves before its own.  wt may
-// be written again only after another barrier.
-template <int NT>
-__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t* wt, uint32_t& pa, uint32_t& pb) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t ta, tb;
-  pa = wave_exclusive_scan(a, ta);
-  pb = wave_exclusive_scan(b, tb);
-  if (lane == 0) { wt[wave] = ta; wt[NW + wave] = tb; }
-  __syncthreads();
-  static_assert(NW % 4 == 0, "wave totals are read four at a time");
-#pragma unroll
-  for (int q = 0; q < NW / 4; ++q) {  // 16-byte reads of the wave totals (wt is 16-byte aligned)
-    const v4i ya = reinterpret_cast<const v4i*>(wt)[q], yb = reinterpret_cast<const v4i*>(wt + NW)[q];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * q + e < wave) {
-        pa += (uint32_t)ya[e];
-        pb += (uint32_t)yb[e];
-      }
-  }
-}
-
 constexpr int kResPages = 4096;  // page-table entries a resolve block stages in LDS
 
 // LDS of the resolve step.
 struct ResolveLds {
   uint32_t key[kCap];
   int32_t pos[kCap];
-  uint32_t h[kTopkBins];
+  alignas(16) uint32_t h[kTopkBins];  // candidate histogram, then the refine passes' digit histograms
   uint32_t seg_start[kTopkMaxBlocksPerRow + 1];
   uint32_t seg_src[kTopkMaxBlocksPerRow];
   uint32_t scan[1024 / 64 + 1];  // one word per wave of the largest block, plus the total
   alignas(16) uint32_t scan2[2 * (1024 / 64)];
-  uint32_t bin[64];               // low digits of the keys in bin (b1, b2), when there are at most 64
+  uint32_t bin[64];               // low 12 bits of the keys of the threshold's 20-bit prefix, when at most 64
   int32_t pt[kResPages];          // page ids of the row's sequence, when they fit
 };
 
@@ -358,13 +329,26 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
 #pragma unroll
       for (int q = 0; q < kGroup; ++q) {
         const int j = threadIdx.x + (g * kGroup + q) * NT;
-        if (j < runs)
+        if (j < runs) {
+          // the four scores of a run often share a bin: equal neighbours are counted with one atomic, which
+          // keeps same-address LDS atomics of a wave few
+          uint32_t bin = 0, cntb = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t key = order_key(x[q][e]);
-            if ((n > kCh || 4 * j + e < n) && (uint32_t)((uint64_t)key >> (shift + bits)) == prefix)
-              atomicAdd(&h[(key >> shift) & ((1u << bits) - 1u)], 1u);
+            const bool in = (n > kCh || 4 * j + e < n) && (uint32_t)((uint64_t)key >> (shift + bits)) == prefix;
+            const uint32_t b = (key >> shift) & ((1u << bits) - 1u);
+            if (in && cntb && b != bin) {
+              atomicAdd(&h[bin], cntb);
+              cntb = 0;
+            }
+            if (in) {
+              bin = b;
+              ++cntb;
+            }
           }
+          if (cntb) atomicAdd(&h[bin], cntb);
+        }
       }
     }
   };
@@ -410,8 +394,8 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t floor20) {
 
 __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
                                                            const int32_t* __restrict__ row_len, int max_row_len,
-                                                           int k, uint32_t* __restrict__ hist,
-                                                           uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
+                                                           int k, uint32_t* __restrict__ cnt,
+                                                           uint32_t* __restrict__ thr,
                                                            uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
                                                            int nblk_max, int cpb) {
@@ -429,7 +413,6 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   // every block ranks the sample itself instead of waiting for one block to publish the floor
   const uint32_t fl = floor_prefix<kTpb>(row, n, keff, false, h, scan, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
-  uint32_t* hc = hist + (int64_t)r * kTopkBins;
   const int c1 = min(nchunk, c0 + cpb);
   auto filter = [&](int ch, const v4f& x) __attribute__((always_inline)) {
     const int64_t first = (int64_t)ch * kCh + threadIdx.x * kEpt;
@@ -440,10 +423,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
     for (int e = 0; e < kEpt; ++e) {
       key[e] = order_key(x[e]);
       keep[e] = first + e < n && (key[e] >> 12) >= fl;
-      if (keep[e]) {
-        ++c;
-        atomicAdd(&hc[cand_bin(key[e], fl)], 1u);
-      }
+      c += keep[e];
     }
     uint32_t total;
     const uint32_t off = block_exclusive_scan(c, scan, total);  // per chunk: cheaper than block_scan1 under load
@@ -474,22 +454,21 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
 }
 
 // Filter for blocks that cover several chunks (long rows, large batches).  The chunk loop stages each chunk's
-// candidates in LDS (position order within the chunk, chunks in order) and counts them in an LDS copy of the
-// candidate histogram, so its only memory traffic is the next chunk's scores, loaded while the current one is
-// filtered.  When the stage is full, and at the end, the block reserves one range of the row's candidate list
-// with one atomic, copies the stage out and writes the segment table of the chunks it holds; the histogram is
-// merged once at the end.
+// candidates in LDS (position order within the chunk, chunks in order), so its only memory traffic is the next
+// chunk's scores, loaded while the current one is filtered.  When the stage is full, and at the end, the block
+// reserves one range of the row's candidate list with one atomic, copies the stage out and writes the segment
+// table of the chunks it holds.
 constexpr int kStageCap = 6144;  // staged candidates per block (48 KiB; two 1024-thread blocks fit a CU)
 static_assert(kCh <= kStageCap, "one chunk always fits an empty stage");
 
 __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int max_row_len, int k,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
     uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand, int nblk_max,
     int cpb) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ uint64_t stage[kStageCap];
-  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histogram, then the candidates'
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histogram
   __shared__ uint32_t chunk_n[kTopkMaxBlocksPerRow];  // candidates of each staged chunk
   __shared__ uint32_t seg_base, s_f[4];
   const int r = blockIdx.y;
@@ -500,7 +479,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, true, h, scan, s_f);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, false, h, scan, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
@@ -537,7 +516,6 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
       if (first + e < n && (key[e] >> 12) >= fl) {
         ++c;
         take |= 1u << e;
-        atomicAdd(&h[cand_bin(key[e], fl)], 1u);
       }
     }
     uint32_t total;
@@ -550,9 +528,8 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     if (threadIdx.x == 0) chunk_n[ch - cs] = total;
     staged += total;
   }
-  __syncthreads();  // the stage, chunk counts and histogram are complete
+  __syncthreads();  // the stage and chunk counts are complete
   flush(c1);
-  hist_merge<kTpb>(h, hist + (int64_t)r * kTopkBins);
 }
 
 constexpr int kRes = 1024;  // threads of the resolve block
@@ -580,7 +557,6 @@ __device__ __attribute__((noinline)) void select_and_write(List L, int len, uint
 __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ row_len, int max_row_len,
                                                             int k, const uint32_t* __restrict__ thr,
-                                                            const uint32_t* __restrict__ hist,
                                                             const uint32_t* __restrict__ cnt,
                                                             const uint32_t* __restrict__ seg_cnt,
                                                             const uint32_t* __restrict__ seg_off,
@@ -608,9 +584,8 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   if (pt_lds)  // read before the first barrier below, used after it
     for (int i = threadIdx.x; i < pr.max_pages; i += kRes) S.pt[i] = gpt[i];
   const float* row = scores + (int64_t)r * ld;
-  // every read that does not depend on another is issued here, together: the floor, the candidate count, the
-  // segment tables and the candidate histogram; the candidates follow as soon as their count arrives and stay in
-  // flight through the block scan
+  // every read that does not depend on another is issued here, together: the floor, the candidate count and the
+  // segment tables; the candidates follow as soon as their count arrives
   const int nblk = (n + kCh - 1) / kCh;
   const int t = threadIdx.x;
   const uint32_t fl = thr[4 * r + 0];
@@ -618,12 +593,8 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   const uint32_t c = t < nblk ? seg_cnt[(int64_t)r * nblk_max + t] : 0u;
   const uint32_t src = t < nblk ? seg_off[(int64_t)r * nblk_max + t] : 0u;
   constexpr int kPerBin = kTopkBins / kRes;
-  uint32_t hv[kPerBin];
-  {
-    const uint32_t* gh = hist + (int64_t)r * kTopkBins + (kRes - 1 - t) * kPerBin;  // top bins first
-#pragma unroll
-    for (int j = 0; j < kPerBin; ++j) hv[j] = gh[j];
-  }
+  static_assert(kPerBin == 4, "one 16-byte LDS read of histogram bins per thread");
+  for (int i = t; i < kTopkBins; i += kRes) S.h[i] = 0u;  // the candidate histogram, cleared before a barrier
   // the first candidates load before their count is known (entries past it are ignored)
   constexpr int kPer = (kCap + kRes - 1) / kRes;
   constexpr int kFirst = 4;
@@ -636,42 +607,24 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       const int i = j * kRes + t;
       e[j] = i < (int)len ? cand[(int64_t)r * kCap + i] : 0ull;
     }
-    // the candidate bin holding the k_eff-th largest key -- thread t owning bins (kRes - 1 - t) * kPerBin .. top
-    // first -- and the segment starts in position order (thread t = chunk t): two scans, one barrier
-    uint32_t hl = 0;
-#pragma unroll
-    for (int j = 0; j < kPerBin; ++j) hl += hv[j];
-    uint32_t above, start;
+    // the segment starts in position order (thread t = chunk t); the scan's barrier also publishes the cleared
+    // histogram, into which every candidate then counts by its 20-bit prefix relative to the floor
+    uint32_t ctot;
+    const uint32_t start = block_scan1<kRes>(c, S.scan2, ctot);
     if (t == 0) {  // the open bin, unless the scan finds the threshold (it does: the bins hold len >= k_eff keys)
       s_nbin = 0;
       s_bin = kTopkBins - 1;
       s_above = 0;
       s_nb = 0;
     }
-    block_scan2<kRes>(hl, c, S.scan2, above, start);
-    if (above < (uint32_t)keff && above + hl >= (uint32_t)keff) {
-      uint32_t run = above;
-      for (int j = kPerBin - 1; j >= 0; --j) {
-        if (run + hv[j] >= (uint32_t)keff) {
-          s_bin = (uint32_t)((kRes - 1 - t) * kPerBin + j);
-          s_above = run;
-          s_nb = hv[j];
-          break;
-        }
-        run += hv[j];
-      }
-    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j * kRes + t < (int)len) atomicAdd(&S.h[cand_bin((uint32_t)e[j], fl)], 1u);
     if (t < nblk) {
       S.seg_start[t] = start;
       S.seg_src[t] = src;
     }
     __syncthreads();
-    // nb keys share the threshold's 20-bit prefix, unless the threshold lies in the open-ended top bin
-    const uint32_t bin = s_bin, nb = s_nb;
-    const bool open = bin == kTopkBins - 1;
-    const uint32_t prefix = fl + bin;
-    const int lane = t & 63;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // every candidate goes to its chunk's segment start + its offset within the segment
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -684,6 +637,30 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
         S.pos[dst] = (int32_t)pos;
       }
     }
+    // the bin holding the k_eff-th largest key, thread t owning bins (kRes - 1 - t) * kPerBin .. (top first)
+    const v4i hv = reinterpret_cast<const v4i*>(S.h)[kRes - 1 - t];
+    const uint32_t hl = (uint32_t)(hv[0] + hv[1] + hv[2] + hv[3]);
+    uint32_t htot;
+    const uint32_t above = block_scan1<kRes>(hl, S.scan2, htot);
+    if (above < (uint32_t)keff && above + hl >= (uint32_t)keff) {
+      uint32_t run = above;
+      for (int j = kPerBin - 1; j >= 0; --j) {
+        if (run + (uint32_t)hv[j] >= (uint32_t)keff) {
+          s_bin = (uint32_t)((kRes - 1 - t) * kPerBin + j);
+          s_above = run;
+          s_nb = (uint32_t)hv[j];
+          break;
+        }
+        run += (uint32_t)hv[j];
+      }
+    }
+    __syncthreads();
+    // nb keys share the threshold's 20-bit prefix, unless the threshold lies in the open-ended top bin
+    const uint32_t bin = s_bin, nb = s_nb;
+    const bool open = bin == kTopkBins - 1;
+    const uint32_t prefix = fl + bin;
+    const int lane = t & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // the low 12 bits of the keys of the threshold's prefix, when they fit one wave (their order does not matter)
     const bool few = !open && nb <= 64u;
     if (few) {
@@ -740,18 +717,18 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
 size_t topk_workspace_bytes(const Geo& g) {
   const size_t nblk = (size_t)std::max(1, (g.max_row_len + kCh - 1) / kCh);
   const size_t R = (size_t)g.R;
-  return align_up(4 * R * kTopkBins) + 2 * align_up(16 * R) + 2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
+  return 2 * align_up(16 * R) + 2 * align_up(4 * R * nblk) + align_up(8 * R * kCap);
 }
 
 TopkState topk_state(const Geo& g, void* workspace) {
   const Ws w = carve(g, workspace);
-  return TopkState{w.hist, w.cnt};
+  return TopkState{w.cnt};
 }
 
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
-  topk_zero_kernel<<<g.R, 256, 0, stream>>>(w.hist, w.cnt);
+  topk_zero_kernel<<<(g.R + 255) / 256, 256, 0, stream>>>(w.cnt, g.R);
   return hipGetLastError();
 }
 
@@ -771,12 +748,12 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const int cpb = chunks_per_block(g, w.nblk);
   dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
   if (cpb > 1)
-    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist, w.cnt,
-                                                         w.thr, w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
+    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr,
+                                                         w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
   else
-    topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.hist, w.cnt, w.thr,
+    topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr,
                                                   w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
-  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.hist, w.cnt,
+  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
                                                 w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx,
                                                 PoolRows{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages,
                                                          g.num_pages, g.log2ps});
