@@ -38,7 +38,7 @@ constexpr int kIdxSub = 4;                          // 32-position subtiles per 
 constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread block
 
 template <int HB>  // HB = number of 32-head blocks (H_I = 32 * HB)
-__global__ __launch_bounds__(256) void indexer_f8_kernel(
+__global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
@@ -118,34 +118,48 @@ __global__ __launch_bounds__(256) void indexer_f8_kernel(
   for (int hb = 0; hb < HB; ++hb) require_loaded(a[hb]);
   const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)r * ld, (short)0, n * 4, kBufferWord3);
 
+  // A tile is kUnits (pair p, subtile 2 p + u of the pair, head block hb) MFMA units in that order.  The MFMA of
+  // unit k + 1 is issued into a second accumulator before the epilogue of unit k (sched_barrier keeps that
+  // order), so the matrix core works while the VALU reduces: with one accumulator every MFMA waited for the
+  // previous epilogue and every epilogue for its MFMA.
+  constexpr int kUnits = kIdxSub * HB;
   auto compute = [&](int t, const TileLoad& cur) __attribute__((always_inline)) {
+    auto unit_mfma = [&](int k) __attribute__((always_inline)) {
+      const v16f zero = {};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[k % HB], cur.b[k / HB], zero, 0, 0, 0, 0, 0, 0);
+    };
+    v16f acc = unit_mfma(0);
+    // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
+    // fmaxf would also need a NaN-quieting max
+    float lin = 0.f, ab = 0.f;
+    float part[2];
 #pragma unroll
-    for (int p = 0; p < kIdxSub / 2; ++p) {
-      // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
-      // fmaxf would also need a NaN-quieting max
-      float part[2];
+    for (int k = 0; k < kUnits; ++k) {
+      const int sub = k / HB, hb = k % HB, p = sub / 2, u = sub % 2;
+      v16f nxt;
+      if (k + 1 < kUnits) nxt = unit_mfma(k + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float lin = 0.f, ab = 0.f;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          v16f acc = {};
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], cur.b[2 * p + u], acc, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            lin = fmaf(wq[hb][i], acc[i], lin);
-            ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
-          }
-        }
-        part[u] = lin + ab;
+      for (int i = 0; i < 16; ++i) {
+        lin = fmaf(wq[hb][i], acc[i], lin);
+        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
       }
-      // half 0 finishes subtile 2 p and half 1 subtile 2 p + 1: v_permlane32_swap of the two subtiles' partial
-      // sums hands each half the other half's sum of the subtile it stores
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-      const float v = cur.skm[p] * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1])));
-      const int64_t pos = position(t, 2 * p + half);
-      // the buffer ends at the row's visible length: stores past it are dropped
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)pos * 4, 0, 0);
+      if (hb == HB - 1) {
+        part[u] = lin + ab;
+        lin = 0.f;
+        ab = 0.f;
+      }
+      if (hb == HB - 1 && u == 1) {
+        // half 0 finishes subtile 2 p and half 1 subtile 2 p + 1: v_permlane32_swap of the two subtiles' partial
+        // sums hands each half the other half's sum of the subtile it stores
+        const auto sw =
+            __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+        const float v = cur.skm[p] * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1])));
+        const int64_t pos = position(t, 2 * p + half);
+        // the buffer ends at the row's visible length: stores past it are dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)pos * 4, 0, 0);
+      }
+      if (k + 1 < kUnits) acc = nxt;
     }
   };
 
