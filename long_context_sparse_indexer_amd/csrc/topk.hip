@@ -244,58 +244,61 @@ struct ResolveLds {
   int32_t pt[kResPages];          // page ids of the row's sequence, when they fit
 };
 
-// The bin b of LDS histogram h (kTopkBins bins, complete: a barrier after its last update) holding the need-th
-// largest entry, counting from the top bin, and the number of entries in the bins above it; both stay as the
-// caller preset them when the histogram holds fewer than `need` entries.  With `clear`, every thread zeroes the
-// bins it read, so h is all zero on return.  Called by all NT threads; ends with a barrier, after which *b and
-// *above are valid.
-template <int NT>
-__device__ __forceinline__ void lds_threshold_bin(uint32_t* h, uint32_t need, bool clear, uint32_t* scan,
-                                                  uint32_t* b, uint32_t* above_out) {
-  constexpr int kPer = kTopkBins / NT;
-  const int grp = NT - 1 - threadIdx.x;  // thread 0 owns the top bins
-  uint32_t c[kPer];
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    c[j] = h[grp * kPer + j];
-    local += c[j];
-  }
-  if (clear)
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) h[grp * kPer + j] = 0u;
-  uint32_t total;
-  uint32_t above = block_scan1<NT>(local, scan, total);
-  if (above < need && above + local >= need) {
-    for (int j = kPer - 1; j >= 0; --j) {
-      if (above + c[j] >= need) {
-        *b = (uint32_t)(grp * kPer + j);
-        *above_out = above;
-        break;
-      }
-      above += c[j];
-    }
-  }
-  __syncthreads();
-}
-
 // A sampled row of n scores is sampled about n / kSampleDiv times (n / 64 measured slower: 1.7 us more per
 // 128K-position decode step, 8% more for a 4096-row prefill chunk, from the extra candidates).
 constexpr int kSampleDiv = 32;
 
+// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, found by wave 0
+// alone in two levels: lane l sums the kBins/64 bins (63 - l) * kBins/64 .. (lane 0 the top ones) with 16-byte
+// reads and a DPP scan over the lanes picks the lane L holding the bin; then lanes g < kBins/256 take L's groups
+// of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
+// number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
+// Called by wave 0 only; the caller publishes the result with a barrier.
+template <int kBins>
+__device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
+  constexpr int kPer = kBins / 64, kGroups = kPer / 4;
+  static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
+  const int lane = threadIdx.x;
+  const v4i* hb = reinterpret_cast<const v4i*>(h);
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const v4i x = hb[(63 - lane) * kGroups + q];
+    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  }
+  uint32_t tot;
+  const uint32_t above = wave_exclusive_scan(local, tot);
+  const uint64_t hit = __ballot(above < need && above + local >= need);
+  if (!hit) return;  // uniform: fewer than `need` entries
+  const int L = __builtin_ctzll(hit);
+  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+  const v4i z = {0, 0, 0, 0};
+  const v4i x = lane < kGroups ? hb[(63 - L) * kGroups + (kGroups - 1 - lane)] : z;
+  const uint32_t gsum = (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  uint32_t tot2;
+  uint32_t a = above_l + wave_exclusive_scan(gsum, tot2);
+  if (lane < kGroups && a < need && a + gsum >= need) {
+    int e = 3;
+    while (e > 0 && a + (uint32_t)x[e] < need) a += (uint32_t)x[e--];
+    *b = (uint32_t)((63 - L) * kPer + 4 * (kGroups - 1 - lane) + e);
+    *above_out = a;
+  }
+}
+
 // The row's floor: the first 20 bits of the m-th largest score of a sample of the row, ranked in two rounds of an
-// LDS histogram: bits 31..20 of every sampled key, then bits 19..12 of those in the bin found (256 bins, scanned by
-// one wave).  The sample is S scores in S/4 runs of four (one 16-byte load each) spread evenly over the row, with
-// S the power of two in (n / 2d, n / d] for d = kSampleDiv, kept within [1024, 16384] (up to 65536 for rows past
-// 2^21): it reads a small part of the row and is the same in every block.  With mu = k_eff S/n the expected number
-// of sampled scores among the row's k_eff largest, m = mu + 8 sqrt(mu) + 16 puts the floor far enough below the
-// k_eff-th largest score that a row rarely has fewer than k_eff scores at or above it, while about
-// n m / S = k_eff + 8 sqrt(k_eff n / S) + 16 n / S scores reach it.  A row of at most one chunk is its own sample,
-// with m = k_eff: its floor is exactly the 20-bit prefix of the k_eff-th largest score.  h: kTopkBins words of
-// LDS, left all zero when `clear`; s: 4 words of LDS.  Called by all NT threads; ends with a barrier.
+// LDS histogram: bits 31..20 of every sampled key (4096 bins in h), then bits 19..12 of those in the bin found
+// (256 bins in h2), each ranked by one wave.  The sample is S scores in S/4 runs of four (one 16-byte load each)
+// spread evenly over the row, with S the power of two in (n / 2d, n / d] for d = kSampleDiv, kept within
+// [1024, 16384] (up to 65536 for rows past 2^21): it reads a small part of the row and is the same in every block.
+// With mu = k_eff S/n the expected number of sampled scores among the row's k_eff largest, m = mu + 8 sqrt(mu) + 16
+// puts the floor far enough below the k_eff-th largest score that a row rarely has fewer than k_eff scores at or
+// above it, while about n m / S = k_eff + 8 sqrt(k_eff n / S) + 16 n / S scores reach it.  A row of at most one
+// chunk is its own sample, with m = k_eff: its floor is exactly the 20-bit prefix of the k_eff-th largest score.
+// h, h2: kTopkBins and 256 words of LDS, 16-byte aligned; s: 4 words of LDS.  Called by all NT threads; ends with
+// a barrier.
 template <int NT>
-__device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, bool clear,
-                                                 uint32_t* h, uint32_t* scan, uint32_t* s) {
+__device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, uint32_t* h,
+                                                 uint32_t* h2, uint32_t* s) {
   constexpr int kGroup = 4;  // runs per thread held in registers: all of them up to S = 16384
   int runs, m, step = 4;  // run j starts at position j * step (rounded down to a multiple of 4)
   if (n <= kCh) {
@@ -322,7 +325,7 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
   };
   // one histogram round over the sample: bin (key >> shift) & mask of every sampled key whose bits from
   // shift + bits up equal `prefix`
-  auto round = [&](int shift, int bits, uint32_t prefix, bool reload) __attribute__((always_inline)) {
+  auto round = [&](uint32_t* hist, int shift, int bits, uint32_t prefix, bool reload) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int g = 0; g < ngroups; ++g) {
       if (g > 0 || reload) load(g);
@@ -339,7 +342,7 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
             const bool in = (n > kCh || 4 * j + e < n) && (uint32_t)((uint64_t)key >> (shift + bits)) == prefix;
             const uint32_t b = (key >> shift) & ((1u << bits) - 1u);
             if (in && cntb && b != bin) {
-              atomicAdd(&h[bin], cntb);
+              atomicAdd(&hist[bin], cntb);
               cntb = 0;
             }
             if (in) {
@@ -347,41 +350,26 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
               ++cntb;
             }
           }
-          if (cntb) atomicAdd(&h[bin], cntb);
+          if (cntb) atomicAdd(&hist[bin], cntb);
         }
       }
     }
   };
-  load(0);  // in flight while the histogram is cleared
+  load(0);  // in flight while the histograms are cleared
   for (int i = threadIdx.x; i < kTopkBins; i += NT) h[i] = 0u;
+  for (int i = threadIdx.x; i < 256; i += NT) h2[i] = 0u;
   if (threadIdx.x == 0) {  // a floor of 0 keeps every key, should the sample rank fail
     s[0] = s[1] = s[2] = s[3] = 0u;
   }
   __syncthreads();
-  round(20, 12, 0u, false);
+  round(h, 20, 12, 0u, false);
   __syncthreads();
-  lds_threshold_bin<NT>(h, (uint32_t)m, true, scan, &s[0], &s[1]);
+  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins>(h, (uint32_t)m, &s[0], &s[1]);
+  __syncthreads();
   const uint32_t b1 = s[0];
-  round(12, 8, b1, ngroups > 1);
+  round(h2, 12, 8, b1, ngroups > 1);
   __syncthreads();
-  if (threadIdx.x < 64) {  // wave 0 ranks the 256 bins, lane l owning bins 252 - 4 l .. 255 - 4 l (top first)
-    const int lane = threadIdx.x;
-    const uint32_t need = (uint32_t)m - s[1];
-    const v4i c = reinterpret_cast<const v4i*>(h)[63 - lane];
-    if (clear) reinterpret_cast<v4i*>(h)[63 - lane] = v4i{0, 0, 0, 0};
-    const uint32_t local = (uint32_t)(c[0] + c[1] + c[2] + c[3]);
-    uint32_t tot;
-    uint32_t above = wave_exclusive_scan(local, tot);
-    if (above < need && above + local >= need) {
-      for (int j = 3; j >= 0; --j) {
-        if (above + (uint32_t)c[j] >= need) {
-          s[2] = (uint32_t)(4 * (63 - lane) + j);
-          break;
-        }
-        above += (uint32_t)c[j];
-      }
-    }
-  }
+  if (threadIdx.x < 64) wave_threshold_bin<256>(h2, (uint32_t)m - s[1], &s[2], &s[3]);
   __syncthreads();
   return (b1 << 8) | s[2];
 }
@@ -401,6 +389,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
                                                            int nblk_max, int cpb) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h2[256];
   __shared__ uint32_t seg_base, s_f[4];
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
@@ -411,7 +400,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const float* row = scores + (int64_t)r * ld;
   v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
   // every block ranks the sample itself instead of waiting for one block to publish the floor
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, false, h, scan, s_f);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   auto filter = [&](int ch, const v4f& x) __attribute__((always_inline)) {
@@ -468,7 +457,8 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     int cpb) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ uint64_t stage[kStageCap];
-  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histogram
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histograms
+  __shared__ __attribute__((aligned(16))) uint32_t h2[256];
   __shared__ uint32_t chunk_n[kTopkMaxBlocksPerRow];  // candidates of each staged chunk
   __shared__ uint32_t seg_base, s_f[4];
   const int r = blockIdx.y;
@@ -479,7 +469,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, false, h, scan, s_f);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
