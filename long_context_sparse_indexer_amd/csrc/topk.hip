@@ -142,8 +142,7 @@ template <int NT, class List, class Rows>
 __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_need, int keff, int32_t* out,
                                 const Rows& rows) {
   constexpr int NW = NT / 64;
-  static_assert(NW % 4 == 0, "wave counts are read four at a time");
-  __shared__ __attribute__((aligned(16))) uint32_t w_gt[NW], w_eq[NW];
+  __shared__ uint32_t w_gt[NW], w_eq[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int span = ((len + NW * 64 - 1) / (NW * 64)) * 64;
   const int lo = wave * span, hi = min(len, lo + span);
@@ -166,14 +165,17 @@ __device__ void write_selection(const List& L, int len, uint32_t T, uint32_t eq_
   }
   if (lane == 0) { w_gt[wave] = gt; w_eq[wave] = eq; }
   __syncthreads();
-  // this wave's first slot and its rank among the keys equal to T: the waves before it take all their keys
-  // above T and their share of the equal ones, in list order
-  uint32_t eq_run = 0, slot_run = 0;
-  for (int w = 0; w < wave; ++w) {
-    const uint32_t we = w_eq[w];
-    slot_run += w_gt[w] + (eq_run >= eq_need ? 0u : min(we, eq_need - eq_run));
-    eq_run += we;
-  }
+  // this wave's first slot and its rank among the keys equal to T.  The waves before it take all their keys above
+  // T and, in list order, the equal ones while fewer than eq_need are taken: the share of wave w is
+  // min(E_w+1, eq_need) - min(E_w, eq_need) for E_w the equal keys of the waves before w, so the shares of the
+  // waves before this one add up to min(E, eq_need).  Both prefixes come from DPP scans over the wave counts.
+  static_assert(NW <= 64, "one lane per wave");
+  const uint32_t gl = lane < NW ? w_gt[lane] : 0u, el = lane < NW ? w_eq[lane] : 0u;
+  uint32_t gsum, esum;
+  const uint32_t gpre = wave_exclusive_scan(gl, gsum), epre = wave_exclusive_scan(el, esum);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t eq_run = (uint32_t)__builtin_amdgcn_readlane((int)epre, wv);
+  uint32_t slot_run = (uint32_t)__builtin_amdgcn_readlane((int)gpre, wv) + min(eq_run, eq_need);
   for (int base = lo; base < hi; base += 64 * U) {
     uint32_t key[U];
     int32_t pos[U];
