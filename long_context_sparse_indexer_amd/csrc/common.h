@@ -94,24 +94,21 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t& to
   return (uint32_t)x - v;
 }
 
-// Block-wide exclusive scan of one value per thread.  `scratch` holds blockDim.x / 64 + 1 words of LDS.
-// Must be called by every thread of the block.
+// Block-wide exclusive scan of one value per thread.  `scratch` holds blockDim.x / 64 + 1 words of LDS.  Every
+// wave scans its lanes and publishes its total; after one barrier every wave scans the wave totals itself (one
+// per lane, DPP) and takes the prefix of its own with v_readlane.  A trailing barrier lets the next call reuse
+// `scratch`.  Must be called by every thread of the block.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
   uint32_t wt;
   uint32_t x = wave_exclusive_scan(v, wt);
   if (lane == 0) scratch[wave] = wt;
   __syncthreads();
-  if (wave == 0) {  // the wave totals, scanned by one wave (at most 64 waves per block)
-    const uint32_t t = lane < nwaves ? scratch[lane] : 0u;
-    uint32_t run;
-    const uint32_t ex = wave_exclusive_scan(t, run);
-    if (lane < nwaves) scratch[lane] = ex;
-    if (lane == 0) scratch[nwaves] = run;
-  }
-  __syncthreads();
-  x += scratch[wave];
-  total = scratch[nwaves];
+  const uint32_t t = lane < nwaves ? scratch[lane] : 0u;  // at most 64 waves per block
+  uint32_t tot;
+  const uint32_t pre = wave_exclusive_scan(t, tot);
+  x += (uint32_t)__builtin_amdgcn_readlane((int)pre, __builtin_amdgcn_readfirstlane(wave));
+  total = tot;
   __syncthreads();
   return x;
 }
