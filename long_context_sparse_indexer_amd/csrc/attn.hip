@@ -631,58 +631,62 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s,
-// in fp32.  One 128-thread block per (row, head), thread t owning latent columns 4t .. 4t+3 (d_c = 512).  Every
-// load -- the first wave's split lse values, each thread's 8-byte pieces of up to kCombineBatch partial rows
-// and their exponents -- is issued before any is used, so the weights and the rows arrive in one round trip.
+// in fp32.  One 256-thread block per (row, head): wave w takes splits w, w + 4, ..., lane l latent columns
+// 8l .. 8l+7 (d_c = 512) as one 16-byte load per split.  Every load is issued before any is used, so the weights
+// and the rows arrive in one round trip; waves 1-3 hand their sums to wave 0 through LDS.
 constexpr int kMaxSplit = 64;
-constexpr int kCombineBatch = 32;
-__global__ __launch_bounds__(128) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
                                                            const int32_t* __restrict__ part_exp,
                                                            const float* __restrict__ part_lse, int H, int nsplit,
                                                            unsigned short* __restrict__ out, float* __restrict__ lse) {
-  static_assert(kDC == 4 * 128, "four latent columns per thread");
-  __shared__ float wts[kMaxSplit];
+  static_assert(kDC == 8 * 64, "eight latent columns per lane");
+  static_assert(kMaxSplit <= 64, "one split per lane for the weights");
+  constexpr int kPerWave = kMaxSplit / 4;
+  __shared__ float red[3][8][64];  // waves 1..3: their partial sums, column-major per lane
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
-  const int d = 4 * threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t row0 = (int64_t)r * nsplit * H + h;  // partial row of split 0; split j is j * H further
-  float ls = -INFINITY;
-  if (threadIdx.x < 64 && (int)threadIdx.x < nsplit) ls = part_lse[row0 + (int64_t)threadIdx.x * H];
-  auto piece = [&](int j) { return *reinterpret_cast<const v4s*>(part_o + (row0 + (int64_t)j * H) * kDC + d); };
-  auto expo = [&](int j) { return part_exp[row0 + (int64_t)j * H]; };
-  v4s v[kCombineBatch];
-  int ex[kCombineBatch];
+  // every load first: lane j holds split j's lse and exponent (every wave reads them), and each wave the eight
+  // columns of lane `lane` of its splits wave, wave + 4, ...
+  const bool has = lane < nsplit;
+  const float ls = has ? part_lse[row0 + (int64_t)lane * H] : -INFINITY;
+  const int ex = has ? part_exp[row0 + (int64_t)lane * H] : 0;
+  v8us v[kPerWave];
 #pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j) {
-    v[j] = j < nsplit ? piece(j) : v4s{0, 0, 0, 0};
-    ex[j] = j < nsplit ? expo(j) : 0;
+  for (int q = 0; q < kPerWave; ++q) {
+    const int j = wave + 4 * q;
+    if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
   }
-  if (threadIdx.x < 64) {
-    const float mx = wave_max(ls);
-    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
-    const float wsum = wave_sum(w);
-    wts[threadIdx.x] = wsum > 0.f ? w / wsum : 0.f;
-    if (threadIdx.x == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  // split weights w_j = exp(lse_j - max) / sum, each wave for itself; lane j also folds in split j's exponent
+  const float mx = wave_max(ls);
+  const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
+  const float wsum = wave_sum(w);
+  const float wl = ldexpf(wsum > 0.f ? w / wsum : 0.f, ex);
+  auto half_f = [](unsigned short b) { return (float)__builtin_bit_cast(_Float16, b); };
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int j = wave + 4 * q;
+    if (j < nsplit) {
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
+    }
   }
+  if (wave > 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave - 1][e][lane] = acc[e];
   __syncthreads();
-  auto half_f = [](short b) { return (float)__builtin_bit_cast(_Float16, (unsigned short)b); };
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0) {
+    v8us b;
 #pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j) {
-    const float w = ldexpf(wts[j], ex[j]);  // wts[j] = 0 past nsplit
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, half_f(v[j][e]), acc[e]);
+    for (int e = 0; e < 8; ++e) b[e] = float_to_bf16_bits(acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane]);
+    *reinterpret_cast<v8us*>(out + ((int64_t)r * H + h) * kDC + lane * 8) = b;  // 16-byte aligned
+    if (lane == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
-  for (int j = kCombineBatch; j < nsplit; ++j) {
-    const v4s x = piece(j);
-    const float w = ldexpf(wts[j], expo(j));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, half_f(x[e]), acc[e]);
-  }
-  v4s b;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) b[e] = (short)float_to_bf16_bits(acc[e]);
-  *reinterpret_cast<v4s*>(out + ((int64_t)r * H + h) * kDC + d) = b;  // 8-byte aligned: d is a multiple of 4
 }
 
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
@@ -869,7 +873,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                             nullptr, pt.o, pt.ex, pt.lse);
     }
     if (p.nsplit > 1)
-      attn_combine_kernel<<<g.R * g.H, 128, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit,
+      attn_combine_kernel<<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit,
                                                        static_cast<unsigned short*>(out), lse);
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
