@@ -66,6 +66,13 @@ def test_index_heads_32_and_small_budgets():
     _run(synth.get("decode_128k", lengths=[5000], k=1, H=16, anchors=16, recent=32))
 
 
+def test_large_budgets_multi_chunk_splits():
+    # k = 8000 over one row: the 16-head kernel runs two 64-slot chunks per split (63 splits, register gathers
+    # double-buffered); k = 8192 over two rows: the all-heads kernel with splits of its own, merged by the combine
+    _run(synth.get("decode_128k", lengths=[100000], k=8000, anchors=64, recent=128))
+    _run(synth.get("decode_128k", lengths=[40000, 30000], k=8192, H=128, anchors=64, recent=128))
+
+
 def test_softmax_scale_and_signed_weights():
     def signed(prob):
         rng = np.random.default_rng(123)
