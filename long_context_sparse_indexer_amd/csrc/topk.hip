@@ -617,18 +617,6 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
       S.seg_src[t] = src;
     }
     __syncthreads();
-    // every candidate goes to its chunk's segment start + its offset within the segment
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = j * kRes + t;
-      if (i < (int)len) {
-        const uint32_t pos = (uint32_t)(e[j] >> 32);
-        const int chunk = (int)(pos / kCh);
-        const uint32_t dst = S.seg_start[chunk] + ((uint32_t)i - S.seg_src[chunk]);
-        S.key[dst] = (uint32_t)e[j];
-        S.pos[dst] = (int32_t)pos;
-      }
-    }
     // the bin holding the k_eff-th largest key, thread t owning bins (kRes - 1 - t) * kPerBin .. (top first)
     const v4i hv = reinterpret_cast<const v4i*>(S.h)[kRes - 1 - t];
     const uint32_t hl = (uint32_t)(hv[0] + hv[1] + hv[2] + hv[3]);
@@ -653,13 +641,21 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     const uint32_t prefix = fl + bin;
     const int lane = t & 63;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    // the low 12 bits of the keys of the threshold's prefix, when they fit one wave (their order does not matter)
+    // every candidate goes to its chunk's segment start + its offset within the segment; beside, the low 12 bits
+    // of the keys of the threshold's prefix are collected when they fit one wave (their order does not matter)
     const bool few = !open && nb <= 64u;
-    if (few) {
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = j * kRes + t;
-        const uint32_t key = (uint32_t)e[j];
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kRes + t;
+      const uint32_t key = (uint32_t)e[j];
+      if (i < (int)len) {
+        const uint32_t pos = (uint32_t)(e[j] >> 32);
+        const int chunk = (int)(pos / kCh);
+        const uint32_t dst = S.seg_start[chunk] + ((uint32_t)i - S.seg_src[chunk]);
+        S.key[dst] = key;
+        S.pos[dst] = (int32_t)pos;
+      }
+      if (few) {
         const bool match = i < (int)len && (key >> 12) == prefix;
         const uint64_t mm = __ballot(match);
         if (mm) {  // uniform over the wave
@@ -676,9 +672,7 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
     uint32_t need = (uint32_t)keff - s_above;  // keys of the threshold's bin still to take
     uint32_t T;
     if (few) {
-      // every wave finds the low bits itself, by a radix select over the nb keys held one per lane: from the top
-      // bit down, keep the lanes whose bit is set if they hold at least `need` keys, else take those keys and keep
-      // the others
+      // every wave finds the low bits itself: lane x ranks the low bits of the x-th key of the prefix among all nb
       const uint32_t dx = lane < (int)nb ? S.bin[lane] : 0u;
       uint32_t gt = 0, ge = 0;
       for (uint32_t y = 0; y < nb; ++y) {
