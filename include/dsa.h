@@ -61,7 +61,7 @@ typedef struct {
   int32_t num_rows;      /* R: query rows in the call (one per sequence in decode, one per position in prefill) */
   int32_t num_seqs;      /* S: rows of page_table */
   int32_t idx_heads;     /* H_I: indexer heads.  F8E4M3: 32 or 64.  F32: 1..64 */
-  int32_t idx_dim;       /* d_I: indexer head width.  F8E4M3: 64.  F32: 1..128 */
+  int32_t idx_dim;       /* d_I: indexer head width.  F8E4M3: 64 or 128.  F32: 1..128 */
   int32_t attn_heads;    /* H: attention heads sharing one latent row.  BF16: multiple of 16, <= 256.  F32: <= 256 */
   int32_t latent_dim;    /* d_c: latent width.  BF16: 512.  F32: 1..1024 */
   int32_t topk;          /* k: positions kept per row, 1..16384 */

@@ -64,7 +64,8 @@ dsa_status_t check_problem(const dsa_problem_t* p, const dsa_layout_t* lay, bool
     DSA_CHECK(p->idx_dtype == DSA_F8E4M3 || p->idx_dtype == DSA_F32, DSA_EINVAL, "idx_dtype = %d invalid",
               p->idx_dtype);
     if (p->idx_dtype == DSA_F8E4M3) {
-      DSA_CHECK(p->idx_dim == 64, DSA_EUNSUPPORTED, "fp8 indexer needs idx_dim = 64 (got %d)", p->idx_dim);
+      DSA_CHECK(p->idx_dim == 64 || p->idx_dim == 128, DSA_EUNSUPPORTED,
+                "fp8 indexer needs idx_dim = 64 or 128 (got %d)", p->idx_dim);
       DSA_CHECK(p->idx_heads == 32 || p->idx_heads == 64, DSA_EUNSUPPORTED,
                 "fp8 indexer needs idx_heads of 32 or 64 (got %d)", p->idx_heads);
     } else {

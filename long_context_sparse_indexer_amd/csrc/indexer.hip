@@ -4,17 +4,17 @@
 // (DeepSeek Sparse Attention explained, "How Does the Lightning Indexer Score a Token?": H_I heads, one
 // shared key per position, ReLU, head-weighted sum; head weights carry no sign constraint).
 //
-// fp8 path.  The per-row contraction [H_I x d_I] x [d_I x n] is a dense GEMM with K = d_I = 64, which is
-// exactly the K of v_mfma_f32_32x32x64_f8f6f4.  Heads are the M dimension, positions the N dimension:
+// fp8 path.  The per-row contraction [H_I x d_I] x [d_I x n] is a dense GEMM with K = d_I = 64 or 128: one or
+// two chained v_mfma_f32_32x32x64_f8f6f4 (K = 64 each).  Heads are the M dimension, positions the N dimension:
 // lane l of a wave holds head (l % 32) of the A operand and position (l % 32) of the B operand, each with
 // the 32 bytes of K half (l / 32); the 32x32 fp32 result leaves 16 heads of one position in each lane, so
 // the ReLU and the head-weighted sum run in-lane and finish with one cross-half exchange.  The fp8 codes
-// are OCP e4m3fn (the format gfx950's f8f6f4 MFMA reads with format code 0), products are exact and the 64
+// are OCP e4m3fn (the format gfx950's f8f6f4 MFMA reads with format code 0), products are exact and the d_I
 // terms accumulate in fp32.  Because the per-vector scales are positive they move outside the ReLU:
 // max(0, sq*sk*x) = sq*sk*max(0, x), so the epilogue weight of head j is w[j]*sq[j] and sk multiplies
 // the finished sum.  The ReLU-weighted sum is formed as (sum_j wq_j x_j + sum_j wq_j |x_j|) / 2.
 //
-// Every key row is read once, as 32-byte pieces: one wave covers 32 consecutive positions = 2 KiB of
+// Every key row is read once, as 32-byte pieces: one wave covers 32 consecutive positions = 32 d_I bytes of
 // contiguous pool memory (a 32-aligned run never crosses a page of >= 32 positions).
 //
 // In the fused step block 0 of each row also clears the row's top-k state once its scores are out, so the
@@ -37,14 +37,17 @@ __device__ __forceinline__ void require_loaded(const v8i& x) { asm volatile("" :
 constexpr int kIdxSub = 4;                          // 32-position subtiles per wave
 constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread block
 
-template <int HB>  // HB = number of 32-head blocks (H_I = 32 * HB)
-__global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
+// HB = number of 32-head blocks (H_I = 32 * HB); KB = number of 64-byte K blocks (d_I = 64 * KB), one
+// v_mfma_f32_32x32x64_f8f6f4 each, chained on one accumulator.  Three waves per SIMD fit d_I = 64; the doubled key
+// and query operands of d_I = 128 leave room for two.
+template <int HB, int KB>
+__global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
     int tiles_per_block) {
-  constexpr int H_I = 32 * HB;
+  constexpr int H_I = 32 * HB, D_I = 64 * KB;
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int64_t first = (int64_t)blockIdx.x * tiles_per_block * kIdxTile;
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
   // per tile and lane: the key rows of the four subtiles (MFMA B operands) and the scales of the two positions
   // the lane stores (subtile 2 p + half of each pair p)
   struct TileLoad {
-    v8i b[kIdxSub];
+    v8i b[kIdxSub][KB];
     float skm[kIdxSub / 2];
   };
   auto issue = [&](int t, TileLoad& L) __attribute__((always_inline)) {
@@ -90,7 +93,10 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
 #pragma unroll
     for (int s = 0; s < kIdxSub; ++s) prow[s] = subtile_rows(t, s);
 #pragma unroll
-    for (int s = 0; s < kIdxSub; ++s) L.b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
+    for (int s = 0; s < kIdxSub; ++s)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        L.b[s][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * D_I + kb * 64 + half * 32);
 #pragma unroll
     for (int p = 0; p < kIdxSub / 2; ++p) {
       // the store subtile's row, picked arithmetically (an indexed pick would put prow in scratch)
@@ -101,11 +107,14 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
 
   TileLoad cur;
   issue(0, cur);
-  v8i a[HB];
+  v8i a[HB][KB];
   float wq[HB][16];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    a[hb] = *reinterpret_cast<const v8i*>(q_idx + ((int64_t)r * H_I + hb * 32 + col) * 64 + half * 32);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      a[hb][kb] =
+          *reinterpret_cast<const v8i*>(q_idx + ((int64_t)r * H_I + hb * 32 + col) * D_I + kb * 64 + half * 32);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int head = hb * 32 + half * 4 + (i & 3) + 8 * (i >> 2);
@@ -115,7 +124,9 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
   // the row's query operands are complete before the loop (an asm use makes the compiler wait here once
   // instead of inside every iteration)
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) require_loaded(a[hb]);
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) require_loaded(a[hb][kb]);
   const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)r * ld, (short)0, n * 4, kBufferWord3);
 
   // A tile is kUnits (pair p, subtile 2 p + u of the pair, head block hb) MFMA units in that order.  The MFMA of
@@ -125,8 +136,11 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_kernel(
   constexpr int kUnits = kIdxSub * HB;
   auto compute = [&](int t, const TileLoad& cur) __attribute__((always_inline)) {
     auto unit_mfma = [&](int k) __attribute__((always_inline)) {
-      const v16f zero = {};
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[k % HB], cur.b[k / HB], zero, 0, 0, 0, 0, 0, 0);
+      v16f acc = {};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[k % HB][kb], cur.b[k / HB][kb], acc, 0, 0, 0, 0, 0, 0);
+      return acc;
     };
     v16f acc = unit_mfma(0);
     // max(0, x) = (x + |x|) / 2: two single-instruction FMAs per element (|x| is a source modifier), where
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 }  // namespace
 
-template <int HB>
+template <int HB, int KB>
 void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w, const uint8_t* kp,
                const float* k_idx_scale, float* scores, int64_t ld, const TopkState* fuse, hipStream_t stream) {
   // one 512-position tile per block up to kIdxTargetBlocks blocks (small, latency-bound problems spread as
@@ -477,7 +491,7 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
   const int64_t tiles = (int64_t)tiles_row * g.R;
   const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / kIdxTargetBlocks));
   dim3 grid((tiles_row + per - 1) / per, g.R);
-  indexer_f8_kernel<HB><<<grid, 256, 0, stream>>>(
+  indexer_f8_kernel<HB, KB><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
       g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr}, per);
 }
@@ -493,7 +507,10 @@ void launch_f8_tiled(const Geo& g, const uint8_t* qp, const float* q_idx_scale, 
       g.log2ps, g.max_row_len, g.R, g.rows_per_seq, tiles_per_group, scores, ld);
 }
 
-bool indexer_tiled(const Geo& g) { return g.idx_dtype == 2 /* F8E4M3 */ && g.rows_per_seq >= kTiledMinRows; }
+// the tiled kernel is written for d_I = 64; other fp8 shapes take the per-row kernel for every row
+bool indexer_tiled(const Geo& g) {
+  return g.idx_dtype == 2 /* F8E4M3 */ && g.d_I == 64 && g.rows_per_seq >= kTiledMinRows;
+}
 
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
@@ -510,8 +527,14 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
   if (g.idx_dtype == 2 /* F8E4M3 */) {
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
-    if (g.H_I == 64) launch_f8<2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
-    else launch_f8<1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    if (g.d_I == 128) {
+      if (g.H_I == 64) launch_f8<2, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+      else launch_f8<1, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    } else if (g.H_I == 64) {
+      launch_f8<2, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    } else {
+      launch_f8<1, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, fuse, stream);
+    }
   } else {
     if (fuse) return hipErrorInvalidValue;  // only the fp8 kernel clears the top-k state
     dim3 grid((g.max_row_len + 255) / 256, g.R);

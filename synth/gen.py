@@ -13,7 +13,7 @@ Recipe (per sequence, fp32 masters, "N(0, v)" means variance v):
   attention queries q[h] ~ N(0, 1/d_c) for each of the H heads (already in latent space);
   boosted positions (random anchors drawn without replacement outside the most recent window, plus that
     window) get k_I[s] += 0.5 * mean_j q_I[j], which makes the score spiky at planted positions;
-  fp8 operands: scale = amax / 448 per 64-vector (1 for an all-zero vector), code = e4m3fn(RNE(x / scale)).
+  fp8 operands: scale = amax / 448 per d_I-vector (1 for an all-zero vector), code = e4m3fn(RNE(x / scale)).
 Pages are 64 positions; a paged workload places every logical page of every sequence at a random physical
 page of one shared pool, the others place them in order.
 """

@@ -61,7 +61,7 @@ def test_null_problem_and_layout():
     (dict(max_row_len=4097), dsa.DSA_EINVAL, "max_row_len"),
     (dict(max_row_len=-5), dsa.DSA_EINVAL, "max_row_len"),
     (dict(rows_per_seq=0), dsa.DSA_EINVAL, "rows_per_seq"),
-    (dict(idx_dim=128), dsa.DSA_EUNSUPPORTED, "idx_dim"),
+    (dict(idx_dim=96), dsa.DSA_EUNSUPPORTED, "idx_dim"),
     (dict(idx_heads=48), dsa.DSA_EUNSUPPORTED, "idx_heads"),
     (dict(idx_dtype=7), dsa.DSA_EINVAL, "idx_dtype"),
     (dict(num_pages=0), dsa.DSA_EINVAL, "num_pages"),

@@ -66,6 +66,15 @@ def test_index_heads_32_and_small_budgets():
     _run(synth.get("decode_128k", lengths=[5000], k=1, H=16, anchors=16, recent=32))
 
 
+def test_index_dim_128_and_shipped_budgets():
+    # the shipped indexer shape (64 heads x 128 dims: two chained fp8 MFMAs per unit) at budgets 2048, 1024 and
+    # 512; decode rows, a paged batch, 32 index heads, and chunked-prefill rows (the per-row kernel serves them)
+    _run(synth.get("decode_128k", lengths=[20000], d_I=128, anchors=64, recent=96))
+    _run(synth.get("batched_paged", batch=5, length_range=(3000, 9000), d_I=128, k=1024, H=32))
+    _run(synth.get("decode_128k", lengths=[9000], H_I=32, d_I=128, k=512, H=16, anchors=16, recent=32))
+    _run(synth.get("prefill_chunk", cache_len=6000, rows=24, H=32, d_I=128, k=1024))
+
+
 def test_large_budgets_multi_chunk_splits():
     # k = 8000 over one row: the 16-head kernel runs two 64-slot chunks per split (63 splits, register gathers
     # double-buffered); k = 8192 over two rows: the all-heads kernel with splits of its own, merged by the combine
