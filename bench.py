@@ -10,6 +10,10 @@ Prints one JSON line.  `value` = query rows completed per second of wall time (t
 on both sides of exactly --steps steps).  `roofline` = the indexer kernel (the dominant one) against the
 8 TB/s HBM peak: algorithmic bytes per launch over its mean launch time, from HIP events on its stream.
 `cpu_baseline` = the fp64 CPU oracle timed on this host over a bounded sample of the same workload.
+
+`--crossover` instead times the sparse step against dense attention over every visible position
+(dsa_dense_mla_attn) for one query row at a range of context lengths, one JSON line per length: the short-context
+fallback's break-even on this GPU.
 """
 from __future__ import annotations
 
@@ -50,6 +54,68 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def crossover(lengths, rows: int, steps: int) -> int:
+    """Sparse step vs dense attention, one JSON line per context length (graph replay, rotated inputs)."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_indexer_amd as dsa
+    from long_context_sparse_indexer_amd import cost
+    import synth
+    from synth.device import upload
+
+    dev = torch.device("cuda:0")
+    names = ["q_idx", "q_idx_scale", "head_w", "k_idx_pool", "k_idx_scale", "q", "kv_pool"]
+    for n in lengths:
+        prob = synth.make_problem(synth.get("decode_128k", lengths=[n] * rows, seed=7))
+        base = upload(prob, dev)
+        P = dsa.make_problem(**base.fields)
+        L = dsa.make_layout(base.row_seq, base.row_len, base.page_table)
+        sparse_bytes = cost.decode_row_bytes(n, prob.k, prob.H_I, prob.d_I, prob.H, prob.d_c)
+        touched = rows * max(sparse_bytes, n * prob.d_c * 2)
+        copies = max(2, min(32, int(np.ceil(3 * 256e6 / touched))))
+        sets = [{m: getattr(base, m) for m in names}] + [{m: getattr(base, m).clone() for m in names}
+                                                         for _ in range(copies - 1)]
+        idx = torch.empty((prob.R, prob.k), dtype=torch.int32, device=dev)
+        out = torch.empty((prob.R, prob.H, prob.d_c), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((prob.R, prob.H), dtype=torch.float32, device=dev)
+        ws_bytes = max(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_STEP), dsa.dsa_workspace_bytes(P, dsa.DSA_OP_DENSE))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def sparse(s, st):
+            dsa.dsa_decode_step(P, L, s["q_idx"], s["q_idx_scale"], s["head_w"], s["k_idx_pool"], s["k_idx_scale"],
+                                s["q"], s["kv_pool"], idx, out, lse, ws, st)
+
+        def dense(s, st):
+            dsa.dsa_dense_mla_attn(P, L, s["q"], s["kv_pool"], out, lse, ws, st)
+
+        res = {}
+        for mode, fn in (("sparse", sparse), ("dense", dense)):
+            for s in sets:
+                fn(s, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in sets:
+                    fn(s, torch.cuda.current_stream().cuda_stream)
+            reps = max(1, steps // copies)
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            res[mode] = (time.perf_counter() - t0) * 1e6 / (reps * copies)
+        print(json.dumps({"crossover": True, "context": n, "rows": rows, "k": prob.k,
+                          "sparse_us": round(res["sparse"], 2), "dense_us": round(res["dense"], 2),
+                          "faster": "dense" if res["dense"] < res["sparse"] else "sparse",
+                          "input_copies": copies}), flush=True)
+        del base, sets, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -64,6 +130,9 @@ def main() -> int:
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch every step from the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the sparse step against dense attention over context lengths, then exit")
+    ap.add_argument("--crossover-rows", type=int, default=1)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 4 times (reference dispatches for byte counters)")
     args = ap.parse_args()
@@ -71,6 +140,8 @@ def main() -> int:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding design); "
               "run with --gpus 1", file=sys.stderr)
         return 2
+    if args.crossover:
+        return crossover([2048, 4096, 8192, 16384, 32768, 65536, 131072], args.crossover_rows, min(args.steps, 400))
 
     import numpy as np
     import torch

@@ -54,7 +54,7 @@ typedef enum {
   DSA_F8E4M3 = 2   /* OCP FP8 E4M3FN codes (bias 7, max 448, no inf) with one fp32 scale per stored vector */
 } dsa_dtype_t;
 
-typedef enum { DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_STEP = 3 } dsa_op_t;
+typedef enum { DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_STEP = 3, DSA_OP_DENSE = 4 } dsa_op_t;
 
 /* Shapes, dtypes and bounds of one call.  Host memory, read during the call only. */
 typedef struct {
@@ -138,6 +138,21 @@ dsa_status_t dsa_decode_step(const dsa_problem_t *problem, const dsa_layout_t *l
                              const void *k_idx_pool, const float *k_idx_scale,
                              const void *q, const void *kv_pool, int32_t *topk_idx,
                              void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dense MLA attention in MQA mode over every visible position of each row (no indexer, no selection): the
+ * short-context fallback.  Below a crossover context the indexer's fixed cost outweighs what it saves, and a
+ * dense step is faster (milos-mitrovic, "When Does DSA Beat Dense Attention, and When Doesn't It?": the
+ * crossover lies near 40K-64K tokens for decode; kgptalkie, "DeepSeek Sparse Attention explained", "What Does
+ * It Cost?": a masked dense mode serves short prefills).  Row r attends to positions 0 .. n_r - 1 of its
+ * sequence; problem->topk is not used.
+ *   q, kv_pool, out, lse as for dsa_sparse_mla_attn
+ *   workspace >= dsa_workspace_bytes(problem, DSA_OP_DENSE) (the identity selection and split partials)
+ * Supported up to max_row_len = 131072 for bf16 latents and 4096 for fp32 (DSA_EUNSUPPORTED above).
+ */
+dsa_status_t dsa_dense_mla_attn(const dsa_problem_t *problem, const dsa_layout_t *layout, const void *q,
+                                const void *kv_pool, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Workspace bytes an operation needs for this problem (0 on an invalid problem; see dsa_last_error). */
 size_t dsa_workspace_bytes(const dsa_problem_t *problem, int32_t op);

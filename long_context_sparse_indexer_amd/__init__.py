@@ -14,7 +14,7 @@ from . import _build
 
 DSA_OK, DSA_EINVAL, DSA_EUNSUPPORTED, DSA_EWORKSPACE, DSA_EHIP = range(5)
 DSA_F32, DSA_BF16, DSA_F8E4M3 = 0, 1, 2
-DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_STEP = 1, 2, 3
+DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_STEP, DSA_OP_DENSE = 1, 2, 3, 4
 DTYPES = {"f32": DSA_F32, "bf16": DSA_BF16, "f8": DSA_F8E4M3}
 
 
@@ -51,7 +51,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk.argtypes = [PP, PL, P, I64, P, P, SZ, P]
         L.dsa_sparse_mla_attn.argtypes = [PP, PL, P, P, P, P, P, P, SZ, P]
         L.dsa_decode_step.argtypes = [PP, PL, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
-        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step"):
+        L.dsa_dense_mla_attn.argtypes = [PP, PL, P, P, P, P, P, SZ, P]
+        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [PP, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = SZ
@@ -131,6 +132,12 @@ def dsa_sparse_mla_attn(problem, layout, q, kv_pool, topk_idx, out, lse, workspa
                                      _ptr(kv_pool, "kv_pool"), _ptr(topk_idx, "topk_idx"), _ptr(out, "out"),
                                      _ptr(lse, "lse"), _ptr(workspace, "workspace"), _nbytes(workspace),
                                      _stream(stream)))
+
+
+def dsa_dense_mla_attn(problem, layout, q, kv_pool, out, lse, workspace, stream=None):
+    _check(lib().dsa_dense_mla_attn(ctypes.byref(problem), ctypes.byref(layout), _ptr(q, "q"),
+                                    _ptr(kv_pool, "kv_pool"), _ptr(out, "out"), _ptr(lse, "lse"),
+                                    _ptr(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
 
 
 def dsa_decode_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx,

@@ -160,6 +160,21 @@ dsa_status_t hip_status(hipError_t e, const char* what) {
 
 int64_t step_ld(const dsa::Geo& g) { return ((int64_t)std::max(g.max_row_len, 1) + 63) / 64 * 64; }
 
+// Dense attention is the sparse kernels over the identity selection of every visible position: the selection
+// width becomes the longest row (at least 1), within what the attention kernels split over (64 splits of 2048
+// slots for the bf16 all-heads kernel; the fp32 kernel's 4096).
+dsa_status_t dense_geo(dsa::Geo* g) {
+  const int cap = g->kv_dtype == DSA_BF16 ? 131072 : 4096;
+  DSA_CHECK(g->max_row_len <= cap, DSA_EUNSUPPORTED, "dense attention supports max_row_len <= %d (got %d)", cap,
+            g->max_row_len);
+  g->k = std::max(1, g->max_row_len);
+  return DSA_OK;
+}
+
+size_t dense_bytes(const dsa::Geo& g) {
+  return dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) + dsa::attn_workspace_bytes(g);
+}
+
 size_t step_bytes(const dsa::Geo& g) {
   return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) +
          2 * dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
@@ -208,6 +223,24 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* problem, const dsa_layout_
                     "attention launch");
 }
 
+dsa_status_t dsa_dense_mla_attn(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q,
+                                const void* kv_pool, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, false, true, &g);
+  if (st != DSA_OK) return st;
+  if ((st = dense_geo(&g)) != DSA_OK) return st;
+  DSA_CHECK(q && kv_pool && out, DSA_EINVAL, "q, kv_pool and out must be non-NULL");
+  DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
+            "q, kv_pool and out must be 16-byte aligned");
+  if ((st = check_ws(workspace, workspace_bytes, dense_bytes(g))) != DSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = static_cast<int32_t*>(workspace);
+  void* attn_ws = static_cast<char*>(workspace) + dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  if ((st = hip_status(dsa::launch_identity_selection(g, idx, s), "dense selection launch")) != DSA_OK) return st;
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, attn_ws, nullptr, s), "attention launch");
+}
+
 dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,
                              const float* q_idx_scale, const float* head_w, const void* k_idx_pool,
                              const float* k_idx_scale, const void* q, const void* kv_pool, int32_t* topk_idx,
@@ -254,12 +287,13 @@ size_t dsa_workspace_bytes(const dsa_problem_t* problem, int32_t op) {
   dsa_layout_t dummy{reinterpret_cast<const int32_t*>(16), reinterpret_cast<const int32_t*>(16),
                      reinterpret_cast<const int32_t*>(16)};
   dsa::Geo g;
-  const bool idx = op == DSA_OP_STEP, attn = op == DSA_OP_ATTN || op == DSA_OP_STEP;
+  const bool idx = op == DSA_OP_STEP, attn = op == DSA_OP_ATTN || op == DSA_OP_STEP || op == DSA_OP_DENSE;
   if (check_problem(problem, &dummy, idx, attn, &g) != DSA_OK) return 0;
   switch (op) {
     case DSA_OP_TOPK: return dsa::topk_workspace_bytes(g);
     case DSA_OP_ATTN: return dsa::attn_workspace_bytes(g);
     case DSA_OP_STEP: return step_bytes(g);
+    case DSA_OP_DENSE: return dense_geo(&g) == DSA_OK ? dense_bytes(g) : 0;
     default: fail(DSA_EINVAL, "unknown op %d", op); return 0;
   }
 }

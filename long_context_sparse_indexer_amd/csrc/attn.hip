@@ -830,7 +830,23 @@ void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const
         (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex, pt.lse);
 }
 
+// The identity selection of dense attention: slot s of row r is position s while s < n_r.
+__global__ __launch_bounds__(256) void identity_selection_kernel(const int32_t* __restrict__ row_len, int max_row_len,
+                                                                 int k, int32_t* __restrict__ idx) {
+  const int r = blockIdx.y;
+  const int n = clamp_len(row_len[r], max_row_len);
+  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < k; s += gridDim.x * blockDim.x)
+    idx[(int64_t)r * k + s] = s < n ? s : -1;
+}
+
 }  // namespace
+
+hipError_t launch_identity_selection(const Geo& g, int32_t* idx, hipStream_t stream) {
+  if (g.R == 0 || g.k == 0) return hipSuccess;
+  dim3 grid(std::min(64, (g.k + 255) / 256), g.R);
+  identity_selection_kernel<<<grid, 256, 0, stream>>>(g.row_len, g.max_row_len, g.k, idx);
+  return hipGetLastError();
+}
 
 size_t attn_workspace_bytes(const Geo& g) {
   const AttnPlan p = plan(g);

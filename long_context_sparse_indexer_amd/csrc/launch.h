@@ -56,5 +56,7 @@ size_t attn_workspace_bytes(const Geo& g);
 // looking the positions up in the page table (bf16 latents)
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
                        float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream);
+// The identity selection of dense attention: idx[r][s] = s for s < n_r, -1 after ([R, k] int32).
+hipError_t launch_identity_selection(const Geo& g, int32_t* idx, hipStream_t stream);
 
 }  // namespace dsa

@@ -21,8 +21,8 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_workspace_bytes",
-            "dsa_status_str", "dsa_last_error", "dsa_abi_version"} <= set(names)
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn",
+            "dsa_workspace_bytes", "dsa_status_str", "dsa_last_error", "dsa_abi_version"} <= set(names)
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -115,6 +115,25 @@ def test_attention_validation():
     assert st == dsa.DSA_EWORKSPACE
     st = L.dsa_sparse_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, None, FAKE, None, FAKE, need, None)
     assert st == dsa.DSA_EINVAL
+
+
+def test_dense_attention_validation():
+    # dense attention attends to every visible position: its selection width is the longest row, within what
+    # the attention kernels split over (131072 bf16, 4096 fp32)
+    L = dsa.lib()
+    p = _problem(num_rows=1, max_row_len=60000, max_pages=1024, num_pages=1024)
+    need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_DENSE)
+    assert need >= 4 * 60000  # the identity selection alone
+    st = L.dsa_dense_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, None, FAKE, need - 1, None)
+    assert st == dsa.DSA_EWORKSPACE
+    st = L.dsa_dense_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), None, FAKE, FAKE, None, FAKE, need, None)
+    assert st == dsa.DSA_EINVAL
+    for kw in (dict(max_row_len=131073, max_pages=4096, num_pages=4096),
+               dict(kv_dtype="f32", latent_dim=64, max_row_len=4097, max_pages=128, num_pages=128)):
+        p = _problem(num_rows=1, **kw)
+        st = L.dsa_dense_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+        assert st == dsa.DSA_EUNSUPPORTED, (kw, dsa.dsa_last_error())
+        assert "dense attention" in dsa.dsa_last_error()
 
 
 def test_decode_step_validation():

@@ -12,7 +12,7 @@ import torch
 import long_context_sparse_indexer_amd as dsa
 import oracle
 import synth
-from harness import full_check, gpu_step, say, check_topk_exact, sampled_check
+from harness import full_check, gpu_step, say, check_topk_exact, sampled_check, check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,37 @@ def test_prefill_chunk_full_size():
 def test_decode_1m_full_size():
     # 8 sequences of 2^20 positions; two rows checked against the oracle
     _sampled("decode_1m", lambda p: [0, 7])
+
+
+# ------------------------------------------------------------------------------- dense attention fallback
+
+def _dense(cfg):
+    say(f"dense case {({k: v for k, v in cfg.items() if k not in ('name',)})}")
+    from synth.device import upload
+    prob = synth.make_problem(cfg)
+    d = upload(prob)
+    P = dsa.make_problem(**d.fields)
+    L = dsa.make_layout(d.row_seq, d.row_len, d.page_table)
+    out_dt = torch.bfloat16 if prob.kv_dtype == "bf16" else torch.float32
+    out = torch.empty((prob.R, prob.H, prob.d_c), dtype=out_dt, device="cuda")
+    lse = torch.empty((prob.R, prob.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_DENSE), 256), dtype=torch.uint8, device="cuda")
+    dsa.dsa_dense_mla_attn(P, L, d.q, d.kv_pool, out, lse, ws)
+    torch.cuda.synchronize()
+    width = max(1, int(prob.row_len.max()))
+    idx = np.full((prob.R, width), -1, np.int32)
+    for r in range(prob.R):
+        idx[r, :prob.row_len[r]] = np.arange(prob.row_len[r], dtype=np.int32)
+    err = check_attention(prob, out.float().cpu().numpy(), lse.cpu().numpy(), idx)
+    say(f"  ok: dense attention err {err:.2e}")
+
+
+def test_dense_attention_every_visible_position():
+    # the short-context fallback: attention over positions 0 .. n_r - 1 of every row, no indexer or selection
+    _dense(synth.get("decode_128k", lengths=[5000], anchors=64, recent=96))          # 16-head kernel, 40 splits
+    _dense(synth.get("decode_128k", lengths=[60000], anchors=64, recent=96, H=32))   # 63 splits of 15 chunks
+    _dense(synth.get("batched_paged", batch=4, lengths=[9000, 3000, 0, 1], H=128, anchors=8, recent=8))  # all heads
+    _dense(synth.get("tiny_fp32", lengths=[1000, 4095], H=8))                         # fp32 path
 
 
 # ------------------------------------------------------------------------------- top-k on crafted scores
