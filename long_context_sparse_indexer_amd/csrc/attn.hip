@@ -118,18 +118,22 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Work unit (row, head group of the all-heads kernel) and split of this block.  Workgroups are handed to the
-// eight XCDs in turn (block b runs on XCD b % 8), so the splits of one unit get block ids 8 apart: they share an
-// XCD, whose L2 then serves the unit's queries, read by every split, after one HBM read.  The grid has
-// ceil(units / 8) * 8 * nsplit blocks; a block past the last unit has no work.
+// Work of one block: a (row, split) pair and a head group.  Workgroups are handed to the eight XCDs in turn
+// (block b runs on XCD b % 8).  The head groups of one pair gather the same rows, so they get block ids 8 apart
+// and share an XCD and its L2; pair p = row * nsplit + split runs on XCD p % 8, so that the splits of even a
+// single row spread over the whole chip.  The grid has ceil(R nsplit / 8) * 8 * ngroups blocks; a block past
+// the last pair has no work.
 struct BlockWork {
-  int unit, split;
+  int r, split, group;
 };
-__device__ __forceinline__ BlockWork block_work(int nsplit) {
+__device__ __forceinline__ BlockWork block_work(int nsplit, int ngroups) {
   const int b = blockIdx.x, slot = b >> 3;
-  return BlockWork{(slot / nsplit) * 8 + (b & 7), slot % nsplit};
+  const int pair = (slot / ngroups) * 8 + (b & 7);
+  return BlockWork{pair / nsplit, pair % nsplit, slot % ngroups};
 }
-__host__ __forceinline__ int work_blocks(int64_t units, int nsplit) { return (int)((units + 7) / 8 * 8 * nsplit); }
+__host__ __forceinline__ int work_blocks(int64_t pairs, int ngroups) {
+  return (int)((pairs + 7) / 8 * 8 * ngroups);
+}
 
 template <bool kSplit>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
@@ -146,16 +150,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
   __shared__ int wave_first[4];               // first slot with a position among each wave's slots
 
-  // Block b runs on XCD b % 8.  The 16-head groups of one (row, split) gather the same rows, so they get block
-  // ids 8 apart and share an XCD and its L2: pair p = row * nsplit + split runs on XCD p % 8, and the grid has
-  // ceil(R nsplit / 8) * 8 * ngroups blocks (a block past the last pair has no work).
   const int ngroups = H / kHG;
-  const int slot = blockIdx.x >> 3;
-  const int grp16 = slot % ngroups;
-  const int pair = (slot / ngroups) * 8 + (blockIdx.x & 7);
-  if (pair >= units / ngroups * nsplit) return;
-  const int split = pair % nsplit;
-  const int r = pair / nsplit;
+  const BlockWork bw = block_work(nsplit, ngroups);
+  if (bw.r >= units / ngroups) return;
+  const int split = bw.split, grp16 = bw.group, r = bw.r;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
 
@@ -400,11 +398,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   __shared__ int wave_first[NW], overflow;  // first slot with a position among each wave's slots
 
   const int ngroups = H / (32 * NW);
-  const BlockWork bw = block_work(nsplit);
-  if (bw.unit >= units) return;
-  const int split = bw.split;
-  const int hg = bw.unit % ngroups;
-  const int r = bw.unit / ngroups;
+  const BlockWork bw = block_work(nsplit, ngroups);
+  if (bw.r >= units / ngroups) return;
+  const int split = bw.split, hg = bw.group, r = bw.r;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int hw = hg * 32 * NW + wave * 32;  // first head of this wave
@@ -631,49 +627,73 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s,
-// in fp32.  One 256-thread block per (row, head): wave w takes splits w, w + 4, ..., lane l latent columns
-// 8l .. 8l+7 (d_c = 512) as one 16-byte load per split.  Every load is issued before any is used, so the weights
-// and the rows arrive in one round trip; waves 1-3 hand their sums to wave 0 through LDS.
-constexpr int kMaxSplit = 64;
+// in fp32.  One 256-thread block per (row, head) and up to 64 L splits: lane l holds the lse and exponent of
+// splits l, l + 64, ... and latent columns 8l .. 8l+7 (d_c = 512); in round i wave w takes splits
+// 64 i + w, 64 i + w + 4, ... as one 16-byte load per split.  The first round's loads are issued before the
+// weights are formed, so with L = 1 the weights and the rows arrive in one round trip; waves 1-3 hand their
+// sums to wave 0 through LDS.
+constexpr int kMaxSplit = 64;       // splits of the 16-head kernel
+constexpr int kMaxSplitWide = 256;  // splits of the all-heads kernel (the combine's limit)
+template <int L>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
                                                            const int32_t* __restrict__ part_exp,
                                                            const float* __restrict__ part_lse, int H, int nsplit,
                                                            unsigned short* __restrict__ out, float* __restrict__ lse) {
   static_assert(kDC == 8 * 64, "eight latent columns per lane");
-  static_assert(kMaxSplit <= 64, "one split per lane for the weights");
-  constexpr int kPerWave = kMaxSplit / 4;
+  constexpr int kPerWave = 16;  // splits of one round per wave
   __shared__ float red[3][8][64];  // waves 1..3: their partial sums, column-major per lane
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t row0 = (int64_t)r * nsplit * H + h;  // partial row of split 0; split j is j * H further
-  // every load first: lane j holds split j's lse and exponent (every wave reads them), and each wave the eight
-  // columns of lane `lane` of its splits wave, wave + 4, ...
-  const bool has = lane < nsplit;
-  const float ls = has ? part_lse[row0 + (int64_t)lane * H] : -INFINITY;
-  const int ex = has ? part_exp[row0 + (int64_t)lane * H] : 0;
-  v8us v[kPerWave];
+  float ls[L];
+  int ex[L];
 #pragma unroll
-  for (int q = 0; q < kPerWave; ++q) {
-    const int j = wave + 4 * q;
-    if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
+  for (int i = 0; i < L; ++i) {
+    const int j = 64 * i + lane;
+    ls[i] = j < nsplit ? part_lse[row0 + (int64_t)j * H] : -INFINITY;
+    ex[i] = j < nsplit ? part_exp[row0 + (int64_t)j * H] : 0;
   }
-  // split weights w_j = exp(lse_j - max) / sum, each wave for itself; lane j also folds in split j's exponent
-  const float mx = wave_max(ls);
-  const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
-  const float wsum = wave_sum(w);
-  const float wl = ldexpf(wsum > 0.f ? w / wsum : 0.f, ex);
+  v8us v[kPerWave];
+  auto load_round = [&](int i) {
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q) {
+      const int j = 64 * i + wave + 4 * q;
+      if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
+    }
+  };
+  load_round(0);
+  // split weights w_j = exp(lse_j - max) / sum, each wave for itself; the lane that holds split j also folds in
+  // its exponent
+  float m = ls[0];
+#pragma unroll
+  for (int i = 1; i < L; ++i) m = fmaxf(m, ls[i]);
+  const float mx = wave_max(m);
+  float w[L], part = 0.f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    w[i] = ls[i] == -INFINITY ? 0.f : expf(ls[i] - mx);
+    part += w[i];
+  }
+  const float wsum = wave_sum(part);
+  float wl[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) wl[i] = ldexpf(wsum > 0.f ? w[i] / wsum : 0.f, ex[i]);
   auto half_f = [](unsigned short b) { return (float)__builtin_bit_cast(_Float16, b); };
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int q = 0; q < kPerWave; ++q) {
-    const int j = wave + 4 * q;
-    if (j < nsplit) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+  for (int i = 0; i < L; ++i) {
+    if (i > 0) load_round(i);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
+    for (int q = 0; q < kPerWave; ++q) {
+      const int j = 64 * i + wave + 4 * q;
+      if (j < nsplit) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[i]), wave + 4 * q));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
+      }
     }
   }
   if (wave > 0)
@@ -771,7 +791,7 @@ AttnPlan plan(const Geo& g) {
     const int64_t groups = (int64_t)g.R * (g.H / (32 * p.nw));
     const int min_split = (chunks * kNC + kWideMaxSplitLen - 1) / kWideMaxSplitLen;
     int64_t want = (256 + groups - 1) / groups;
-    int nsplit = (int)std::max<int64_t>(min_split, std::min<int64_t>(want, std::min(chunks, kMaxSplit)));
+    int nsplit = (int)std::max<int64_t>(min_split, std::min<int64_t>(want, std::min(chunks, kMaxSplitWide)));
     const int per = (chunks + nsplit - 1) / nsplit;
     p.nsplit = (chunks + per - 1) / per;
     p.split_len = per * kNC;
@@ -817,7 +837,7 @@ void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const
                 const int32_t* topk_idx, const int32_t* pool_rows, void* out, float* lse, const Partials& pt,
                 float scale_log2, hipStream_t stream) {
   const int64_t units = (int64_t)g.R * (g.H / (32 * NW));
-  const int nblocks = work_blocks(units, p.nsplit);
+  const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / (32 * NW));
   if (p.nsplit == 1)
     attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
         qp, kp, topk_idx, g.k, pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
@@ -873,7 +893,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       }
     } else {
       const int64_t units = (int64_t)g.R * (g.H / kHG);
-      const int nblocks = (int)(((int64_t)g.R * p.nsplit + 7) / 8 * 8 * (g.H / kHG));
+      const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / kHG);
       if (p.nsplit == 1)
         attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_seq,
                                                              g.page_table,
@@ -888,9 +908,15 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                             p.nsplit, (int)units, p.split_len, scale_log2, nullptr,
                                                             nullptr, pt.o, pt.ex, pt.lse);
     }
-    if (p.nsplit > 1)
-      attn_combine_kernel<<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit,
-                                                       static_cast<unsigned short*>(out), lse);
+    if (p.nsplit > 1) {
+      auto* o = static_cast<unsigned short*>(out);
+      if (p.nsplit <= 64)
+        attn_combine_kernel<1><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+      else if (p.nsplit <= 128)
+        attn_combine_kernel<2><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+      else
+        attn_combine_kernel<4><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+    }
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
     attn_f32_kernel<<<g.R * g.H, 256, lds, stream>>>(static_cast<const float*>(q), static_cast<const float*>(kv_pool),
