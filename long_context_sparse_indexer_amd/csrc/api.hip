@@ -160,9 +160,9 @@ dsa_status_t hip_status(hipError_t e, const char* what) {
 
 int64_t step_ld(const dsa::Geo& g) { return ((int64_t)std::max(g.max_row_len, 1) + 63) / 64 * 64; }
 
-// Dense attention is the sparse kernels over the identity selection of every visible position: the selection
-// width becomes the longest row (at least 1), within what the attention kernels split over (64 splits of 2048
-// slots for the bf16 all-heads kernel; the fp32 kernel's 4096).
+// Dense attention is the sparse kernels with no selection list: slot s of row r is position s while s < n_r.
+// The selection width becomes the longest row (at least 1), within what the attention kernels take (the bf16
+// kernels split up to 131072 slots over their blocks; the fp32 kernel stages at most 4096 in LDS).
 dsa_status_t dense_geo(dsa::Geo* g) {
   const int cap = g->kv_dtype == DSA_BF16 ? 131072 : 4096;
   DSA_CHECK(g->max_row_len <= cap, DSA_EUNSUPPORTED, "dense attention supports max_row_len <= %d (got %d)", cap,
@@ -171,9 +171,7 @@ dsa_status_t dense_geo(dsa::Geo* g) {
   return DSA_OK;
 }
 
-size_t dense_bytes(const dsa::Geo& g) {
-  return dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) + dsa::attn_workspace_bytes(g);
-}
+size_t dense_bytes(const dsa::Geo& g) { return dsa::attn_workspace_bytes(g); }
 
 size_t step_bytes(const dsa::Geo& g) {
   return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) +
@@ -234,11 +232,9 @@ dsa_status_t dsa_dense_mla_attn(const dsa_problem_t* problem, const dsa_layout_t
   DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
             "q, kv_pool and out must be 16-byte aligned");
   if ((st = check_ws(workspace, workspace_bytes, dense_bytes(g))) != DSA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* idx = static_cast<int32_t*>(workspace);
-  void* attn_ws = static_cast<char*>(workspace) + dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
-  if ((st = hip_status(dsa::launch_identity_selection(g, idx, s), "dense selection launch")) != DSA_OK) return st;
-  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, attn_ws, nullptr, s), "attention launch");
+  return hip_status(dsa::launch_attn(g, q, kv_pool, nullptr, out, lse, workspace, nullptr,
+                                     static_cast<hipStream_t>(stream)),
+                    "attention launch");
 }
 
 dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,

@@ -135,11 +135,31 @@ __host__ __forceinline__ int work_blocks(int64_t pairs, int ngroups) {
   return (int)((pairs + 7) / 8 * 8 * ngroups);
 }
 
+// Where slot s of a split (row r, slots begin ..) gets its row: the pool rows the fused top-k wrote beside the
+// selection (already physical), the selected positions, or, with no selection (dense attention), position
+// begin + s itself while it is below n_r.
+struct SlotSource {
+  const int32_t* list;  // nullptr: the identity selection
+  int dense_n;          // identity: slots below this are positions
+  int begin;
+  bool physical;        // the entries are pool rows, not positions
+  __device__ __forceinline__ int at(int s) const {
+    return list ? list[s] : (s < dense_n ? begin + s : -1);
+  }
+};
+__device__ __forceinline__ SlotSource slot_source(const int32_t* topk_idx, const int32_t* pool_rows,
+                                                  const int32_t* row_len, int max_row_len, int r, int k, int begin) {
+  const int64_t off = (int64_t)r * k + begin;
+  if (pool_rows) return SlotSource{pool_rows + off, 0, begin, true};
+  if (topk_idx) return SlotSource{topk_idx + off, 0, begin, false};
+  return SlotSource{nullptr, clamp_len(row_len[r], max_row_len) - begin, begin, false};
+}
+
 template <bool kSplit>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
-    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_len, int max_row_len,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
     unsigned short* __restrict__ out,
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
@@ -162,18 +182,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   const int end = min(k, begin + split_len);
   const int len = max(end - begin, 0);
   const int nch = (len + kNC - 1) / kNC;
-  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
 
   // Every slot of the split -> physical row before any gather, so that the gathers are the only loads in
   // flight later: all position loads are issued together, then all page-table loads (two round trips), or the
   // pool rows the top-k wrote beside the selection are loaded directly (one).
   constexpr int kSlotsPerThread = kMaxSplitLen / 256;
-  const int32_t* slot_src = pool_rows ? pool_rows + (int64_t)r * k + begin : idx;
+  const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
   int pr[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int s = j * 256 + threadIdx.x;
-    pr[j] = s < len ? slot_src[s] : -1;
+    pr[j] = s < len ? src.at(s) : -1;
   }
 
   // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 32);
   }
 
-  if (!pool_rows)
+  if (!src.physical)
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j)
       pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
@@ -380,8 +399,8 @@ __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restri
 template <int NW, bool kSplit>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
-    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_len, int max_row_len,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int H, int nsplit, int units, int split_len, float scale_log2,
     unsigned short* __restrict__ out,
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
@@ -411,18 +430,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   const int len = max(end - begin, 0);
   const int nch = (len + kCW - 1) / kCW;  // chunks of kCW slots
   const int n64 = (len + 63) / 64;
-  const int32_t* idx = topk_idx + (int64_t)r * k + begin;
 
   // Slots -> physical rows: all position loads are issued together, then all page-table loads.  Slot
   // j * 64 NW + 64 wave + lane belongs to 64-slot group j NW + wave, so a ballot gives the validity bits of
   // two chunks.
   constexpr int kSlotsPerThread = kWideMaxSplitLen / (64 * NW);
-  const int32_t* slot_src = pool_rows ? pool_rows + (int64_t)r * k + begin : idx;  // pool rows: no lookup
+  const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
   int pr[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int sl = (j * NW + wave) * 64 + lane;
-    pr[j] = sl < len ? slot_src[sl] : -1;
+    pr[j] = sl < len ? src.at(sl) : -1;
   }
   // the queries load while the positions and then the page-table entries arrive
   // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   }
   v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
 
-  if (!pool_rows)
+  if (!src.physical)
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j)
       pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
@@ -627,24 +645,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s,
-// in fp32.  One 256-thread block per (row, head) and up to 64 L splits: lane l holds the lse and exponent of
-// splits l, l + 64, ... and latent columns 8l .. 8l+7 (d_c = 512); in round i wave w takes splits
-// 64 i + w, 64 i + w + 4, ... as one 16-byte load per split.  The first round's loads are issued before the
-// weights are formed, so with L = 1 the weights and the rows arrive in one round trip; waves 1-3 hand their
-// sums to wave 0 through LDS.
+// in fp32.  One block of 4 L waves per (row, head) and up to 64 L splits: lane l holds the lse and exponent of
+// splits l, l + 64, ... and latent columns 8l .. 8l+7 (d_c = 512); wave 4 i + u takes the 16 splits 64 i + u,
+// 64 i + u + 4, ... as one 16-byte load each.  Every load is issued before any is used, so the weights and the
+// rows arrive in one round trip; the other waves hand their sums to wave 0 through LDS.
 constexpr int kMaxSplit = 64;       // splits of the 16-head kernel
 constexpr int kMaxSplitWide = 256;  // splits of the all-heads kernel (the combine's limit)
 template <int L>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
-                                                           const int32_t* __restrict__ part_exp,
-                                                           const float* __restrict__ part_lse, int H, int nsplit,
-                                                           unsigned short* __restrict__ out, float* __restrict__ lse) {
+__global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
+                                                               const int32_t* __restrict__ part_exp,
+                                                               const float* __restrict__ part_lse, int H, int nsplit,
+                                                               unsigned short* __restrict__ out,
+                                                               float* __restrict__ lse) {
   static_assert(kDC == 8 * 64, "eight latent columns per lane");
-  constexpr int kPerWave = 16;  // splits of one round per wave
-  __shared__ float red[3][8][64];  // waves 1..3: their partial sums, column-major per lane
+  constexpr int kNW = 4 * L, kPerWave = 16;
+  __shared__ float red[kNW - 1][8][64];  // waves 1..: their partial sums, column-major per lane
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh % H;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int grp = wave >> 2, u = wave & 3;         // this wave's 64 splits, and its offset among them
   const int64_t row0 = (int64_t)r * nsplit * H + h;  // partial row of split 0; split j is j * H further
   float ls[L];
   int ex[L];
@@ -655,14 +674,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short*
     ex[i] = j < nsplit ? part_exp[row0 + (int64_t)j * H] : 0;
   }
   v8us v[kPerWave];
-  auto load_round = [&](int i) {
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) {
-      const int j = 64 * i + wave + 4 * q;
-      if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
-    }
-  };
-  load_round(0);
+  for (int q = 0; q < kPerWave; ++q) {
+    const int j = 64 * grp + u + 4 * q;
+    if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
+  }
   // split weights w_j = exp(lse_j - max) / sum, each wave for itself; the lane that holds split j also folds in
   // its exponent
   float m = ls[0];
@@ -676,24 +692,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short*
     part += w[i];
   }
   const float wsum = wave_sum(part);
-  float wl[L];
+  float wl = 0.f;  // weight of split 64 grp + lane
 #pragma unroll
-  for (int i = 0; i < L; ++i) wl[i] = ldexpf(wsum > 0.f ? w[i] / wsum : 0.f, ex[i]);
+  for (int i = 0; i < L; ++i)
+    if (i == grp) wl = ldexpf(wsum > 0.f ? w[i] / wsum : 0.f, ex[i]);
   auto half_f = [](unsigned short b) { return (float)__builtin_bit_cast(_Float16, b); };
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    if (i > 0) load_round(i);
+  for (int q = 0; q < kPerWave; ++q) {
+    if (64 * grp + u + 4 * q < nsplit) {
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u + 4 * q));
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) {
-      const int j = 64 * i + wave + 4 * q;
-      if (j < nsplit) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[i]), wave + 4 * q));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
     }
   }
   if (wave > 0)
@@ -701,9 +713,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short*
     for (int e = 0; e < 8; ++e) red[wave - 1][e][lane] = acc[e];
   __syncthreads();
   if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < kNW - 1; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += red[t][e][lane];
     v8us b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = float_to_bf16_bits(acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane]);
+    for (int e = 0; e < 8; ++e) b[e] = float_to_bf16_bits(acc[e]);
     *reinterpret_cast<v8us*>(out + ((int64_t)r * H + h) * kDC + lane * 8) = b;  // 16-byte aligned
     if (lane == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
@@ -712,6 +728,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const unsigned short*
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kv,
                                                        const int32_t* __restrict__ topk_idx, int k,
+                                                       const int32_t* __restrict__ row_len, int max_row_len,
                                                        const int32_t* __restrict__ row_seq,
                                                        const int32_t* __restrict__ page_table, int num_seqs,
                                                        int max_pages, int num_pages, int log2ps, int H, int d_c,
@@ -726,8 +743,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   const int seq = clamp_seq(row_seq[r], num_seqs);
   const float* qrow = q + ((int64_t)r * H + h) * d_c;
   for (int d = threadIdx.x; d < d_c; d += blockDim.x) qs[d] = qrow[d];
+  const SlotSource src = slot_source(topk_idx, nullptr, row_len, max_row_len, r, k, 0);
   for (int s = threadIdx.x; s < k; s += blockDim.x) {
-    const int pos = topk_idx[(int64_t)r * k + s];
+    const int pos = src.at(s);
     prow[s] = pos >= 0 ? phys_row(page_table, max_pages, num_pages, log2ps, seq, pos) : -1;
   }
   __syncthreads();
@@ -840,33 +858,17 @@ void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const
   const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / (32 * NW));
   if (p.nsplit == 1)
     attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
+        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
         (int)units,
         p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr, nullptr);
   else
     attn_bf16_mqa_kernel<NW, true><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
+        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
         p.nsplit,
         (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex, pt.lse);
 }
 
-// The identity selection of dense attention: slot s of row r is position s while s < n_r.
-__global__ __launch_bounds__(256) void identity_selection_kernel(const int32_t* __restrict__ row_len, int max_row_len,
-                                                                 int k, int32_t* __restrict__ idx) {
-  const int r = blockIdx.y;
-  const int n = clamp_len(row_len[r], max_row_len);
-  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < k; s += gridDim.x * blockDim.x)
-    idx[(int64_t)r * k + s] = s < n ? s : -1;
-}
-
 }  // namespace
-
-hipError_t launch_identity_selection(const Geo& g, int32_t* idx, hipStream_t stream) {
-  if (g.R == 0 || g.k == 0) return hipSuccess;
-  dim3 grid(std::min(64, (g.k + 255) / 256), g.R);
-  identity_selection_kernel<<<grid, 256, 0, stream>>>(g.row_len, g.max_row_len, g.k, idx);
-  return hipGetLastError();
-}
 
 size_t attn_workspace_bytes(const Geo& g) {
   const AttnPlan p = plan(g);
@@ -895,14 +897,16 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       const int64_t units = (int64_t)g.R * (g.H / kHG);
       const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / kHG);
       if (p.nsplit == 1)
-        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_seq,
+        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
+                                                             g.max_row_len, g.row_seq,
                                                              g.page_table,
                                                              g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
                                                              (int)units, p.split_len, scale_log2,
                                                              static_cast<unsigned short*>(out), lse, nullptr,
                                                              nullptr, nullptr);
       else
-        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_seq,
+        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
+                                                             g.max_row_len, g.row_seq,
                                                             g.page_table,
                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
                                                             p.nsplit, (int)units, p.split_len, scale_log2, nullptr,
@@ -913,14 +917,15 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       if (p.nsplit <= 64)
         attn_combine_kernel<1><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
       else if (p.nsplit <= 128)
-        attn_combine_kernel<2><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+        attn_combine_kernel<2><<<g.R * g.H, 512, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
       else
-        attn_combine_kernel<4><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+        attn_combine_kernel<4><<<g.R * g.H, 1024, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
     }
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
     attn_f32_kernel<<<g.R * g.H, 256, lds, stream>>>(static_cast<const float*>(q), static_cast<const float*>(kv_pool),
-                                                      topk_idx, g.k, g.row_seq, g.page_table, g.S,
+                                                      topk_idx, g.k, g.row_len, g.max_row_len, g.row_seq,
+                                                      g.page_table, g.S,
                                                       g.max_pages, g.num_pages, g.log2ps, g.H, g.d_c, g.softmax_scale,
                                                       static_cast<float*>(out), lse);
   }

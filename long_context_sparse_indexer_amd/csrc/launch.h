@@ -53,10 +53,9 @@ hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* t
 // attn.hip
 size_t attn_workspace_bytes(const Geo& g);
 // pool_rows: if non-NULL, the pool row of every selected slot (as written by the top-k), used instead of
-// looking the positions up in the page table (bf16 latents)
+// looking the positions up in the page table (bf16 latents).  topk_idx and pool_rows both NULL: dense
+// attention, slot s of row r is position s while s < n_r (g.k = the longest row).
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
                        float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream);
-// The identity selection of dense attention: idx[r][s] = s for s < n_r, -1 after ([R, k] int32).
-hipError_t launch_identity_selection(const Geo& g, int32_t* idx, hipStream_t stream);
 
 }  // namespace dsa

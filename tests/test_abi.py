@@ -123,7 +123,7 @@ def test_dense_attention_validation():
     L = dsa.lib()
     p = _problem(num_rows=1, max_row_len=60000, max_pages=1024, num_pages=1024)
     need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_DENSE)
-    assert need >= 4 * 60000  # the identity selection alone
+    assert need > 0  # one row splits its 60000 positions over many blocks
     st = L.dsa_dense_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, None, FAKE, need - 1, None)
     assert st == dsa.DSA_EWORKSPACE
     st = L.dsa_dense_mla_attn(ctypes.byref(p), ctypes.byref(LAYOUT), None, FAKE, FAKE, None, FAKE, need, None)
