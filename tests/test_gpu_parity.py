@@ -79,7 +79,7 @@ def test_large_budgets_multi_chunk_splits():
     # k = 8000 over one row: the 16-head kernel runs two 64-slot chunks per split (63 splits, register gathers
     # double-buffered); k = 8192 over two rows: the all-heads kernel with splits of its own, merged by the combine
     _run(synth.get("decode_128k", lengths=[100000], k=8000, anchors=64, recent=128))
-    _run(synth.get("decode_128k", lengths=[40000, 30000], k=8192, H=128, anchors=64, recent=128))
+    _run(synth.get("decode_128k", lengths=[40000, 30000], k=8192, H=128, anchors=64, recent=128))  # 128 splits
 
 
 def test_softmax_scale_and_signed_weights():
@@ -200,7 +200,7 @@ def _dense(cfg):
 def test_dense_attention_every_visible_position():
     # the short-context fallback: attention over positions 0 .. n_r - 1 of every row, no indexer or selection
     _dense(synth.get("decode_128k", lengths=[5000], anchors=64, recent=96))          # 16-head kernel, 40 splits
-    _dense(synth.get("decode_128k", lengths=[60000], anchors=64, recent=96, H=32))   # 63 splits of 15 chunks
+    _dense(synth.get("decode_128k", lengths=[60000], anchors=64, recent=96, H=32))   # 235 splits of 4 chunks
     _dense(synth.get("batched_paged", batch=4, lengths=[9000, 3000, 0, 1], H=128, anchors=8, recent=8))  # all heads
     _dense(synth.get("tiny_fp32", lengths=[1000, 4095], H=8))                         # fp32 path
 
