@@ -41,6 +41,14 @@ def lib() -> ctypes.CDLL:
         L.dsa_oracle_topk.restype = ctypes.c_int
         L.dsa_oracle_sparse_attn.argtypes = [I32, I32, I32, I32, P, P, P, I32, P, P, I32, I32, D, P, P]
         L.dsa_oracle_sparse_attn.restype = ctypes.c_int
+        L.dsa_oracle_e4m3_nearest.argtypes = [ctypes.c_float]
+        L.dsa_oracle_e4m3_nearest.restype = ctypes.c_uint8
+        L.dsa_oracle_quantize_key.argtypes = [I32, P, P, P]
+        L.dsa_oracle_quantize_key.restype = None
+        L.dsa_oracle_key_projection.argtypes = [I32, I32, I32, I32, P, P, P]
+        L.dsa_oracle_key_projection.restype = ctypes.c_int
+        L.dsa_oracle_key_append.argtypes = [I32, I32, P, P, P, P, I32, I32, I32, P, P]
+        L.dsa_oracle_key_append.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -123,3 +131,47 @@ def decode_step(prob):
     o, lse = sparse_attn(prob.q, prob.kv_pool, idx, prob.row_seq, prob.page_table, prob.page_size, prob.kv_dtype,
                          prob.softmax_scale)
     return scores, idx, kth, o, lse
+
+
+def e4m3_nearest(y: float) -> int:
+    """The e4m3 code nearest to the fp32 value y (ties to the even code, clamped to +-448, sign kept)."""
+    return int(lib().dsa_oracle_e4m3_nearest(float(y)))
+
+
+def quantize_key(x) -> tuple[np.ndarray, float]:
+    """(codes uint8 [d], scale) of one fp32 key vector: scale = max|x| / 448, codes nearest x / scale."""
+    x = _c(x, np.float32)
+    codes = np.empty(x.shape[-1], np.uint8)
+    scale = np.empty(1, np.float32)
+    lib().dsa_oracle_quantize_key(x.shape[-1], _p(x), _p(codes), _p(scale))
+    return codes, float(scale[0])
+
+
+def key_projection(c, w, c_dtype: str) -> np.ndarray:
+    """k = c W_KI in fp64 ([R, d_c] x [d_c, d_I], d ascending), from bf16 bit patterns or fp32 values."""
+    code_t = np.uint16 if c_dtype == "bf16" else np.float32
+    c, w = _c(c, code_t), _c(w, code_t)
+    R, d_c = c.shape
+    d_I = w.shape[1]
+    if w.shape[0] != d_c:
+        raise ValueError("c and w disagree on d_c")
+    k = np.empty((R, d_I), np.float64)
+    if lib().dsa_oracle_key_projection(R, d_c, d_I, _DT[c_dtype], _p(c), _p(w), _p(k)):
+        raise ValueError("oracle key projection rejected its arguments")
+    return k
+
+
+def key_append(k32, positions, row_seq, page_table, page_size: int, pool, pool_scale=None):
+    """Writes fp32 keys k32 [R, d_I] into copies of the pool (uint8 codes + scales, or fp32 with no scales)
+    at each row's position; returns (pool, pool_scale)."""
+    k32 = _c(k32, np.float32)
+    R, d_I = k32.shape
+    f8 = pool.dtype == np.uint8
+    pool = np.array(pool, copy=True)
+    pool_scale = np.array(pool_scale, np.float32, copy=True) if f8 else None
+    positions, row_seq, page_table = _c(positions, np.int32), _c(row_seq, np.int32), _c(page_table, np.int32)
+    rc = lib().dsa_oracle_key_append(R, d_I, _p(k32), _p(positions), _p(row_seq), _p(page_table),
+                                     page_table.shape[1], page_size, F8E4M3 if f8 else F32, _p(pool), _p(pool_scale))
+    if rc:
+        raise ValueError("oracle key append rejected its arguments")
+    return pool, pool_scale

@@ -26,6 +26,15 @@
  *      latent rows, which serve as both key and value:
  *          l_i = scale * <q[h], c[T_i]>,  p = softmax(l),  o[h] = sum_i p_i c[T_i],  lse[h] = log sum exp l.
  *      An empty selection gives o = 0 and lse = -inf.
+ *   5. Indexer-key append, the cache write before the step (kiadev "How DSA works", stage 1: the key
+ *      projection W_KI in R^{d_c x d_I} maps each cached latent row c to k_I = c W_KI; kgptalkie "What Does
+ *      the GPU Actually Run?": the indexer cache holds the key's FP8 numbers and one scale per token).
+ *      Reading (the pages fix one fp32 scale per key but not how it is chosen): max-abs scaling over the
+ *      whole e4m3 range, scale = max_j |k_j| / 448 (1 for an all-zero key), code_j = the e4m3 value nearest
+ *      to k_j / scale, ties to the even code, clamped to +-448; the code keeps the sign bit of k_j / scale.
+ *      The code is an integer decided by floating point, so the decision is taken in fp32: the key is
+ *      rounded once to fp32, then scale = amax / 448 and k_j / scale are IEEE fp32 divisions.  The
+ *      projection is the plain fp64 sum over d = 0 .. d_c-1 of exact products (bf16 or fp32 operands).
  *   Cached positions are addressed through a page table: physical row = table[seq][pos / P] * P + pos % P
  *   (the selected positions are "an address list into the paged KV cache", "How Does the Selector Pick").
  */
@@ -174,6 +183,70 @@ int dsa_oracle_sparse_attn(int32_t R, int32_t H, int32_t d_c, int32_t kv_dtype, 
       free(logit);
     }
     free(rows);
+  }
+  return 0;
+}
+
+/* ---- 5. indexer-key append ----------------------------------------------------------------------- */
+
+/* The e4m3 code nearest to y: every finite non-negative code is tried and the closest value to |y| kept,
+ * ties going to the code with an even mantissa (the even code of the two).  For an fp32 y every distance
+ * near a midpoint is exact in fp64.  |y| above 448 takes 448; the sign bit of y is kept, so a negative value
+ * that rounds to zero gives 0x80. */
+uint8_t dsa_oracle_e4m3_nearest(float y) {
+  double a = fabs((double)y);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(a - dsa_oracle_e4m3_value((uint8_t)c));
+    if (d < best_d || (d == best_d && (c & 1) == 0)) { best = c; best_d = d; }
+  }
+  return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* One key vector of d fp32 values -> d codes and its scale (the reading of section 5 above). */
+void dsa_oracle_quantize_key(int32_t d, const float *x, uint8_t *codes, float *scale) {
+  float amax = 0.0f;
+  for (int32_t j = 0; j < d; ++j) if (fabsf(x[j]) > amax) amax = fabsf(x[j]);
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int32_t j = 0; j < d; ++j) {
+    float y = x[j] / s;
+    if (y > 448.0f) y = 448.0f;
+    if (y < -448.0f) y = -448.0f;
+    codes[j] = dsa_oracle_e4m3_nearest(y);
+  }
+  *scale = s;
+}
+
+/* k[r][j] = sum_d c[r][d] * w[d][j] in fp64, d ascending; c [R, d_c] and w [d_c, d_I] in c_dtype. */
+int dsa_oracle_key_projection(int32_t R, int32_t d_c, int32_t d_I, int32_t c_dtype, const void *c, const void *w,
+                              double *k) {
+  if (R < 0 || d_c <= 0 || d_I <= 0 || c_dtype == ORACLE_F8E4M3) return 1;
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t j = 0; j < d_I; ++j) {
+      double sum = 0.0;
+      for (int32_t d = 0; d < d_c; ++d)
+        sum += elem(c, c_dtype, (int64_t)r * d_c + d) * elem(w, c_dtype, (int64_t)d * d_I + j);
+      k[(int64_t)r * d_I + j] = sum;
+    }
+  return 0;
+}
+
+/* Writes the key of row r at position positions[r] of sequence row_seq[r] (rows with a negative position are
+ * skipped): fp32 keys k32 [R, d_I] go to the pool as e4m3 codes plus a scale (pool_dtype F8E4M3) or as they are
+ * (F32, no scales).  Pool rows no row addresses are left untouched. */
+int dsa_oracle_key_append(int32_t R, int32_t d_I, const float *k32, const int32_t *positions, const int32_t *row_seq,
+                          const int32_t *page_table, int32_t max_pages, int32_t page_size, int32_t pool_dtype,
+                          void *pool, float *pool_scale) {
+  if (R < 0 || d_I <= 0 || page_size <= 0 || (pool_dtype != ORACLE_F8E4M3 && pool_dtype != ORACLE_F32)) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    if (positions[r] < 0) continue;
+    int64_t row = phys_row(page_table, max_pages, page_size, row_seq[r], positions[r]);
+    const float *x = k32 + (int64_t)r * d_I;
+    if (pool_dtype == ORACLE_F8E4M3)
+      dsa_oracle_quantize_key(d_I, x, (uint8_t *)pool + row * d_I, pool_scale + row);
+    else
+      memcpy((float *)pool + row * d_I, x, sizeof(float) * (size_t)d_I);
   }
   return 0;
 }

@@ -189,3 +189,28 @@ def make_problem(cfg: dict) -> Problem:
         row_seq=np.asarray(row_seq, np.int32), row_len=np.asarray(row_len, np.int32),
         page_table=page_table, boosted=boosted,
         rows_per_seq=cfg["rows"] if cfg["kind"] == "prefill" else 1)
+
+
+def append_inputs(prob: Problem, seed: int) -> dict:
+    """Inputs of the indexer-key append for the problem's rows: the newest token of each row (position
+    row_len - 1; rows with no position get -1 and are skipped).
+
+      c [R, d_c]: latent rows ~ N(0, 1), stored in the problem's latent dtype; row 0 is all zero when R > 1
+        (a zero key);
+      w [d_c, d_I]: W_KI ~ N(0, 1/d_c) in the same dtype;
+      k32 [R, d_I]: fp32 keys for the append of already-projected keys, ~ N(0, 1) with one entry per row
+        30x larger (its small neighbours then fall among the e4m3 subnormals) and a zero row 0 when R > 1.
+    """
+    rng = _child(seed, 7)
+    d_c, d_I, R = prob.d_c, prob.d_I, prob.R
+    c = rng.standard_normal((R, d_c), dtype=np.float32)
+    w = rng.standard_normal((d_c, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
+    k32 = rng.standard_normal((R, d_I), dtype=np.float32)
+    k32[np.arange(R), rng.integers(0, d_I, R)] *= np.float32(30.0)
+    if R > 1:
+        c[0] = 0.0
+        k32[0] = 0.0
+    c_bits, _ = _round_kv(c, prob.kv_dtype)
+    w_bits, _ = _round_kv(w, prob.kv_dtype)
+    positions = np.where(prob.row_len > 0, prob.row_len - 1, -1).astype(np.int32)
+    return dict(c=np.ascontiguousarray(c_bits), w=np.ascontiguousarray(w_bits), k32=k32, positions=positions)

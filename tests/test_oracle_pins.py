@@ -340,3 +340,108 @@ def test_attention_heads_share_one_latent_row():
     for h in range(H):
         o_h, _ = _attn(q[:, h:h + 1], c, sel, n, "f32", 1.0)
         assert np.array_equal(o_all[0, h], o_h[0, 0])
+
+
+# ------------------------------------------------------------------------------------ indexer-key append
+
+def _e4m3_table():
+    return oracle.decode(np.arange(256, dtype=np.uint8), "f8")
+
+
+def test_e4m3_nearest_round_trips_every_finite_code():
+    vals = _e4m3_table()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.e4m3_nearest(np.float32(vals[c])) == c, hex(c)
+
+
+def test_e4m3_nearest_midpoints_go_to_the_even_code():
+    vals = _e4m3_table()
+    for c in range(0x7E):
+        mid = np.float32((vals[c] + vals[c + 1]) / 2)  # at most 5 significant bits: exact in fp32
+        assert float(mid) == (vals[c] + vals[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_nearest(mid) == even
+        assert oracle.e4m3_nearest(np.nextafter(mid, np.float32(np.inf))) == c + 1
+        assert oracle.e4m3_nearest(np.nextafter(mid, np.float32(-np.inf))) == c
+        assert oracle.e4m3_nearest(-mid) == 0x80 | even
+
+
+def test_e4m3_nearest_matches_torch_cast():
+    # torch's float -> float8_e4m3fn conversion rounds to nearest even and keeps the sign bit
+    rng = np.random.default_rng(11)
+    mag = np.exp2(rng.uniform(-14, np.log2(448.0), 20000)).astype(np.float32)
+    x = np.concatenate([mag * rng.choice([-1, 1], mag.size), np.float32([0.0, -0.0, 448.0, -448.0, 1e-30, -1e-30])])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_nearest(v) for v in x], np.uint8)
+    assert np.array_equal(mine, ref)
+    assert oracle.e4m3_nearest(np.float32(1e6)) == 0x7E and oracle.e4m3_nearest(np.float32(-1e6)) == 0xFE
+
+
+def test_quantize_key_closed_forms_and_error_bound():
+    vals = _e4m3_table()
+    # all-zero key: scale 1, zero codes
+    codes, s = oracle.quantize_key(np.zeros(64, np.float32))
+    assert s == 1.0 and not codes.any()
+    # the largest magnitude takes the largest code, with its sign; a power-of-two amax gives an exact scale
+    x = np.zeros(64, np.float32)
+    x[5], x[9] = -7.0, 3.5
+    codes, s = oracle.quantize_key(x)
+    assert s == np.float32(7.0) / np.float32(448.0) and codes[5] == 0xFE and codes[9] == 0x76  # 3.5/7 * 448 = 224
+    assert np.count_nonzero(codes) == 2
+    # any key: every dequantised value lies within half an e4m3 step of the fp32 key
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        x = (rng.standard_normal(128) * np.exp2(rng.uniform(-20, 20))).astype(np.float32)
+        x[rng.integers(128)] *= 30  # one outlier: many small values fall in the subnormal range
+        codes, s = oracle.quantize_key(x)
+        assert s == np.float32(np.abs(x).max()) / np.float32(448.0)
+        y = x.astype(np.float64) / s
+        deq = vals[codes]
+        normal = np.abs(y) >= 2.0 ** -6
+        assert np.all(np.abs(deq - y)[normal] <= 2.0 ** -4 * np.abs(y)[normal] * (1 + 1e-6))
+        assert np.all(np.abs(deq - y)[~normal] <= 2.0 ** -10 * (1 + 1e-6))
+        assert np.array_equal(np.signbit(deq), np.signbit(y.astype(np.float32)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_key_projection_exact_integer_matmul(dtype):
+    # small integers: every product and partial sum is exact, so k = c W must equal the integer matmul; d_c != d_I
+    # and an asymmetric W catch a transposed operand
+    rng = np.random.default_rng(3)
+    c = rng.integers(-8, 9, size=(5, 96)).astype(np.float32)
+    w = rng.integers(-8, 9, size=(96, 40)).astype(np.float32)
+    enc = (lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)) \
+        if dtype == "bf16" else (lambda a: a)
+    k = oracle.key_projection(enc(c), enc(w), dtype)
+    assert np.array_equal(k, c.astype(np.int64) @ w.astype(np.int64))
+
+
+def test_key_projection_matches_library_matmul():
+    rng = np.random.default_rng(4)
+    c = rng.standard_normal((3, 512)).astype(np.float32)
+    w = (rng.standard_normal((512, 128)) / 22).astype(np.float32)
+    k = oracle.key_projection(c, w, "f32")
+    assert np.allclose(k, c.astype(np.float64) @ w.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def test_key_append_places_rows_through_the_page_table():
+    page_size, d_I = 4, 8
+    page_table = np.array([[2, 0, -1], [1, 3, -1]], np.int32)  # sequence 0: pages 2, 0; sequence 1: pages 1, 3
+    pool = np.full((4 * page_size, d_I), 0xAA, np.uint8)
+    scale = np.full(4 * page_size, -5.0, np.float32)
+    k = np.arange(4 * d_I, dtype=np.float32).reshape(4, d_I) - 10
+    positions = np.array([0, 5, -1, 7], np.int32)
+    row_seq = np.array([0, 0, 1, 1], np.int32)
+    out, sc = oracle.key_append(k, positions, row_seq, page_table, page_size, pool, scale)
+    targets = {0: 2 * page_size + 0, 1: 0 * page_size + 1, 3: 3 * page_size + 3}  # row -> physical row
+    for r, phys in targets.items():
+        codes, s = oracle.quantize_key(k[r])
+        assert np.array_equal(out[phys], codes) and sc[phys] == np.float32(s)
+    untouched = np.setdiff1d(np.arange(4 * page_size), list(targets.values()))
+    assert (out[untouched] == 0xAA).all() and (sc[untouched] == -5.0).all()
+    # an fp32 pool stores the keys as they are
+    fpool, none = oracle.key_append(k, positions, row_seq, page_table, page_size, np.zeros((16, d_I), np.float32))
+    assert none is None and np.array_equal(fpool[targets[3]], k[3]) and not fpool[untouched].any()
