@@ -232,15 +232,15 @@ int dsa_oracle_key_projection(int32_t R, int32_t d_c, int32_t d_I, int32_t c_dty
   return 0;
 }
 
-/* Writes the key of row r at position positions[r] of sequence row_seq[r] (rows with a negative position are
- * skipped): fp32 keys k32 [R, d_I] go to the pool as e4m3 codes plus a scale (pool_dtype F8E4M3) or as they are
+/* Writes the key of row r at position positions[r] of sequence row_seq[r] (rows with a negative position, or
+ * one the page table cannot reach, at or beyond max_pages * page_size, are skipped): fp32 keys k32 [R, d_I] go to the pool as e4m3 codes plus a scale (pool_dtype F8E4M3) or as they are
  * (F32, no scales).  Pool rows no row addresses are left untouched. */
 int dsa_oracle_key_append(int32_t R, int32_t d_I, const float *k32, const int32_t *positions, const int32_t *row_seq,
                           const int32_t *page_table, int32_t max_pages, int32_t page_size, int32_t pool_dtype,
                           void *pool, float *pool_scale) {
   if (R < 0 || d_I <= 0 || page_size <= 0 || (pool_dtype != ORACLE_F8E4M3 && pool_dtype != ORACLE_F32)) return 1;
   for (int32_t r = 0; r < R; ++r) {
-    if (positions[r] < 0) continue;
+    if (positions[r] < 0 || (int64_t)positions[r] >= (int64_t)max_pages * page_size) continue;
     int64_t row = phys_row(page_table, max_pages, page_size, row_seq[r], positions[r]);
     const float *x = k32 + (int64_t)r * d_I;
     if (pool_dtype == ORACLE_F8E4M3)

@@ -432,9 +432,9 @@ def test_key_append_places_rows_through_the_page_table():
     page_table = np.array([[2, 0, -1], [1, 3, -1]], np.int32)  # sequence 0: pages 2, 0; sequence 1: pages 1, 3
     pool = np.full((4 * page_size, d_I), 0xAA, np.uint8)
     scale = np.full(4 * page_size, -5.0, np.float32)
-    k = np.arange(4 * d_I, dtype=np.float32).reshape(4, d_I) - 10
-    positions = np.array([0, 5, -1, 7], np.int32)
-    row_seq = np.array([0, 0, 1, 1], np.int32)
+    k = np.arange(5 * d_I, dtype=np.float32).reshape(5, d_I) - 10
+    positions = np.array([0, 5, -1, 7, 12], np.int32)  # 12 = 3 pages x 4: beyond the table, skipped
+    row_seq = np.array([0, 0, 1, 1, 0], np.int32)
     out, sc = oracle.key_append(k, positions, row_seq, page_table, page_size, pool, scale)
     targets = {0: 2 * page_size + 0, 1: 0 * page_size + 1, 3: 3 * page_size + 3}  # row -> physical row
     for r, phys in targets.items():
