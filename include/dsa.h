@@ -155,6 +155,28 @@ dsa_status_t dsa_dense_mla_attn(const dsa_problem_t *problem, const dsa_layout_t
                                 const void *kv_pool, void *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/*
+ * Indexer-key append, the cache write before step 1: the key of each new token is its latent row times the key
+ * projection, k_I = c W_KI (kiadev, "How DSA works", stage 1), written into the indexer cache at position
+ * positions[r] of sequence row_seq[r] as the cache stores it ("What Does the GPU Actually Run?": FP8 numbers
+ * and one scale per token).
+ *   positions   [R] int32 position of row r's token; a row with a negative position, or one at or beyond
+ *               max_pages * page_size, is skipped.  Rows that address the same cached position race.
+ *   src         w_k non-NULL: [R, d_c] latent rows in kv_dtype (BF16 or F32), d_c = latent_dim <= 1024;
+ *               w_k NULL: [R, d_I] fp32 keys, already projected
+ *   w_k         [d_c, d_I] W_KI in kv_dtype, row-major, or NULL
+ *   k_idx_pool, k_idx_scale  the indexer cache as dsa_indexer_scores reads it.  F8E4M3: scale = max_j |k_j| / 448
+ *               (1 for a zero key) and code_j = the e4m3 value nearest to k_j / scale, ties to the even code,
+ *               clamped to +-448, sign bit kept.  F32: the keys themselves (k_idx_scale NULL).
+ * The projection sums exact fp64 products over d ascending and rounds each key once to fp32; the scale and
+ * k_j / scale are IEEE fp32 divisions.  Codes and scales are therefore reproducible bit for bit.  Only the
+ * addressed pool rows are written.  Keys must be finite.  The problem's indexer fields are checked as for
+ * dsa_indexer_scores; the layout's row_len is not read.
+ */
+dsa_status_t dsa_indexer_key_append(const dsa_problem_t *problem, const dsa_layout_t *layout,
+                                    const int32_t *positions, const void *src, const void *w_k,
+                                    void *k_idx_pool, float *k_idx_scale, void *stream);
+
 /* Workspace bytes an operation needs for this problem (0 on an invalid problem; see dsa_last_error). */
 size_t dsa_workspace_bytes(const dsa_problem_t *problem, int32_t op);
 

@@ -52,7 +52,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_attn.argtypes = [PP, PL, P, P, P, P, P, P, SZ, P]
         L.dsa_decode_step.argtypes = [PP, PL, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.dsa_dense_mla_attn.argtypes = [PP, PL, P, P, P, P, P, SZ, P]
-        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn"):
+        L.dsa_indexer_key_append.argtypes = [PP, PL, P, P, P, P, P, P]
+        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn",
+                  "dsa_indexer_key_append"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [PP, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = SZ
@@ -138,6 +140,12 @@ def dsa_dense_mla_attn(problem, layout, q, kv_pool, out, lse, workspace, stream=
     _check(lib().dsa_dense_mla_attn(ctypes.byref(problem), ctypes.byref(layout), _ptr(q, "q"),
                                     _ptr(kv_pool, "kv_pool"), _ptr(out, "out"), _ptr(lse, "lse"),
                                     _ptr(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+
+
+def dsa_indexer_key_append(problem, layout, positions, src, w_k, k_idx_pool, k_idx_scale, stream=None):
+    _check(lib().dsa_indexer_key_append(ctypes.byref(problem), ctypes.byref(layout), _ptr(positions, "positions"),
+                                        _ptr(src, "src"), _ptr(w_k, "w_k"), _ptr(k_idx_pool, "k_idx_pool"),
+                                        _ptr(k_idx_scale, "k_idx_scale"), _stream(stream)))
 
 
 def dsa_decode_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx,

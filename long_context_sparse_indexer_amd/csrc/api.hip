@@ -221,6 +221,32 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* problem, const dsa_layout_
                     "attention launch");
 }
 
+dsa_status_t dsa_indexer_key_append(const dsa_problem_t* problem, const dsa_layout_t* layout,
+                                    const int32_t* positions, const void* src, const void* w_k, void* k_idx_pool,
+                                    float* k_idx_scale, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_problem(problem, layout, true, false, &g);
+  if (st != DSA_OK) return st;
+  DSA_CHECK(positions && src && k_idx_pool, DSA_EINVAL, "positions, src and k_idx_pool must be non-NULL");
+  if (g.idx_dtype == DSA_F8E4M3)
+    DSA_CHECK(k_idx_scale != nullptr, DSA_EINVAL, "an fp8 indexer cache needs k_idx_scale");
+  else
+    DSA_CHECK(k_idx_scale == nullptr, DSA_EINVAL, "an fp32 indexer cache takes no scales (pass NULL)");
+  if (w_k) {
+    DSA_CHECK(g.kv_dtype == DSA_BF16 || g.kv_dtype == DSA_F32, DSA_EINVAL, "kv_dtype = %d invalid", g.kv_dtype);
+    DSA_CHECK(g.d_c >= 1 && g.d_c <= dsa::key_append_max_latent_dim(), DSA_EUNSUPPORTED,
+              "key projection: latent_dim = %d not in 1..%d", g.d_c, dsa::key_append_max_latent_dim());
+    const uintptr_t a = g.kv_dtype == DSA_BF16 ? 1 : 3;
+    DSA_CHECK(((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(w_k)) & a) == 0, DSA_EINVAL,
+              "src and w_k must be aligned to their element size");
+  } else {
+    DSA_CHECK((reinterpret_cast<uintptr_t>(src) & 3) == 0, DSA_EINVAL, "fp32 keys must be 4-byte aligned");
+  }
+  return hip_status(dsa::launch_key_append(g, positions, src, w_k, k_idx_pool, k_idx_scale,
+                                           static_cast<hipStream_t>(stream)),
+                    "key append launch");
+}
+
 dsa_status_t dsa_dense_mla_attn(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q,
                                 const void* kv_pool, void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream) {

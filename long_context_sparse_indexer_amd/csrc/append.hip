@@ -1,0 +1,180 @@
+// Indexer-key append for gfx950: the cache write that precedes the scoring step.  Each new token's indexer key
+// is its latent row times the key projection, k_I = c W_KI (kiadev "How DSA works", stage 1), and the indexer
+// cache keeps it as d_I e4m3 codes plus one fp32 scale (kgptalkie "DeepSeek Sparse Attention explained",
+// "What Does the GPU Actually Run?"), or as fp32 in an fp32 cache.
+//
+// Scale and codes: scale = max_j |k_j| / 448, the largest e4m3 magnitude (1 for a zero key); code_j = the e4m3
+// value nearest to k_j / scale, ties to the even code, clamped to +-448, sign bit kept.  These are integers
+// decided by floating point, so every step is fixed: each product c_d w_dj of bf16 or fp32 operands is exact in
+// fp64, each output sums them in fp64 over d ascending (one FMA chain), the sum is rounded once to fp32, and the
+// scale and k_j / scale are IEEE fp32 divisions.  The codes are then reproducible bit for bit.
+//
+// The work is d_c x d_I multiply-adds per token (64 K for the shipped 512 x 128), so the kernel is bound by the
+// latency of its FMA chains at decode batch sizes.  A block of 256 threads takes 8 tokens (d_I = 128: two row
+// groups of 128 columns) or 16 (d_I <= 64: four groups of 64); a thread runs four chains, one per token of its
+// group, so a wave issues four independent FMAs per step.  The latent rows are staged in LDS as fp32 (exact for
+// bf16), W_KI too when it is bf16 with d_c <= 512, so the chain loop reads only LDS.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kRowsPerThread = 4;
+constexpr int kStageMaxDc = 512;     // W_KI staged in LDS up to this latent width (bf16)
+constexpr int kGlobalMaxDc = 1024;   // latent width of the unstaged path
+
+// fp32 -> OCP e4m3fn code for |y| <= 448, round to nearest even; the sign bit of y is kept.  Below 2^-6 the codes
+// are the subnormals m * 2^-9 (m = 8 is the smallest normal, code 0x08); above, the fp32 mantissa is cut to three
+// bits with a carry into the exponent field.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t e = (b >> 23) - 127 + 7;  // biased e4m3 exponent, 1 .. 15
+  uint32_t m3 = (b >> 20) & 7u;
+  const uint32_t rest = b & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
+  return sign | ((e << 3) + m3);  // m3 = 8 carries into the exponent
+}
+
+// kMode 0: the keys arrive as fp32 (no projection).  1: bf16 latent rows and W_KI, W_KI staged in LDS (d_c <= 512,
+// d_I == kCols).  2: latent rows and W_KI in the latent dtype, W_KI read from global memory.
+template <int kMode, int kCols>
+__global__ __launch_bounds__(256) void key_append_kernel(
+    const void* __restrict__ src, const void* __restrict__ w, int c_bf16, int R, int d_c, int d_I,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ page_table, int num_seqs, int max_pages, int num_pages, int log2ps, int pool_f8,
+    void* __restrict__ pool, float* __restrict__ pool_scale) {
+  constexpr int kGroups = 256 / kCols, kRpb = kGroups * kRowsPerThread;
+  constexpr int kMaxDc = kMode == 1 ? kStageMaxDc : kGlobalMaxDc;
+  __shared__ __attribute__((aligned(16))) float c_lds[kMode == 0 ? 4 : kMaxDc * kRpb];  // [d][row slot]
+  __shared__ __attribute__((aligned(16))) unsigned short w_lds[kMode == 1 ? kStageMaxDc * kCols : 8];  // [d][col]
+  __shared__ float amax_lds[4][kRowsPerThread];
+  const int t = threadIdx.x, col = t % kCols, grp = t / kCols, lane = t & 63, wave = t >> 6;
+  const int r0 = blockIdx.x * kRpb;
+  float k[kRowsPerThread];
+
+  if constexpr (kMode == 0) {
+    const float* x = static_cast<const float*>(src);
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int r = r0 + grp * kRowsPerThread + i;
+      k[i] = r < R && col < d_I ? x[(int64_t)r * d_I + col] : 0.f;
+    }
+  } else {
+    if constexpr (kMode == 1) {
+      // W_KI [d_c, kCols] bf16 is contiguous: copy it as 16-byte pieces, eight per thread in flight at a time
+      const v4i* wg = static_cast<const v4i*>(w);
+      const int n16 = d_c * kCols / 8;
+      for (int b = 0; b < n16; b += 8 * 256) {
+        v4i buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b + j * 256 + t < n16) buf[j] = wg[b + j * 256 + t];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b + j * 256 + t < n16) *reinterpret_cast<v4i*>(&w_lds[(b + j * 256 + t) * 8]) = buf[j];
+      }
+    }
+    // latent rows of the block's tokens, transposed so that a thread's four tokens sit in one 16-byte word
+    for (int i = t; i < kRpb * d_c; i += 256) {
+      const int rs = i / d_c, d = i - rs * d_c, r = r0 + rs;
+      float v = 0.f;
+      if (r < R) {
+        const int64_t e = (int64_t)r * d_c + d;
+        v = c_bf16 ? bf16_bits_to_float(static_cast<const unsigned short*>(src)[e]) : static_cast<const float*>(src)[e];
+      }
+      c_lds[d * kRpb + rs] = v;
+    }
+    __syncthreads();
+    double acc[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) acc[i] = 0.0;
+    if (col < d_I) {
+      for (int d = 0; d < d_c; ++d) {
+        const v4f cv = *reinterpret_cast<const v4f*>(&c_lds[d * kRpb + grp * kRowsPerThread]);
+        float wv;
+        if constexpr (kMode == 1) {
+          wv = bf16_bits_to_float(w_lds[d * kCols + col]);
+        } else {
+          const int64_t e = (int64_t)d * d_I + col;
+          wv = c_bf16 ? bf16_bits_to_float(static_cast<const unsigned short*>(w)[e]) : static_cast<const float*>(w)[e];
+        }
+        const double wd = (double)wv;
+#pragma unroll
+        for (int i = 0; i < kRowsPerThread; ++i) acc[i] = fma((double)cv[i], wd, acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) k[i] = (float)acc[i];
+  }
+
+  // largest magnitude of each token's key: over the wave, then over the group's waves (two when kCols = 128)
+  if (pool_f8) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const float m = wave_max(fabsf(k[i]));
+      if (lane == 0) amax_lds[wave][i] = m;
+    }
+    __syncthreads();
+  }
+  const int64_t cap = (int64_t)max_pages << log2ps;
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int r = r0 + grp * kRowsPerThread + i;
+    if (r >= R || col >= d_I) continue;
+    const int pos = positions[r];
+    if (pos < 0 || pos >= cap) continue;
+    const int64_t row = phys_row(page_table, max_pages, num_pages, log2ps, clamp_seq(row_seq[r], num_seqs), pos);
+    if (pool_f8) {
+      const float amax = kCols == 128 ? fmaxf(amax_lds[2 * grp][i], amax_lds[2 * grp + 1][i]) : amax_lds[grp][i];
+      const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+      const float y = fminf(fmaxf(k[i] / scale, -448.0f), 448.0f);
+      static_cast<uint8_t*>(pool)[row * d_I + col] = (uint8_t)e4m3_code(y);
+      if (col == 0) pool_scale[row] = scale;
+    } else {
+      static_cast<float*>(pool)[row * d_I + col] = k[i];
+    }
+  }
+}
+
+template <int kCols>
+hipError_t launch_cols(const Geo& g, const int32_t* positions, const void* src, const void* w, int mode, void* pool,
+                       float* pool_scale, hipStream_t stream) {
+  constexpr int kRpb = 256 / kCols * kRowsPerThread;
+  const int blocks = (g.R + kRpb - 1) / kRpb;
+  const int c_bf16 = g.kv_dtype == 1 /* BF16 */;
+  const int f8 = g.idx_dtype == 2 /* F8E4M3 */;
+#define DSA_APPEND_ARGS                                                                                        \
+  src, w, c_bf16, g.R, g.d_c, g.d_I, positions, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, \
+      f8, pool, pool_scale
+  switch (mode) {
+    case 0: key_append_kernel<0, kCols><<<blocks, 256, 0, stream>>>(DSA_APPEND_ARGS); break;
+    case 1: key_append_kernel<1, kCols><<<blocks, 256, 0, stream>>>(DSA_APPEND_ARGS); break;
+    default: key_append_kernel<2, kCols><<<blocks, 256, 0, stream>>>(DSA_APPEND_ARGS); break;
+  }
+#undef DSA_APPEND_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_key_append(const Geo& g, const int32_t* positions, const void* src, const void* w, void* pool,
+                             float* pool_scale, hipStream_t stream) {
+  if (g.R == 0) return hipSuccess;
+  const int cols = g.d_I <= 64 ? 64 : 128;
+  int mode = 0;
+  if (w) {
+    const bool stage = g.kv_dtype == 1 && g.d_c <= kStageMaxDc && g.d_I == cols &&
+                       (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+    mode = stage ? 1 : 2;
+  }
+  return cols == 64 ? launch_cols<64>(g, positions, src, w, mode, pool, pool_scale, stream)
+                    : launch_cols<128>(g, positions, src, w, mode, pool, pool_scale, stream);
+}
+
+int key_append_max_latent_dim() { return kGlobalMaxDc; }
+
+}  // namespace dsa

@@ -55,6 +55,11 @@ size_t attn_workspace_bytes(const Geo& g);
 // pool_rows: if non-NULL, the pool row of every selected slot (as written by the top-k), used instead of
 // looking the positions up in the page table (bf16 latents).  topk_idx and pool_rows both NULL: dense
 // attention, slot s of row r is position s while s < n_r (g.k = the longest row).
+// append.hip.  w NULL: src holds fp32 keys [R, d_I]; otherwise latent rows [R, d_c] and W_KI [d_c, d_I] in
+// g.kv_dtype.  The pool is fp8 codes + scales (g.idx_dtype F8E4M3) or fp32.
+hipError_t launch_key_append(const Geo& g, const int32_t* positions, const void* src, const void* w, void* pool,
+                             float* pool_scale, hipStream_t stream);
+int key_append_max_latent_dim();
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
                        float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream);
 

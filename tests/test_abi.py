@@ -167,3 +167,20 @@ def test_binding_rejects_host_tensors():
     lay = dsa.dsa_layout_t(FAKE, FAKE, FAKE)
     with pytest.raises(ValueError):
         dsa.dsa_indexer_scores(p, lay, torch.zeros(4), None, None, None, None, torch.zeros(4), 4096, stream=0)
+
+
+def test_key_append_validation():
+    L = dsa.lib()
+    p = _problem(idx_dim=128)
+
+    def call(p=p, positions=FAKE, src=FAKE, w=FAKE, pool=FAKE, scale=FAKE):
+        return L.dsa_indexer_key_append(ctypes.byref(p), ctypes.byref(LAYOUT), positions, src, w, pool, scale, None)
+    assert call(positions=None) == dsa.DSA_EINVAL and "non-NULL" in dsa.dsa_last_error()
+    assert call(scale=None) == dsa.DSA_EINVAL and "k_idx_scale" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_dtype="f32")) == dsa.DSA_EINVAL and "no scales" in dsa.dsa_last_error()
+    assert call(src=FAKE + 1) == dsa.DSA_EINVAL and "aligned" in dsa.dsa_last_error()
+    assert call(p=_problem(kv_dtype=9)) == dsa.DSA_EINVAL and "kv_dtype" in dsa.dsa_last_error()
+    assert call(p=_problem(latent_dim=1025, kv_dtype="f32")) == dsa.DSA_EUNSUPPORTED
+    assert "latent_dim" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_dim=96)) == dsa.DSA_EUNSUPPORTED  # the fp8 cache widths of the indexer
+    assert call(w=None, src=FAKE + 2) == dsa.DSA_EINVAL and "4-byte" in dsa.dsa_last_error()
