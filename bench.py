@@ -116,6 +116,54 @@ def crossover(lengths, rows: int, steps: int) -> int:
     return 0
 
 
+def append_sweep(steps: int) -> int:
+    """Indexer-key append (bf16 latent rows x W_KI -> e4m3 codes + scale), one JSON line per (tokens, d_I): graph
+    replay of one call on the same inputs, which the preceding kernels of a layer would have left in cache."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_indexer_amd as dsa
+    import synth
+    from synth.device import upload
+
+    dev = torch.device("cuda:0")
+    for d_I in (128, 64):
+        for rows in (1, 64, 4096):
+            prob = synth.make_problem(synth.get("prefill_chunk", cache_len=8192, rows=rows, H=16, d_I=d_I, seed=9))
+            app = synth.append_inputs(prob, 9)
+            d = upload(prob, dev)
+            P = dsa.make_problem(**d.fields)
+            L = dsa.make_layout(d.row_seq, d.row_len, d.page_table)
+            pos = torch.from_numpy(app["positions"]).to(dev)
+            c = torch.from_numpy(app["c"].view(np.int16)).to(dev)
+            w = torch.from_numpy(app["w"].view(np.int16)).to(dev)
+            pool, scale = d.k_idx_pool.clone(), d.k_idx_scale.clone()
+
+            def call():
+                dsa.dsa_indexer_key_append(P, L, pos, c, w, pool, scale, torch.cuda.current_stream().cuda_stream)
+            call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(10):
+                    call()
+            reps = max(1, steps // 10)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / (reps * 10)
+            flops = 2.0 * rows * prob.d_c * d_I
+            print(json.dumps({"append": True, "tokens": rows, "d_c": prob.d_c, "d_I": d_I, "us_per_call": round(us, 2),
+                              "tokens_per_s": round(rows / us * 1e6, 1),
+                              "fp64_tflops": round(flops / us * 1e-6, 3), "fp64_peak_tflops": 78.6}), flush=True)
+            del d, pool, scale
+            torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +181,8 @@ def main() -> int:
     ap.add_argument("--crossover", action="store_true",
                     help="time the sparse step against dense attention over context lengths, then exit")
     ap.add_argument("--crossover-rows", type=int, default=1)
+    ap.add_argument("--append", action="store_true",
+                    help="time the indexer-key append for 1, 64 and 4096 tokens at d_I = 128 and 64, then exit")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 4 times (reference dispatches for byte counters)")
     args = ap.parse_args()
@@ -142,6 +192,8 @@ def main() -> int:
         return 2
     if args.crossover:
         return crossover([2048, 4096, 8192, 16384, 32768, 65536, 131072], args.crossover_rows, min(args.steps, 400))
+    if args.append:
+        return append_sweep(min(args.steps, 1000))
 
     import numpy as np
     import torch
