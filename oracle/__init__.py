@@ -49,6 +49,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_oracle_key_projection.restype = ctypes.c_int
         L.dsa_oracle_key_append.argtypes = [I32, I32, P, P, P, P, I32, I32, I32, P, P]
         L.dsa_oracle_key_append.restype = ctypes.c_int
+        L.dsa_oracle_fp8_entry_key.argtypes = [P, P]
+        L.dsa_oracle_fp8_entry_key.restype = None
+        L.dsa_oracle_sparse_attn_fp8.argtypes = [I32, I32, P, P, P, I32, P, P, I32, I32, D, P, P]
+        L.dsa_oracle_sparse_attn_fp8.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -128,8 +132,12 @@ def decode_step(prob):
     scores = indexer_scores(prob.q_idx, prob.q_idx_scale, prob.head_w, prob.k_idx_pool, prob.k_idx_scale,
                             prob.row_seq, prob.row_len, prob.page_table, prob.page_size, prob.idx_dtype)
     idx, kth = topk(scores, prob.row_len, prob.k)
-    o, lse = sparse_attn(prob.q, prob.kv_pool, idx, prob.row_seq, prob.page_table, prob.page_size, prob.kv_dtype,
-                         prob.softmax_scale)
+    if prob.kv_dtype == "f8":
+        o, lse = sparse_attn_fp8(prob.q, prob.kv_pool, idx, prob.row_seq, prob.page_table, prob.page_size,
+                                 prob.softmax_scale)
+    else:
+        o, lse = sparse_attn(prob.q, prob.kv_pool, idx, prob.row_seq, prob.page_table, prob.page_size,
+                             prob.kv_dtype, prob.softmax_scale)
     return scores, idx, kth, o, lse
 
 
@@ -175,3 +183,34 @@ def key_append(k32, positions, row_seq, page_table, page_size: int, pool, pool_s
     if rc:
         raise ValueError("oracle key append rejected its arguments")
     return pool, pool_scale
+
+
+FP8_ENTRY_BYTES = 656
+
+
+def fp8_entry_key(entry) -> np.ndarray:
+    """The 576-wide fp64 key of one 656-byte latent cache entry (512 dequantised latent values, 64 RoPE values)."""
+    entry = _c(entry, np.uint8)
+    if entry.size != FP8_ENTRY_BYTES:
+        raise ValueError("an fp8 latent entry has 656 bytes")
+    key = np.empty(576, np.float64)
+    lib().dsa_oracle_fp8_entry_key(_p(entry), _p(key))
+    return key
+
+
+def sparse_attn_fp8(q, pool, topk_idx, row_seq, page_table, page_size: int, scale: float):
+    """(o [R, H, 512], lse [R, H]) in fp64 over the selected 656-byte entries; q [R, H, 576] bf16 bit patterns."""
+    q = _c(q, np.uint16)
+    R, H, width = q.shape
+    if width != 576:
+        raise ValueError("the fp8-latent query is 576 wide")
+    pool = _c(pool, np.uint8)
+    topk_idx, row_seq, page_table = _c(topk_idx, np.int32), _c(row_seq, np.int32), _c(page_table, np.int32)
+    k = topk_idx.shape[1]
+    out = np.empty((R, H, 512), np.float64)
+    lse = np.empty((R, H), np.float64)
+    rc = lib().dsa_oracle_sparse_attn_fp8(R, H, _p(q), _p(pool), _p(topk_idx), k, _p(row_seq), _p(page_table),
+                                          page_table.shape[1], page_size, float(scale), _p(out), _p(lse))
+    if rc:
+        raise ValueError(f"oracle fp8 attention rejected its arguments (code {rc})")
+    return out, lse

@@ -35,6 +35,13 @@
  *      The code is an integer decided by floating point, so the decision is taken in fp32: the key is
  *      rounded once to fp32, then scale = amax / 448 and k_j / scale are IEEE fp32 divisions.  The
  *      projection is the plain fp64 sum over d = 0 .. d_c-1 of exact products (bf16 or fp32 operands).
+ *   6. Sparse attention over the FP8 latent cache ("What Does the GPU Actually Run?": each token's entry is 656
+ *      bytes, 512 values in float8_e4m3, 4 fp32 scale factors and the 64 RoPE numbers kept in bf16; "Why Is
+ *      Decoding Held Back by Memory?": one 576-number entry per token).  Readings: the parts lie in that order
+ *      (codes at bytes 0..511, scales at 512..527, RoPE at 528..655); scale t covers values 128t .. 128t+127;
+ *      the key of a position is the 576-vector [c ; r] (dequantised latent, RoPE part) and its value is c, so
+ *      with a 576-wide query q = [q_c ; q_r]:
+ *          l_i = scale * (<q_c, c[T_i]> + <q_r, r[T_i]>),  o = sum_i softmax(l)_i c[T_i]  (512 wide).
  *   Cached positions are addressed through a page table: physical row = table[seq][pos / P] * P + pos % P
  *   (the selected positions are "an address list into the paged KV cache", "How Does the Selector Pick").
  */
@@ -247,6 +254,70 @@ int dsa_oracle_key_append(int32_t R, int32_t d_I, const float *k32, const int32_
       dsa_oracle_quantize_key(d_I, x, (uint8_t *)pool + row * d_I, pool_scale + row);
     else
       memcpy((float *)pool + row * d_I, x, sizeof(float) * (size_t)d_I);
+  }
+  return 0;
+}
+
+/* ---- 6. sparse attention over the FP8 latent cache ------------------------------------------------- */
+
+enum { F8_ENTRY = 656, F8_LATENT = 512, F8_ROPE = 64, F8_TILE = 128 };
+
+/* Dequantised 576-wide key of one cache entry: the 512 latent values code * scale[tile], then the 64 RoPE values. */
+void dsa_oracle_fp8_entry_key(const uint8_t *entry, double *key) {
+  for (int d = 0; d < F8_LATENT; ++d) {
+    float sc;
+    memcpy(&sc, entry + F8_LATENT + 4 * (d / F8_TILE), sizeof sc);
+    key[d] = dsa_oracle_e4m3_value(entry[d]) * (double)sc;
+  }
+  for (int d = 0; d < F8_ROPE; ++d) {
+    uint16_t b;
+    memcpy(&b, entry + F8_LATENT + 16 + 2 * d, sizeof b);
+    key[F8_LATENT + d] = dsa_oracle_bf16_value(b);
+  }
+}
+
+/* q [R, H, 576] bf16; pool [rows, 656] bytes; out [R, H, 512] and lse [R, H] in fp64.  Entries < 0 of topk_idx are
+ * ignored; an empty selection gives o = 0 and lse = -inf. */
+int dsa_oracle_sparse_attn_fp8(int32_t R, int32_t H, const uint16_t *q, const uint8_t *pool, const int32_t *topk_idx,
+                               int32_t k, const int32_t *row_seq, const int32_t *page_table, int32_t max_pages,
+                               int32_t page_size, double scale, double *out, double *lse) {
+  const int KD = F8_LATENT + F8_ROPE;
+  if (R < 0 || H <= 0 || k <= 0 || page_size <= 0) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    double *keys = (double *)malloc(sizeof(double) * (size_t)k * KD);
+    if (!keys) return 2;
+    int32_t m = 0;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t pos = topk_idx[(int64_t)r * k + i];
+      if (pos < 0) continue;
+      int64_t row = phys_row(page_table, max_pages, page_size, row_seq[r], pos);
+      dsa_oracle_fp8_entry_key(pool + row * F8_ENTRY, keys + (int64_t)m * KD);
+      ++m;
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t h = 0; h < H; ++h) {
+      double *o = out + ((int64_t)r * H + h) * F8_LATENT;
+      for (int32_t d = 0; d < F8_LATENT; ++d) o[d] = 0.0;
+      if (m == 0) { lse[(int64_t)r * H + h] = -INFINITY; continue; }
+      const uint16_t *qh = q + ((int64_t)r * H + h) * KD;
+      double *logit = (double *)malloc(sizeof(double) * (size_t)m);
+      double mx = -INFINITY;
+      for (int32_t i = 0; i < m; ++i) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < KD; ++d) dot += dsa_oracle_bf16_value(qh[d]) * keys[(int64_t)i * KD + d];
+        logit[i] = scale * dot;
+        if (logit[i] > mx) mx = logit[i];
+      }
+      double z = 0.0;
+      for (int32_t i = 0; i < m; ++i) { logit[i] = exp(logit[i] - mx); z += logit[i]; }
+      for (int32_t i = 0; i < m; ++i) {
+        double p = logit[i] / z;
+        for (int32_t d = 0; d < F8_LATENT; ++d) o[d] += p * keys[(int64_t)i * KD + d];
+      }
+      lse[(int64_t)r * H + h] = mx + log(z);
+      free(logit);
+    }
+    free(keys);
   }
   return 0;
 }

@@ -21,15 +21,16 @@ def _t(a, device, dtype=None):
 def upload(p: Problem, device="cuda") -> types.SimpleNamespace:
     """Device tensors of every input plus the problem fields of the C ABI (as a dict)."""
     f8 = p.idx_dtype == "f8"
-    kv_t = torch.int16 if p.kv_dtype == "bf16" else None
+    kv_t = torch.int16 if p.kv_dtype in ("bf16", "f8") else None  # f8 latents: bf16 queries, byte entries
     d = types.SimpleNamespace()
     d.q_idx = _t(p.q_idx, device)
     d.q_idx_scale = _t(p.q_idx_scale, device)
     d.head_w = _t(p.head_w, device)
     d.k_idx_pool = _t(p.k_idx_pool, device)
     d.k_idx_scale = _t(p.k_idx_scale, device)
-    d.q = _t(p.q.view(np.int16) if p.kv_dtype == "bf16" else p.q, device, kv_t and torch.bfloat16)
-    d.kv_pool = _t(p.kv_pool.view(np.int16) if p.kv_dtype == "bf16" else p.kv_pool, device, kv_t and torch.bfloat16)
+    d.q = _t(p.q.view(np.int16) if kv_t else p.q, device, kv_t and torch.bfloat16)
+    d.kv_pool = _t(p.kv_pool.view(np.int16) if p.kv_dtype == "bf16" else p.kv_pool, device,
+                   torch.bfloat16 if p.kv_dtype == "bf16" else None)
     d.row_seq = _t(p.row_seq, device)
     d.row_len = _t(p.row_len, device)
     d.page_table = _t(p.page_table, device)

@@ -13,7 +13,10 @@ Recipe (per sequence, fp32 masters, "N(0, v)" means variance v):
   attention queries q[h] ~ N(0, 1/d_c) for each of the H heads (already in latent space);
   boosted positions (random anchors drawn without replacement outside the most recent window, plus that
     window) get k_I[s] += 0.5 * mean_j q_I[j], which makes the score spiky at planted positions;
-  fp8 operands: scale = amax / 448 per d_I-vector (1 for an all-zero vector), code = e4m3fn(RNE(x / scale)).
+  fp8 operands: scale = amax / 448 per d_I-vector (1 for an all-zero vector), code = e4m3fn(RNE(x / scale));
+  an fp8 latent cache ("f8" latent dtype) stores 656-byte entries: the latent quantised the same way per
+    128-value tile, the 4 tile scales, and 64 RoPE values r[s] ~ N(0, 1) as bf16; its queries gain 64 RoPE
+    dims ~ N(0, 1/576) (drawn after every other value of the sequence); k_I uses the dequantised latent.
 Pages are 64 positions; a paged workload places every logical page of every sequence at a random physical
 page of one shared pool, the others place them in order.
 """
@@ -83,6 +86,20 @@ def _quant_rows(x: np.ndarray):
     return codes, scale
 
 
+def _fp8_latent(c: np.ndarray, rope: np.ndarray):
+    """656-byte latent cache entries: 512 e4m3 codes quantised per 128-value tile (scale = tile amax / 448, 1 for
+    a zero tile), the 4 fp32 tile scales, the 64 RoPE values as bf16; and the fp32 value of the stored latent."""
+    n = c.shape[0]
+    codes, scale = _quant_rows(c.reshape(n, 4, 128))
+    deq = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy() * scale[..., None]
+    ent = np.zeros((n, 656), np.uint8)
+    ent[:, :512] = codes.reshape(n, 512)
+    ent[:, 512:528] = np.ascontiguousarray(scale, np.float32).view(np.uint8).reshape(n, 16)
+    rope_bits, _ = _round_kv(rope, "bf16")
+    ent[:, 528:] = np.ascontiguousarray(rope_bits).view(np.uint8).reshape(n, 128)
+    return ent, deq.reshape(n, 512).astype(np.float32)
+
+
 def _draw_sequence(rng: np.random.Generator, n: int, cfg: dict, W_KI: np.ndarray):
     d_c, d_I, H_I, H = cfg["d_c"], cfg["d_I"], cfg["H_I"], cfg["H"]
     c = rng.standard_normal((n, d_c), dtype=np.float32)
@@ -93,7 +110,13 @@ def _draw_sequence(rng: np.random.Generator, n: int, cfg: dict, W_KI: np.ndarray
     A = min(cfg["anchors"], n - W)
     anchors = rng.choice(n - W, size=A, replace=False) if A > 0 else np.zeros(0, np.int64)
     boosted = np.sort(np.concatenate([anchors.astype(np.int64), np.arange(n - W, n, dtype=np.int64)]))
-    c_bits, c_val = _round_kv(c, cfg["kv_dtype"])
+    if cfg["kv_dtype"] == "f8":
+        # RoPE parts of the cache entries and of the query, drawn after everything else
+        c_bits, c_val = _fp8_latent(c, rng.standard_normal((n, 64), dtype=np.float32))
+        q = np.concatenate([q, rng.standard_normal((H, 64), dtype=np.float32) * np.float32(math.sqrt(1.0 / 576))],
+                           axis=1)
+    else:
+        c_bits, c_val = _round_kv(c, cfg["kv_dtype"])
     del c
     k_I = c_val @ W_KI
     k_I[boosted] += np.float32(0.5) * q_I.mean(axis=0)
@@ -105,6 +128,9 @@ def _extra_row(rng: np.random.Generator, cfg: dict):
     q_I = rng.standard_normal((H_I, d_I), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_I))
     w = rng.random(H_I, dtype=np.float32)
     q = rng.standard_normal((H, d_c), dtype=np.float32) * np.float32(math.sqrt(1.0 / d_c))
+    if cfg["kv_dtype"] == "f8":
+        q = np.concatenate([q, rng.standard_normal((H, 64), dtype=np.float32) * np.float32(math.sqrt(1.0 / 576))],
+                           axis=1)
     return q_I, w, q
 
 
@@ -136,10 +162,10 @@ def make_problem(cfg: dict) -> Problem:
         off += npg
 
     f8 = cfg["idx_dtype"] == "f8"
-    kv_np = np.uint16 if cfg["kv_dtype"] == "bf16" else np.float32
+    kv_np = {"bf16": np.uint16, "f32": np.float32, "f8": np.uint8}[cfg["kv_dtype"]]
     k_pool = np.zeros((num_pages * ps, d_I), np.uint8 if f8 else np.float32)
     k_scale = np.ones(num_pages * ps, np.float32) if f8 else None
-    kv_pool = np.zeros((num_pages * ps, d_c), kv_np)
+    kv_pool = np.zeros((num_pages * ps, 656 if cfg["kv_dtype"] == "f8" else d_c), kv_np)
 
     q_I_rows, w_rows, q_rows, row_seq, row_len, boosted = [], [], [], [], [], []
     for b, n in enumerate(lengths):
@@ -177,8 +203,9 @@ def make_problem(cfg: dict) -> Problem:
         q_idx, q_idx_scale = _quant_rows(q_I)
     else:
         q_idx, q_idx_scale = q_I.astype(np.float32), None
-    q_all = np.stack(q_rows) if R else np.zeros((0, H, d_c), np.float32)
-    q_bits, _ = _round_kv(q_all, cfg["kv_dtype"])
+    q_width = d_c + 64 if cfg["kv_dtype"] == "f8" else d_c
+    q_all = np.stack(q_rows) if R else np.zeros((0, H, q_width), np.float32)
+    q_bits, _ = _round_kv(q_all, "bf16" if cfg["kv_dtype"] == "f8" else cfg["kv_dtype"])
     return Problem(
         cfg=cfg, R=R, S=S, H_I=H_I, d_I=d_I, H=H, d_c=d_c, k=cfg["k"], page_size=ps, max_pages=max_pages,
         num_pages=num_pages, idx_dtype=cfg["idx_dtype"], kv_dtype=cfg["kv_dtype"],

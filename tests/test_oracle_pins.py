@@ -445,3 +445,80 @@ def test_key_append_places_rows_through_the_page_table():
     # an fp32 pool stores the keys as they are
     fpool, none = oracle.key_append(k, positions, row_seq, page_table, page_size, np.zeros((16, d_I), np.float32))
     assert none is None and np.array_equal(fpool[targets[3]], k[3]) and not fpool[untouched].any()
+
+
+# ------------------------------------------------------------------------- attention over the fp8 latent cache
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+def _fp8_entries(rng, n, pow2_scales=False, rope_zero=False):
+    codes = rng.integers(0, 256, size=(n, 512)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    if pow2_scales:
+        scales = np.exp2(rng.integers(-8, 3, size=(n, 4))).astype(np.float32)
+    else:
+        scales = rng.uniform(0.001, 0.02, size=(n, 4)).astype(np.float32)
+    rope = np.zeros((n, 64), np.float32) if rope_zero else rng.standard_normal((n, 64)).astype(np.float32)
+    ent = np.zeros((n, 656), np.uint8)
+    ent[:, :512] = codes
+    ent[:, 512:528] = scales.view(np.uint8).reshape(n, 16)
+    ent[:, 528:] = _bf16_bits(rope).view(np.uint8).reshape(n, 128)
+    return ent
+
+
+def test_fp8_entry_layout_by_hand():
+    ent = np.zeros(656, np.uint8)
+    ent[0], ent[130], ent[300], ent[511] = 0x38, 0xB8, 0x40, 0x7E  # 1.0, -1.0, 2.0, 448
+    ent[512:528] = np.array([2.0, 0.5, 4.0, 0.25], np.float32).view(np.uint8)
+    rope = np.zeros(64, np.float32)
+    rope[5], rope[63] = 1.5, -3.0
+    ent[528:] = _bf16_bits(rope).view(np.uint8)
+    key = oracle.fp8_entry_key(ent)
+    vals = oracle.decode(np.array([0x38, 0xB8, 0x40, 0x7E], np.uint8), "f8")
+    assert vals[0] == 1.0 and vals[1] == -1.0 and vals[3] == 448.0
+    assert key[0] == 2.0 and key[130] == -0.5 and key[300] == vals[2] * 4.0 and key[511] == 448.0 * 0.25
+    assert key[512 + 5] == 1.5 and key[575] == -3.0
+    assert np.count_nonzero(key) == 6
+
+
+@pytest.mark.parametrize("scale", [1.0, 1 / math.sqrt(576)])
+def test_fp8_attention_full_selection_equals_sdpa(scale):
+    # the whole selection: softmax(scale * q [c; r]^T) c, with a 576-wide key and a 512-wide value
+    rng = np.random.default_rng(21)
+    n, H = 40, 6
+    ent = _fp8_entries(rng, n)
+    q = _bf16_bits(rng.standard_normal((1, H, 576)) * 0.05)
+    page_table = np.arange(1, dtype=np.int32).reshape(1, 1)
+    o, lse = oracle.sparse_attn_fp8(q, ent, np.arange(n, dtype=np.int32)[None], np.zeros(1, np.int32),
+                                    page_table, 64, scale)
+    keys = torch.from_numpy(np.stack([oracle.fp8_entry_key(e) for e in ent]))
+    qf = torch.from_numpy(oracle.decode(q, "bf16")[0])
+    ref = torch.nn.functional.scaled_dot_product_attention(qf[None], keys[None], keys[None, :, :512], scale=scale)[0]
+    assert np.allclose(o[0], ref.numpy(), rtol=1e-10, atol=1e-12)
+    logits = scale * (qf @ keys.T)
+    assert np.allclose(lse[0], torch.logsumexp(logits, dim=1).numpy(), rtol=1e-12)
+
+
+def test_fp8_attention_reduces_to_latent_attention_without_rope():
+    # power-of-two scales make every dequantised value an exact fp32, and zero RoPE values leave only <q_c, c>: the
+    # fp8 entry attention must equal the plain latent attention over an fp32 pool of those values
+    rng = np.random.default_rng(22)
+    n, H, page_size = 70, 4, 32
+    ent = _fp8_entries(rng, n + 26, pow2_scales=True, rope_zero=True)
+    f32_pool = np.stack([oracle.fp8_entry_key(e)[:512] for e in ent]).astype(np.float32)
+    assert np.array_equal(f32_pool.astype(np.float64), np.stack([oracle.fp8_entry_key(e)[:512] for e in ent]))
+    q = _bf16_bits(rng.standard_normal((2, H, 576)) * 0.05)
+    page_table = np.array([[2, 0, 1], [1, 2, 0]], np.int32)
+    sel = np.array([[5, 70, -1, 33, 0, 64], [1, 2, 3, 90, 95, -1]], np.int32)
+    row_seq = np.array([0, 1], np.int32)
+    o, lse = oracle.sparse_attn_fp8(q, ent, sel, row_seq, page_table, page_size, 0.7)
+    qc = oracle.decode(q, "bf16")[:, :, :512].astype(np.float32)
+    o2, lse2 = oracle.sparse_attn(qc, f32_pool, sel, row_seq, page_table, page_size, "f32", 0.7)
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-14) and np.allclose(lse, lse2, rtol=1e-12)
+    # an empty selection
+    o3, lse3 = oracle.sparse_attn_fp8(q[:1], ent, np.full((1, 4), -1, np.int32), row_seq[:1], page_table, page_size,
+                                      1.0)
+    assert not o3.any() and np.isneginf(lse3).all()
