@@ -62,8 +62,9 @@ typedef struct {
   int32_t num_seqs;      /* S: rows of page_table */
   int32_t idx_heads;     /* H_I: indexer heads.  F8E4M3: 32 or 64.  F32: 1..64 */
   int32_t idx_dim;       /* d_I: indexer head width.  F8E4M3: 64 or 128.  F32: 1..128 */
-  int32_t attn_heads;    /* H: attention heads sharing one latent row.  BF16: multiple of 16, <= 256.  F32: <= 256 */
-  int32_t latent_dim;    /* d_c: latent width.  BF16: 512.  F32: 1..1024 */
+  int32_t attn_heads;    /* H: attention heads sharing one latent row.  BF16, F8E4M3: multiple of 16, <= 256.
+                            F32: <= 256 */
+  int32_t latent_dim;    /* d_c: latent width.  BF16, F8E4M3: 512.  F32: 1..1024 */
   int32_t topk;          /* k: positions kept per row, 1..16384 */
   int32_t page_size;     /* positions per page: power of two, 32..4096 */
   int32_t max_pages;     /* row stride of page_table */
@@ -72,7 +73,8 @@ typedef struct {
   int32_t rows_per_seq;  /* >= 1.  Consecutive groups of this many rows share one sequence (a chunked prefill);
                             the caller guarantees row_seq is constant within each group.  1 for plain decode */
   int32_t idx_dtype;     /* dsa_dtype_t of q_idx / k_idx_pool: DSA_F8E4M3 (scales required) or DSA_F32 (scales NULL) */
-  int32_t kv_dtype;      /* dsa_dtype_t of q / kv_pool / out: DSA_BF16 or DSA_F32 */
+  int32_t kv_dtype;      /* dsa_dtype_t of the latent cache: DSA_BF16 or DSA_F32 (q, kv_pool and out in that type), or
+                            DSA_F8E4M3: 656-byte cache entries (see dsa_sparse_mla_attn), bf16 q and out */
   float softmax_scale;   /* logits = softmax_scale * <q[h], c[s]> */
 } dsa_problem_t;
 
@@ -122,6 +124,12 @@ dsa_status_t dsa_topk(const dsa_problem_t *problem, const dsa_layout_t *layout, 
  *   lse       [R, H] fp32 out (may be NULL): natural-log sum of exp(logits); -inf for an empty selection,
  *             whose output is 0
  * The bf16 path runs QK^T and PV on bf16 MFMA with fp32 accumulation and an fp32 online softmax.
+ * kv_dtype DSA_F8E4M3 (the FP8 cache of "What Does the GPU Actually Run?": 656 bytes per position): each kv_pool
+ * row holds 512 e4m3 latent codes (bytes 0..511), 4 fp32 scales, scale t for values 128t..128t+127 (bytes
+ * 512..527), and 64 bf16 RoPE values (bytes 528..655).  q is bf16 [R, H, 576] (latent dims, then RoPE dims) and
+ * the logits are softmax_scale * (<q[:512], code * scale> + <q[512:], rope>); out [R, H, 512] is the softmax-
+ * weighted sum of the dequantised latent rows.  The latent values are dequantised to bf16 on chip, as the bf16
+ * path then computes.
  */
 dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t *problem, const dsa_layout_t *layout, const void *q,
                                  const void *kv_pool, const int32_t *topk_idx, void *out, float *lse,

@@ -76,15 +76,16 @@ dsa_status_t check_problem(const dsa_problem_t* p, const dsa_layout_t* lay, bool
     }
   }
   if (need_attn) {
-    DSA_CHECK(p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_F32, DSA_EINVAL, "kv_dtype = %d invalid", p->kv_dtype);
+    DSA_CHECK(p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_F32 || p->kv_dtype == DSA_F8E4M3, DSA_EINVAL,
+              "kv_dtype = %d invalid", p->kv_dtype);
     DSA_CHECK(p->attn_heads >= 1 && p->attn_heads <= 256, DSA_EUNSUPPORTED, "attn_heads = %d not in 1..256",
               p->attn_heads);
     DSA_CHECK(p->softmax_scale == p->softmax_scale, DSA_EINVAL, "softmax_scale is NaN");
-    if (p->kv_dtype == DSA_BF16) {
-      DSA_CHECK(p->latent_dim == 512, DSA_EUNSUPPORTED, "bf16 attention needs latent_dim = 512 (got %d)",
+    if (p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_F8E4M3) {
+      DSA_CHECK(p->latent_dim == 512, DSA_EUNSUPPORTED, "bf16 and fp8-entry attention need latent_dim = 512 (got %d)",
                 p->latent_dim);
-      DSA_CHECK(p->attn_heads % 16 == 0, DSA_EUNSUPPORTED, "bf16 attention needs attn_heads %% 16 == 0 (got %d)",
-                p->attn_heads);
+      DSA_CHECK(p->attn_heads % 16 == 0, DSA_EUNSUPPORTED,
+                "bf16 and fp8-entry attention need attn_heads %% 16 == 0 (got %d)", p->attn_heads);
       DSA_CHECK((int64_t)p->num_pages * p->page_size < ((int64_t)1 << 31), DSA_EUNSUPPORTED,
                 "bf16 attention addresses latent rows with 31 bits (num_pages * page_size = %lld)",
                 (long long)p->num_pages * p->page_size);
@@ -162,9 +163,10 @@ int64_t step_ld(const dsa::Geo& g) { return ((int64_t)std::max(g.max_row_len, 1)
 
 // Dense attention is the sparse kernels with no selection list: slot s of row r is position s while s < n_r.
 // The selection width becomes the longest row (at least 1), within what the attention kernels take (the bf16
-// kernels split up to 131072 slots over their blocks; the fp32 kernel stages at most 4096 in LDS).
+// kernels (bf16 and fp8-entry latents) split up to 131072 slots over their blocks; the fp32 kernel stages at most
+// 4096 in LDS).
 dsa_status_t dense_geo(dsa::Geo* g) {
-  const int cap = g->kv_dtype == DSA_BF16 ? 131072 : 4096;
+  const int cap = g->kv_dtype == DSA_F32 ? 4096 : 131072;
   DSA_CHECK(g->max_row_len <= cap, DSA_EUNSUPPORTED, "dense attention supports max_row_len <= %d (got %d)", cap,
             g->max_row_len);
   g->k = std::max(1, g->max_row_len);

@@ -63,6 +63,50 @@ __device__ __forceinline__ void store_chunk_regs(char* buf, int wave, int lane, 
   for (int t = 0; t < 16; ++t) *reinterpret_cast<v4i*>(buf + (wave * 16 + t) * kRowB + lane * 16) = gv[t];
 }
 
+// FP8 latent entries of 656 bytes: 512 e4m3 codes, 4 fp32 scales (one per 128-value tile), 64 bf16 RoPE values.
+// Lane l loads codes 8l .. 8l+7 of each of the wave's 16 rows, the scale of their tile and RoPE value l; the store
+// writes the latent values code * scale, rounded to bf16, at the bf16 row layout (lane l: 16 bytes at 16 l) and
+// the RoPE values into rows of their own.
+constexpr int kF8Entry = 656;
+constexpr int kRope = 64;
+constexpr int kRopeRowB = kRope * 2 + 16;  // LDS row stride of the RoPE part (bytes)
+struct F8Rows {
+  uint2 codes[16];
+  float scale[16];
+  unsigned short rope[16];
+};
+__device__ __forceinline__ void load_chunk_fp8(const uint8_t* __restrict__ kv, const int32_t* prow, int dummy,
+                                               int wave, int lane, F8Rows& f) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    int pr = prow[wave * 16 + t];
+    if (pr < 0) pr = dummy;
+    const uint8_t* e = kv + (int64_t)pr * kF8Entry;
+    f.codes[t] = *reinterpret_cast<const uint2*>(e + lane * 8);
+    f.scale[t] = *reinterpret_cast<const float*>(e + 512 + 4 * (lane >> 4));
+    f.rope[t] = *reinterpret_cast<const unsigned short*>(e + 528 + 2 * lane);
+  }
+}
+__device__ __forceinline__ void store_chunk_fp8(char* buf, char* rope_buf, int wave, int lane, const F8Rows& f) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int word = (int)(h ? f.codes[t].y : f.codes[t].x);
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      v[4 * h + 0] = lo[0] * f.scale[t];
+      v[4 * h + 1] = lo[1] * f.scale[t];
+      v[4 * h + 2] = hi[0] * f.scale[t];
+      v[4 * h + 3] = hi[1] * f.scale[t];
+    }
+    const int row = wave * 16 + t;
+    *reinterpret_cast<v8bf*>(buf + row * kRowB + lane * 16) = pack8(v);
+    *reinterpret_cast<unsigned short*>(rope_buf + row * kRopeRowB + lane * 2) = f.rope[t];
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
 constexpr int kWaitVmOnly(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }  // vmcnt <= n only
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
@@ -155,7 +199,8 @@ __device__ __forceinline__ SlotSource slot_source(const int32_t* topk_idx, const
   return SlotSource{nullptr, clamp_len(row_len[r], max_row_len) - begin, begin, false};
 }
 
-template <bool kSplit>
+// kFp8: the latent rows are 656-byte FP8 entries and the queries 576 wide (latent, then RoPE dims).
+template <bool kSplit, bool kFp8>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
     int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_len, int max_row_len,
@@ -169,6 +214,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float s_lds[kHG][kNC + 4];
   __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
   __shared__ int wave_first[4];               // first slot with a position among each wave's slots
+  // RoPE rows of the FP8 path: read only by QK, so one buffer serves (a chunk's QK ends at its mid barrier, and
+  // the next chunk's rows are stored after it)
+  __shared__ __attribute__((aligned(16))) char rope_lds[kFp8 ? kNC * kRopeRowB : 16];
+  constexpr int kQW = kFp8 ? kDC + kRope : kDC;  // query width
 
   const int ngroups = H / kHG;
   const BlockWork bw = block_work(nsplit, ngroups);
@@ -195,12 +244,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     pr[j] = s < len ? src.at(s) : -1;
   }
 
-  // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8
+  // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8 (and the RoPE dims 512 + kd*32 + g*8 .. +8)
   v8bf qa[kDC / 32];
+  v8bf qr[kFp8 ? kRope / 32 : 1];
   {
-    const unsigned short* qrow = q + ((int64_t)r * H + grp16 * kHG + i) * kDC + g * 8;
+    const unsigned short* qrow = q + ((int64_t)r * H + grp16 * kHG + i) * kQW + g * 8;
 #pragma unroll
     for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 32);
+    if constexpr (kFp8)
+#pragma unroll
+      for (int kd = 0; kd < kRope / 32; ++kd) qr[kd] = *reinterpret_cast<const v8bf*>(qrow + kDC + kd * 32);
   }
 
   if (!src.physical)
@@ -232,9 +285,23 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const int dummy = prow_lds[first_valid];
     // one chunk: wait for its rows (the next chunk's gather stays in flight), then QK^T, softmax, PV.
     // `cur` and `nxt` are fixed per call site, so the compiler can tell the DMA target from the buffer read.
-    v4i gv[16];
+    const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
+    v4i gv[kFp8 ? 1 : 16];
+    F8Rows fv;
+    auto gather = [&](const int32_t* prow) __attribute__((always_inline)) {
+      if constexpr (kFp8)
+        load_chunk_fp8(kv8, prow, dummy, wave, lane, fv);
+      else
+        load_chunk_regs(kv, prow, dummy, wave, lane, gv);
+    };
+    auto place = [&](char* buf) __attribute__((always_inline)) {
+      if constexpr (kFp8)
+        store_chunk_fp8(buf, rope_lds, wave, lane, fv);
+      else
+        store_chunk_regs(buf, wave, lane, gv);
+    };
     auto chunk = [&](const int c, const char* cur, char* nxt) __attribute__((always_inline)) {
-      if (c + 1 < nch) load_chunk_regs(kv, prow_lds + (c + 1) * kNC, dummy, wave, lane, gv);
+      if (c + 1 < nch) gather(prow_lds + (c + 1) * kNC);
       // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
       v4f sacc = {0.f, 0.f, 0.f, 0.f};
       {
@@ -243,6 +310,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
         for (int kd = 0; kd < kDC / 32; ++kd) {
           const v8bf b = *reinterpret_cast<const v8bf*>(brow + kd * 64);
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kd], b, sacc, 0, 0, 0);
+        }
+        if constexpr (kFp8) {
+          const char* rrow = rope_lds + (wave * 16 + i) * kRopeRowB + g * 16;
+#pragma unroll
+          for (int kd = 0; kd < kRope / 32; ++kd) {
+            const v8bf b = *reinterpret_cast<const v8bf*>(rrow + kd * 64);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr[kd], b, sacc, 0, 0, 0);
+          }
         }
       }
       const bool valid = prow_lds[c * kNC + wave * 16 + i] >= 0;
@@ -298,11 +373,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[dt], 0, 0, 0);
         }
       }
-      if (c + 1 < nch) store_chunk_regs(nxt, wave, lane, gv);
+      if (c + 1 < nch) place(nxt);
       lds_barrier();  // every wave is done with `cur` and s_lds before they are overwritten; `nxt` is written
     };
-    load_chunk_regs(kv, prow_lds, dummy, wave, lane, gv);
-    store_chunk_regs(kv_lds0, wave, lane, gv);
+    gather(prow_lds);
+    place(kv_lds0);
     lds_barrier();
     for (int c = 0; c < nch; c += 2) {
       chunk(c, kv_lds0, kv_lds1);
@@ -799,9 +874,10 @@ struct AttnPlan {
 AttnPlan plan(const Geo& g) {
   const int chunks = std::max(1, (g.k + kNC - 1) / kNC);
   AttnPlan p{1, chunks * kNC, 0};
-  if (g.kv_dtype != 1 /* BF16 */) return p;
+  if (g.kv_dtype == 0 /* F32 */) return p;
   const int nw = g.H % 128 == 0 ? 4 : g.H % 64 == 0 ? 2 : 1;  // waves per block divide the 64 gathers of a chunk
-  if (g.H % 32 == 0 && (int64_t)g.R * (g.H / (32 * nw)) * chunks >= 128) {
+  // the all-heads kernel reads bf16 latent rows only; FP8 entries always take the 16-head kernel
+  if (g.kv_dtype == 1 && g.H % 32 == 0 && (int64_t)g.R * (g.H / (32 * nw)) * chunks >= 128) {
     // all-heads kernel: one block per (row, head group of <= 128, split), one block per CU at a time; split
     // the selection only as far as needed to give every CU a block.  With fewer than 128 (row, group, chunk)
     // units it could not spread over the chip, and the 16-head kernel below runs instead.
@@ -881,7 +957,8 @@ size_t attn_workspace_bytes(const Geo& g) {
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
                        float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
-  if (g.kv_dtype == 1 /* BF16 */) {
+  if (g.kv_dtype == 1 /* BF16 */ || g.kv_dtype == 2 /* FP8 entries */) {
+    const bool fp8 = g.kv_dtype == 2;
     const AttnPlan p = plan(g);
     const float scale_log2 = g.softmax_scale * kLog2e;
     auto* qp = static_cast<const unsigned short*>(q);
@@ -897,7 +974,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
       const int64_t units = (int64_t)g.R * (g.H / kHG);
       const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / kHG);
       if (p.nsplit == 1)
-        attn_bf16_kernel<false><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
+        (fp8 ? attn_bf16_kernel<false, true> : attn_bf16_kernel<false, false>)<<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
                                                              g.max_row_len, g.row_seq,
                                                              g.page_table,
                                                              g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
@@ -905,7 +982,7 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                              static_cast<unsigned short*>(out), lse, nullptr,
                                                              nullptr, nullptr);
       else
-        attn_bf16_kernel<true><<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
+        (fp8 ? attn_bf16_kernel<true, true> : attn_bf16_kernel<true, false>)<<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
                                                              g.max_row_len, g.row_seq,
                                                             g.page_table,
                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H,

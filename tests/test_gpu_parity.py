@@ -183,7 +183,7 @@ def _dense(cfg):
     d = upload(prob)
     P = dsa.make_problem(**d.fields)
     L = dsa.make_layout(d.row_seq, d.row_len, d.page_table)
-    out_dt = torch.bfloat16 if prob.kv_dtype == "bf16" else torch.float32
+    out_dt = torch.float32 if prob.kv_dtype == "f32" else torch.bfloat16
     out = torch.empty((prob.R, prob.H, prob.d_c), dtype=out_dt, device="cuda")
     lse = torch.empty((prob.R, prob.H), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(dsa.dsa_workspace_bytes(P, dsa.DSA_OP_DENSE), 256), dtype=torch.uint8, device="cuda")
@@ -203,6 +203,23 @@ def test_dense_attention_every_visible_position():
     _dense(synth.get("decode_128k", lengths=[60000], anchors=64, recent=96, H=32))   # 235 splits of 4 chunks
     _dense(synth.get("batched_paged", batch=4, lengths=[9000, 3000, 0, 1], H=128, anchors=8, recent=8))  # all heads
     _dense(synth.get("tiny_fp32", lengths=[1000, 4095], H=8))                         # fp32 path
+    _dense(synth.get("decode_128k", lengths=[7000], anchors=64, recent=96, kv_dtype="f8", H=32))  # fp8 entries
+
+
+# ----------------------------------------------------------------------------------- FP8 latent cache entries
+
+def test_fp8_latent_entries_decode_and_paged():
+    # 656-byte entries (e4m3 latent, 4 tile scales, bf16 RoPE) through the 16-head kernel: one long row with
+    # several splits, and a paged batch with an empty, a one-position and a short row; 16 and 32 heads
+    _run(synth.get("decode_128k", lengths=[20000], anchors=64, recent=96, kv_dtype="f8"))
+    _run(synth.get("batched_paged", batch=5, lengths=[0, 1, 1500, 6000, 9000], anchors=8, recent=8, kv_dtype="f8",
+                   H=16))
+    _run(synth.get("batched_paged", batch=3, length_range=(3000, 9000), kv_dtype="f8", H=32, k=512))
+
+
+def test_fp8_latent_full_size():
+    # the 128K decode workload over fp8 entries, checked element by element against the oracle
+    _sampled("decode_128k_fp8kv", lambda p: [0])
 
 
 # ------------------------------------------------------------------------------- top-k on crafted scores
