@@ -170,7 +170,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode_128k",
-                    choices=["decode_128k", "batched_paged", "decode_1m", "prefill_chunk", "decode_128k_di128"])
+                    choices=["decode_128k", "batched_paged", "decode_1m", "prefill_chunk", "decode_128k_di128",
+                             "decode_128k_fp8kv"])
     ap.add_argument("--copies", type=int, default=0, help="distinct input copies to rotate (0 = auto)")
     ap.add_argument("--phase-iters", type=int, default=400)
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,
@@ -215,7 +216,8 @@ def main() -> int:
 
     # distinct copies of every per-step input, enough to exceed the 256 MiB Infinity Cache several times
     prefill = prob.rows_per_seq > 1
-    touched = sum(cost.decode_row_bytes(int(n), prob.k, prob.H_I, prob.d_I, prob.H, prob.d_c) for n in prob.row_len)
+    touched = sum(cost.decode_row_bytes(int(n), prob.k, prob.H_I, prob.d_I, prob.H, prob.d_c,
+                                        fp8_entries=prob.kv_dtype == "f8") for n in prob.row_len)
     copies = args.copies or (2 if prefill else max(2, min(64, int(np.ceil(3 * 256e6 / touched)))))
     names = ["q_idx", "q_idx_scale", "head_w", "k_idx_pool", "k_idx_scale", "q", "kv_pool"]
     sets = [{n: getattr(base, n) for n in names}]
@@ -334,7 +336,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-indexer/bf16-attention",
+        "dtype": "fp8e4m3-indexer/fp8e4m3-latent-bf16-attention" if prob.kv_dtype == "f8"
+                 else "fp8e4m3-indexer/bf16-attention",
         "data": "synthetic",
         "config": {"workload": args.workload, "rows": R, "context": int(prob.max_row_len), "k": prob.k,
                    "H_I": prob.H_I, "d_I": prob.d_I, "H": prob.H, "d_c": prob.d_c, "page_size": prob.page_size,

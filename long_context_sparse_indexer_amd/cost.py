@@ -64,14 +64,21 @@ def decode_kv_read_bytes(n: int, k: int, layers: int, entry_bytes: int, key_byte
 
 # ----------------------------------------------------------------- this library's decode row, one layer
 
+FP8_ENTRY_BYTES = 656  # 512 e4m3 latent values + 4 fp32 tile scales + 64 bf16 RoPE values
+FP8_QUERY_WIDTH = 576  # latent dims + RoPE dims
+
+
 def decode_row_bytes(n: int, k: int, H_I: int = 64, d_I: int = 64, H: int = 128, d_c: int = 512,
-                     kv_bytes: int = 2, idx_code_bytes: int = 1) -> int:
+                     kv_bytes: int = 2, idx_code_bytes: int = 1, fp8_entries: bool = False) -> int:
     """Algorithmic HBM bytes of one decode row: indexer keys + scales, indexer query + scales + weights,
-    the k_eff gathered latent rows, and the attention query in / output out."""
+    the k_eff gathered latent rows, and the attention query in / output out.  fp8_entries: the latent cache holds
+    656-byte FP8 entries and the bf16 query is 576 wide."""
     keff = min(k, n)
     scale = 4 if idx_code_bytes == 1 else 0
-    return (n * (d_I * idx_code_bytes + scale) + H_I * (d_I * idx_code_bytes + scale + 4)
-            + keff * d_c * kv_bytes + 2 * H * d_c * kv_bytes)
+    indexer = n * (d_I * idx_code_bytes + scale) + H_I * (d_I * idx_code_bytes + scale + 4)
+    if fp8_entries:
+        return indexer + keff * FP8_ENTRY_BYTES + H * (FP8_QUERY_WIDTH + d_c) * 2
+    return indexer + keff * d_c * kv_bytes + 2 * H * d_c * kv_bytes
 
 
 def indexer_row_bytes(n: int, H_I: int = 64, d_I: int = 64, idx_code_bytes: int = 1) -> int:

@@ -54,4 +54,6 @@ def test_decode_row_bytes_of_the_128k_workload():
     b = cost.decode_row_bytes(131_072, 2_048)
     assert b == 131_072 * 68 + 64 * 72 + 2_048 * 1_024 + 2 * 128 * 1_024 == 11_276_800
     assert cost.decode_row_bytes(100, 2_048) == 100 * 68 + 64 * 72 + 100 * 1_024 + 2 * 128 * 1_024
+    # FP8 latent entries: 656 bytes gathered per selected position, a 576-wide query in and 512-wide output out
+    assert cost.decode_row_bytes(100, 2_048, fp8_entries=True) == 100 * 68 + 64 * 72 + 100 * 656 + 128 * 1_088 * 2
     assert math.isclose(cost.attention_row_flops(2048, 131072) / 1e6, 536.870912)
