@@ -64,12 +64,15 @@ __device__ __forceinline__ void store_chunk_regs(char* buf, int wave, int lane, 
 }
 
 // FP8 latent entries of 656 bytes: 512 e4m3 codes, 4 fp32 scales (one per 128-value tile), 64 bf16 RoPE values.
-// Lane l loads codes 8l .. 8l+7 of each of the wave's 16 rows, the scale of their tile and RoPE value l; the store
-// writes the latent values code * scale, rounded to bf16, at the bf16 row layout (lane l: 16 bytes at 16 l) and
-// the RoPE values into rows of their own.
+// Lane l loads codes 8l .. 8l+7 of each of the wave's 16 rows, the scale of their tile and RoPE value l.  The
+// store widens the codes to bf16, which is exact, at the bf16 row layout (lane l: 16 bytes at 16 l); the scales
+// go to a [tile][slot] table and the RoPE values into rows of their own.  The scales are applied outside the
+// MFMAs: QK accumulates each 128-dim tile apart and sums the four with the slot's scales, and PV multiplies each
+// slot's probability by its scale for the tile of the wave's 128 output columns.  No dequantised value is ever
+// rounded.
 constexpr int kF8Entry = 656;
 constexpr int kRope = 64;
-constexpr int kRopeRowB = kRope * 2 + 16;  // LDS row stride of the RoPE part (bytes)
+constexpr int kRopeRowB = kRope * 2;  // LDS row stride of the RoPE part (bytes)
 struct F8Rows {
   uint2 codes[16];
   float scale[16];
@@ -87,23 +90,18 @@ __device__ __forceinline__ void load_chunk_fp8(const uint8_t* __restrict__ kv, c
     f.rope[t] = *reinterpret_cast<const unsigned short*>(e + 528 + 2 * lane);
   }
 }
-__device__ __forceinline__ void store_chunk_fp8(char* buf, char* rope_buf, int wave, int lane, const F8Rows& f) {
+__device__ __forceinline__ void store_chunk_fp8(char* buf, char* rope_buf, float* scale_buf, int wave, int lane,
+                                                const F8Rows& f) {
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    float v[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int word = (int)(h ? f.codes[t].y : f.codes[t].x);
-      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-      v[4 * h + 0] = lo[0] * f.scale[t];
-      v[4 * h + 1] = lo[1] * f.scale[t];
-      v[4 * h + 2] = hi[0] * f.scale[t];
-      v[4 * h + 3] = hi[1] * f.scale[t];
-    }
+    const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].x, 1.f, false);
+    const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].x, 1.f, true);
+    const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].y, 1.f, false);
+    const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].y, 1.f, true);
     const int row = wave * 16 + t;
-    *reinterpret_cast<v8bf*>(buf + row * kRowB + lane * 16) = pack8(v);
+    *reinterpret_cast<v8bf*>(buf + row * kRowB + lane * 16) = v8bf{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
     *reinterpret_cast<unsigned short*>(rope_buf + row * kRopeRowB + lane * 2) = f.rope[t];
+    if ((lane & 15) == 0) scale_buf[(lane >> 4) * kNC + row] = f.scale[t];
   }
 }
 
@@ -217,6 +215,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   // RoPE rows of the FP8 path: read only by QK, so one buffer serves (a chunk's QK ends at its mid barrier, and
   // the next chunk's rows are stored after it)
   __shared__ __attribute__((aligned(16))) char rope_lds[kFp8 ? kNC * kRopeRowB : 16];
+  __shared__ __attribute__((aligned(16))) float scale_lds[kFp8 ? 4 * kNC : 4];  // [tile][slot], same lifetime:
+  // every read of a chunk's scales happens before its mid barrier
   constexpr int kQW = kFp8 ? kDC + kRope : kDC;  // query width
 
   const int ngroups = H / kHG;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     };
     auto place = [&](char* buf) __attribute__((always_inline)) {
       if constexpr (kFp8)
-        store_chunk_fp8(buf, rope_lds, wave, lane, fv);
+        store_chunk_fp8(buf, rope_lds, scale_lds, wave, lane, fv);
       else
         store_chunk_regs(buf, wave, lane, gv);
     };
@@ -304,20 +304,38 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       if (c + 1 < nch) gather(prow_lds + (c + 1) * kNC);
       // S for slots wave*16 + (0..15): B operand = row (wave*16 + i), d = kd*32 + g*8 .. +8
       v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      {
+      v4f pvs[kFp8 ? 4 : 1];  // FP8: the PV scales, read before the mid-chunk barrier (the table is rewritten after)
+      if constexpr (!kFp8) {
         const char* brow = cur + (wave * 16 + i) * kRowB + g * 16;
 #pragma unroll
         for (int kd = 0; kd < kDC / 32; ++kd) {
           const v8bf b = *reinterpret_cast<const v8bf*>(brow + kd * 64);
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kd], b, sacc, 0, 0, 0);
         }
-        if constexpr (kFp8) {
-          const char* rrow = rope_lds + (wave * 16 + i) * kRopeRowB + g * 16;
+      } else {
+        // one accumulator per 128-dim tile of codes, then the RoPE dims; the lane's slot is wave*16 + i
+        v4f st[4] = {};
+        const char* brow = cur + (wave * 16 + i) * kRowB + g * 16;
 #pragma unroll
-          for (int kd = 0; kd < kRope / 32; ++kd) {
-            const v8bf b = *reinterpret_cast<const v8bf*>(rrow + kd * 64);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr[kd], b, sacc, 0, 0, 0);
-          }
+        for (int kd = 0; kd < kDC / 32; ++kd) {
+          const v8bf b = *reinterpret_cast<const v8bf*>(brow + kd * 64);
+          st[kd >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kd], b, st[kd >> 2], 0, 0, 0);
+        }
+        const char* rrow = rope_lds + (wave * 16 + i) * kRopeRowB + g * 16;
+#pragma unroll
+        for (int kd = 0; kd < kRope / 32; ++kd) {
+          const v8bf b = *reinterpret_cast<const v8bf*>(rrow + kd * 64);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr[kd], b, sacc, 0, 0, 0);
+        }
+        const float* sl = scale_lds + wave * 16 + i;
+        const float s0 = sl[0], s1 = sl[kNC], s2 = sl[2 * kNC], s3 = sl[3 * kNC];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sacc[v] = fmaf(st[3][v], s3, fmaf(st[2][v], s2, fmaf(st[1][v], s1, fmaf(st[0][v], s0, sacc[v]))));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pvs[2 * kk] = *reinterpret_cast<const v4f*>(&scale_lds[wave * kNC + kk * 32 + 8 * g]);
+          pvs[2 * kk + 1] = *reinterpret_cast<const v4f*>(&scale_lds[wave * kNC + kk * 32 + 8 * g + 4]);
         }
       }
       const bool valid = prow_lds[c * kNC + wave * 16 + i] >= 0;
@@ -358,6 +376,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
         }
 
       // O += P V.  A operand element e of K-step kk is slot kk*32 + 8g + perm[e], perm = {0,2,4,6,1,3,5,7}.
+      // FP8 entries: the wave's 128 output columns are tile `wave`, so each probability takes its slot's scale
+      // for that tile
+      if constexpr (kFp8)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[kk * 8 + e] *= pvs[2 * kk][e];
+            sv[kk * 8 + 4 + e] *= pvs[2 * kk + 1][e];
+          }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const float pe[8] = {sv[kk * 8 + 0], sv[kk * 8 + 2], sv[kk * 8 + 4], sv[kk * 8 + 6],

@@ -27,7 +27,8 @@ from synth.device import upload
 
 U32 = 2.0 ** -24
 TIE_BAND = 1e-3
-# fp8 latent entries: the dequantised latent is rounded to bf16 on chip (2^-9 relative), then the bf16 path runs
+# fp8 latent entries: exact products as in the bf16 path (codes widened to bf16 exactly, scales applied in fp32);
+# the probability times its scale is rounded to bf16 for PV as the probability alone is in the bf16 path
 ATOL = {"bf16": 2e-2, "f32": 1e-4, "f8": 2e-2}
 
 
@@ -154,29 +155,9 @@ def check_attention(prob, out, lse, idx):
     fin = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(lse), fin), "lse finiteness differs"
     if fin.any():
-        ltol = 1e-3 + (fp8_logit_bound(prob, idx) if prob.kv_dtype == "f8" else 0.0)
-        lerr = np.where(fin, np.abs(lse - ref_lse), 0.0)
-        assert (lerr <= ltol).all(), f"lse error {float(lerr.max()):.3e} over its bound"
+        lerr = float(np.abs(lse[fin] - ref_lse[fin]).max())
+        assert lerr <= 1e-3, f"lse error {lerr:.3e}"
     return err
-
-
-def fp8_logit_bound(prob, idx):
-    """[R, H] bound on the logit change from rounding the dequantised fp8 latent to bf16 on chip (half an ulp,
-    2^-9 relative): softmax_scale * max over the selected rows of sum_d |q_d| |c_d| * 2^-9.  The lse moves by at
-    most the largest logit change."""
-    out = np.zeros((prob.R, prob.H))
-    for r in range(prob.R):
-        sel = idx[r][idx[r] >= 0].astype(np.int64)
-        if sel.size == 0:
-            continue
-        phys = (prob.page_table[prob.row_seq[r], sel // prob.page_size].astype(np.int64) * prob.page_size
-                + sel % prob.page_size)
-        ent = prob.kv_pool[phys]
-        scales = np.ascontiguousarray(ent[:, 512:528]).view(np.float32).astype(np.float64)  # [m, 4]
-        c = np.abs(oracle.decode(ent[:, :512], "f8")) * np.repeat(scales, 128, axis=1)
-        q = np.abs(oracle.decode(prob.q[r][:, :512], "bf16"))
-        out[r] = abs(prob.softmax_scale) * (q @ c.T).max(axis=1) * 2.0 ** -9
-    return out
 
 
 def check_selection_valid(prob, gpu_idx):
