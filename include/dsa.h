@@ -157,7 +157,7 @@ dsa_status_t dsa_decode_step(const dsa_problem_t *problem, const dsa_layout_t *l
  *   q, kv_pool, out, lse as for dsa_sparse_mla_attn
  *   workspace >= dsa_workspace_bytes(problem, DSA_OP_DENSE) (split partials; 0 bytes, and workspace may be
  *               NULL, when every row fits one block)
- * Supported up to max_row_len = 131072 for bf16 latents and 4096 for fp32 (DSA_EUNSUPPORTED above).
+ * Supported up to max_row_len = 131072 for bf16 latents and FP8 entries, 4096 for fp32 (DSA_EUNSUPPORTED above).
  */
 dsa_status_t dsa_dense_mla_attn(const dsa_problem_t *problem, const dsa_layout_t *layout, const void *q,
                                 const void *kv_pool, void *out, float *lse, void *workspace,
