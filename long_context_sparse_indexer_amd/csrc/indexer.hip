@@ -223,17 +223,18 @@ constexpr int kPfSub = 4;                 // 32-position subtiles per wave
 constexpr int kPfTile = 4 * kPfSub * 32;  // positions per pass of a 256-thread block
 constexpr int kPfPasses = 8;              // passes per block: the row staging is paid once per 4096 positions
 
-template <int HB>
-__global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
+// KB = d_I / 64 K blocks: each (head block, subtile) unit chains KB fp8 MFMAs, the linear MFMA takes 4 KB K-steps.
+template <int HB, int KB>
+__global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, int R, int rows_per_seq, int tiles_per_group,
     float* __restrict__ scores, int64_t ld) {
-  constexpr int H_I = 32 * HB;
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32];    // lane l's fp8 A operand
-  __shared__ __attribute__((aligned(16))) float w_lds[kPfRows][HB][2][16];       // wq of each lane half's heads
-  __shared__ __attribute__((aligned(16))) __bf16 u_lds[kPfRows / 8][4][64][8];   // linear-MFMA A operands
+  constexpr int H_I = 32 * HB, D = 64 * KB;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32 * KB];  // lane l's fp8 A operands
+  __shared__ __attribute__((aligned(16))) float w_lds[kPfRows][HB][2][16];          // wq of each lane half's heads
+  __shared__ __attribute__((aligned(16))) __bf16 u_lds[kPfRows / 8][4 * KB][64][8];  // linear-MFMA A operands
   __shared__ __attribute__((aligned(16))) int n_lds[kPfRows];
   const int group = (int)blockIdx.y / tiles_per_group;
   const int r0 = group * rows_per_seq + ((int)blockIdx.y % tiles_per_group) * kPfRows;
@@ -250,19 +251,21 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r0], num_seqs);  // shared by the group's rows
 
-  // stage the rows' A operands (16-byte pieces: c = (q * HB + hb) * 128 + l * 2 + piece) and epilogue weights;
-  // every load is issued before the first LDS write so the block pays one memory round trip, not one per piece
+  // stage the rows' A operands (16-byte pieces: c = ((q * HB + hb) * KB + kb) * 128 + l * 2 + piece; K block kb
+  // of lane l holds query bytes 64 kb + 32 (l / 32) .. +32 of head l % 32) and epilogue weights; every load is
+  // issued before the first LDS write so the block pays one memory round trip, not one per piece
   {
-    constexpr int kA = kPfRows * HB * 128 / 256;  // A pieces per thread
+    constexpr int kA = kPfRows * HB * KB * 128 / 256;  // A pieces per thread
     constexpr int kW = kPfRows * H_I / 256;       // weights per thread
     v4i av[kA];
     float wv[kW], sv[kW];
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
+      const int q = c / (HB * KB * 128), hb = (c / (KB * 128)) % HB, kb = (c / 128) % KB, l = (c >> 1) & 63,
+                piece = c & 1;
       if (q < rows)
-        av[i] = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)(r0 + q) * H_I + hb * 32 + (l & 31)) * 64 +
+        av[i] = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)(r0 + q) * H_I + hb * 32 + (l & 31)) * D + kb * 64 +
                                               (l >> 5) * 32 + piece * 16);
     }
 #pragma unroll
@@ -276,8 +279,9 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const int q = c / (HB * 128), hb = (c / 128) % HB, l = (c >> 1) & 63, piece = c & 1;
-      if (q < rows) *reinterpret_cast<v4i*>(&a_lds[q][hb][l][piece * 16]) = av[i];
+      const int q = c / (HB * KB * 128), hb = (c / (KB * 128)) % HB, kb = (c / 128) % KB, l = (c >> 1) & 63,
+                piece = c & 1;
+      if (q < rows) *reinterpret_cast<v4i*>(&a_lds[q][hb][l][kb * 32 + piece * 16]) = av[i];
     }
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
@@ -288,9 +292,10 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
   }
   __syncthreads();
 
-  // u[q][d] = sum_j wq_j q8[q][j][d] in fp32, split into bf16 pieces placed as linear-MFMA A operands
+  // u[q][d] = sum_j wq_j q8[q][j][d] in fp32, split into bf16 pieces placed as linear-MFMA A operands; dim
+  // d = 64 kb + dd sits in K block kb, lane half dd / 32, byte dd % 32
   {
-    constexpr int kTpr = 256 / kPfRows, kDpt = 64 / kTpr;  // threads per row, dims per thread
+    constexpr int kTpr = 256 / kPfRows, kDpt = D / kTpr;  // threads per row, dims per thread
     const int q = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * kDpt;
     float u[kDpt];
 #pragma unroll
@@ -300,7 +305,9 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
         const float w = w_lds[q][j >> 5][(j >> 2) & 1][(j & 3) + 4 * ((j >> 3) & 3)];
 #pragma unroll
         for (int t = 0; t < kDpt; t += 2) {
-          const uint16_t codes = *reinterpret_cast<const uint16_t*>(&a_lds[q][j >> 5][((d0 + t) >> 5) * 32 + (j & 31)][(d0 + t) & 31]);
+          const int d = d0 + t, dd = d & 63;
+          const uint16_t codes =
+              *reinterpret_cast<const uint16_t*>(&a_lds[q][j >> 5][(dd >> 5) * 32 + (j & 31)][(d >> 6) * 32 + (dd & 31)]);
           const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)codes, 1.f, false);
           u[t] = fmaf(w, x.x, u[t]);
           u[t + 1] = fmaf(w, x.y, u[t + 1]);
@@ -315,14 +322,15 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
       for (int c = 0; c < 4; ++c) {
         const __bf16 p = (__bf16)rest;  // round to nearest even; rest - p is exact
         rest -= (float)p;
-        u_lds[q >> 3][(d >> 3) & 3][(d >> 5) * 32 + 8 * c + (q & 7)][d & 7] = p;
+        // K-step 4 kb + m, lane half h covers dims 64 kb + 32 h + 8 m .. +8
+        u_lds[q >> 3][(d >> 6) * 4 + ((d >> 3) & 3)][((d >> 5) & 1) * 32 + 8 * c + (q & 7)][d & 7] = p;
       }
     }
   }
   __syncthreads();
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  v8i b[kPfSub];
+  v8i b[kPfSub][KB];
   for (int pass = 0; pass < kPfPasses; ++pass) {
     const int64_t tile0 = span0 + (int64_t)pass * kPfTile;
     if (tile0 >= nmax) break;  // uniform
@@ -342,7 +350,10 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
       prow[s] = row0 + (base < nmax ? min((int64_t)col, nmax - 1 - base) : 0);
     }
 #pragma unroll
-    for (int s = 0; s < kPfSub; ++s) b[s] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * 64 + half * 32);
+    for (int s = 0; s < kPfSub; ++s)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        b[s][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[s] * D + kb * 64 + half * 32);
 
     // per pass, per lane: half 0 stores subtile 2p and half 1 subtile 2p + 1 of each pair p; 0.5 sk of that
     // position (the 1/2 of (lin + abs) folded in, exact) and its byte offset within the row
@@ -370,15 +381,17 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
           const int s = 2 * p + t;
           v16f acc = {};
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, false);
-            const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m], 1.f, true);
-            const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, false);
-            const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][2 * m + 1], 1.f, true);
-            const v8bf kb = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(&u_lds[g][m][lane][0]), kb,
-                                                          acc, 0, 0, 0);
-          }
+          for (int kq = 0; kq < KB; ++kq)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][kq][2 * m], 1.f, false);
+              const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][kq][2 * m], 1.f, true);
+              const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][kq][2 * m + 1], 1.f, false);
+              const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)b[s][kq][2 * m + 1], 1.f, true);
+              const v8bf kv8 = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  *reinterpret_cast<const v8bf*>(&u_lds[g][kq * 4 + m][lane][0]), kv8, acc, 0, 0, 0);
+            }
 #pragma unroll
           for (int e = 0; e < 4; ++e) lin[t][e] = ((acc[12 + e] + acc[8 + e]) + acc[4 + e]) + acc[e];
         }
@@ -401,11 +414,12 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
         for (int e = 0; e < 4; ++e) {
           const int q = 8 * g + 4 * hq + e;
           if (tile0 >= nq[e]) continue;  // uniform; also rows past the tile's end
-          v8i a[HB];
+          v8i a[HB][KB];
           float wq[HB][16];
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
-            a[hb] = *reinterpret_cast<const v8i*>(&a_lds[q][hb][lane][0]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) a[hb][kb] = *reinterpret_cast<const v8i*>(&a_lds[q][hb][lane][kb * 32]);
 #pragma unroll
             for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
           }
@@ -415,13 +429,21 @@ __global__ __launch_bounds__(256, 3) void indexer_f8_tiled_kernel(
           constexpr int U = 2 * HB;             // units per subtile pair
           constexpr int K = (kPfSub / 2) * U;   // units per row
           float ab[2] = {0.f, 0.f};
-          v16f prev = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], b[0], v16f{}, 0, 0, 0, 0, 0, 0);
+          // one unit: KB chained fp8 MFMAs over the K blocks
+          auto unit = [&](int hb, int s) __attribute__((always_inline)) {
+            v16f x = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb][0], b[s][0], v16f{}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb)
+              x = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb][kb], b[s][kb], x, 0, 0, 0, 0, 0, 0);
+            return x;
+          };
+          v16f prev = unit(0, 0);
 #pragma unroll
           for (int k = 1; k <= K; ++k) {
             v16f next;
             if (k < K) {
               const int p = k / U, hb = (k % U) >> 1, t = k & 1;
-              next = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[hb], b[2 * p + t], v16f{}, 0, 0, 0, 0, 0, 0);
+              next = unit(hb, 2 * p + t);
             }
             __builtin_amdgcn_sched_barrier(0);
             {
@@ -496,20 +518,20 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
       g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr}, per);
 }
 
-template <int HB>
+template <int HB, int KB>
 void launch_f8_tiled(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w,
                      const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, hipStream_t stream) {
   const int tiles_per_group = (g.rows_per_seq + kPfRows - 1) / kPfRows;
   const int groups = (g.R + g.rows_per_seq - 1) / g.rows_per_seq;
   dim3 grid((g.max_row_len + kPfPasses * kPfTile - 1) / (kPfPasses * kPfTile), groups * tiles_per_group);
-  indexer_f8_tiled_kernel<HB><<<grid, 256, 0, stream>>>(
+  indexer_f8_tiled_kernel<HB, KB><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
       g.log2ps, g.max_row_len, g.R, g.rows_per_seq, tiles_per_group, scores, ld);
 }
 
-// the tiled kernel is written for d_I = 64; other fp8 shapes take the per-row kernel for every row
+// fp8 rows that come in groups sharing a sequence take the tiled kernel (d_I = 64 or 128)
 bool indexer_tiled(const Geo& g) {
-  return g.idx_dtype == 2 /* F8E4M3 */ && g.d_I == 64 && g.rows_per_seq >= kTiledMinRows;
+  return g.idx_dtype == 2 /* F8E4M3 */ && (g.d_I == 64 || g.d_I == 128) && g.rows_per_seq >= kTiledMinRows;
 }
 
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
@@ -520,8 +542,14 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
     if (fuse) return hipErrorInvalidValue;  // the tiled kernel does not clear the top-k state
     auto* qp = static_cast<const uint8_t*>(q_idx);
     auto* kp = static_cast<const uint8_t*>(k_idx_pool);
-    if (g.H_I == 64) launch_f8_tiled<2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
-    else launch_f8_tiled<1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    if (g.d_I == 128) {
+      if (g.H_I == 64) launch_f8_tiled<2, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+      else launch_f8_tiled<1, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    } else if (g.H_I == 64) {
+      launch_f8_tiled<2, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    } else {
+      launch_f8_tiled<1, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
+    }
     return hipGetLastError();
   }
   if (g.idx_dtype == 2 /* F8E4M3 */) {

@@ -108,6 +108,13 @@ def test_prefill_tiled_row_groups(rows, H_I):
     _run(synth.get("prefill_paged", rows=rows, H_I=H_I, batch=2, k=700, H=16))
 
 
+@pytest.mark.parametrize("rows,H_I", [(8, 64), (9, 64), (23, 32)])
+def test_prefill_tiled_index_dim_128(rows, H_I):
+    # the shipped 64 x 128 indexer keys through the tiled kernel: two chained fp8 MFMAs per unit and a 128-wide
+    # linear term over eight bf16 K-steps
+    _run(synth.get("prefill_paged", rows=rows, H_I=H_I, batch=2, k=700, H=16, d_I=128))
+
+
 def test_prefill_rows_through_the_per_row_kernel():
     # the same prefill chunk declared as independent rows runs the per-row kernel and must agree as well
     _run(synth.get("prefill_paged", rows=20, H=16), fields=dict(rows_per_seq=1))
@@ -215,6 +222,13 @@ def test_fp8_latent_entries_decode_and_paged():
     _run(synth.get("batched_paged", batch=5, lengths=[0, 1, 1500, 6000, 9000], anchors=8, recent=8, kv_dtype="f8",
                    H=16))
     _run(synth.get("batched_paged", batch=3, length_range=(3000, 9000), kv_dtype="f8", H=32, k=512))
+
+
+def test_fp8_latent_with_prefill_rows_and_wide_index_keys():
+    # FP8 entries under chunked-prefill rows (the tiled indexer, rows of one sequence) and with the shipped
+    # 64 x 128 indexer keys over a paged batch
+    _run(synth.get("prefill_chunk", cache_len=6000, rows=24, H=32, kv_dtype="f8"))
+    _run(synth.get("batched_paged", batch=3, length_range=(3000, 9000), d_I=128, k=1024, H=32, kv_dtype="f8"))
 
 
 def test_fp8_latent_full_size():
