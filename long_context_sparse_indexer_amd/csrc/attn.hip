@@ -64,45 +64,55 @@ __device__ __forceinline__ void store_chunk_regs(char* buf, int wave, int lane, 
 }
 
 // FP8 latent entries of 656 bytes: 512 e4m3 codes, 4 fp32 scales (one per 128-value tile), 64 bf16 RoPE values.
-// Lane l loads codes 8l .. 8l+7 of each of the wave's 16 rows, the scale of their tile and RoPE value l.  The
-// store widens the codes to bf16, which is exact, at the bf16 row layout (lane l: 16 bytes at 16 l); the scales
-// go to a [tile][slot] table and the RoPE values into rows of their own.  The scales are applied outside the
-// MFMAs: QK accumulates each 128-dim tile apart and sums the four with the slot's scales, and PV multiplies each
-// slot's probability by its scale for the tile of the wave's 128 output columns.  No dequantised value is ever
-// rounded.
+// The wave's 16 rows arrive in 11 loads per lane: load t (8 of them) gives lane l codes 16 (l % 32) .. +16 of
+// row 2t + l / 32, one load gives lane l scale l % 4 of row l / 4, and two give lane l RoPE bytes 16 (l % 8) ..
+// +16 of row 8j + l / 8.  The store widens the codes to bf16, which is exact, at the bf16 row layout (32 bytes
+// at 32 (l % 32)); the scales go to a [tile][slot] table and the RoPE values into rows of their own.  The
+// scales are applied outside the MFMAs: QK accumulates each 128-dim tile apart and sums the four with the slot's
+// scales, and PV multiplies each slot's probability by its scale for the tile of the wave's 128 output columns.
+// No dequantised value is ever rounded.
 constexpr int kF8Entry = 656;
 constexpr int kRope = 64;
 constexpr int kRopeRowB = kRope * 2;  // LDS row stride of the RoPE part (bytes)
 struct F8Rows {
-  uint2 codes[16];
-  float scale[16];
-  unsigned short rope[16];
+  v4i codes[8];
+  float scale;
+  v4i rope[2];
 };
 __device__ __forceinline__ void load_chunk_fp8(const uint8_t* __restrict__ kv, const int32_t* prow, int dummy,
                                                int wave, int lane, F8Rows& f) {
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    int pr = prow[wave * 16 + t];
+  auto entry = [&](int row) {
+    int pr = prow[wave * 16 + row];
     if (pr < 0) pr = dummy;
-    const uint8_t* e = kv + (int64_t)pr * kF8Entry;
-    f.codes[t] = *reinterpret_cast<const uint2*>(e + lane * 8);
-    f.scale[t] = *reinterpret_cast<const float*>(e + 512 + 4 * (lane >> 4));
-    f.rope[t] = *reinterpret_cast<const unsigned short*>(e + 528 + 2 * lane);
-  }
+    return kv + (int64_t)pr * kF8Entry;
+  };
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    f.codes[t] = *reinterpret_cast<const v4i*>(entry(2 * t + (lane >> 5)) + (lane & 31) * 16);
+  f.scale = *reinterpret_cast<const float*>(entry(lane >> 2) + 512 + 4 * (lane & 3));
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    f.rope[j] = *reinterpret_cast<const v4i*>(entry(8 * j + (lane >> 3)) + 528 + 16 * (lane & 7));
 }
 __device__ __forceinline__ void store_chunk_fp8(char* buf, char* rope_buf, float* scale_buf, int wave, int lane,
                                                 const F8Rows& f) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].x, 1.f, false);
-    const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].x, 1.f, true);
-    const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].y, 1.f, false);
-    const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t].y, 1.f, true);
-    const int row = wave * 16 + t;
-    *reinterpret_cast<v8bf*>(buf + row * kRowB + lane * 16) = v8bf{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
-    *reinterpret_cast<unsigned short*>(rope_buf + row * kRopeRowB + lane * 2) = f.rope[t];
-    if ((lane & 15) == 0) scale_buf[(lane >> 4) * kNC + row] = f.scale[t];
+  for (int t = 0; t < 8; ++t) {
+    const int row = wave * 16 + 2 * t + (lane >> 5);
+    char* dst = buf + row * kRowB + (lane & 31) * 32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t][2 * h], 1.f, false);
+      const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t][2 * h], 1.f, true);
+      const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t][2 * h + 1], 1.f, false);
+      const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.codes[t][2 * h + 1], 1.f, true);
+      *reinterpret_cast<v8bf*>(dst + 16 * h) = v8bf{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+    }
   }
+  scale_buf[(lane & 3) * kNC + wave * 16 + (lane >> 2)] = f.scale;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *reinterpret_cast<v4i*>(rope_buf + (wave * 16 + 8 * j + (lane >> 3)) * kRopeRowB + 16 * (lane & 7)) = f.rope[j];
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
