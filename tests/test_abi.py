@@ -184,3 +184,14 @@ def test_key_append_validation():
     assert "latent_dim" in dsa.dsa_last_error()
     assert call(p=_problem(idx_dim=96)) == dsa.DSA_EUNSUPPORTED  # the fp8 cache widths of the indexer
     assert call(w=None, src=FAKE + 2) == dsa.DSA_EINVAL and "4-byte" in dsa.dsa_last_error()
+
+
+def test_zero_rows_enqueue_nothing():
+    # R = 0 is valid everywhere and returns before any HIP call (no GPU needed)
+    L = dsa.lib()
+    p = _problem(num_rows=0, idx_dim=128)
+    assert L.dsa_indexer_key_append(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
+    assert L.dsa_indexer_key_append(ctypes.byref(p), ctypes.byref(LAYOUT), FAKE, FAKE, None, FAKE, FAKE, None) == 0
+    pf = _problem(num_rows=0, kv_dtype="f8")
+    assert dsa.dsa_workspace_bytes(pf, dsa.DSA_OP_DENSE) == 0
+    assert L.dsa_dense_mla_attn(ctypes.byref(pf), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, None, None, 0, None) == 0
