@@ -171,7 +171,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode_128k",
                     choices=["decode_128k", "batched_paged", "decode_1m", "prefill_chunk", "decode_128k_di128",
-                             "decode_128k_fp8kv", "prefill_chunk_di128"])
+                             "decode_128k_fp8kv", "prefill_chunk_di128", "batched_paged_fp8kv"])
     ap.add_argument("--copies", type=int, default=0, help="distinct input copies to rotate (0 = auto)")
     ap.add_argument("--phase-iters", type=int, default=400)
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,

@@ -46,6 +46,11 @@ CONFIGS = {
         kind="decode", batch=1, lengths=[131072], H_I=64, d_I=64, k=2048, H=128, d_c=512,
         idx_dtype="f8", kv_dtype="f8", anchors=256, recent=512, paged=False, seed=10, page_size=64,
         softmax_scale=1.0),
+    # the batched decode over the FP8 latent cache
+    "batched_paged_fp8kv": dict(
+        kind="decode", batch=64, length_range=(16384, 65536), H_I=64, d_I=64, k=2048, H=128, d_c=512,
+        idx_dtype="f8", kv_dtype="f8", anchors=256, recent=512, paged=True, seed=12, page_size=64,
+        softmax_scale=1.0),
     # the chunked prefill with the shipped indexer shape (64 heads x 128 dims)
     "prefill_chunk_di128": dict(
         kind="prefill", cache_len=131072, rows=4096, H_I=64, d_I=128, k=2048, H=128, d_c=512,
@@ -64,7 +69,7 @@ CONFIGS = {
 }
 
 ORDER = ["tiny_fp32", "decode_128k", "batched_paged", "prefill_chunk", "decode_1m", "prefill_paged",
-         "decode_128k_di128", "decode_128k_fp8kv", "prefill_chunk_di128"]
+         "decode_128k_di128", "decode_128k_fp8kv", "prefill_chunk_di128", "batched_paged_fp8kv"]
 
 
 def get(name: str, **overrides) -> dict:
