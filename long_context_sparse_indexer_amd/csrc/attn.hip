@@ -764,16 +764,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 // rows arrive in one round trip; the other waves hand their sums to wave 0 through LDS.
 constexpr int kMaxSplit = 64;       // splits of the 16-head kernel
 constexpr int kMaxSplitWide = 256;  // splits of the all-heads kernel (the combine's limit)
-template <int L>
+// kP blocks share one (row, head): block part p merges columns 512 p / kP .. +512 / kP (8 / kP per lane), so that
+// a small batch still spreads the merge over the chip.
+template <int L, int kP>
 __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned short* __restrict__ part_o,
                                                                const int32_t* __restrict__ part_exp,
                                                                const float* __restrict__ part_lse, int H, int nsplit,
                                                                unsigned short* __restrict__ out,
                                                                float* __restrict__ lse) {
-  static_assert(kDC == 8 * 64, "eight latent columns per lane");
+  static_assert(kDC == 8 * 64, "eight latent columns per lane and part");
+  constexpr int kE = 8 / kP;  // columns per lane
+  typedef unsigned short vcol __attribute__((ext_vector_type(kE)));
   constexpr int kNW = 4 * L, kPerWave = 16;
-  __shared__ float red[kNW - 1][8][64];  // waves 1..: their partial sums, column-major per lane
-  const int rh = blockIdx.x;
+  __shared__ float red[kNW - 1][kE][64];  // waves 1..: their partial sums, column-major per lane
+  const int rh = blockIdx.x / kP, col0 = (blockIdx.x % kP) * (kDC / kP) + (int)(threadIdx.x & 63) * kE;
   const int r = rh / H, h = rh % H;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int grp = wave >> 2, u = wave & 3;         // this wave's 64 splits, and its offset among them
@@ -786,11 +790,11 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
     ls[i] = j < nsplit ? part_lse[row0 + (int64_t)j * H] : -INFINITY;
     ex[i] = j < nsplit ? part_exp[row0 + (int64_t)j * H] : 0;
   }
-  v8us v[kPerWave];
+  vcol v[kPerWave];
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     const int j = 64 * grp + u + 4 * q;
-    if (j < nsplit) v[q] = *reinterpret_cast<const v8us*>(part_o + (row0 + (int64_t)j * H) * kDC + lane * 8);
+    if (j < nsplit) v[q] = *reinterpret_cast<const vcol*>(part_o + (row0 + (int64_t)j * H) * kDC + col0);
   }
   // split weights w_j = exp(lse_j - max) / sum, each wave for itself; the lane that holds split j also folds in
   // its exponent
@@ -810,31 +814,31 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
   for (int i = 0; i < L; ++i)
     if (i == grp) wl = ldexpf(wsum > 0.f ? w[i] / wsum : 0.f, ex[i]);
   auto half_f = [](unsigned short b) { return (float)__builtin_bit_cast(_Float16, b); };
-  float acc[8];
+  float acc[kE];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     if (64 * grp + u + 4 * q < nsplit) {
       const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u + 4 * q));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
+      for (int e = 0; e < kE; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
     }
   }
   if (wave > 0)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[wave - 1][e][lane] = acc[e];
+    for (int e = 0; e < kE; ++e) red[wave - 1][e][lane] = acc[e];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int t = 0; t < kNW - 1; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += red[t][e][lane];
-    v8us b;
+      for (int e = 0; e < kE; ++e) acc[e] += red[t][e][lane];
+    vcol b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = float_to_bf16_bits(acc[e]);
-    *reinterpret_cast<v8us*>(out + ((int64_t)r * H + h) * kDC + lane * 8) = b;  // 16-byte aligned
-    if (lane == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+    for (int e = 0; e < kE; ++e) b[e] = float_to_bf16_bits(acc[e]);
+    *reinterpret_cast<vcol*>(out + ((int64_t)r * H + h) * kDC + col0) = b;  // 16- or 8-byte aligned
+    if (lane == 0 && col0 == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
 }
 
@@ -1028,13 +1032,21 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
                                                             nullptr, pt.o, pt.ex, pt.lse);
     }
     if (p.nsplit > 1) {
+      // fewer (row, head) pairs than CUs: two blocks per pair, half the columns each
       auto* o = static_cast<unsigned short*>(out);
-      if (p.nsplit <= 64)
-        attn_combine_kernel<1><<<g.R * g.H, 256, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
-      else if (p.nsplit <= 128)
-        attn_combine_kernel<2><<<g.R * g.H, 512, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
-      else
-        attn_combine_kernel<4><<<g.R * g.H, 1024, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse);
+      const int64_t rh = (int64_t)g.R * g.H;
+      const bool two = rh < 256;
+      const int nb = (int)(two ? 2 * rh : rh);
+#define DSA_COMBINE(L_, P_) \
+  attn_combine_kernel<L_, P_><<<nb, 256 * L_, 0, stream>>>(pt.o, pt.ex, pt.lse, g.H, p.nsplit, o, lse)
+      if (p.nsplit <= 64) {
+        if (two) DSA_COMBINE(1, 2); else DSA_COMBINE(1, 1);
+      } else if (p.nsplit <= 128) {
+        if (two) DSA_COMBINE(2, 2); else DSA_COMBINE(2, 1);
+      } else {
+        if (two) DSA_COMBINE(4, 2); else DSA_COMBINE(4, 1);
+      }
+#undef DSA_COMBINE
     }
   } else {
     const size_t lds = (size_t)g.k * (sizeof(int64_t) + sizeof(float)) + sizeof(float) * (size_t)g.d_c;
