@@ -95,6 +95,7 @@ typedef struct {
  *   scores      [R, scores_ld]  fp32 out: scores[r][s] = sum_j w[r][j] * max(0, <q_I[r][j], k_I[s]>) for
  *                               s < n_r, with q_I = scale * code; entries s >= n_r are not written.
  *   scores_ld   >= max_row_len
+ * q_idx and k_idx_pool must be 16-byte aligned, and for F8E4M3 also head_w and q_idx_scale.
  * The fp8 path computes the per-head dot products exactly (fp8 x fp8 products, fp32 accumulation of 64
  * terms) and applies the positive scales outside the ReLU, max(0, a*b*x) = a*b*max(0, x).
  */

@@ -121,9 +121,11 @@ dsa_status_t check_indexer_args(const dsa::Geo& g, const void* q_idx, const floa
                                 const void* k_idx_pool, const float* k_idx_scale) {
   DSA_CHECK(q_idx && head_w && k_idx_pool, DSA_EINVAL, "q_idx, head_w and k_idx_pool must be non-NULL");
   DSA_CHECK(aligned16(q_idx) && aligned16(k_idx_pool), DSA_EINVAL, "q_idx and k_idx_pool must be 16-byte aligned");
-  if (g.idx_dtype == DSA_F8E4M3)
+  if (g.idx_dtype == DSA_F8E4M3) {
     DSA_CHECK(q_idx_scale && k_idx_scale, DSA_EINVAL, "fp8 indexer needs q_idx_scale and k_idx_scale");
-  else
+    DSA_CHECK(aligned16(head_w) && aligned16(q_idx_scale), DSA_EINVAL,
+              "fp8 indexer: head_w and q_idx_scale must be 16-byte aligned");
+  } else
     DSA_CHECK(!q_idx_scale && !k_idx_scale, DSA_EINVAL, "fp32 indexer takes no scales (pass NULL)");
   return DSA_OK;
 }
@@ -175,6 +177,9 @@ dsa_status_t dense_geo(dsa::Geo* g) {
 
 size_t dense_bytes(const dsa::Geo& g) { return dsa::attn_workspace_bytes(g); }
 
+// The fused step's workspace: scores, the selection (when the caller passes none) and the pool row of every
+// selected slot, then one region that the top-k state and, once the selection is written, the attention's split
+// partials share.
 size_t step_bytes(const dsa::Geo& g) {
   return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) +
          2 * dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
@@ -284,25 +289,26 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
   ws += dsa::align_up(sizeof(float) * (size_t)g.R * ld);
   int32_t* idx = reinterpret_cast<int32_t*>(ws);
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
-  if (topk_idx) idx = topk_idx;
-  // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
-  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  int32_t* pool_rows_ws = reinterpret_cast<int32_t*>(ws);
   ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  char* const tail = ws;  // top-k state, then the attention's split partials
   // the per-row fp8 indexer clears the top-k state once its scores are out, sparing the top-k its zeroing launch
   const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
-  const dsa::TopkState tstate = dsa::topk_state(g, ws);
+  const dsa::TopkState tstate = dsa::topk_state(g, tail);
   if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,
                                            fuse ? &tstate : nullptr, s),
                        "indexer launch")) != DSA_OK)
     return st;
+  if (topk_idx) idx = topk_idx;
+  // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
+  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? pool_rows_ws : nullptr;
   if (fuse) {
-    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, ws, pool_rows, s), "top-k launch")) !=
-        DSA_OK)
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK)
       return st;
-  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, ws, pool_rows, s), "top-k launch")) != DSA_OK) {
+  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK) {
     return st;
   }
-  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, pool_rows, s), "attention launch");
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, tail, pool_rows, s), "attention launch");
 }
 
 size_t dsa_workspace_bytes(const dsa_problem_t* problem, int32_t op) {

@@ -16,6 +16,8 @@
 #include "common.h"
 #include "launch.h"
 
+DSA_TIMELINE_UNIT(attn)
+
 namespace dsa {
 namespace {
 
@@ -217,17 +219,28 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     unsigned short* __restrict__ out,
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
     float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char kv_lds0[kNC * kRowB];
-  __shared__ __attribute__((aligned(16))) char kv_lds1[kNC * kRowB];
-  __shared__ __attribute__((aligned(16))) float s_lds[kHG][kNC + 4];
+  struct ChunkLds {
+    char kv0[kNC * kRowB];
+    char kv1[kNC * kRowB];
+    float s[kHG][kNC + 4];
+    // RoPE rows of the FP8 path: read only by QK, so one buffer serves (a chunk's QK ends at its mid barrier, and
+    // the next chunk's rows are stored after it)
+    char rope[kFp8 ? kNC * kRopeRowB : 16];
+    float scale[kFp8 ? 4 * kNC : 4];  // [tile][slot], same lifetime: every read of a chunk's scales happens before
+                                      // its mid barrier
+  };
+  __shared__ __attribute__((aligned(16))) ChunkLds U;
   __shared__ int32_t prow_lds[kMaxSplitLen];  // physical row of every slot of the split, -1 = no position
   __shared__ int wave_first[4];               // first slot with a position among each wave's slots
-  // RoPE rows of the FP8 path: read only by QK, so one buffer serves (a chunk's QK ends at its mid barrier, and
-  // the next chunk's rows are stored after it)
-  __shared__ __attribute__((aligned(16))) char rope_lds[kFp8 ? kNC * kRopeRowB : 16];
-  __shared__ __attribute__((aligned(16))) float scale_lds[kFp8 ? 4 * kNC : 4];  // [tile][slot], same lifetime:
-  // every read of a chunk's scales happens before its mid barrier
+  char* const kv_lds0 = U.kv0;
+  char* const kv_lds1 = U.kv1;
+  float (*const s_lds)[kNC + 4] = U.s;
+  char* const rope_lds = U.rope;
+  float* const scale_lds = U.scale;
   constexpr int kQW = kFp8 ? kDC + kRope : kDC;  // query width
+  args_to_sgprs(q, kv, topk_idx, k, pool_rows, row_len, max_row_len, row_seq, page_table, num_seqs, max_pages,
+                num_pages, log2ps, H, nsplit, units, split_len);
+  DSA_STAMP(3, 0);
 
   const int ngroups = H / kHG;
   const BlockWork bw = block_work(nsplit, ngroups);
@@ -236,41 +249,67 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
 
-  const int seq = clamp_seq(row_seq[r], num_seqs);
   const int begin = split * split_len;
   const int end = min(k, begin + split_len);
   const int len = max(end - begin, 0);
   const int nch = (len + kNC - 1) / kNC;
 
+  // The group's queries (16 heads x kQW bf16, contiguous) are read once per block, each load instruction one
+  // contiguous 1 KiB run, and staged in the second chunk buffer (free until chunk 0 has been computed); the MFMA
+  // A operands are read from there after the prologue's barrier.  Reading them straight into the operand layout
+  // would make every lane fetch 16 bytes of a different row, which the vector L1 serves about a lane per cycle.
+  constexpr int kQBytes = kHG * kQW * 2;          // per block
+  constexpr int kQRowB = kQW * 2 + 16;            // LDS row stride of the staged queries
+  constexpr int kQPieces = (kQBytes / 16 + 255) / 256;  // 16-byte pieces per thread (the last may be partial)
+  static_assert(kQBytes % 16 == 0 && kHG * kQRowB <= kNC * kRowB, "queries fit the second chunk buffer");
+  v4i qpiece[kQPieces];
+  {
+    const char* qsrc = reinterpret_cast<const char*>(q + ((int64_t)r * H + grp16 * kHG) * kQW);
+#pragma unroll
+    for (int j = 0; j < kQPieces; ++j)  // a piece past the group's queries rereads its last one (not stored)
+      qpiece[j] = *reinterpret_cast<const v4i*>(qsrc + (size_t)min(j * 256 + (int)threadIdx.x, kQBytes / 16 - 1) * 16);
+  }
+  DSA_STAMP(3, 6);
+
   // Every slot of the split -> physical row before any gather, so that the gathers are the only loads in
-  // flight later: all position loads are issued together, then all page-table loads (two round trips), or the
-  // pool rows the top-k wrote beside the selection are loaded directly (one).
+  // flight later.  With a list, every entry load is issued at once (after the queries) from an in-range address
+  // (the value is dropped past the split's end); positions then take one round of page-table loads, issued
+  // together, or the pool rows the top-k wrote beside the selection are used directly.
   constexpr int kSlotsPerThread = kMaxSplitLen / 256;
-  const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
   int pr[kSlotsPerThread];
-#pragma unroll
-  for (int j = 0; j < kSlotsPerThread; ++j) {
-    const int s = j * 256 + threadIdx.x;
-    pr[j] = s < len ? src.at(s) : -1;
-  }
-
-  // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8 (and the RoPE dims 512 + kd*32 + g*8 .. +8)
-  v8bf qa[kDC / 32];
-  v8bf qr[kFp8 ? kRope / 32 : 1];
   {
-    const unsigned short* qrow = q + ((int64_t)r * H + grp16 * kHG + i) * kQW + g * 8;
+    const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
+    if (src.list) {
+      if (len > 0)
 #pragma unroll
-    for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 32);
-    if constexpr (kFp8)
+        for (int j = 0; j < kSlotsPerThread; ++j) {
+          const int s = j * 256 + threadIdx.x;
+          const int v = src.list[min(s, len - 1)];
+          pr[j] = s < len ? v : -1;
+        }
+      else
 #pragma unroll
-      for (int kd = 0; kd < kRope / 32; ++kd) qr[kd] = *reinterpret_cast<const v8bf*>(qrow + kDC + kd * 32);
+        for (int j = 0; j < kSlotsPerThread; ++j) pr[j] = -1;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSlotsPerThread; ++j) {
+        const int s = j * 256 + threadIdx.x;
+        pr[j] = s < len && s < src.dense_n ? begin + s : -1;
+      }
+    }
   }
-
-  if (!src.physical)
-#pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j)
-      pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+  DSA_STAMP(3, 7);
   {
+    const bool physical = pool_rows != nullptr;
+    if (!physical) {
+      const int32_t* pt = page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages;
+      int pg[kSlotsPerThread];
+#pragma unroll
+      for (int j = 0; j < kSlotsPerThread; ++j) pg[j] = pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)];
+#pragma unroll
+      for (int j = 0; j < kSlotsPerThread; ++j)
+        pr[j] = pr[j] >= 0 ? (min(max(pg[j], 0), num_pages - 1) << log2ps) | (pr[j] & ((1 << log2ps) - 1)) : -1;
+    }
     // slot j * 256 + 64 wave + lane; the wave's first slot with a position comes from the ballots
     int first = 0x7fffffff;
 #pragma unroll
@@ -282,12 +321,30 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     }
     if (lane == 0) wave_first[wave] = first;
   }
+  DSA_STAMP(3, 1);
+#pragma unroll
+  for (int j = 0; j < kQPieces; ++j) {
+    const int piece = j * 256 + threadIdx.x, b = piece * 16;  // byte b of the group's queries
+    if (b < kQBytes) *reinterpret_cast<v4i*>(kv_lds1 + (b / (kQW * 2)) * kQRowB + b % (kQW * 2)) = qpiece[j];
+  }
+  DSA_STAMP(3, 9);
 
   v4f o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // running max (log2 domain) and sum for head i
   __syncthreads();
+  // Q as A operands: head grp16*16 + i, d = kd*32 + g*8 .. +8 (and the RoPE dims 512 + kd*32 + g*8 .. +8)
+  v8bf qa[kDC / 32];
+  v8bf qr[kFp8 ? kRope / 32 : 1];
+  {
+    const char* qrow = kv_lds1 + i * kQRowB + g * 16;
+#pragma unroll
+    for (int kd = 0; kd < kDC / 32; ++kd) qa[kd] = *reinterpret_cast<const v8bf*>(qrow + kd * 64);
+    if constexpr (kFp8)
+#pragma unroll
+      for (int kd = 0; kd < kRope / 32; ++kd) qr[kd] = *reinterpret_cast<const v8bf*>(qrow + kDC * 2 + kd * 64);
+  }
   const int first_valid = min(min(wave_first[0], wave_first[1]), min(wave_first[2], wave_first[3]));
   // a split with no selected row contributes nothing; otherwise slots without a position read a selected row
   // of this split instead (their logits are -inf, so they carry zero weight)
@@ -414,13 +471,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       if (c + 1 < nch) place(nxt);
       lds_barrier();  // every wave is done with `cur` and s_lds before they are overwritten; `nxt` is written
     };
+    DSA_STAMP(3, 2);
     gather(prow_lds);
     place(kv_lds0);
     lds_barrier();
+    DSA_STAMP(3, 3);
     for (int c = 0; c < nch; c += 2) {
       chunk(c, kv_lds0, kv_lds1);
       if (c + 1 < nch) chunk(c + 1, kv_lds1, kv_lds0);
     }
+    DSA_STAMP(3, 4);
   }
 
   // finish: O rows are heads g*4 + v, columns wave*128 + dt*16 + i
@@ -438,6 +498,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     }
     __syncthreads();
   }
+  // split partials go out as 16-byte stores: each wave stages its 16 heads x 128 columns of fp16 bits in LDS
+  // (rows padded to 136 halves so the four heads of one write land on different banks), then every lane stores
+  // four 8-column pieces; the chunk buffers are free once the last chunk's barrier has passed
+  constexpr int kStgRow = 136;
+  unsigned short* stg = reinterpret_cast<unsigned short*>(kv_lds0) + wave * (kHG * kStgRow);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int hh = g * 4 + v;
@@ -449,12 +514,25 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       const int e = part_exponent(mx * inv);
       const int64_t prow = ((int64_t)r * nsplit + split) * H + grp16 * kHG + hh;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) part_o[prow * kDC + wave * 128 + dt * 16 + i] = part_bits(o[dt][v] * inv, e);
+      for (int dt = 0; dt < 8; ++dt) stg[hh * kStgRow + dt * 16 + i] = part_bits(o[dt][v] * inv, e);
       if (wave == 0 && i == 0) part_exp[prow] = e;
     } else {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         out[(head0 + hh) * kDC + wave * 128 + dt * 16 + i] = float_to_bf16_bits(o[dt][v] * inv);
+    }
+  }
+  if (kSplit) {
+    // this wave's own staging rows: its LDS writes are complete before its reads (no other wave touches them);
+    // the empty asm keeps the compiler from moving the 16-byte reads above the 2-byte writes
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    const int64_t prow0 = ((int64_t)r * nsplit + split) * H + grp16 * kHG;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = j * 64 + lane, hh = piece >> 4, c8 = piece & 15;  // head, 8-column piece
+      const v4i x = *reinterpret_cast<const v4i*>(stg + hh * kStgRow + c8 * 8);
+      *reinterpret_cast<v4i*>(part_o + (prow0 + hh) * kDC + wave * 128 + c8 * 8) = x;
     }
   }
   if (wave == 0 && g == 0) {
@@ -464,6 +542,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     else if (lse)
       lse[head0 + i] = lz;
   }
+  DSA_STAMP(3, 5);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -519,6 +598,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
     float* __restrict__ part_lse) {
   static_assert(kCW % NW == 0, "every wave gathers the same number of rows");
+  args_to_sgprs(q, kv, topk_idx, k, pool_rows, row_len, max_row_len, row_seq, page_table, num_seqs, max_pages,
+                num_pages, log2ps, H, nsplit, units, split_len);
   constexpr int kRows = kCW / NW;  // rows each wave gathers per chunk
   // chunks gathered ahead: at the wait for chunk c, the kDepth - 1 chunks after it may still be in flight,
   // which must fit vmcnt (at most 63 outstanding loads per wave)
@@ -537,26 +618,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int hw = hg * 32 * NW + wave * 32;  // first head of this wave
 
-  const int seq = clamp_seq(row_seq[r], num_seqs);
   const int begin = split * split_len;
   const int end = min(k, begin + split_len);
   const int len = max(end - begin, 0);
   const int nch = (len + kCW - 1) / kCW;  // chunks of kCW slots
   const int n64 = (len + 63) / 64;
 
-  // Slots -> physical rows: all position loads are issued together, then all page-table loads.  Slot
-  // j * 64 NW + 64 wave + lane belongs to 64-slot group j NW + wave, so a ballot gives the validity bits of
-  // two chunks.
-  constexpr int kSlotsPerThread = kWideMaxSplitLen / (64 * NW);
-  const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
-  int pr[kSlotsPerThread];
-#pragma unroll
-  for (int j = 0; j < kSlotsPerThread; ++j) {
-    const int sl = (j * NW + wave) * 64 + lane;
-    pr[j] = sl < len ? src.at(sl) : -1;
-  }
-  // the queries load while the positions and then the page-table entries arrive
-  // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8
+  // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8; issued first so that
+  // they load while the positions and then the page-table entries arrive
   v8bf qb[kDC / 16];
   {
     const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kDC + 8 * half;
@@ -565,10 +634,35 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   }
   v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
 
-  if (!src.physical)
+  // Slots -> physical rows: all position loads are issued together (from in-range addresses, the values dropped
+  // past the split's end), then all page-table loads.  Slot j * 64 NW + 64 wave + lane belongs to 64-slot group
+  // j NW + wave, so a ballot gives the validity bits of two chunks.
+  constexpr int kSlotsPerThread = kWideMaxSplitLen / (64 * NW);
+  const SlotSource src = slot_source(topk_idx, pool_rows, row_len, max_row_len, r, k, begin);
+  int pr[kSlotsPerThread];
+  if (src.list && len > 0) {
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int sl = (j * NW + wave) * 64 + lane;
+      const int v = src.list[min(sl, len - 1)];
+      pr[j] = sl < len ? v : -1;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int sl = (j * NW + wave) * 64 + lane;
+      pr[j] = !src.list && sl < len && sl < src.dense_n ? begin + sl : -1;
+    }
+  }
+  if (!src.physical) {
+    const int32_t* pt = page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages;
+    int pg[kSlotsPerThread];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) pg[j] = pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)];
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j)
-      pr[j] = pr[j] >= 0 ? (int)phys_row(page_table, max_pages, num_pages, log2ps, seq, pr[j]) : -1;
+      pr[j] = pr[j] >= 0 ? (min(max(pg[j], 0), num_pages - 1) << log2ps) | (pr[j] & ((1 << log2ps) - 1)) : -1;
+  }
   {
     int first = 0x7fffffff;
 #pragma unroll
@@ -777,6 +871,8 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
   typedef unsigned short vcol __attribute__((ext_vector_type(kE)));
   constexpr int kNW = 4 * L, kPerWave = 16;
   __shared__ float red[kNW - 1][kE][64];  // waves 1..: their partial sums, column-major per lane
+  args_to_sgprs(part_o, part_exp, part_lse, H, nsplit, out, lse);
+  DSA_STAMP(4, 0);
   const int rh = blockIdx.x / kP, col0 = (blockIdx.x % kP) * (kDC / kP) + (int)(threadIdx.x & 63) * kE;
   const int r = rh / H, h = rh % H;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -809,6 +905,7 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
     part += w[i];
   }
   const float wsum = wave_sum(part);
+  DSA_STAMP(4, 1);
   float wl = 0.f;  // weight of split 64 grp + lane
 #pragma unroll
   for (int i = 0; i < L; ++i)
@@ -825,6 +922,7 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
       for (int e = 0; e < kE; ++e) acc[e] = fmaf(wj, half_f(v[q][e]), acc[e]);
     }
   }
+  DSA_STAMP(4, 2);
   if (wave > 0)
 #pragma unroll
     for (int e = 0; e < kE; ++e) red[wave - 1][e][lane] = acc[e];
@@ -840,6 +938,7 @@ __global__ __launch_bounds__(256 * L) void attn_combine_kernel(const unsigned sh
     *reinterpret_cast<vcol*>(out + ((int64_t)r * H + h) * kDC + col0) = b;  // 16- or 8-byte aligned
     if (lane == 0 && col0 == 0 && lse) lse[(int64_t)r * H + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
   }
+  DSA_STAMP(4, 3);
 }
 
 // fp32 path: one block per (row, head); logits and physical rows staged in LDS.
@@ -1015,21 +1114,15 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
     } else {
       const int64_t units = (int64_t)g.R * (g.H / kHG);
       const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / kHG);
-      if (p.nsplit == 1)
-        (fp8 ? attn_bf16_kernel<false, true> : attn_bf16_kernel<false, false>)<<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
-                                                             g.max_row_len, g.row_seq,
-                                                             g.page_table,
-                                                             g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
-                                                             (int)units, p.split_len, scale_log2,
-                                                             static_cast<unsigned short*>(out), lse, nullptr,
-                                                             nullptr, nullptr);
-      else
-        (fp8 ? attn_bf16_kernel<true, true> : attn_bf16_kernel<true, false>)<<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len,
-                                                             g.max_row_len, g.row_seq,
-                                                            g.page_table,
-                                                            g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
-                                                            p.nsplit, (int)units, p.split_len, scale_log2, nullptr,
-                                                            nullptr, pt.o, pt.ex, pt.lse);
+      auto go = [&](auto kern, bool split) {
+        kern<<<nblocks, 256, 0, stream>>>(qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq,
+                                          g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
+                                          split ? p.nsplit : 1, (int)units, p.split_len, scale_log2,
+                                          split ? nullptr : static_cast<unsigned short*>(out), split ? nullptr : lse,
+                                          pt.o, pt.ex, pt.lse);
+      };
+      if (p.nsplit > 1) go(fp8 ? attn_bf16_kernel<true, true> : attn_bf16_kernel<true, false>, true);
+      else go(fp8 ? attn_bf16_kernel<false, true> : attn_bf16_kernel<false, false>, false);
     }
     if (p.nsplit > 1) {
       // fewer (row, head) pairs than CUs: two blocks per pair, half the columns each

@@ -4,6 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Timeline probes for profiling builds.  Compiled out unless DSA_TIMELINE is defined; a profiling build then
+// records s_memrealtime (a 100 MHz clock common to the whole device) at marked points of each block into a
+// device buffer that the host installs with dsa_timeline_set_<unit>(), one per translation unit.
+#ifdef DSA_TIMELINE
+static __constant__ unsigned long long* g_timeline;  // constant: stamps never reload it
+#define DSA_TIMELINE_UNIT(name)                                                               \
+  extern "C" int dsa_timeline_set_##name(void* p) {                                           \
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &p, sizeof p);                      \
+  }
+#define DSA_STAMP(kernel, point)                                                              \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && g_timeline) {                                                     \
+      const unsigned blk = blockIdx.x + blockIdx.y * gridDim.x;                               \
+      if (blk < 4096) g_timeline[((kernel) * 4096u + blk) * 16u + (point)] = __builtin_amdgcn_s_memrealtime(); \
+    }                                                                                         \
+  } while (0)
+#else
+#define DSA_TIMELINE_UNIT(name)
+#define DSA_STAMP(kernel, point) ((void)0)
+#endif
+
 namespace dsa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -29,6 +50,19 @@ __device__ __forceinline__ int64_t phys_row(const int32_t* __restrict__ page_tab
   int page = page_table[(int64_t)seq * max_pages + lp];
   page = min(max(page, 0), num_pages - 1);
   return ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
+}
+
+// Makes the compiler read kernel arguments into scalar registers at this point.  Left to itself it sinks each
+// argument's load into the first block that uses it, and a prologue then pays a separate load-and-wait round for
+// each group of arguments; called at a kernel's entry with the arguments of its prologue, it turns those rounds
+// into one.
+template <class T>
+__device__ __forceinline__ void arg_to_sgpr(const T& a) {
+  asm volatile("" ::"s"(a));
+}
+template <class... T>
+__device__ __forceinline__ void args_to_sgprs(const T&... a) {
+  (arg_to_sgpr(a), ...);
 }
 
 __device__ __forceinline__ int clamp_len(int n, int max_len) { return min(max(n, 0), max_len); }

@@ -26,6 +26,8 @@
 #include "launch.h"
 #include "topk_common.h"
 
+DSA_TIMELINE_UNIT(indexer)
+
 namespace dsa {
 namespace {
 
@@ -48,7 +50,33 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
     int tiles_per_block) {
   constexpr int H_I = 32 * HB, D_I = 64 * KB;
+  args_to_sgprs(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages, num_pages,
+                log2ps, max_row_len, scores, ld, clear.cnt, tiles_per_block);
+  DSA_STAMP(0, 0);
   const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  // The row's query operands and epilogue weights depend on nothing but the row: they are requested first, so
+  // that they arrive while the row length, the page ids and the keys make their dependent round trips.  Lane
+  // half h holds heads 4 h + {0..3} + 8 m of each 32-head block (accumulator entry 4 m + e), four runs of four
+  // consecutive heads: one 16-byte load each of weights and scales.
+  v8i a[HB][KB];
+  float wq[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      a[hb][kb] =
+          *reinterpret_cast<const v8i*>(q_idx + ((int64_t)r * H_I + hb * 32 + col) * D_I + kb * 64 + half * 32);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t h0 = (int64_t)r * H_I + hb * 32 + half * 4 + 8 * m;
+      const v4f w4 = *reinterpret_cast<const v4f*>(head_w + h0);
+      const v4f s4 = *reinterpret_cast<const v4f*>(q_scale + h0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wq[hb][4 * m + e] = w4[e] * s4[e];
+    }
+  }
   const int n = clamp_len(row_len[r], max_row_len);
   const int64_t first = (int64_t)blockIdx.x * tiles_per_block * kIdxTile;
   // the row's top-k state, cleared by block 0 as its last work (stores issued earlier would hold up the waits
@@ -60,9 +88,8 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     clear_state();
     return;
   }
+  DSA_STAMP(0, 1);
   const int ntile = (int)min((int64_t)tiles_per_block, (n - first + kIdxTile - 1) / kIdxTile);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
 
   // Tile t of the block covers positions first + 512 t .. +512; wave w owns 128 of them as four 32-position
@@ -107,26 +134,13 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
 
   TileLoad cur;
   issue(0, cur);
-  v8i a[HB][KB];
-  float wq[HB][16];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      a[hb][kb] =
-          *reinterpret_cast<const v8i*>(q_idx + ((int64_t)r * H_I + hb * 32 + col) * D_I + kb * 64 + half * 32);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int head = hb * 32 + half * 4 + (i & 3) + 8 * (i >> 2);
-      wq[hb][i] = head_w[(int64_t)r * H_I + head] * q_scale[(int64_t)r * H_I + head];
-    }
-  }
   // the row's query operands are complete before the loop (an asm use makes the compiler wait here once
   // instead of inside every iteration)
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) require_loaded(a[hb][kb]);
+  DSA_STAMP(0, 2);
   const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)r * ld, (short)0, n * 4, kBufferWord3);
 
   // A tile is kUnits (pair p, subtile 2 p + u of the pair, head block hb) MFMA units in that order.  The MFMA of
@@ -188,6 +202,7 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     if (t + 2 < ntile) issue(t + 2, cur);
     compute(t + 1, other);
   }
+  DSA_STAMP(0, 3);
   clear_state();
 }
 

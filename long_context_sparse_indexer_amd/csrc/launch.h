@@ -40,6 +40,7 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
 constexpr int kTopkMaxBlocksPerRow = 1024;
 constexpr int kTopkChunk = 4096;
 size_t topk_workspace_bytes(const Geo& g);
+
 TopkState topk_state(const Geo& g, void* workspace);
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream);
 // Selection over stored scores whose top-k state is already zero (launch_topk_zero, or the fused indexer).
