@@ -149,6 +149,25 @@ dsa_status_t dsa_decode_step(const dsa_problem_t *problem, const dsa_layout_t *l
                              void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * dsa_decode_step without a workspace argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): its scratch is a 64 MiB array in the
+ * library's device code, one copy per device, held until the process ends.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call); the first call on a device looks the array's address up once.
+ *   - Problems whose dsa_workspace_bytes(problem, DSA_OP_STEP) exceeds 64 MiB return DSA_EUNSUPPORTED (enough for
+ *     16 rows of 128K positions or 64 rows of 64K).
+ *   - `stream` must belong to the current device (DSA_EINVAL otherwise).
+ *   - Every call on a device shares that device's scratch, which keeps the last call's contents (nothing in it
+ *     needs to start at zero): calls that may overlap on one device (different streams, or several host threads)
+ *     race and must be serialised by the caller.
+ * Other arguments and results as dsa_decode_step.
+ */
+dsa_status_t dsa_decode_step_static(const dsa_problem_t *problem, const dsa_layout_t *layout,
+                                    const void *q_idx, const float *q_idx_scale, const float *head_w,
+                                    const void *k_idx_pool, const float *k_idx_scale,
+                                    const void *q, const void *kv_pool, int32_t *topk_idx,
+                                    void *out, float *lse, void *stream);
+
+/*
  * Dense MLA attention in MQA mode over every visible position of each row (no indexer, no selection): the
  * short-context fallback.  Below a crossover context the indexer's fixed cost outweighs what it saves, and a
  * dense step is faster (milos-mitrovic, "When Does DSA Beat Dense Attention, and When Doesn't It?": the

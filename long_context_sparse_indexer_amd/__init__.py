@@ -51,10 +51,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk.argtypes = [PP, PL, P, I64, P, P, SZ, P]
         L.dsa_sparse_mla_attn.argtypes = [PP, PL, P, P, P, P, P, P, SZ, P]
         L.dsa_decode_step.argtypes = [PP, PL, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.dsa_decode_step_static.argtypes = [PP, PL, P, P, P, P, P, P, P, P, P, P, P]
         L.dsa_dense_mla_attn.argtypes = [PP, PL, P, P, P, P, P, SZ, P]
         L.dsa_indexer_key_append.argtypes = [PP, PL, P, P, P, P, P, P]
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn",
-                  "dsa_indexer_key_append"):
+                  "dsa_indexer_key_append", "dsa_decode_step_static"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [PP, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = SZ
@@ -155,6 +156,14 @@ def dsa_decode_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_i
         _ptr(head_w, "head_w"), _ptr(k_idx_pool, "k_idx_pool"), _ptr(k_idx_scale, "k_idx_scale"), _ptr(q, "q"),
         _ptr(kv_pool, "kv_pool"), _ptr(topk_idx, "topk_idx"), _ptr(out, "out"), _ptr(lse, "lse"),
         _ptr(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+
+
+def dsa_decode_step_static(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool,
+                           topk_idx, out, lse, stream=None):
+    _check(lib().dsa_decode_step_static(
+        ctypes.byref(problem), ctypes.byref(layout), _ptr(q_idx, "q_idx"), _ptr(q_idx_scale, "q_idx_scale"),
+        _ptr(head_w, "head_w"), _ptr(k_idx_pool, "k_idx_pool"), _ptr(k_idx_scale, "k_idx_scale"), _ptr(q, "q"),
+        _ptr(kv_pool, "kv_pool"), _ptr(topk_idx, "topk_idx"), _ptr(out, "out"), _ptr(lse, "lse"), _stream(stream)))
 
 
 def dsa_workspace_bytes(problem, op: int) -> int:

@@ -5,10 +5,15 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dsa.h"
 #include "launch.h"
+
+// Scratch of dsa_decode_step_static (see static_scratch below).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -186,6 +191,78 @@ size_t step_bytes(const dsa::Geo& g) {
          std::max(dsa::topk_workspace_bytes(g), dsa::attn_workspace_bytes(g));
 }
 
+// The step on a validated problem and workspace.
+dsa_status_t decode_step(const dsa::Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                         const void* k_idx_pool, const float* k_idx_scale, const void* q, const void* kv_pool,
+                         int32_t* topk_idx, void* out, float* lse, void* workspace, hipStream_t s) {
+  dsa_status_t st;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t ld = step_ld(g);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += dsa::align_up(sizeof(float) * (size_t)g.R * ld);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws);
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  int32_t* pool_rows_ws = reinterpret_cast<int32_t*>(ws);
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  char* const tail = ws;  // top-k state, then the attention's split partials
+  // the per-row fp8 indexer clears the top-k state once its scores are out, sparing the top-k its zeroing launch
+  const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
+  const dsa::TopkState tstate = dsa::topk_state(g, tail);
+  if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,
+                                           fuse ? &tstate : nullptr, s),
+                       "indexer launch")) != DSA_OK)
+    return st;
+  if (topk_idx) idx = topk_idx;
+  // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
+  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? pool_rows_ws : nullptr;
+  if (fuse) {
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK)
+      return st;
+  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK) {
+    return st;
+  }
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, tail, pool_rows, s), "attention launch");
+}
+
+dsa_status_t check_step(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,
+                        const float* q_idx_scale, const float* head_w, const void* k_idx_pool, const float* k_idx_scale,
+                        const void* q, const void* kv_pool, const void* out, dsa::Geo* g) {
+  dsa_status_t st = check_problem(problem, layout, true, true, g);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_args(*g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale)) != DSA_OK) return st;
+  DSA_CHECK(q && kv_pool && out, DSA_EINVAL, "q, kv_pool and out must be non-NULL");
+  DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
+            "q, kv_pool and out must be 16-byte aligned");
+  return DSA_OK;
+}
+
+// The scratch of dsa_decode_step_static: a file-scope device array, one copy on every device the library runs on,
+// held until the process ends.  Host code must not pass `scratch` itself to a kernel (on the host it is only a
+// stand-in for the symbol); its device address is looked up once per device, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status_t static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_EHIP, "no usable current device (%d)", dev);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return fail(DSA_EHIP, "hipStreamGetDevice failed");
+    DSA_CHECK(sdev == dev, DSA_EINVAL, "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(DSA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,40 +352,30 @@ dsa_status_t dsa_decode_step(const dsa_problem_t* problem, const dsa_layout_t* l
                              const float* k_idx_scale, const void* q, const void* kv_pool, int32_t* topk_idx,
                              void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   dsa::Geo g;
-  dsa_status_t st = check_problem(problem, layout, true, true, &g);
+  dsa_status_t st = check_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, out,
+                               &g);
   if (st != DSA_OK) return st;
-  if ((st = check_indexer_args(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale)) != DSA_OK) return st;
-  DSA_CHECK(q && kv_pool && out, DSA_EINVAL, "q, kv_pool and out must be non-NULL");
-  DSA_CHECK(aligned16(q) && aligned16(kv_pool) && aligned16(out), DSA_EINVAL,
-            "q, kv_pool and out must be 16-byte aligned");
   if ((st = check_ws(workspace, workspace_bytes, step_bytes(g))) != DSA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const int64_t ld = step_ld(g);
-  float* scores = reinterpret_cast<float*>(ws);
-  ws += dsa::align_up(sizeof(float) * (size_t)g.R * ld);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws);
-  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
-  int32_t* pool_rows_ws = reinterpret_cast<int32_t*>(ws);
-  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
-  char* const tail = ws;  // top-k state, then the attention's split partials
-  // the per-row fp8 indexer clears the top-k state once its scores are out, sparing the top-k its zeroing launch
-  const bool fuse = g.idx_dtype == DSA_F8E4M3 && !dsa::indexer_tiled(g);
-  const dsa::TopkState tstate = dsa::topk_state(g, tail);
-  if ((st = hip_status(dsa::launch_indexer(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld,
-                                           fuse ? &tstate : nullptr, s),
-                       "indexer launch")) != DSA_OK)
-    return st;
-  if (topk_idx) idx = topk_idx;
-  // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
-  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? pool_rows_ws : nullptr;
-  if (fuse) {
-    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK)
-      return st;
-  } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK) {
-    return st;
-  }
-  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, tail, pool_rows, s), "attention launch");
+  return decode_step(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx, out, lse,
+                     workspace, static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_decode_step_static(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q_idx,
+                                    const float* q_idx_scale, const float* head_w, const void* k_idx_pool,
+                                    const float* k_idx_scale, const void* q, const void* kv_pool, int32_t* topk_idx,
+                                    void* out, float* lse, void* stream) {
+  dsa::Geo g;
+  dsa_status_t st = check_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, out,
+                               &g);
+  if (st != DSA_OK) return st;
+  const size_t need = step_bytes(g);
+  DSA_CHECK(need <= kStaticScratchBytes, DSA_EUNSUPPORTED,
+            "this problem needs %zu bytes of scratch, above the static scratch of %zu bytes (use dsa_decode_step "
+            "with a workspace)", need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(static_cast<hipStream_t>(stream), &ws)) != DSA_OK) return st;
+  return decode_step(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx, out, lse, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 size_t dsa_workspace_bytes(const dsa_problem_t* problem, int32_t op) {

@@ -195,3 +195,17 @@ def test_zero_rows_enqueue_nothing():
     pf = _problem(num_rows=0, kv_dtype="f8")
     assert dsa.dsa_workspace_bytes(pf, dsa.DSA_OP_DENSE) == 0
     assert L.dsa_dense_mla_attn(ctypes.byref(pf), ctypes.byref(LAYOUT), FAKE, FAKE, FAKE, None, None, 0, None) == 0
+
+
+def test_static_scratch_step_rejects_oversized_problems():
+    """The allocation-free step checks its problem against its fixed scratch before any device work."""
+    P = _problem(num_rows=64, num_seqs=64, max_pages=16384, num_pages=16384 * 64, max_row_len=1048576)
+    st = dsa.lib().dsa_decode_step_static(ctypes.byref(P), ctypes.byref(LAYOUT), *([FAKE] * 10), None)
+    assert st == dsa.DSA_EUNSUPPORTED and "static scratch" in dsa.dsa_last_error()
+    assert dsa.dsa_workspace_bytes(P, dsa.DSA_OP_STEP) > 64 << 20
+
+
+def test_fp8_indexer_weights_must_be_aligned():
+    p = _problem()
+    assert _idx(p, w=MISALIGNED) == dsa.DSA_EINVAL and "16-byte aligned" in dsa.dsa_last_error()
+    assert _idx(p, qs=MISALIGNED) == dsa.DSA_EINVAL and "16-byte aligned" in dsa.dsa_last_error()
