@@ -444,7 +444,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 
       // O += P V.  A operand element e of K-step kk is slot kk*32 + 8g + perm[e], perm = {0,2,4,6,1,3,5,7}.
       // FP8 entries: the wave's 128 output columns are tile `wave`, so each probability takes its slot's scale
-      // for that tile
+      // for that tile; that product is split into its bf16 rounding and the bf16 rounding of what is left (2^-17
+      // relative together), and both go through the MFMA, so no dequantised value is rounded on its way to O
       if constexpr (kFp8)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -458,6 +459,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
         const float pe[8] = {sv[kk * 8 + 0], sv[kk * 8 + 2], sv[kk * 8 + 4], sv[kk * 8 + 6],
                              sv[kk * 8 + 1], sv[kk * 8 + 3], sv[kk * 8 + 5], sv[kk * 8 + 7]};
         const v8bf pa = pack8(pe);
+        v8bf pa_lo;
+        if constexpr (kFp8) {
+          float rest[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rest[e] = pe[e] - (float)pa[e];  // exact: the low part of pe[e]
+          pa_lo = pack8(rest);
+        }
         const int row1 = kk * 32 + 8 * g + 2 * (i >> 2);
         const char* p1 = cur + row1 * kRowB + (wave * 128 + 4 * (i & 3)) * 2;
 #pragma unroll
@@ -466,6 +474,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
           const v4bf hi4 = lds_tr_read(p1 + kRowB + dt * 32);
           const v8bf b = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[dt], 0, 0, 0);
+          if constexpr (kFp8) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, b, o[dt], 0, 0, 0);
         }
       }
       if (c + 1 < nch) place(nxt);

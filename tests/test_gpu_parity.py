@@ -224,6 +224,40 @@ def test_fp8_latent_entries_decode_and_paged():
     _run(synth.get("batched_paged", batch=3, length_range=(3000, 9000), kv_dtype="f8", H=32, k=512))
 
 
+def _large_fp8_latents(prob, seed=41):
+    # every entry's 512 latent codes drawn from the e4m3 values of magnitude 256..448 (exponent field 15, signed)
+    # with all four tile scales 1/60, so every dequantised latent value lies in [4.26, 7.47]
+    rng = np.random.default_rng(seed)
+    n = prob.kv_pool.shape[0]
+    mag = rng.integers(0x78, 0x7F, size=(n, 512), dtype=np.uint8)
+    prob.kv_pool[:, :512] = mag | (rng.integers(0, 2, size=(n, 512), dtype=np.uint8) << 7)
+    prob.kv_pool[:, 512:528] = np.full((n, 4), 1.0 / 60.0, np.float32).view(np.uint8)
+
+
+def test_fp8_latent_large_values_one_and_two_positions():
+    # Rows of one and two positions over entries whose dequantised latent values lie in [4, 8): a one-position row's
+    # output is its latent row, a two-position row's a convex combination of two.  Every product of a probability
+    # and a tile scale reaches the MFMAs unrounded, so the only error left is the bf16 rounding of the output, at
+    # most half a bf16 ulp of |o| (1/64 in [4, 8)); rounding those products to bf16 would add up to 8 * 2^-9.
+    prob = synth.make_problem(synth.get("batched_paged", batch=4, lengths=[1, 2, 1, 2], anchors=0, recent=0,
+                                        kv_dtype="f8", H=16, k=64, seed=40))
+    _large_fp8_latents(prob)
+    res = gpu_step(prob)
+    ref_o, ref_lse = oracle.sparse_attn_fp8(prob.q, prob.kv_pool, res.idx, prob.row_seq, prob.page_table,
+                                            prob.page_size, prob.softmax_scale)
+    # half a bf16 ulp (8 significant bits) of the larger of |o| and |o_gpu|, plus 2^-12 for the fp32 sums where a
+    # two-position row's mixed signs bring o near zero
+    mag = np.maximum(np.maximum(np.abs(ref_o), np.abs(res.out)), 1e-30)
+    bound = np.exp2(np.floor(np.log2(mag)) - 8) + 2.0 ** -12
+    err = np.abs(res.out - ref_o)
+    say(f"  max err {err.max():.3e}, max |o| {np.abs(ref_o).max():.2f}, worst err / bound {(err / bound).max():.3f}")
+    assert np.abs(ref_o).max() > 4.0
+    assert (err <= bound).all()
+    assert err.max() <= 2e-2
+    assert np.abs(res.lse - ref_lse).max() <= 1e-3
+    assert np.array_equal(res.out_step, res.out)
+
+
 def test_fp8_latent_with_prefill_rows_and_wide_index_keys():
     # FP8 entries under chunked-prefill rows (the tiled indexer, rows of one sequence) and with the shipped
     # 64 x 128 indexer keys over a paged batch
