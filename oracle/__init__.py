@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_oracle_quantize_key.restype = None
         L.dsa_oracle_key_projection.argtypes = [I32, I32, I32, I32, P, P, P]
         L.dsa_oracle_key_projection.restype = ctypes.c_int
+        L.dsa_oracle_query_projection.argtypes = [I32, I32, I32, I32, I32, P, P, P, I32, P, P, P]
+        L.dsa_oracle_query_projection.restype = ctypes.c_int
         L.dsa_oracle_key_append.argtypes = [I32, I32, P, P, P, P, I32, I32, I32, P, P]
         L.dsa_oracle_key_append.restype = ctypes.c_int
         L.dsa_oracle_fp8_entry_key.argtypes = [P, P]
@@ -167,6 +169,26 @@ def key_projection(c, w, c_dtype: str) -> np.ndarray:
     if lib().dsa_oracle_key_projection(R, d_c, d_I, _DT[c_dtype], _p(c), _p(w), _p(k)):
         raise ValueError("oracle key projection rejected its arguments")
     return k
+
+
+def query_projection(h, w_q, w_w, H_I: int, h_dtype: str, idx_dtype: str):
+    """(q [R, H_I, d_I], q_scale [R, H_I] or None, head_w [R, H_I]) of hidden states h [R, d_model] through
+    W_QI [d_model, H_I d_I] and W_w [d_model, H_I]; q holds e4m3 codes ("f8") or fp32 values ("f32")."""
+    code_t = np.uint16 if h_dtype == "bf16" else np.float32
+    h, w_q, w_w = _c(h, code_t), _c(w_q, code_t), _c(w_w, code_t)
+    R, d_model = h.shape
+    if w_q.shape[0] != d_model or w_w.shape != (d_model, H_I) or w_q.shape[1] % H_I:
+        raise ValueError("h, w_q and w_w disagree on their shapes")
+    d_I = w_q.shape[1] // H_I
+    f8 = idx_dtype == "f8"
+    q = np.empty((R, H_I, d_I), np.uint8 if f8 else np.float32)
+    q_scale = np.empty((R, H_I), np.float32) if f8 else None
+    head_w = np.empty((R, H_I), np.float32)
+    rc = lib().dsa_oracle_query_projection(R, d_model, H_I, d_I, _DT[h_dtype], _p(h), _p(w_q), _p(w_w),
+                                           _DT[idx_dtype], _p(q), _p(q_scale), _p(head_w))
+    if rc:
+        raise ValueError(f"oracle query projection rejected its arguments (code {rc})")
+    return q, q_scale, head_w
 
 
 def key_append(k32, positions, row_seq, page_table, page_size: int, pool, pool_scale=None):

@@ -35,6 +35,13 @@
  *      The code is an integer decided by floating point, so the decision is taken in fp32: the key is
  *      rounded once to fp32, then scale = amax / 448 and k_j / scale are IEEE fp32 divisions.  The
  *      projection is the plain fp64 sum over d = 0 .. d_c-1 of exact products (bf16 or fp32 operands).
+ *   5b. Indexer-query projection, the other input of the scorer (lizeman DSA page section 2, stage 1: W_{Q_I} in
+ *      R^{d_model x d_I} maps the token's hidden state h_t to q_I = h_t W_{Q_I}; kgptalkie "How Does the Lightning
+ *      Indexer Score a Token?": the new token is projected into H_I query vectors plus H_I head weights).  Readings:
+ *      W_QI is [d_model, H_I * d_I] (head j owns columns j d_I .. j d_I + d_I - 1) and the head weights are a
+ *      second projection w = h W_w with W_w in R^{d_model x H_I}; both sums are the plain fp64 sum over d
+ *      ascending of exact products, rounded once to fp32 (as for the key); each head's d_I-vector is then
+ *      quantised like a key (max-abs scale, nearest e4m3 code) when the indexer runs in FP8.
  *   6. Sparse attention over the FP8 latent cache ("What Does the GPU Actually Run?": each token's entry is 656
  *      bytes, 512 values in float8_e4m3, 4 fp32 scale factors and the 64 RoPE numbers kept in bf16; "Why Is
  *      Decoding Held Back by Memory?": one 576-number entry per token).  Readings: the parts lie in that order
@@ -256,6 +263,44 @@ int dsa_oracle_key_append(int32_t R, int32_t d_I, const float *k32, const int32_
       memcpy((float *)pool + row * d_I, x, sizeof(float) * (size_t)d_I);
   }
   return 0;
+}
+
+/* ---- 5b. indexer-query projection ------------------------------------------------------------------ */
+
+/* q_I and head weights of R tokens from their hidden states h [R, d_model] (h_dtype BF16 or F32), W_QI
+ * [d_model, H_I * d_I] and W_w [d_model, H_I] in the same dtype.  idx_dtype F8E4M3: q_out receives [R, H_I, d_I]
+ * e4m3 codes and q_scale [R, H_I] one scale per head vector; F32: q_out receives the fp32 values and q_scale is not
+ * written.  head_w [R, H_I] fp32. */
+int dsa_oracle_query_projection(int32_t R, int32_t d_model, int32_t H_I, int32_t d_I, int32_t h_dtype, const void *h,
+                                const void *w_q, const void *w_w, int32_t idx_dtype, void *q_out, float *q_scale,
+                                float *head_w) {
+  if (R < 0 || d_model <= 0 || H_I <= 0 || d_I <= 0 || (idx_dtype != ORACLE_F8E4M3 && idx_dtype != ORACLE_F32))
+    return 1;
+  const int32_t nq = H_I * d_I;
+  double *q = (double *)malloc(sizeof(double) * ((size_t)R * nq + (size_t)R * H_I));
+  if (!q) return 2;
+  double *w = q + (size_t)R * nq;
+  int rc = dsa_oracle_key_projection(R, d_model, nq, h_dtype, h, w_q, q);
+  if (!rc) rc = dsa_oracle_key_projection(R, d_model, H_I, h_dtype, h, w_w, w);
+  if (!rc) {
+    float *x = (float *)malloc(sizeof(float) * (size_t)d_I);
+    if (!x) rc = 2;
+    for (int32_t r = 0; !rc && r < R; ++r) {
+      for (int32_t j = 0; j < H_I; ++j) {
+        const double *v = q + (size_t)r * nq + (size_t)j * d_I;
+        for (int32_t e = 0; e < d_I; ++e) x[e] = (float)v[e];
+        const size_t o = (size_t)r * nq + (size_t)j * d_I;
+        if (idx_dtype == ORACLE_F8E4M3)
+          dsa_oracle_quantize_key(d_I, x, (uint8_t *)q_out + o, q_scale + (size_t)r * H_I + j);
+        else
+          memcpy((float *)q_out + o, x, sizeof(float) * (size_t)d_I);
+        head_w[(size_t)r * H_I + j] = (float)w[(size_t)r * H_I + j];
+      }
+    }
+    free(x);
+  }
+  free(q);
+  return rc;
 }
 
 /* ---- 6. sparse attention over the FP8 latent cache ------------------------------------------------- */

@@ -427,6 +427,75 @@ def test_key_projection_matches_library_matmul():
     assert np.allclose(k, c.astype(np.float64) @ w.astype(np.float64), rtol=1e-12, atol=1e-12)
 
 
+def _enc_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_query_projection_exact_integer_matmul_and_head_columns(dtype):
+    # integer operands: q_I = h W_QI and w = h W_w are exact; head j must own columns j d_I .. j d_I + d_I - 1
+    # (d_model, H_I, d_I all different so a transposed or mis-strided operand fails)
+    rng = np.random.default_rng(11)
+    R, d_model, H_I, d_I = 3, 80, 4, 16
+    h = rng.integers(-6, 7, size=(R, d_model)).astype(np.float32)
+    wq = rng.integers(-6, 7, size=(d_model, H_I * d_I)).astype(np.float32)
+    ww = rng.integers(-6, 7, size=(d_model, H_I)).astype(np.float32)
+    enc = _enc_bf16 if dtype == "bf16" else (lambda a: a)
+    q, qs, w = oracle.query_projection(enc(h), enc(wq), enc(ww), H_I, dtype, "f32")
+    exact_q = (h.astype(np.int64) @ wq.astype(np.int64)).reshape(R, H_I, d_I)
+    assert qs is None and q.shape == (R, H_I, d_I)
+    assert np.array_equal(q, exact_q) and np.array_equal(w, h.astype(np.int64) @ ww.astype(np.int64))
+
+
+def test_query_projection_one_hot_state_gives_known_codes_and_per_head_scales():
+    # h = e_d picks row d of W_QI; head j's slice is an e4m3-representable vector v_j (holding +-448) times 2^j, so
+    # the scale is exactly 2^j and the codes are those of v_j
+    vals = _e4m3_table()
+    rng = np.random.default_rng(12)
+    d_model, H_I, d_I, d = 24, 5, 32, 7
+    wq = rng.standard_normal((d_model, H_I * d_I)).astype(np.float32)
+    want = np.empty((H_I, d_I), np.uint8)
+    for j in range(H_I):
+        codes = rng.integers(0, 0x7F, d_I).astype(np.uint8) | (rng.integers(0, 2, d_I).astype(np.uint8) << 7)
+        codes[rng.integers(d_I)] = 0x7E if j % 2 else 0xFE  # +448 or -448
+        want[j] = codes
+        wq[d, j * d_I:(j + 1) * d_I] = vals[codes] * 2.0 ** j
+    ww = rng.standard_normal((d_model, H_I)).astype(np.float32)
+    h = np.zeros((1, d_model), np.float32)
+    h[0, d] = 1
+    q, qs, w = oracle.query_projection(h, wq, ww, H_I, "f32", "f8")
+    neg_zero = (want & 0x7F) == 0  # -0 in the weight is +0 after the sum
+    assert np.array_equal(q[0][~neg_zero], want[~neg_zero]) and not (q[0][neg_zero] & 0x7F).any()
+    assert np.array_equal(qs[0], 2.0 ** np.arange(H_I)) and np.array_equal(w[0], ww[d])
+
+
+def test_query_projection_zero_state_power_of_two_scaling_and_empty():
+    rng = np.random.default_rng(13)
+    R, d_model, H_I, d_I = 4, 64, 8, 64
+    h = rng.standard_normal((R, d_model)).astype(np.float32)
+    wq = (rng.standard_normal((d_model, H_I * d_I)) / 8).astype(np.float32)
+    ww = (rng.standard_normal((d_model, H_I)) / 8).astype(np.float32)
+    q, qs, w = oracle.query_projection(np.zeros_like(h), wq, ww, H_I, "f32", "f8")
+    assert not q.any() and (qs == 1).all() and not w.any()
+    # scaling h by 2^m scales every sum exactly: codes unchanged, scales and head weights times 2^m
+    q1, s1, w1 = oracle.query_projection(h, wq, ww, H_I, "f32", "f8")
+    q2, s2, w2 = oracle.query_projection(h * 8, wq, ww, H_I, "f32", "f8")
+    assert np.array_equal(q1, q2) and np.array_equal(s2, s1 * 8) and np.array_equal(w2, w1 * 8)
+    # against a library fp64 matmul rounded to fp32 (both within one fp32 rounding of the exact sum)
+    qf, _, wf = oracle.query_projection(h, wq, ww, H_I, "f32", "f32")
+    ref_q = (h.astype(np.float64) @ wq.astype(np.float64)).reshape(R, H_I, d_I)
+    assert np.allclose(qf, ref_q, rtol=2.0 ** -23, atol=1e-30)
+    assert np.allclose(wf, h.astype(np.float64) @ ww.astype(np.float64), rtol=2.0 ** -23, atol=1e-30)
+    # fp8 codes are the per-head quantisation of the fp32 projection
+    for r in range(R):
+        for j in range(H_I):
+            c, sc = oracle.quantize_key(qf[r, j])
+            assert np.array_equal(q1[r, j], c) and s1[r, j] == np.float32(sc)
+    qe, se, we = oracle.query_projection(h[:0], wq, ww, H_I, "f32", "f8")
+    assert qe.shape == (0, H_I, d_I) and se.shape == (0, H_I) and we.shape == (0, H_I)
+
+
 def test_key_append_places_rows_through_the_page_table():
     page_size, d_I = 4, 8
     page_table = np.array([[2, 0, -1], [1, 3, -1]], np.int32)  # sequence 0: pages 2, 0; sequence 1: pages 1, 3
