@@ -320,6 +320,26 @@ def append_sweep(steps: int) -> int:
                               "fp64_tflops": round(flops / us * 1e-6, 3), "fp64_peak_tflops": 78.6}), flush=True)
             del d, pool, scale
             torch.cuda.empty_cache()
+    # indexer-query projection: h [R, 7168] bf16 through W_QI (64 heads x 64) and W_w, e4m3 codes + scales
+    for rows in (1, 64):
+        H_I, d_I, d_model = 64, 64, 7168
+        inp = synth.query_proj_inputs(rows, d_model, H_I, d_I, "bf16", 10)
+        h, wq, ww = (torch.from_numpy(inp[k].view(np.int16)).to(dev) for k in ("h", "w_q", "w_w"))
+        q = torch.empty((rows, H_I, d_I), dtype=torch.uint8, device=dev)
+        qs = torch.empty((rows, H_I), dtype=torch.float32, device=dev)
+        hw = torch.empty((rows, H_I), dtype=torch.float32, device=dev)
+        P = dsa.make_problem(num_rows=rows, idx_heads=H_I, idx_dim=d_I, idx_dtype="f8", kv_dtype="bf16", topk=1,
+                             max_pages=1, num_pages=1, max_row_len=0)
+
+        def qcall(i):
+            dsa.dsa_indexer_query_proj(P, d_model, h, wq, ww, q, qs, hw)
+        us = median_us_per_call(torch, qcall, max(10, min(steps, 100)), stream)
+        wbytes = d_model * (H_I * d_I + H_I) * 2
+        print(json.dumps({"query_proj": True, "tokens": rows, "d_model": d_model, "H_I": H_I, "d_I": d_I,
+                          "us_per_call": round(us, 2), "tokens_per_s": round(rows / us * 1e6, 1),
+                          "weight_read_gbps": round(wbytes / us * 1e-3, 1),
+                          "fp64_tflops": round(2.0 * rows * d_model * (H_I * d_I + H_I) / us * 1e-6, 3)}),
+              flush=True)
     return 0
 
 

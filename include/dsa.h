@@ -184,6 +184,30 @@ dsa_status_t dsa_dense_mla_attn(const dsa_problem_t *problem, const dsa_layout_t
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Indexer-query projection, the producer of step 1's query side: a token's hidden state h is projected to H_I
+ * query vectors q_I = h W_QI (one d_I-wide slice per head) and to H_I head weights w = h W_w (lizeman DSA page,
+ * section 2 stage 1 and the section 3 sketch; "How Does the Lightning Indexer Score a Token?": 64 small query
+ * vectors plus 64 plain head weights per token).  The outputs are what dsa_indexer_scores takes.
+ *   problem     num_rows (R), idx_heads (H_I, a multiple of 8 -- 4 for F32 -- and <= 128), idx_dim (d_I, a power
+ *               of two, 8..128 -- 4..128 for F32), idx_dtype (F8E4M3 or F32), kv_dtype (BF16 or F32: the dtype of
+ *               h, w_q and w_w) are read; no other field is
+ *   d_model     width of the hidden state, a multiple of 8 (4 for F32)
+ *   h           [R, d_model] hidden states, row-major
+ *   w_q         [d_model, H_I * d_I] W_QI, row-major; head j owns columns j*d_I .. j*d_I + d_I - 1
+ *   w_w         [d_model, H_I] the head-weight projection, row-major
+ *   q_idx       [R, H_I, d_I] out.  F8E4M3: codes; F32: the fp32 projection
+ *   q_idx_scale [R, H_I] out (F8E4M3; NULL for F32): per (row, head) scale = max |q| / 448 over the head's d_I
+ *               values (1 for an all-zero head), code = the e4m3 value nearest to q / scale, ties to the even
+ *               code, clamped to +-448, sign bit kept
+ *   head_w      [R, H_I] out, fp32
+ * Every output is the fp64 sum over d ascending of exact products, rounded once to fp32; scales and q / scale
+ * are IEEE fp32 divisions, so codes, scales and weights are reproducible bit for bit.  h, w_q, w_w must be
+ * 16-byte aligned; outputs need their element alignment.  Unsupported shapes give DSA_EUNSUPPORTED.
+ */
+dsa_status_t dsa_indexer_query_proj(const dsa_problem_t *problem, int32_t d_model, const void *h, const void *w_q,
+                                    const void *w_w, void *q_idx, float *q_idx_scale, float *head_w, void *stream);
+
+/*
  * Indexer-key append, the cache write before step 1: the key of each new token is its latent row times the key
  * projection, k_I = c W_KI (kiadev, "How DSA works", stage 1), written into the indexer cache at position
  * positions[r] of sequence row_seq[r] as the cache stores it ("What Does the GPU Actually Run?": FP8 numbers

@@ -54,8 +54,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_step_static.argtypes = [PP, PL, P, P, P, P, P, P, P, P, P, P, P]
         L.dsa_dense_mla_attn.argtypes = [PP, PL, P, P, P, P, P, SZ, P]
         L.dsa_indexer_key_append.argtypes = [PP, PL, P, P, P, P, P, P]
+        L.dsa_indexer_query_proj.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, P]
         for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_step", "dsa_dense_mla_attn",
-                  "dsa_indexer_key_append", "dsa_decode_step_static"):
+                  "dsa_indexer_key_append", "dsa_decode_step_static", "dsa_indexer_query_proj"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [PP, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = SZ
@@ -147,6 +148,12 @@ def dsa_indexer_key_append(problem, layout, positions, src, w_k, k_idx_pool, k_i
     _check(lib().dsa_indexer_key_append(ctypes.byref(problem), ctypes.byref(layout), _ptr(positions, "positions"),
                                         _ptr(src, "src"), _ptr(w_k, "w_k"), _ptr(k_idx_pool, "k_idx_pool"),
                                         _ptr(k_idx_scale, "k_idx_scale"), _stream(stream)))
+
+
+def dsa_indexer_query_proj(problem, d_model, h, w_q, w_w, q_idx, q_idx_scale, head_w, stream=None):
+    _check(lib().dsa_indexer_query_proj(ctypes.byref(problem), d_model, _ptr(h, "h"), _ptr(w_q, "w_q"),
+                                        _ptr(w_w, "w_w"), _ptr(q_idx, "q_idx"), _ptr(q_idx_scale, "q_idx_scale"),
+                                        _ptr(head_w, "head_w"), _stream(stream)))
 
 
 def dsa_decode_step(problem, layout, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx,

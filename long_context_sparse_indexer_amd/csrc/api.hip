@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -326,9 +327,42 @@ dsa_status_t dsa_indexer_key_append(const dsa_problem_t* problem, const dsa_layo
   } else {
     DSA_CHECK((reinterpret_cast<uintptr_t>(src) & 3) == 0, DSA_EINVAL, "fp32 keys must be 4-byte aligned");
   }
+  if (w_k && dsa::key_proj_supported(g, src, w_k))
+    return hip_status(dsa::launch_key_proj(g, positions, src, w_k, k_idx_pool, k_idx_scale,
+                                           static_cast<hipStream_t>(stream)),
+                      "key append launch");
   return hip_status(dsa::launch_key_append(g, positions, src, w_k, k_idx_pool, k_idx_scale,
                                            static_cast<hipStream_t>(stream)),
                     "key append launch");
+}
+
+dsa_status_t dsa_indexer_query_proj(const dsa_problem_t* problem, int32_t d_model, const void* h, const void* w_q,
+                                    const void* w_w, void* q_idx, float* q_idx_scale, float* head_w,
+                                    void* stream) {
+  DSA_CHECK(problem != nullptr, DSA_EINVAL, "problem is NULL");
+  const dsa_problem_t& p = *problem;
+  DSA_CHECK(p.num_rows >= 0 && p.num_rows <= 65535 * 4, DSA_EINVAL, "num_rows = %d not in 0..262140", p.num_rows);
+  DSA_CHECK(p.idx_dtype == DSA_F8E4M3 || p.idx_dtype == DSA_F32, DSA_EINVAL, "idx_dtype = %d invalid", p.idx_dtype);
+  DSA_CHECK(p.kv_dtype == DSA_BF16 || p.kv_dtype == DSA_F32, DSA_EINVAL,
+            "kv_dtype (the dtype of h and the weights) = %d must be BF16 or F32", p.kv_dtype);
+  DSA_CHECK(d_model >= 1, DSA_EINVAL, "d_model = %d < 1", d_model);
+  DSA_CHECK(p.idx_heads >= 1 && p.idx_dim >= 1, DSA_EINVAL, "idx_heads = %d, idx_dim = %d must be >= 1",
+            p.idx_heads, p.idx_dim);
+  DSA_CHECK(h && w_q && w_w && q_idx && head_w, DSA_EINVAL, "h, w_q, w_w, q_idx and head_w must be non-NULL");
+  const bool f8 = p.idx_dtype == DSA_F8E4M3;
+  if (f8)
+    DSA_CHECK(q_idx_scale != nullptr, DSA_EINVAL, "an fp8 query needs q_idx_scale");
+  else
+    DSA_CHECK(q_idx_scale == nullptr, DSA_EINVAL, "an fp32 query takes no scales (pass NULL)");
+  DSA_CHECK(((reinterpret_cast<uintptr_t>(head_w) | reinterpret_cast<uintptr_t>(q_idx_scale) |
+              (f8 ? 0 : reinterpret_cast<uintptr_t>(q_idx))) & 3) == 0,
+            DSA_EINVAL, "head_w, q_idx_scale and fp32 q_idx must be 4-byte aligned");
+  const bool bf16 = p.kv_dtype == DSA_BF16;
+  const char* why = dsa::query_proj_unsupported(d_model, p.idx_heads, p.idx_dim, bf16, h, w_q, w_w);
+  DSA_CHECK(why == nullptr, why && std::strstr(why, "aligned") ? DSA_EINVAL : DSA_EUNSUPPORTED, "%s", why);
+  return hip_status(dsa::launch_query_proj(p.num_rows, d_model, p.idx_heads, p.idx_dim, bf16, f8, h, w_q, w_w, q_idx,
+                                           q_idx_scale, head_w, static_cast<hipStream_t>(stream)),
+                    "query projection launch");
 }
 
 dsa_status_t dsa_dense_mla_attn(const dsa_problem_t* problem, const dsa_layout_t* layout, const void* q,

@@ -24,21 +24,6 @@ namespace {
 constexpr int kStageMaxDc = 512;     // W_KI staged in LDS up to this latent width (bf16)
 constexpr int kGlobalMaxDc = 1024;   // latent width of the unstaged path
 
-// fp32 -> OCP e4m3fn code for |y| <= 448, round to nearest even; the sign bit of y is kept.  Below 2^-6 the codes
-// are the subnormals m * 2^-9 (m = 8 is the smallest normal, code 0x08); above, the fp32 mantissa is cut to three
-// bits with a carry into the exponent field.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
-  const uint32_t b = __float_as_uint(a);
-  const uint32_t e = (b >> 23) - 127 + 7;  // biased e4m3 exponent, 1 .. 15
-  uint32_t m3 = (b >> 20) & 7u;
-  const uint32_t rest = b & 0xfffffu;
-  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
-  return sign | ((e << 3) + m3);  // m3 = 8 carries into the exponent
-}
-
 // kMode 0: the keys arrive as fp32 (no projection).  1: bf16 latent rows and W_KI, W_KI staged in LDS (d_c <= 512,
 // d_I == kCols, 16-byte aligned rows).  2: latent rows and W_KI in the latent dtype, W_KI read from global memory.
 // A thread runs kRpt chains (tokens) for one column; kRpt = 1 spreads few tokens over more blocks.

@@ -117,20 +117,6 @@ __device__ __forceinline__ void store_chunk_fp8(char* buf, char* rope_buf, float
     *reinterpret_cast<v4i*>(rope_buf + (wave * 16 + 8 * j + (lane >> 3)) * kRopeRowB + 16 * (lane & 7)) = f.rope[j];
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-constexpr int kWaitVmOnly(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }  // vmcnt <= n only
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
-
-// Workgroup barrier for data this wave wrote with ds_* instructions.  Unlike __syncthreads() it does not wait
-// for vector-memory operations, so the next chunk's LDS-DMA gather stays in flight across it; the empty asm
-// statements keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Split partials.  A split's o_s is a convex combination of its rows; it is stored as fp16 scaled by 2^-e per
 // (row, split, head), e being the frexp exponent of the head's largest magnitude, so every stored value lies in
 // (-1, 1) and its rounding is below 2^-12 of that maximum.  e is kept beside it.

@@ -41,6 +41,35 @@ typedef unsigned short v8us __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int kWaitVmOnly(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }  // vmcnt <= n only
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);                               // lgkmcnt == 0 only
+
+// Workgroup barrier for data this wave wrote with ds_* instructions.  Unlike __syncthreads() it does not wait
+// for vector-memory operations, so loads issued for later chunks stay in flight across it; the empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// fp32 -> OCP e4m3fn code for |y| <= 448, round to nearest even; the sign bit of y is kept.  Below 2^-6 the codes
+// are the subnormals m * 2^-9 (m = 8 is the smallest normal, code 0x08); above, the fp32 mantissa is cut to three
+// bits with a carry into the exponent field.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t e = (b >> 23) - 127 + 7;  // biased e4m3 exponent, 1 .. 15
+  uint32_t m3 = (b >> 20) & 7u;
+  const uint32_t rest = b & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
+  return sign | ((e << 3) + m3);  // m3 = 8 carries into the exponent
+}
+
 // Physical pool row of logical position `pos` (>= 0) of sequence `seq`.  The logical page is clamped to
 // [0, max_pages) and the page id to [0, num_pages), so corrupt metadata never addresses memory outside the
 // table or the pools.

@@ -61,6 +61,15 @@ size_t attn_workspace_bytes(const Geo& g);
 hipError_t launch_key_append(const Geo& g, const int32_t* positions, const void* src, const void* w, void* pool,
                              float* pool_scale, hipStream_t stream);
 int key_append_max_latent_dim();
+// proj.hip: fp64-chain projections with per-group e4m3 quantisation.
+const char* query_proj_unsupported(int d_model, int H_I, int d_I, bool bf16, const void* h, const void* w_q,
+                                   const void* w_w);  // NULL when supported, else the reason
+hipError_t launch_query_proj(int R, int d_model, int H_I, int d_I, bool bf16, bool f8, const void* h,
+                             const void* w_q, const void* w_w, void* q, float* q_scale, float* head_w,
+                             hipStream_t stream);
+bool key_proj_supported(const Geo& g, const void* src, const void* w);
+hipError_t launch_key_proj(const Geo& g, const int32_t* positions, const void* src, const void* w, void* pool,
+                           float* pool_scale, hipStream_t stream);
 hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const int32_t* topk_idx, void* out,
                        float* lse, void* workspace, const int32_t* pool_rows, hipStream_t stream);
 

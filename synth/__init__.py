@@ -3,4 +3,4 @@
 Holds random draws and storage-format casts only; none of the step's arithmetic.
 """
 from .configs import CONFIGS, ORDER, get  # noqa: F401
-from .gen import Problem, append_inputs, make_problem  # noqa: F401
+from .gen import Problem, append_inputs, make_problem, query_proj_inputs  # noqa: F401

@@ -241,3 +241,30 @@ def append_inputs(prob: Problem, seed: int) -> dict:
     w_bits, _ = _round_kv(w, prob.kv_dtype)
     positions = np.where(prob.row_len > 0, prob.row_len - 1, -1).astype(np.int32)
     return dict(c=np.ascontiguousarray(c_bits), w=np.ascontiguousarray(w_bits), k32=k32, positions=positions)
+
+
+def query_proj_inputs(R: int, d_model: int, H_I: int, d_I: int, act_dtype: str, seed: int) -> dict:
+    """Inputs of the indexer-query projection for R tokens.
+
+      h [R, d_model]: hidden states ~ N(0, 1) in act_dtype ("bf16" bit patterns or "f32"); row 0 is all zero when
+        R > 1 (every head then has scale 1 and zero codes), and one entry per row is 30x larger;
+      w_q [d_model, H_I * d_I]: W_QI ~ N(0, 1/d_model); the columns of head H_I - 1 are zero when H_I > 1 (a zero
+        head in every row);
+      w_w [d_model, H_I]: the head-weight projection ~ N(0, 1/d_model).
+    """
+    rng = _child(seed, 8)
+    h = rng.standard_normal((R, d_model), dtype=np.float32)
+    if R:
+        h[np.arange(R), rng.integers(0, d_model, R)] *= np.float32(30.0)
+    if R > 1:
+        h[0] = 0.0
+    sd = np.float32(math.sqrt(1.0 / d_model))
+    w_q = rng.standard_normal((d_model, H_I * d_I), dtype=np.float32) * sd
+    if H_I > 1:
+        w_q[:, (H_I - 1) * d_I:] = 0.0
+    w_w = rng.standard_normal((d_model, H_I), dtype=np.float32) * sd
+    out = {}
+    for name, a in (("h", h), ("w_q", w_q), ("w_w", w_w)):
+        bits, _ = _round_kv(a, act_dtype)
+        out[name] = np.ascontiguousarray(bits)
+    return out

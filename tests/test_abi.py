@@ -186,6 +186,29 @@ def test_key_append_validation():
     assert call(w=None, src=FAKE + 2) == dsa.DSA_EINVAL and "4-byte" in dsa.dsa_last_error()
 
 
+def test_query_projection_validation():
+    L = dsa.lib()
+
+    def call(p=None, d_model=7168, h=FAKE, wq=FAKE, ww=FAKE, q=FAKE, qs=FAKE, hw=FAKE):
+        p = p if p is not None else _problem()
+        return L.dsa_indexer_query_proj(ctypes.byref(p), d_model, h, wq, ww, q, qs, hw, None)
+    assert L.dsa_indexer_query_proj(None, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == dsa.DSA_EINVAL
+    assert call(h=None) == dsa.DSA_EINVAL and "non-NULL" in dsa.dsa_last_error()
+    assert call(qs=None) == dsa.DSA_EINVAL and "q_idx_scale" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_dtype="f32", kv_dtype="f32")) == dsa.DSA_EINVAL and "no scales" in dsa.dsa_last_error()
+    assert call(p=_problem(kv_dtype="f8")) == dsa.DSA_EINVAL and "kv_dtype" in dsa.dsa_last_error()
+    assert call(d_model=0) == dsa.DSA_EINVAL and "d_model" in dsa.dsa_last_error()
+    assert call(d_model=7164) == dsa.DSA_EUNSUPPORTED and "d_model" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_dim=96)) == dsa.DSA_EUNSUPPORTED and "idx_dim" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_dim=256)) == dsa.DSA_EUNSUPPORTED and "idx_dim" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_heads=60)) == dsa.DSA_EUNSUPPORTED and "idx_heads" in dsa.dsa_last_error()
+    assert call(p=_problem(idx_heads=136)) == dsa.DSA_EUNSUPPORTED and "idx_heads" in dsa.dsa_last_error()
+    assert call(wq=FAKE + 8) == dsa.DSA_EINVAL and "16-byte" in dsa.dsa_last_error()
+    assert call(hw=FAKE + 2) == dsa.DSA_EINVAL and "4-byte" in dsa.dsa_last_error()
+    # R = 0 returns before any HIP call
+    assert call(p=_problem(num_rows=0)) == dsa.DSA_OK
+
+
 def test_zero_rows_enqueue_nothing():
     # R = 0 is valid everywhere and returns before any HIP call (no GPU needed)
     L = dsa.lib()

@@ -89,6 +89,14 @@ def test_append_bf16_projection_into_fp8_cache(d_I):
     _check(prob, synth.append_inputs(prob, 2), project=True)
 
 
+@pytest.mark.parametrize("d_I", [64, 128])
+def test_append_single_token(d_I):
+    # one token: the single-row launch, where one wave runs the chains and the others stage W_KI
+    prob = synth.make_problem(synth.get("batched_paged", batch=1, length_range=(100, 3000), d_I=d_I, anchors=4,
+                                        recent=4))
+    _check(prob, synth.append_inputs(prob, 11), project=True)
+
+
 def test_append_skips_rows_and_prefill_positions():
     # a chunked-prefill layout: 24 consecutive positions of one sequence, written by 24 rows; rows with a
     # negative position or one beyond the page table's reach are skipped
