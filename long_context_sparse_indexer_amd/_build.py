@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "proj.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "proj.hip", "prefill.hip"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -187,15 +187,46 @@ size_t dense_bytes(const dsa::Geo& g) { return dsa::attn_workspace_bytes(g); }
 // selected slot, then one region that the top-k state and, once the selection is written, the attention's split
 // partials share.
 size_t step_bytes(const dsa::Geo& g) {
-  return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) +
-         2 * dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k) +
+  const size_t lists = 2 * dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  if (dsa::prefill_select_supported(g))  // no score matrix: candidate lists and samples, then the partials
+    return lists + std::max(dsa::prefill_select_bytes(g), dsa::attn_workspace_bytes(g));
+  return dsa::align_up(sizeof(float) * (size_t)g.R * step_ld(g)) + lists +
          std::max(dsa::topk_workspace_bytes(g), dsa::attn_workspace_bytes(g));
+}
+
+// A chunked prefill (rows of one sequence, fp8 indexer): sample pass, floors, filter pass, resolve and fallback,
+// then the attention; the selection's workspace is reused by the attention's partials.
+dsa_status_t prefill_step(const dsa::Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                          const void* k_idx_pool, const float* k_idx_scale, const void* q, const void* kv_pool,
+                          int32_t* topk_idx, void* out, float* lse, void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws);
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  ws += dsa::align_up(sizeof(int32_t) * (size_t)g.R * g.k);
+  if (topk_idx) idx = topk_idx;
+  const dsa::PfSel sel = dsa::prefill_select_carve(g, ws);
+  dsa_status_t st;
+  if ((st = hip_status(dsa::launch_indexer_pf(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, sel, 1, s),
+                       "indexer sample launch")) != DSA_OK ||
+      (st = hip_status(dsa::launch_pf_floor(g, sel, s), "floor launch")) != DSA_OK ||
+      (st = hip_status(dsa::launch_indexer_pf(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, sel, 2, s),
+                       "indexer filter launch")) != DSA_OK ||
+      (st = hip_status(dsa::launch_pf_resolve(g, sel, idx, pool_rows, s), "resolve launch")) != DSA_OK ||
+      (st = hip_status(dsa::launch_pf_fallback(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, sel, idx,
+                                               pool_rows, s),
+                       "fallback launch")) != DSA_OK)
+    return st;
+  return hip_status(dsa::launch_attn(g, q, kv_pool, idx, out, lse, ws, pool_rows, s), "attention launch");
 }
 
 // The step on a validated problem and workspace.
 dsa_status_t decode_step(const dsa::Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
                          const void* k_idx_pool, const float* k_idx_scale, const void* q, const void* kv_pool,
                          int32_t* topk_idx, void* out, float* lse, void* workspace, hipStream_t s) {
+  if (dsa::prefill_select_supported(g))
+    return prefill_step(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, q, kv_pool, topk_idx, out, lse,
+                        workspace, s);
   dsa_status_t st;
   char* ws = static_cast<char*>(workspace);
   const int64_t ld = step_ld(g);

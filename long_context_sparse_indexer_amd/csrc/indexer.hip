@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 #include "topk_common.h"
 
 DSA_TIMELINE_UNIT(indexer)
@@ -42,18 +43,16 @@ constexpr int kIdxTile = 4 * kIdxSub * 32;          // positions per 256-thread 
 // HB = number of 32-head blocks (H_I = 32 * HB); KB = number of 64-byte K blocks (d_I = 64 * KB), one
 // v_mfma_f32_32x32x64_f8f6f4 each, chained on one accumulator.  Three waves per SIMD fit d_I = 64; the doubled key
 // and query operands of d_I = 128 leave room for two.
+// The work of one block: row r, tiles bx * tiles_per_block .. of 512 positions (the kernel below, and the prefill
+// fallback, which scores one row with its whole grid).
 template <int HB, int KB>
-__global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
+__device__ __forceinline__ void index_row_tiles(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
-    int tiles_per_block) {
+    int tiles_per_block, int r, int bx) {
   constexpr int H_I = 32 * HB, D_I = 64 * KB;
-  args_to_sgprs(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages, num_pages,
-                log2ps, max_row_len, scores, ld, clear.cnt, tiles_per_block);
-  DSA_STAMP(0, 0);
-  const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   // The row's query operands and epilogue weights depend on nothing but the row: they are requested first, so
@@ -78,11 +77,11 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     }
   }
   const int n = clamp_len(row_len[r], max_row_len);
-  const int64_t first = (int64_t)blockIdx.x * tiles_per_block * kIdxTile;
+  const int64_t first = (int64_t)bx * tiles_per_block * kIdxTile;
   // the row's top-k state, cleared by block 0 as its last work (stores issued earlier would hold up the waits
   // for its key loads, which count in the same in-order counter)
   auto clear_state = [&]() __attribute__((always_inline)) {
-    if (clear.cnt && blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<v4i*>(clear.cnt)[r] = v4i{0, 0, 0, 0};
+    if (clear.cnt && bx == 0 && threadIdx.x == 0) reinterpret_cast<v4i*>(clear.cnt)[r] = v4i{0, 0, 0, 0};
   };
   if (first >= n) {
     clear_state();
@@ -206,6 +205,22 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
   clear_state();
 }
 
+
+template <int HB, int KB>
+__global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
+    int tiles_per_block) {
+  args_to_sgprs(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages, num_pages,
+                log2ps, max_row_len, scores, ld, clear.cnt, tiles_per_block);
+  DSA_STAMP(0, 0);
+  index_row_tiles<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages,
+                          num_pages, log2ps, max_row_len, scores, ld, clear, tiles_per_block, (int)blockIdx.y,
+                          (int)blockIdx.x);
+}
+
 // Chunked prefill: consecutive rows of one sequence score the same keys, so the contraction is a real GEMM
 // [rows * H_I x d_I] x [d_I x n] (DeepSeek Sparse Attention explained: over a prefill the indexer's cost stays
 // quadratic in the context).  A block owns kPfRows rows of one sequence and kPfPasses * kPfTile positions.
@@ -239,14 +254,45 @@ constexpr int kPfTile = 4 * kPfSub * 32;  // positions per pass of a 256-thread 
 constexpr int kPfPasses = 8;              // passes per block: the row staging is paid once per 4096 positions
 
 // KB = d_I / 64 K blocks: each (head block, subtile) unit chains KB fp8 MFMAs, the linear MFMA takes 4 KB K-steps.
-template <int HB, int KB>
+// The filter pass's hand-over of one 64-lane group of scores: the lanes in `m` (this lane's entry when `keep`)
+// take consecutive places in the row's LDS stage; places past its capacity go straight to the row's list, each
+// with an atomic of its own (a row far denser in candidates than its floor promised).
+__device__ __forceinline__ void stage_candidates(uint64_t m, bool keep, uint64_t entry, uint64_t* stage, uint32_t* n,
+                                                 int cap, uint32_t* row_cnt, uint64_t* row_list) {
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(m);
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const uint32_t idx = base + (uint32_t)__popcll(m & below);
+  if (keep) {
+    if (idx < (uint32_t)cap) {
+      stage[idx] = entry;
+    } else {
+      const uint32_t at = atomicAdd(row_cnt, 1u);
+      if (at < (uint32_t)kPfCap) row_list[at] = entry;
+    }
+  }
+}
+
+// kMode 0: the scores of every visible position into `scores`.  kMode 1 (sample pass): the block's rows score
+// kPfSample sampled positions, 128 runs of 32 consecutive positions spread evenly over the positions every row of
+// the block sees (all of them when fewer), into sel.samp at the sample's own indices.  kMode 2 (filter pass): no
+// score leaves the block; each position whose key reaches its row's floor is staged in LDS as a candidate, and
+// the block appends each row's candidates to the row's list with one atomic.
+template <int HB, int KB, int kMode>
 __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, int R, int rows_per_seq, int tiles_per_group,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, PfSel sel) {
   constexpr int H_I = 32 * HB, D = 64 * KB;
+  // candidates of each row staged per block (filter pass): as many as keep two blocks (d_I = 128) or three per CU
+  constexpr int kStage = KB == 2 ? 64 : 192;
+  __shared__ uint64_t stage[kMode == 2 ? kPfRows : 1][kMode == 2 ? kStage : 1];
+  __shared__ uint32_t stage_n[kPfRows], stage_base[kPfRows], floor_lds[kPfRows];
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32 * KB];  // lane l's fp8 A operands
   __shared__ __attribute__((aligned(16))) float w_lds[kPfRows][HB][2][16];          // wq of each lane half's heads
   __shared__ __attribute__((aligned(16))) __bf16 u_lds[kPfRows / 8][4 * KB][64][8];  // linear-MFMA A operands
@@ -261,6 +307,26 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
   __syncthreads();
   int nmax = 0;
   for (int q = 0; q < rows; ++q) nmax = max(nmax, n_lds[q]);
+  // sample pass: virtual position v is position (v / 32) * step + v % 32; nmax becomes the sample's length
+  int step = 32;
+  if constexpr (kMode == 1) {
+    int nmin = n_lds[0];
+    for (int q = 1; q < rows; ++q) nmin = min(nmin, n_lds[q]);
+    if (nmin >= kPfSample) {
+      step = (nmin / (kPfSample / 32)) & ~31;
+      nmax = kPfSample;
+    } else {
+      nmax = nmin;
+    }
+    if ((int)threadIdx.x < rows) sel.samp_len[r0 + threadIdx.x] = nmax;
+  }
+  if constexpr (kMode == 2) {
+    if ((int)threadIdx.x < kPfRows) {
+      stage_n[threadIdx.x] = 0u;
+      floor_lds[threadIdx.x] = (int)threadIdx.x < rows ? sel.floor[r0 + threadIdx.x] : 0u;
+    }
+    // published by the barrier after the operand staging below
+  }
   if (span0 >= nmax) return;  // uniform: no row of the tile sees these positions
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -357,12 +423,24 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
 #pragma unroll
     for (int s = 0; s < kPfSub; ++s) {
       const int64_t base = tile0 + wave_u * (kPfSub * 32) + s * 32;  // uniform
-      const int64_t bp = base < nmax ? base : nmax - 1;
-      const int lp = (int)min(bp >> log2ps, (int64_t)max_pages - 1);
-      int page = page_table[(int64_t)seq * max_pages + lp];
-      page = min(max(page, 0), num_pages - 1);
-      const int64_t row0 = ((int64_t)page << log2ps) | (bp & ((1 << log2ps) - 1));
-      prow[s] = row0 + (base < nmax ? min((int64_t)col, nmax - 1 - base) : 0);
+      if constexpr (kMode == 1) {
+        // a sampled run: 32 consecutive positions from a multiple of 32, inside one page; a subtile past the
+        // sample's end rereads the last run
+        const int64_t vb = base < nmax ? base : (int64_t)((nmax - 1) & ~31);
+        const int64_t pb = (vb >> 5) * step;
+        const int lp = (int)min(pb >> log2ps, (int64_t)max_pages - 1);
+        int page = page_table[(int64_t)seq * max_pages + lp];
+        page = min(max(page, 0), num_pages - 1);
+        const int64_t row0 = ((int64_t)page << log2ps) | (pb & ((1 << log2ps) - 1));
+        prow[s] = row0 + min((int64_t)col, nmax - 1 - vb);
+      } else {
+        const int64_t bp = base < nmax ? base : nmax - 1;
+        const int lp = (int)min(bp >> log2ps, (int64_t)max_pages - 1);
+        int page = page_table[(int64_t)seq * max_pages + lp];
+        page = min(max(page, 0), num_pages - 1);
+        const int64_t row0 = ((int64_t)page << log2ps) | (bp & ((1 << log2ps) - 1));
+        prow[s] = row0 + (base < nmax ? min((int64_t)col, nmax - 1 - base) : 0);
+      }
     }
 #pragma unroll
     for (int s = 0; s < kPfSub; ++s)
@@ -423,7 +501,10 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
         {
           const v4i nv = *reinterpret_cast<const v4i*>(&n_lds[8 * g + 4 * hq]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nq[e] = __builtin_amdgcn_readfirstlane(nv[e]);
+          for (int e = 0; e < 4; ++e) {
+            nq[e] = __builtin_amdgcn_readfirstlane(nv[e]);
+            if (kMode == 1 && nq[e] > 0) nq[e] = nmax;  // a sampled row's stored length is the sample's
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -439,8 +520,9 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
             for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
           }
           // stores past the row's visible length fall outside the buffer and are dropped
-          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(r0 + q) * ld, (short)0, nq[e] * 4,
-                                                              kBufferWord3);
+          float* const dst_row = kMode == 1 ? sel.samp + (int64_t)(r0 + q) * kPfSample : scores + (int64_t)(r0 + q) * ld;
+          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(dst_row, (short)0, nq[e] * 4, kBufferWord3);
+          const uint32_t fl = kMode == 2 ? floor_lds[q] : 0u;
           constexpr int U = 2 * HB;             // units per subtile pair
           constexpr int K = (kPfSub / 2) * U;   // units per row
           float ab[2] = {0.f, 0.f};
@@ -475,7 +557,16 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
                 const float s1 = fmaf(ownf, lin2[p][1][e], ab[1]);
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
                 const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], soff, 0);
+                if constexpr (kMode == 2) {
+                  const int pos = (int)tile0 + (voff[p] >> 2);
+                  const uint32_t key = order_key(skm[p] * total);
+                  const bool keep = pos < nq[e] && (key >> 12) >= fl;
+                  const uint64_t m = __ballot(keep);
+                  if (m) stage_candidates(m, keep, ((uint64_t)pos << 32) | key, stage[q], &stage_n[q], kStage,
+                                          sel.cnt + r0 + q, sel.cand + (int64_t)(r0 + q) * kPfCap);
+                } else {
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], soff, 0);
+                }
               }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -483,6 +574,21 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
           }
         }
       }
+    }
+  }
+  if constexpr (kMode == 2) {
+    // each row's staged candidates go to its list in one range, reserved with one atomic
+    __syncthreads();
+    if ((int)threadIdx.x < rows) {
+      const uint32_t c = min(stage_n[threadIdx.x], (uint32_t)kStage);
+      stage_base[threadIdx.x] = c ? atomicAdd(sel.cnt + r0 + threadIdx.x, c) : 0u;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows * kStage; i += 256) {
+      const int q = i / kStage, j = i - q * kStage;
+      const uint32_t at = stage_base[q] + (uint32_t)j;
+      if (j < (int)min(stage_n[q], (uint32_t)kStage) && at < (uint32_t)kPfCap)
+        sel.cand[(int64_t)(r0 + q) * kPfCap + at] = stage[q][j];
     }
   }
 }
@@ -533,15 +639,95 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
       g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr}, per);
 }
 
+// Grid-wide barrier of a persistent launch whose blocks are all resident: each block adds one to *bar when it
+// arrives (release) and waits until all nblocks blocks of this round have (acquire); the count only grows, so
+// round `gen` waits for gen * nblocks.  A wait that outlasts its bound gives up and is counted in *timeouts.
+__device__ __forceinline__ void grid_sync(uint32_t* bar, uint32_t nblocks, uint32_t& gen, uint32_t* timeouts) {
+  __syncthreads();
+  ++gen;
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = gen * nblocks;
+    uint32_t spins = 0;
+    while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == (1u << 22)) {
+        atomicAdd(timeouts, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Rows of a chunked prefill whose sampled floor misjudged them (fewer candidates than k_eff, more than the list
+// holds, a threshold beyond the candidate histogram, or more than 1024 keys tied at the threshold) are selected
+// here, exactly and one at a time: the whole grid scores the row's positions into sel.fbuf with the per-row
+// kernel's tiles, and block 0 runs the three-digit radix select over the stored row.  The grid is one block per
+// CU, so every block is resident for the barriers; with no such row every block returns at once.
 template <int HB, int KB>
+__global__ __launch_bounds__(256) void pf_fallback_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int num_pages, int log2ps, int max_row_len, int R, int k, PfSel sel, int32_t* __restrict__ topk_idx,
+    int32_t* __restrict__ pool_rows) {
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t scan[256 / 64 + 1];
+  const uint32_t nfail = min(sel.ctl[0], (uint32_t)R);
+  if (nfail == 0) return;
+  uint32_t gen = 0;
+  for (uint32_t i = 0; i < nfail; ++i) {
+    const int r = sel.fail[i];
+    const int n = clamp_len(row_len[r], max_row_len);
+    const int keff = min(k, n);
+    const int ntile = (n + kIdxTile - 1) / kIdxTile;
+    for (int t = blockIdx.x; t < ntile; t += gridDim.x)
+      index_row_tiles<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs,
+                              max_pages, num_pages, log2ps, max_row_len, sel.fbuf, 0, TopkState{nullptr}, 1, r, t);
+    grid_sync(sel.ctl + 1, gridDim.x, gen, sel.ctl + 2);
+    if (blockIdx.x == 0) {
+      const int32_t* gpt = page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages;
+      int32_t* out = topk_idx + (int64_t)r * k;
+      int32_t* rows_out = pool_rows ? pool_rows + (int64_t)r * k : nullptr;
+      const ListSink sink{out, rows_out, RowMap{gpt, max_pages, num_pages, log2ps}};
+      select_and_write<256>(RowList{sel.fbuf}, n, (uint32_t)keff, keff, sink, h, scan);
+      for (int j = keff + threadIdx.x; j < k; j += 256) {
+        out[j] = -1;
+        if (rows_out) rows_out[j] = -1;
+      }
+    }
+    grid_sync(sel.ctl + 1, gridDim.x, gen, sel.ctl + 2);  // sel.fbuf is free for the next row
+  }
+}
+
+template <int HB, int KB, int kMode>
 void launch_f8_tiled(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const float* head_w,
-                     const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, hipStream_t stream) {
+                     const uint8_t* kp, const float* k_idx_scale, float* scores, int64_t ld, const PfSel& sel,
+                     hipStream_t stream) {
   const int tiles_per_group = (g.rows_per_seq + kPfRows - 1) / kPfRows;
   const int groups = (g.R + g.rows_per_seq - 1) / g.rows_per_seq;
-  dim3 grid((g.max_row_len + kPfPasses * kPfTile - 1) / (kPfPasses * kPfTile), groups * tiles_per_group);
-  indexer_f8_tiled_kernel<HB, KB><<<grid, 256, 0, stream>>>(
+  const int span = kMode == 1 ? kPfSample : g.max_row_len;  // the sample pass covers kPfSample virtual positions
+  dim3 grid((span + kPfPasses * kPfTile - 1) / (kPfPasses * kPfTile), groups * tiles_per_group);
+  indexer_f8_tiled_kernel<HB, KB, kMode><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, g.R, g.rows_per_seq, tiles_per_group, scores, ld);
+      g.log2ps, g.max_row_len, g.R, g.rows_per_seq, tiles_per_group, scores, ld, sel);
+}
+
+template <int kMode>
+void launch_tiled_mode(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                       const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld, const PfSel& sel,
+                       hipStream_t stream) {
+  auto* qp = static_cast<const uint8_t*>(q_idx);
+  auto* kp = static_cast<const uint8_t*>(k_idx_pool);
+  if (g.d_I == 128) {
+    if (g.H_I == 64) launch_f8_tiled<2, 2, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+    else launch_f8_tiled<1, 2, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+  } else if (g.H_I == 64) {
+    launch_f8_tiled<2, 1, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+  } else {
+    launch_f8_tiled<1, 1, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+  }
 }
 
 // fp8 rows that come in groups sharing a sequence take the tiled kernel (d_I = 64 or 128)
@@ -555,16 +741,7 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
   if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
   if (indexer_tiled(g)) {
     if (fuse) return hipErrorInvalidValue;  // the tiled kernel does not clear the top-k state
-    auto* qp = static_cast<const uint8_t*>(q_idx);
-    auto* kp = static_cast<const uint8_t*>(k_idx_pool);
-    if (g.d_I == 128) {
-      if (g.H_I == 64) launch_f8_tiled<2, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
-      else launch_f8_tiled<1, 2>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
-    } else if (g.H_I == 64) {
-      launch_f8_tiled<2, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
-    } else {
-      launch_f8_tiled<1, 1>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, stream);
-    }
+    launch_tiled_mode<0>(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, scores, ld, PfSel{}, stream);
     return hipGetLastError();
   }
   if (g.idx_dtype == 2 /* F8E4M3 */) {
@@ -587,6 +764,44 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
                                                     g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps,
                                                     g.max_row_len, g.H_I, g.d_I, scores, ld);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_pf(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                             const void* k_idx_pool, const float* k_idx_scale, const PfSel& sel, int mode,
+                             hipStream_t stream) {
+  if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
+  if (!indexer_tiled(g)) return hipErrorInvalidValue;
+  if (mode == 1)
+    launch_tiled_mode<1>(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, nullptr, 0, sel, stream);
+  else
+    launch_tiled_mode<2>(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, nullptr, 0, sel, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_fallback(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                              const void* k_idx_pool, const float* k_idx_scale, const PfSel& sel, int32_t* topk_idx,
+                              int32_t* pool_rows, hipStream_t stream) {
+  if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  auto* qp = static_cast<const uint8_t*>(q_idx);
+  auto* kp = static_cast<const uint8_t*>(k_idx_pool);
+#define DSA_PF_FALLBACK(HB, KB)                                                                                   \
+  pf_fallback_kernel<HB, KB><<<std::max(1, cus), 256, 0, stream>>>(                                              \
+      qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages, \
+      g.log2ps, g.max_row_len, g.R, g.k, sel, topk_idx, pool_rows)
+  if (g.d_I == 128) {
+    if (g.H_I == 64) DSA_PF_FALLBACK(2, 2);
+    else DSA_PF_FALLBACK(1, 2);
+  } else if (g.H_I == 64) {
+    DSA_PF_FALLBACK(2, 1);
+  } else {
+    DSA_PF_FALLBACK(1, 1);
+  }
+#undef DSA_PF_FALLBACK
   return hipGetLastError();
 }
 

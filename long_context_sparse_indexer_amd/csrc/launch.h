@@ -36,6 +36,38 @@ hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_sc
                           const void* k_idx_pool, const float* k_idx_scale, float* scores, int64_t ld,
                           const TopkState* fuse, hipStream_t stream);
 
+// Chunked prefill without the score matrix (prefill.hip, and the tiled indexer's sample and filter passes).
+constexpr int kPfSample = 4096;  // sampled positions per row: 128 runs of 32
+constexpr int kPfCap = 12288;    // candidates a row keeps
+struct PfSel {
+  float* samp;         // [R, kPfSample] scores of each row's sampled positions
+  int32_t* samp_len;   // [R] sampled positions written for the row
+  uint32_t* floor;     // [R] the row's floor: 20-bit key prefix a candidate reaches
+  uint32_t* cnt;       // [R] candidates reserved (may exceed kPfCap: the row then falls back)
+  uint64_t* cand;      // [R, kPfCap] candidates, position << 32 | key, in no particular order
+  uint32_t* ctl;       // [4]: rows that fell back, grid-barrier counter, barrier time-outs, unused
+  int32_t* fail;       // [R] rows that fell back
+  float* fbuf;         // [ld] scores of the row being resolved by the fallback
+};
+bool prefill_select_supported(const Geo& g);
+size_t prefill_select_bytes(const Geo& g);
+PfSel prefill_select_carve(const Geo& g, void* workspace);
+// mode 1: sampled scores into sel.samp; mode 2: candidates at or above each row's floor into sel.cand
+hipError_t launch_indexer_pf(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                             const void* k_idx_pool, const float* k_idx_scale, const PfSel& sel, int mode,
+                             hipStream_t stream);
+// prefill.hip: floors from the samples (also clears the candidate counters and the fallback state), then, after
+// the filter pass, each row's selection (pool rows too when pool_rows is non-NULL); rows the sample misjudged go
+// to the fallback list
+hipError_t launch_pf_floor(const Geo& g, const PfSel& sel, hipStream_t stream);
+hipError_t launch_pf_resolve(const Geo& g, const PfSel& sel, int32_t* topk_idx, int32_t* pool_rows,
+                             hipStream_t stream);
+// indexer.hip: the fallback, which scores each listed row in full into sel.fbuf and selects over it (one
+// persistent launch; it returns at once when the list is empty)
+hipError_t launch_pf_fallback(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,
+                              const void* k_idx_pool, const float* k_idx_scale, const PfSel& sel, int32_t* topk_idx,
+                              int32_t* pool_rows, hipStream_t stream);
+
 // topk.hip
 constexpr int kTopkMaxBlocksPerRow = 1024;
 constexpr int kTopkChunk = 4096;

@@ -209,6 +209,16 @@ def test_query_projection_validation():
     assert call(p=_problem(num_rows=0)) == dsa.DSA_OK
 
 
+def test_prefill_step_workspace_holds_no_score_matrix():
+    # a 4096-row chunk over 131072 positions: the step keeps candidate lists and samples, not R x n scores
+    p = _problem(num_rows=4096, rows_per_seq=4096, max_row_len=131072, max_pages=2048, num_pages=2048)
+    need = dsa.dsa_workspace_bytes(p, dsa.DSA_OP_STEP)
+    assert 0 < need < 4096 * 131072 * 4 // 3
+    # per-row decode rows still store their score rows
+    d = _problem(num_rows=8, max_row_len=131072, max_pages=2048, num_pages=2048)
+    assert dsa.dsa_workspace_bytes(d, dsa.DSA_OP_STEP) >= 8 * 131072 * 4
+
+
 def test_zero_rows_enqueue_nothing():
     # R = 0 is valid everywhere and returns before any HIP call (no GPU needed)
     L = dsa.lib()

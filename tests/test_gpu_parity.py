@@ -115,6 +115,24 @@ def test_prefill_tiled_index_dim_128(rows, H_I):
     _run(synth.get("prefill_paged", rows=rows, H_I=H_I, batch=2, k=700, H=16, d_I=128))
 
 
+def test_prefill_selection_ties_take_the_fallback():
+    # zero head weights make every score 0: each row's 9000 candidates tie at the threshold, more than the resolve
+    # sorts out itself, so every row goes to the fallback, which must take the lowest positions
+    def zero_weights(p):
+        p.head_w[:] = 0.0
+    prob, res = _run(synth.get("prefill_chunk", cache_len=9000, rows=24, H=16), mutate=zero_weights)
+    for r in range(prob.R):
+        keff = min(prob.k, int(prob.row_len[r]))
+        assert np.array_equal(res.idx_step[r, :keff], np.arange(keff)), f"row {r}: not the lowest positions"
+
+
+def test_prefill_selection_rows_past_the_candidate_list():
+    # zero head weights again, on rows longer than the candidate list (20000 positions): the filter overflows
+    def zero_weights(p):
+        p.head_w[:] = 0.0
+    _run(synth.get("prefill_chunk", cache_len=20000, rows=16, H=16, k=512), mutate=zero_weights)
+
+
 def test_prefill_rows_through_the_per_row_kernel():
     # the same prefill chunk declared as independent rows runs the per-row kernel and must agree as well
     _run(synth.get("prefill_paged", rows=20, H=16), fields=dict(rows_per_seq=1))
