@@ -363,38 +363,46 @@ def summarize_trace(d: str) -> int:
     return 0
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, step_kernels: list[str]) -> int:
-    """Per-kernel FETCH_SIZE / WRITE_SIZE means from two `--pmc` runs, calibrated against a plain device copy of
-    copy_bytes (read and written once), and the HBM bytes of one decode step (one dispatch of each kernel named
-    in step_kernels); writes the record bench.py reads for `traffic`."""
+FLUSH_BYTES = 768 << 20  # the cache flush reads and writes this many bytes once (cache_flush)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, step_kernels: list[str]) -> int:
+    """Per-kernel FETCH_SIZE / WRITE_SIZE means (KiB per dispatch) from two `--pmc` runs of the bench, each scaled by
+    what the same counter reads for the bench's cache flush, a plain elementwise pass that reads and writes
+    FLUSH_BYTES once; then the HBM bytes of one step (one dispatch of each kernel whose name contains one of
+    step_kernels).  Prints the record bench.py reads for `traffic`."""
     def per_kernel(d, counter):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         acc = {}
         for r in _read_csv(files[0]):
             if r.get("Counter_Name") != counter:
                 continue
-            name = r["Kernel_Name"]
-            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    copy_k = [k for k in fetch if "copyBuffer" in k]
-    fscale = copy_bytes / (fetch[copy_k[0]] * 1024) if copy_k else 1.0
-    wscale = copy_bytes / (write[copy_k[0]] * 1024) if copy_k else 1.0
+    flush = [k for k in fetch if "CUDAFunctorOnSelf_add<unsigned char>" in k]
+    if not flush:
+        print("no cache-flush dispatch in the counter runs", file=sys.stderr)
+        return 1
+    fscale = FLUSH_BYTES / (fetch[flush[0]] * 1024)
+    wscale = FLUSH_BYTES / (write[flush[0]] * 1024)
     kern = {}
     for k in sorted(set(fetch) | set(write)):
-        if "copyBuffer" in k:
+        if k == flush[0] or "copyBuffer" in k:
             continue
         kern[k] = {"fetch_kib": round(fetch.get(k, 0.0), 1), "write_kib": round(write.get(k, 0.0), 1),
                    "hbm_read_bytes": round(fetch.get(k, 0.0) * 1024 * fscale),
                    "hbm_write_bytes": round(write.get(k, 0.0) * 1024 * wscale)}
-    total = 0
+    total, used = 0, []
     for s in step_kernels:
-        m = [k for k in kern if k.startswith(s)]
+        m = [k for k in kern if s in k]
         if m:
+            used.append(m[0])
             total += kern[m[0]]["hbm_read_bytes"] + kern[m[0]]["hbm_write_bytes"]
-    rec = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
-           "calib_copy_bytes": copy_bytes, "step_kernels": step_kernels, "hbm_bytes_per_step": total, "kernels": kern}
+    rec = {"kernel_source_hash": kernel_source_hash(), "calibration": "cache flush, %d bytes read and written" % FLUSH_BYTES,
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4), "step_kernels": used,
+           "hbm_bytes_per_step": total, "kernels": kern}
     print(json.dumps(rec, indent=1))
     return 0
 
@@ -424,11 +432,9 @@ def main() -> int:
     ap.add_argument("--crossover-rows", type=int, default=1)
     ap.add_argument("--append", action="store_true",
                     help="time the indexer-key append for 1, 64 and 4096 tokens at d_I = 128 and 64, then exit")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="after the run, copy a buffer of this many MiB 4 times (reference dispatches for byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--step-kernels", default="")
+    ap.add_argument("--step-kernels", default="", help="';'-separated parts of the names of one step's kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding design); "
@@ -437,8 +443,7 @@ def main() -> int:
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc, args.calib_copy_mib << 20,
-                             [s for s in args.step_kernels.split(",") if s])
+        return summarize_pmc(*args.summarize_pmc, [s for s in args.step_kernels.split(";") if s])
     if args.sweep:
         return sweep(args.steps, args.repeats)
     if args.crossover:
@@ -553,16 +558,6 @@ def main() -> int:
         "phases": phases,
         "gen_seconds": round(gen_s, 2),
     }
-
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calib_copy_bytes"] = n
-        del src, dst
 
     if not args.no_cpu_baseline:
         import copy
