@@ -459,7 +459,6 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
       skm[p] = 0.5f * k_scale[srow];
       voff[p] = (wave * (kPfSub * 32) + (2 * p + half) * 32 + col) * 4;
     }
-    const int soff = (int)tile0 * 4;
 
 #pragma unroll 1
     for (int g = 0; g < kPfRows / 8; ++g) {
@@ -519,9 +518,11 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) wq[hb][i] = w_lds[q][hb][half][i];
           }
-          // stores past the row's visible length fall outside the buffer and are dropped
+          // the buffer starts at the pass's first position and ends at the row's visible length, so a store past
+          // the row's end falls outside it (on its bounds-checked offset) and is dropped
           float* const dst_row = kMode == 1 ? sel.samp + (int64_t)(r0 + q) * kPfSample : scores + (int64_t)(r0 + q) * ld;
-          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(dst_row, (short)0, nq[e] * 4, kBufferWord3);
+          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(dst_row + tile0, (short)0, (nq[e] - (int)tile0) * 4,
+                                                              kBufferWord3);
           const uint32_t fl = kMode == 2 ? floor_lds[q] : 0u;
           constexpr int U = 2 * HB;             // units per subtile pair
           constexpr int K = (kPfSub / 2) * U;   // units per row
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
                   if (m) stage_candidates(m, keep, ((uint64_t)pos << 32) | key, stage[q], &stage_n[q], kStage,
                                           sel.cnt + r0 + q, sel.cand + (int64_t)(r0 + q) * kPfCap);
                 } else {
-                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], soff, 0);
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(skm[p] * total), rsrc, voff[p], 0, 0);
                 }
               }
             }

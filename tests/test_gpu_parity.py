@@ -133,6 +133,29 @@ def test_prefill_selection_rows_past_the_candidate_list():
     _run(synth.get("prefill_chunk", cache_len=20000, rows=16, H=16, k=512), mutate=zero_weights)
 
 
+def test_tiled_scores_leave_positions_past_each_row_untouched():
+    # rows of one sequence (the tiled indexer) into a score buffer whose stride is tight and no multiple of the
+    # 512-position pass: every entry at or past a row's length keeps its sentinel, every entry before it is written
+    from synth.device import upload
+    prob = synth.make_problem(synth.get("prefill_chunk", cache_len=9000, rows=24, H=16))
+    say(f"sentinel case R={prob.R} n={int(prob.row_len.min())}..{int(prob.row_len.max())}")
+    d = upload(prob, "cuda:0")
+    P = dsa.make_problem(**d.fields)
+    L = dsa.make_layout(d.row_seq, d.row_len, d.page_table)
+    ld = (int(prob.row_len.max()) + 3) // 4 * 4 + 4
+    assert ld % 512 != 0 and P.rows_per_seq >= 8
+    sentinel = 12345.0
+    scores = torch.full((prob.R, ld), sentinel, dtype=torch.float32, device="cuda:0")
+    dsa.dsa_indexer_scores(P, L, d.q_idx, d.q_idx_scale, d.head_w, d.k_idx_pool, d.k_idx_scale, scores, ld)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    for r in range(prob.R):
+        n = int(prob.row_len[r])
+        assert (got[r, n:] == sentinel).all(), f"row {r}: entries past n = {n} were written"
+        assert not (got[r, :n] == sentinel).any(), f"row {r}: an entry below n = {n} was not written"
+    say("  ok: only each row's visible positions were written")
+
+
 def test_prefill_rows_through_the_per_row_kernel():
     # the same prefill chunk declared as independent rows runs the per-row kernel and must agree as well
     _run(synth.get("prefill_paged", rows=20, H=16), fields=dict(rows_per_seq=1))
