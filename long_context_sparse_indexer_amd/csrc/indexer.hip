@@ -289,8 +289,8 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_tiled_kernel(
     int num_pages, int log2ps, int max_row_len, int R, int rows_per_seq, int tiles_per_group,
     float* __restrict__ scores, int64_t ld, PfSel sel) {
   constexpr int H_I = 32 * HB, D = 64 * KB;
-  // candidates of each row staged per block (filter pass): as many as keep two blocks (d_I = 128) or three per CU
-  constexpr int kStage = KB == 2 ? 64 : 192;
+  // candidates of each row staged per block (filter pass; d_I = 64 only, which keeps three blocks per CU)
+  constexpr int kStage = KB == 2 ? 1 : 192;
   __shared__ uint64_t stage[kMode == 2 ? kPfRows : 1][kMode == 2 ? kStage : 1];
   __shared__ uint32_t stage_n[kPfRows], stage_base[kPfRows], floor_lds[kPfRows];
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kPfRows][HB][64][32 * KB];  // lane l's fp8 A operands
@@ -721,6 +721,11 @@ void launch_tiled_mode(const Geo& g, const void* q_idx, const float* q_idx_scale
                        hipStream_t stream) {
   auto* qp = static_cast<const uint8_t*>(q_idx);
   auto* kp = static_cast<const uint8_t*>(k_idx_pool);
+  if constexpr (kMode != 0) {  // the sample and filter passes serve d_I = 64 (prefill_select_supported)
+    if (g.H_I == 64) launch_f8_tiled<2, 1, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+    else launch_f8_tiled<1, 1, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
+    return;
+  }
   if (g.d_I == 128) {
     if (g.H_I == 64) launch_f8_tiled<2, 2, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
     else launch_f8_tiled<1, 2, kMode>(g, qp, q_idx_scale, head_w, kp, k_idx_scale, scores, ld, sel, stream);
@@ -772,7 +777,7 @@ hipError_t launch_indexer_pf(const Geo& g, const void* q_idx, const float* q_idx
                              const void* k_idx_pool, const float* k_idx_scale, const PfSel& sel, int mode,
                              hipStream_t stream) {
   if (g.R == 0 || g.max_row_len == 0) return hipSuccess;
-  if (!indexer_tiled(g)) return hipErrorInvalidValue;
+  if (!indexer_tiled(g) || g.d_I != 64) return hipErrorInvalidValue;
   if (mode == 1)
     launch_tiled_mode<1>(g, q_idx, q_idx_scale, head_w, k_idx_pool, k_idx_scale, nullptr, 0, sel, stream);
   else

@@ -312,8 +312,11 @@ __global__ __launch_bounds__(1024) void pf_resolve_kernel(const int32_t* __restr
 
 }  // namespace
 
+// d_I = 128 keeps the stored scores: its filter pass has LDS for 64 staged candidates per row and block only (two
+// blocks per CU beside the doubled query operands), and the overflow's per-candidate atomics made its step slower
+// (8.8 ms against 7.0 ms for the 4096-row chunk).
 bool prefill_select_supported(const Geo& g) {
-  return indexer_tiled(g) && g.max_row_len <= (1 << 20) && g.k <= 4096;
+  return indexer_tiled(g) && g.d_I == 64 && g.max_row_len <= (1 << 20) && g.k <= 4096;
 }
 
 size_t prefill_select_bytes(const Geo& g) {
