@@ -32,7 +32,6 @@ namespace dsa {
 namespace {
 
 constexpr int kPfSmallRow = kPfCap / 2;  // rows this short keep every position as a candidate
-constexpr int kPfMaxTies = 1024;         // keys equal to the threshold key the resolve sorts out itself
 
 __device__ __forceinline__ void list_failed(const PfSel& sel, int r) {
   const uint32_t at = atomicAdd(sel.ctl, 1u);
@@ -127,187 +126,28 @@ __global__ __launch_bounds__(1024) void pf_resolve_kernel(const int32_t* __restr
                                                           int max_pages, int num_pages, int log2ps, PfSel sel,
                                                           int32_t* __restrict__ topk_idx,
                                                           int32_t* __restrict__ pool_rows) {
-  constexpr int NT = 1024, NW = NT / 64;
-  constexpr int kWords = (1 << kBitsLog2) / 32, kWpt = kWords / NT;  // bitmap words, per thread
-  constexpr int kPer = kPfCap / NT;                                   // candidates per thread
-  static_assert(kWpt >= 1 && kWpt % 4 == 0 && kPer * NT == kPfCap, "bitmap and list split evenly");
+  constexpr int kWords = (1 << kBitsLog2) / 32;
   __shared__ __attribute__((aligned(16))) uint32_t bits[kWords];
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
-  __shared__ int32_t eq_pos[kPfMaxTies];
-  __shared__ uint32_t low[64];
-  __shared__ __attribute__((aligned(16))) uint32_t wt[2 * NW];
-  __shared__ uint32_t scan[NW + 1];
-  __shared__ uint32_t s_bin, s_above, s_nb, s_nlow, s_neq, s_T, s_need;
-  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63;
+  __shared__ BitmapScratch S;
+  const int r = blockIdx.x, t = threadIdx.x;
   const int n = clamp_len(row_len[r], max_row_len), keff = min(k, n);
   int32_t* out = topk_idx + (int64_t)r * k;
   int32_t* rows_out = pool_rows ? pool_rows + (int64_t)r * k : nullptr;
-  const RowMap map{page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages, max_pages, num_pages, log2ps};
+  const ListSink sink{out, rows_out,
+                      RowMap{page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages, max_pages, num_pages,
+                             log2ps}};
   if (keff >= n) {  // the whole row
-    for (int i = t; i < k; i += NT) {
-      out[i] = i < n ? i : -1;
-      if (rows_out) rows_out[i] = i < n ? map.row(i) : -1;
-    }
+    for (int i = t; i < k; i += 1024) sink.put_or_pad(i, i < n ? i : -1);
     return;
   }
-  const uint32_t c = sel.cnt[r], fl = sel.floor[r];
-  if (c < (uint32_t)keff || c > (uint32_t)kPfCap || n > (1 << kBitsLog2)) {  // uniform
+  const bool ok = bitmap_select<kWords / 1024>(n, keff, sel.floor[r], sel.cnt[r], sel.cand + (int64_t)r * kPfCap,
+                                               sink, bits, h, S);
+  if (!ok) {  // uniform
     if (t == 0) list_failed(sel, r);
     return;
   }
-  uint64_t e[kPer];
-  const uint64_t* list = sel.cand + (int64_t)r * kPfCap;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) e[j] = list[min(j * NT + t, (int)c - 1)];  // entries past c dropped below
-  for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
-#pragma unroll
-  for (int q = 0; q < kWpt; ++q) bits[t * kWpt + q] = 0u;
-  if (t == 0) {
-    s_bin = kTopkBins - 1;
-    s_above = 0u;
-    s_nb = 0u;
-    s_nlow = 0u;
-    s_neq = 0u;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (j * NT + t < (int)c) atomicAdd(&h[cand_bin((uint32_t)e[j], fl)], 1u);
-  __syncthreads();
-  {  // the bin of the k_eff-th largest key: thread t owns bins (NT - 1 - t) * 4 .. +4, top bins first
-    const v4i y = reinterpret_cast<const v4i*>(h)[NT - 1 - t];
-    const uint32_t hv[4] = {(uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]};
-    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
-    uint32_t tot;
-    uint32_t above = block_scan1<NT>(local, wt, tot);
-    if (above < (uint32_t)keff && above + local >= (uint32_t)keff) {
-      for (int b = 3; b >= 0; --b) {
-        if (above + hv[b] >= (uint32_t)keff) {
-          s_bin = (uint32_t)((NT - 1 - t) * 4 + b);
-          s_above = above;
-          s_nb = hv[b];
-          break;
-        }
-        above += hv[b];
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t bin = s_bin, nb = s_nb;
-  if (bin == kTopkBins - 1) {  // uniform: the threshold lies in the open-ended top bin
-    if (t == 0) list_failed(sel, r);
-    return;
-  }
-  const uint32_t prefix = fl + bin;
-  uint32_t need = (uint32_t)keff - s_above;  // keys of the threshold's prefix still to take
-  if (nb <= 64u) {
-    // the low 12 bits of the keys of that prefix, ranked by one wave
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t key = (uint32_t)e[j];
-      if (j * NT + t < (int)c && (key >> 12) == prefix) low[atomicAdd(&s_nlow, 1u)] = key & 0xfffu;
-    }
-    __syncthreads();
-    if (t < 64) {
-      const uint32_t dx = lane < (int)nb ? low[lane] : 0u;
-      uint32_t gt = 0, ge = 0;
-      for (uint32_t y = 0; y < nb; ++y) {
-        const uint32_t dy = low[y];
-        gt += dy > dx;
-        ge += dy >= dx;
-      }
-      const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);
-      const int src = __builtin_ctzll(hit);
-      if (lane == src) {
-        s_T = (prefix << 12) | dx;
-        s_need = need - gt;
-      }
-    }
-  } else {
-    for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t key = (uint32_t)e[j];
-      if (j * NT + t < (int)c && (key >> 12) == prefix) atomicAdd(&h[key & 0xfffu], 1u);
-    }
-    __syncthreads();
-    const v4i y = reinterpret_cast<const v4i*>(h)[NT - 1 - t];
-    const uint32_t hv[4] = {(uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]};
-    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
-    uint32_t tot;
-    uint32_t above = block_scan1<NT>(local, wt + NW, tot);
-    if (above < need && above + local >= need) {
-      for (int b = 3; b >= 0; --b) {
-        if (above + hv[b] >= need) {
-          s_T = (prefix << 12) | (uint32_t)((NT - 1 - t) * 4 + b);
-          s_need = need - above;
-          break;
-        }
-        above += hv[b];
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t T = s_T;
-  need = s_need;  // keys equal to T to take, lowest positions first
-  // mark the keys above T; list the keys equal to T
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (j * NT + t >= (int)c) continue;
-    const uint32_t key = (uint32_t)e[j];
-    const int32_t pos = (int32_t)(e[j] >> 32);
-    if (key > T) {
-      atomicOr(&bits[pos >> 5], 1u << (pos & 31));
-    } else if (key == T) {
-      const uint32_t at = atomicAdd(&s_neq, 1u);
-      if (at < (uint32_t)kPfMaxTies) eq_pos[at] = pos;
-    }
-  }
-  __syncthreads();
-  const uint32_t neq = s_neq;
-  if (neq > (uint32_t)kPfMaxTies) {  // uniform: too many ties to sort out here
-    if (t == 0) list_failed(sel, r);
-    return;
-  }
-  if (t < (int)neq) {  // an equal key is taken when fewer than `need` equal keys lie at lower positions
-    const int32_t p = eq_pos[t];
-    uint32_t rank = 0;
-    for (uint32_t j = 0; j < neq; ++j) rank += eq_pos[j] < p;
-    if (rank < need) atomicOr(&bits[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-  // slots in position order: thread t owns bitmap words t kWpt .. +kWpt
-  uint32_t w[kWpt], cntw = 0;
-#pragma unroll
-  for (int q = 0; q < kWpt / 4; ++q) {
-    const v4i y = reinterpret_cast<const v4i*>(bits)[t * (kWpt / 4) + q];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      w[4 * q + x] = (uint32_t)y[x];
-      cntw += (uint32_t)__popc((uint32_t)y[x]);
-    }
-  }
-  uint32_t tot;
-  uint32_t slot = block_scan1<NT>(cntw, wt, tot);
-#pragma unroll
-  for (int q = 0; q < kWpt; ++q) {
-    uint32_t b = w[q];
-    while (b) {
-      const int bit = __builtin_ctz(b);
-      b &= b - 1;
-      const int32_t pos = (t * kWpt + q) * 32 + bit;
-      if (slot < (uint32_t)keff) {
-        out[slot] = pos;
-        if (rows_out) rows_out[slot] = map.row(pos);
-      }
-      ++slot;
-    }
-  }
-  for (int i = keff + t; i < k; i += NT) {
-    out[i] = -1;
-    if (rows_out) rows_out[i] = -1;
-  }
+  for (int i = keff + t; i < k; i += 1024) sink.put_or_pad(i, -1);
 }
 
 }  // namespace

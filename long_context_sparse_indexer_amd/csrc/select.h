@@ -1,5 +1,5 @@
-// The resolve step of the top-k selection, shared by the standalone selection kernel and by the sparse-attention
-// kernel of the fused step (which resolves the selection inside each block and keeps only its own slots).
+// The resolve step of the top-k selection (the resolve kernel of topk.hip), and the whole-row radix select that the
+// prefill fallback (indexer.hip) runs over a stored row.
 //
 // For each row keep the k_eff = min(k, n) largest scores (DeepSeek Sparse Attention explained, "How Does the
 // Selector Pick 1,024?"); equal scores are taken lowest position first; the selected positions are numbered in
@@ -75,6 +75,10 @@ struct ListSink {
   __device__ void put(uint32_t slot, int32_t pos) const {
     out[slot] = pos;
     if (rows_out) rows_out[slot] = map.row(pos);
+  }
+  __device__ void put_or_pad(uint32_t slot, int32_t pos) const {  // pos -1: a padding slot
+    out[slot] = pos;
+    if (rows_out) rows_out[slot] = pos >= 0 ? map.row(pos) : -1;
   }
 };
 
@@ -498,6 +502,171 @@ __device__ void resolve_finish(const float* __restrict__ row, int n, int keff, c
   if constexpr (kStamp >= 0) DSA_STAMP(kStamp, 10);
   if (open) select_and_write<NT>(L, (int)len, need, keff, sink, S.h, S.scan);
   else write_selection_lds<NT>(L, (int)len, T, need, keff, sink);
+}
+
+// Selection of one row from an unordered candidate list through a bitmap over the row's positions.  The candidates
+// (position << 32 | order-preserving key, every position whose key's 20-bit prefix reaches the floor `fl`; c of
+// them) are counted by prefix relative to the floor in an LDS histogram, which gives the prefix of the k_eff-th
+// largest key; its low 12 bits are settled among the keys of that prefix (one wave when they are at most 64, else a
+// second histogram).  With T that key, the keys above T and the lowest-position keys equal to T, as many as are
+// still needed, are marked in the bitmap, and a popcount scan of the bitmap hands every selected position to the
+// sink at its slot, in increasing position order.  Returns false, having handed over nothing, when the list cannot
+// settle the row: fewer than k_eff or more than kCap candidates, a threshold in the open-ended top bin, or more than
+// kMaxTies keys equal to T.  Called by all 1024 threads (the result is uniform); `bits` holds kWpt * 1024 words,
+// covering the row's n positions, h kTopkBins words.
+constexpr int kMaxTies = 1024;
+struct BitmapScratch {
+  int32_t eq_pos[kMaxTies];
+  uint32_t low[64];
+  alignas(16) uint32_t wt[2 * 16];
+  uint32_t bin, above, nb, nlow, neq, T, need;
+};
+template <int kWpt>
+__device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const uint64_t* __restrict__ list,
+                              const ListSink& sink, uint32_t* bits, uint32_t* h, BitmapScratch& S) {
+  constexpr int NT = 1024, NW = NT / 64;
+  constexpr int kPer = kCap / NT;  // candidates per thread
+  static_assert(kWpt >= 1 && kWpt % 4 == 0 && kPer * NT == kCap, "bitmap and list split evenly");
+  const int t = threadIdx.x, lane = t & 63;
+  if (c < (uint32_t)keff || c > (uint32_t)kCap || n > kWpt * NT * 32) return false;
+  uint64_t e[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) e[j] = list[min(j * NT + t, (int)c - 1)];  // entries past c dropped below
+  for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) bits[t * kWpt + q] = 0u;
+  if (t == 0) {
+    S.bin = kTopkBins - 1;
+    S.above = 0u;
+    S.nb = 0u;
+    S.nlow = 0u;
+    S.neq = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j * NT + t < (int)c) atomicAdd(&h[cand_bin((uint32_t)e[j], fl)], 1u);
+  __syncthreads();
+  {  // the bin of the k_eff-th largest key: thread t owns bins (NT - 1 - t) * 4 .. +4, top bins first
+    const v4i y = reinterpret_cast<const v4i*>(h)[NT - 1 - t];
+    const uint32_t hv[4] = {(uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]};
+    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+    uint32_t tot;
+    uint32_t above = block_scan1<NT>(local, S.wt, tot);
+    if (above < (uint32_t)keff && above + local >= (uint32_t)keff) {
+      for (int b = 3; b >= 0; --b) {
+        if (above + hv[b] >= (uint32_t)keff) {
+          S.bin = (uint32_t)((NT - 1 - t) * 4 + b);
+          S.above = above;
+          S.nb = hv[b];
+          break;
+        }
+        above += hv[b];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = S.bin, nb = S.nb;
+  if (bin == kTopkBins - 1) return false;  // uniform: the threshold lies in the open-ended top bin
+  const uint32_t prefix = fl + bin;
+  uint32_t need = (uint32_t)keff - S.above;  // keys of the threshold's prefix still to take
+  if (nb <= 64u) {
+    // the low 12 bits of the keys of that prefix, ranked by one wave
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = (uint32_t)e[j];
+      if (j * NT + t < (int)c && (key >> 12) == prefix) S.low[atomicAdd(&S.nlow, 1u)] = key & 0xfffu;
+    }
+    __syncthreads();
+    if (t < 64) {
+      const uint32_t dx = lane < (int)nb ? S.low[lane] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t y = 0; y < nb; ++y) {
+        const uint32_t dy = S.low[y];
+        gt += dy > dx;
+        ge += dy >= dx;
+      }
+      const uint64_t hit = __ballot(lane < (int)nb && gt < need && need <= ge);
+      if (lane == __builtin_ctzll(hit)) {
+        S.T = (prefix << 12) | dx;
+        S.need = need - gt;
+      }
+    }
+  } else {
+    for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = (uint32_t)e[j];
+      if (j * NT + t < (int)c && (key >> 12) == prefix) atomicAdd(&h[key & 0xfffu], 1u);
+    }
+    __syncthreads();
+    const v4i y = reinterpret_cast<const v4i*>(h)[NT - 1 - t];
+    const uint32_t hv[4] = {(uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]};
+    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+    uint32_t tot;
+    uint32_t above = block_scan1<NT>(local, S.wt + NW, tot);
+    if (above < need && above + local >= need) {
+      for (int b = 3; b >= 0; --b) {
+        if (above + hv[b] >= need) {
+          S.T = (prefix << 12) | (uint32_t)((NT - 1 - t) * 4 + b);
+          S.need = need - above;
+          break;
+        }
+        above += hv[b];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t T = S.T;
+  need = S.need;  // keys equal to T to take, lowest positions first
+  // mark the keys above T; list the keys equal to T
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j * NT + t >= (int)c) continue;
+    const uint32_t key = (uint32_t)e[j];
+    const int32_t pos = (int32_t)(e[j] >> 32);
+    if (key > T) {
+      atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+    } else if (key == T) {
+      const uint32_t at = atomicAdd(&S.neq, 1u);
+      if (at < (uint32_t)kMaxTies) S.eq_pos[at] = pos;
+    }
+  }
+  __syncthreads();
+  const uint32_t neq = S.neq;
+  if (neq > (uint32_t)kMaxTies) return false;  // uniform: too many ties to sort out here
+  if (t < (int)neq) {  // an equal key is taken when fewer than `need` equal keys lie at lower positions
+    const int32_t p = S.eq_pos[t];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < neq; ++j) rank += S.eq_pos[j] < p;
+    if (rank < need) atomicOr(&bits[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // slots in position order: thread t owns bitmap words t kWpt .. +kWpt
+  uint32_t w[kWpt], cntw = 0;
+#pragma unroll
+  for (int q = 0; q < kWpt / 4; ++q) {
+    const v4i y = reinterpret_cast<const v4i*>(bits)[t * (kWpt / 4) + q];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      w[4 * q + x] = (uint32_t)y[x];
+      cntw += (uint32_t)__popc((uint32_t)y[x]);
+    }
+  }
+  uint32_t tot;
+  uint32_t slot = block_scan1<NT>(cntw, S.wt, tot);
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) {
+    uint32_t b = w[q];
+    while (b) {
+      const int bit = __builtin_ctz(b);
+      b &= b - 1;
+      if (slot < (uint32_t)keff) sink.put(slot, (t * kWpt + q) * 32 + bit);
+      ++slot;
+    }
+  }
+  return true;
 }
 
 // resolve_issue then resolve_finish, for callers with nothing to overlap.

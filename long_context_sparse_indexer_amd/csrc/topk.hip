@@ -9,8 +9,8 @@
 //            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram.  The
 //            block then writes the keys whose first 20 bits reach the floor, in position order, into a segment of
 //            the row's candidate list.
-//   resolve  one 1024-thread block per row runs the resolve step of select.h and writes the list.  The fused step
-//            instead lets every sparse-attention block resolve the row itself and keep its own slots.
+//   resolve  one 1024-thread block per row runs the resolve step of select.h and writes the list (and, in the
+//            fused step, the pool row of every selected slot for the attention).
 #include <algorithm>
 
 #include "common.h"
@@ -396,6 +396,48 @@ __global__ __launch_bounds__(kRes) void topk_resolve_kernel(const float* __restr
   DSA_STAMP(2, 5);
 }
 
+// One block per row: the selection of select.h's bitmap_select from the filter's candidate list, written in
+// increasing position order, padded with -1, with the pool row of each slot when asked.  A row the list cannot
+// settle (the sample overshot, the list overflowed, heavy ties) is selected over its stored scores instead.  The
+// page ids of the row's sequence are staged in LDS when the bitmap leaves room (rows up to 2^17 positions).
+template <int kBitsLog2>
+__global__ __launch_bounds__(kRes) void topk_bitmap_resolve_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                   const int32_t* __restrict__ row_len,
+                                                                   int max_row_len, int k,
+                                                                   const uint32_t* __restrict__ thr,
+                                                                   const uint32_t* __restrict__ cnt,
+                                                                   const uint64_t* __restrict__ cand,
+                                                                   int32_t* __restrict__ topk_idx, PoolRows pr) {
+  static_assert(kRes == 1024, "bitmap_select runs on 1024 threads");
+  constexpr int kWords = (1 << kBitsLog2) / 32;
+  constexpr bool kStagePages = kBitsLog2 <= 17;
+  __shared__ __attribute__((aligned(16))) uint32_t bits[kWords];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ BitmapScratch S;
+  __shared__ int32_t pt[kStagePages ? kResPages : 1];
+  args_to_sgprs(scores, ld, row_len, max_row_len, k, thr, cnt, cand, topk_idx, pr.out, pr.row_seq, pr.page_table,
+                pr.num_seqs, pr.max_pages, pr.num_pages, pr.log2ps);
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int n = clamp_len(row_len[r], max_row_len);
+  const int keff = min(k, n);
+  const int32_t* gpt = pr.out ? pr.page_table + (int64_t)clamp_seq(pr.row_seq[r], pr.num_seqs) * pr.max_pages : nullptr;
+  const bool pt_lds = kStagePages && pr.out && pr.max_pages <= kResPages;
+  const ListSink sink{topk_idx + (int64_t)r * k, pr.out ? pr.out + (int64_t)r * k : nullptr,
+                      RowMap{pt_lds ? pt : gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
+  if (keff >= n) {
+    const ListSink gsink{sink.out, sink.rows_out, RowMap{gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
+    for (int i = t; i < k; i += kRes) gsink.put_or_pad(i, i < n ? i : -1);
+    return;
+  }
+  if (pt_lds) stage_page_row<kRes>(pt, gpt, pr.max_pages);  // visible after bitmap_select's first barrier
+  if (!bitmap_select<kWords / kRes>(n, keff, thr[4 * r], cnt[4 * r + 2], cand + (int64_t)r * kCap, sink, bits, h,
+                                    S)) {
+    __syncthreads();
+    select_and_write<kRes>(RowList{scores + (int64_t)r * ld}, n, (uint32_t)keff, keff, sink, h, S.wt);
+  }
+  for (int i = keff + t; i < k; i += kRes) sink.put_or_pad(i, -1);
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(const Geo& g) {
@@ -437,10 +479,16 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   else
     topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr,
                                                   w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
-  topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
-                                                w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx,
-                                                PoolRows{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages,
-                                                         g.num_pages, g.log2ps});
+  const PoolRows pr{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps};
+  if (g.max_row_len <= (1 << 17))
+    topk_bitmap_resolve_kernel<17><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
+                                                             w.cand, topk_idx, pr);
+  else if (g.max_row_len <= (1 << 20))
+    topk_bitmap_resolve_kernel<20><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
+                                                             w.cand, topk_idx, pr);
+  else
+    topk_resolve_kernel<<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
+                                                  w.seg_cnt, w.seg_off, w.cand, w.nblk, topk_idx, pr);
   return hipGetLastError();
 }
 
