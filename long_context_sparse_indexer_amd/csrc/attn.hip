@@ -583,7 +583,93 @@ __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restri
   }
 }
 
-template <int NW, bool kSplit>
+// FP8 entries in the all-heads kernel.  A chunk's 32 entries (656 bytes each, 1312 16-byte pieces) are gathered
+// raw by LDS-DMA into one of four staging slots, packed at 656-byte strides: load i of a chunk moves pieces
+// 64 i .. 64 i + 63, wave w issuing loads w, w + 4, ...; the lanes past the last piece reread a piece of a selected
+// entry into the slot's padding.  One chunk ahead of its use, every thread widens 64 codes of the staged chunk to
+// bf16 (exact: an e4m3 value has a 4-bit significand) into a code buffer laid out like the bf16 rows, and the
+// first four lanes of each row copy its tile scales into a table [tile][slot parity][slot / 2], from which a lane
+// reads the scales of its 16 S^T rows as four 16-byte loads.  The scales are applied outside the MFMAs: QK
+// accumulates each 128-dim tile on its own and adds it in with the slot's scale; PV multiplies each probability by
+// its slot's scale for the tile of the output columns and splits that product into a bf16 head and a bf16 rest,
+// both of which go through the MFMA.  No dequantised value is rounded.  The RoPE dims are read by QK straight from
+// the staging slot (656 bytes = 164 dwords, 4 banks mod 32 like the code rows, so the permuted A rows stay
+// conflict-free).
+constexpr int kF8RopeByte = kDC + 16;          // RoPE values follow the codes and the four scales
+constexpr int kF8Pieces = kCW * kF8Entry / 16;  // 1312
+constexpr int kF8Loads = (kF8Pieces + 63) / 64;  // 21 LDS-DMA loads per chunk
+constexpr int kF8LoadsPerWave = (kF8Loads + 3) / 4;  // wave 0 issues 6, waves 1..3 issue 5
+constexpr int kF8Slot = kF8Loads * 1024;         // staging slot bytes
+constexpr int kF8Ring = 4;                       // staging slots: converting, computing (RoPE), two in flight
+constexpr int kCodeTab = kCW * kRowW;            // offset of the scale table in a code buffer
+constexpr int kCodeBuf = kCodeTab + 4 * kCW * 4;
+static_assert(kF8Entry % 16 == 0 && kF8Pieces <= kF8Loads * 64, "pieces fit the loads");
+
+__device__ __forceinline__ void gather_chunk_f8(const uint8_t* __restrict__ kv, const int32_t* prow, int dummy,
+                                                char* slot, int wave, int lane) {
+  // The load index and the LDS address are wave-uniform (scalar registers), and the lane's piece is recomputed
+  // per call: hoisted out of the chunk loop, the per-load offsets had been kept in vector registers and spilled,
+  // and a spill reload waits for every gather in flight (vmcnt counts both).
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)slot));
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int j = 0; j < kF8LoadsPerWave; ++j) {
+    const int i = w + 4 * j;
+    if (i < kF8Loads) {
+      const int pc = 64 * i + lane;
+      int row = pc / (kF8Entry / 16), piece = pc - row * (kF8Entry / 16);
+      int pr = dummy;
+      if (pc < kF8Pieces) {
+        pr = prow[row];
+        if (pr < 0) pr = dummy;
+      } else {
+        piece = 0;
+      }
+      const uint8_t* src = kv + (int64_t)pr * kF8Entry + 16 * piece;
+      const uint32_t lds = base + 1024u * (uint32_t)i;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+    }
+  }
+}
+
+// Thread t widens codes 16 g + 128 j (g = t % 8, j = 0..3) of row t / 8: the eight lanes of a row read 128
+// contiguous bytes per load, and write 32 bytes each per tile as two 16-byte stores, lanes 4..7 of a row in the
+// opposite order so that the eight lanes of one store cover all 32 banks.
+__device__ __forceinline__ void convert_chunk_f8(const char* slot, char* code, int t) {
+  asm volatile("" : "+v"(t));  // recomputed per call, like the gather offsets
+  const int row = t >> 3, g = t & 7, sw = (g >> 2) & 1;
+  const char* src = slot + row * kF8Entry;
+  v4i c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const v4i*>(src + 16 * g + 128 * j);
+  float sc = 0.f;
+  if (g < 4) sc = *reinterpret_cast<const float*>(src + kDC + 4 * g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v4i w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t d = (uint32_t)c[j][2 * h + x];
+        const v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, false);
+        const v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, true);
+        w[h][2 * x] = (int)__builtin_bit_cast(uint32_t, lo);
+        w[h][2 * x + 1] = (int)__builtin_bit_cast(uint32_t, hi);
+      }
+    char* dst = code + row * kRowW + 256 * j + 32 * g;
+    const v4i w0 = sw ? w[1] : w[0], w1 = sw ? w[0] : w[1];  // select whole vectors: no per-lane indexing
+    *reinterpret_cast<v4i*>(dst + 16 * sw) = w0;
+    *reinterpret_cast<v4i*>(dst + 16 * (1 - sw)) = w1;
+  }
+  if (g < 4) reinterpret_cast<float*>(code + kCodeTab)[g * kCW + (row & 1) * (kCW / 2) + (row >> 1)] = sc;
+}
+
+// kFp8: the latent rows are 656-byte FP8 entries (four waves only), dequantised into hi and lo bf16 rows; the
+// queries are 576 wide (latent, then RoPE dims).
+template <int NW, bool kSplit, bool kFp8>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const unsigned short* __restrict__ q, const unsigned short* __restrict__ kv, const int32_t* __restrict__ topk_idx,
     int k, const int32_t* __restrict__ pool_rows, const int32_t* __restrict__ row_len, int max_row_len,
@@ -593,6 +679,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     float* __restrict__ lse, unsigned short* __restrict__ part_o, int32_t* __restrict__ part_exp,
     float* __restrict__ part_lse) {
   static_assert(kCW % NW == 0, "every wave gathers the same number of rows");
+  static_assert(!kFp8 || NW == 4, "FP8 entries: eight rows per wave and chunk");
   args_to_sgprs(q, kv, topk_idx, k, pool_rows, row_len, max_row_len, row_seq, page_table, num_seqs, max_pages,
                 num_pages, log2ps, H, nsplit, units, split_len);
   constexpr int kRows = kCW / NW;  // rows each wave gathers per chunk
@@ -600,7 +687,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   // which must fit vmcnt (at most 63 outstanding loads per wave)
   constexpr int kDepth = kBufW < 63 / kRows + 1 ? kBufW : 63 / kRows + 1;
   static_assert(kDepth >= 2 && (kDepth - 1) * kRows <= 63, "gathers in flight fit vmcnt");
-  __shared__ __attribute__((aligned(16))) char kv_lds[kBufW][kCW * kRowW];
+  // bf16 rows: a ring of kBufW chunks filled by LDS-DMA; FP8 entries: two code buffers, then kF8Ring staging slots
+  constexpr int kPool = kFp8 ? 2 * kCodeBuf + kF8Ring * kF8Slot : kBufW * kCW * kRowW;
+  __shared__ __attribute__((aligned(16))) char kv_pool_lds[kPool];
   __shared__ int32_t prow_lds[kWideMaxSplitLen];           // physical row of every slot, -1 = no position
   __shared__ uint32_t valid_lds[kWideMaxSplitLen / 32];    // bit per slot: it has a position
   __shared__ int wave_first[NW], overflow;  // first slot with a position among each wave's slots
@@ -622,10 +711,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   // Q^T as B operands: lane (half, col) = head hw + col, latent columns 16 ks + 8 half .. +8; issued first so that
   // they load while the positions and then the page-table entries arrive
   v8bf qb[kDC / 16];
+  v8bf qr[kFp8 ? kRope / 16 : 1];  // RoPE dims of the FP8 path
   {
-    const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kDC + 8 * half;
+    constexpr int kQW = kFp8 ? kDC + kRope : kDC;  // query row width
+    const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kQW + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
+    if constexpr (kFp8)
+#pragma unroll
+      for (int ks = 0; ks < kRope / 16; ++ks) qr[ks] = *reinterpret_cast<const v8bf*>(qrow + kDC + 16 * ks);
   }
   v16f o[kDC / 32];  // O tile dt: column 32 dt + col, head 8 (i >> 2) + 4 half + (i & 3)
 
@@ -693,13 +787,60 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const int S16 = lane & 15, qh = (lane >> 4) & 1;  // transpose-read lane roles
     // One chunk: S^T tile, softmax, O += P C.  qk_only: only track the per-head maximum (into m_ref);
     // otherwise accumulate O and l.
-    auto chunk = [&](const int c, const char* cur, const bool qk_only) __attribute__((always_inline)) {
+    // FP8 entries: `cur` is the chunk's code buffer and `raw` its staging slot (RoPE dims).
+    auto chunk = [&](const int c, const char* cur, const char* raw, const bool qk_only) __attribute__((always_inline)) {
       // S^T: slots 0..31 of the chunk (A rows) x this wave's 32 heads (B columns).  The A operands are read
       // kQkDepth K-steps ahead of their MFMAs; sched_barrier keeps the compiler from hoisting further.
       v16f st = {};
-      {
+      const int arow_i = 8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1);  // the slot this lane's A row holds
+      if constexpr (kFp8) {
+        // each 128-dim tile of codes on an accumulator of its own, added in with the scales of this lane's rows
+        // (register i holds slot 8 (i >> 2) + 2 (i & 3) + half, whose scale sits at entry i of the half's table
+        // row), then the RoPE K-steps straight onto st.  Three K-steps of A operands ahead: with four, one Q
+        // register was spilled, and its reload (vmcnt) waited for every gather in flight.
+        constexpr int kQkDepth = 3;
+        const char* arow = cur + arow_i * kRowW + 16 * half;
+        const float* tab = reinterpret_cast<const float*>(cur + kCodeTab) + half * (kCW / 2);
+        v8bf abuf[kQkDepth];
+#pragma unroll
+        for (int ks = 0; ks < kQkDepth; ++ks) abuf[ks] = *reinterpret_cast<const v8bf*>(arow + 32 * ks);
+        v16f acc[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v16f& at = acc[t & 1];
+          at = v16f{};
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int ks = 8 * t + kk;
+            at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kQkDepth], qb[ks], at, 0, 0, 0);
+            if (ks + kQkDepth < kDC / 16)
+              abuf[ks % kQkDepth] = *reinterpret_cast<const v8bf*>(arow + 32 * (ks + kQkDepth));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (t > 0) {  // the previous tile, while this one's MFMAs run
+            const v16f& ap = acc[(t - 1) & 1];
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const v4f s4 = *reinterpret_cast<const v4f*>(tab + (t - 1) * kCW + 4 * a4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) st[4 * a4 + e] = fmaf(ap[4 * a4 + e], s4[e], st[4 * a4 + e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const v4f s4 = *reinterpret_cast<const v4f*>(tab + 3 * kCW + 4 * a4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[4 * a4 + e] = fmaf(acc[1][4 * a4 + e], s4[e], st[4 * a4 + e]);
+        }
+        const char* rrow = raw + arow_i * kF8Entry + kF8RopeByte + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < kRope / 16; ++ks)
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(rrow + 32 * ks), qr[ks], st, 0,
+                                                       0, 0);
+      } else {
         constexpr int kQkDepth = 8;
-        const char* arow = cur + (8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1)) * kRowW + 16 * half;
+        const char* arow = cur + arow_i * kRowW + 16 * half;
         v8bf abuf[kQkDepth];
 #pragma unroll
         for (int ks = 0; ks < kQkDepth; ++ks) abuf[ks] = *reinterpret_cast<const v8bf*>(arow + 32 * ks);
@@ -755,25 +896,64 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
           const v4bf hi4 = lds_tr_read(p + 8 * kRowW);
           return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        v8bf bbuf[kPvDepth];
+        if constexpr (kFp8) {
+          // tile t of the output columns (dt = 4 t .. 4 t + 3): each probability times its slot's scale for the
+          // tile, as a bf16 head and a bf16 rest, on two MFMAs per (K-step, column tile)
+          const float* tab = reinterpret_cast<const float*>(cur + kCodeTab) + half * (kCW / 2);
+          constexpr int kTileSteps = (kCW / 16) * 4;  // (K-step, column tile) pairs of one tile
+          v8bf bbuf[kPvDepth];
+          auto pvb = [&](int v) __attribute__((always_inline)) {  // v: tile-major index of the pairs
+            const int t = v / kTileSteps, w = v % kTileSteps;
+            return bread((w & 1) * (kDC / 32) + 4 * t + (w >> 1));
+          };
 #pragma unroll
-        for (int u = 0; u < kPvDepth; ++u) bbuf[u] = bread(u);
-        v8bf pa[kCW / 16];
+          for (int v = 0; v < kPvDepth; ++v) bbuf[v] = pvb(v);
 #pragma unroll
-        for (int ks = 0; ks < kCW / 16; ++ks)
+          for (int t = 0; t < 4; ++t) {
+            v8bf ph[kCW / 16], pl[kCW / 16];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pa[ks][j] = (__bf16)st[8 * ks + j];
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const v4f s4 = *reinterpret_cast<const v4f*>(tab + t * kCW + 4 * a4);
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-          const int ks = u / (kDC / 32), dt = u % (kDC / 32);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bbuf[u % kPvDepth], o[dt], 0, 0, 0);
-          if (u + kPvDepth < kSteps) bbuf[u % kPvDepth] = bread(u + kPvDepth);
-          __builtin_amdgcn_sched_barrier(0);
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * a4 + e;
+                const float x = st[i] * s4[e];
+                const __bf16 h = (__bf16)x;
+                ph[i >> 3][i & 7] = h;
+                pl[i >> 3][i & 7] = (__bf16)(x - (float)h);  // x - h is exact
+              }
+            }
+#pragma unroll
+            for (int w = 0; w < kTileSteps; ++w) {
+              const int v = t * kTileSteps + w, ks = w & 1, dt = 4 * t + (w >> 1);
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[ks], bbuf[v % kPvDepth], o[dt], 0, 0, 0);
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[ks], bbuf[v % kPvDepth], o[dt], 0, 0, 0);
+              if (v + kPvDepth < 4 * kTileSteps) bbuf[v % kPvDepth] = pvb(v + kPvDepth);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else {
+          v8bf pa[kCW / 16];
+#pragma unroll
+          for (int ks = 0; ks < kCW / 16; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pa[ks][j] = (__bf16)st[8 * ks + j];
+          v8bf bbuf[kPvDepth];
+#pragma unroll
+          for (int u = 0; u < kPvDepth; ++u) bbuf[u] = bread(u);
+#pragma unroll
+          for (int u = 0; u < kSteps; ++u) {
+            const int ks = u / (kDC / 32), dt = u % (kDC / 32);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bbuf[u % kPvDepth], o[dt], 0, 0, 0);
+            if (u + kPvDepth < kSteps) bbuf[u % kPvDepth] = bread(u + kPvDepth);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     };
     // Wait until chunk c has landed while the `ahead` chunks gathered after it stay in flight.  The gathers
     // are opaque to the compiler's wait insertion, so these waits are the only ones on them.
+    auto buf = [&](int c) { return kv_pool_lds + (c % kBufW) * (kCW * kRowW); };
     auto wait_chunk = [&](const int ahead) __attribute__((always_inline)) {
       switch (ahead) {
         case 0: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0)); break;
@@ -782,21 +962,55 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         default: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(3 * kRows < 63 ? 3 * kRows : 63)); break;
       }
     };
-    // One pass over the chunks: kDepth chunks are gathered ahead into a ring of kBufW LDS buffers; after the
-    // barrier that ends chunk c, chunk c + kDepth is gathered into a buffer no wave still reads.
+    // One pass over the chunks.  bf16 rows: kDepth chunks are gathered ahead into a ring of kBufW LDS buffers;
+    // after the barrier that ends chunk c, chunk c + kDepth is gathered into a buffer no wave still reads.
+    // FP8 entries: at the barrier that opens chunk c, chunk c + 1 has landed in its staging slot and every wave is
+    // done with chunk c - 1; chunk c + 3 is then gathered into chunk c - 1's slot and chunk c + 1 converted into
+    // chunk c - 1's code buffer, before chunk c is computed from the buffer converted one chunk earlier.
     auto run = [&](const bool qk_only) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
-      for (int c = 0; c < kDepth && c < nch; ++c)
-        gather_chunk_wide<NW>(kv, prow_lds + c * kCW, dummy, kv_lds[c % kBufW], wave, lane);
-      for (int c = 0; c < nch; ++c) {
-        wait_chunk(min(nch - 1 - c, kDepth - 1));
+      if constexpr (kFp8) {
+        const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
+        char* const code0 = kv_pool_lds;
+        char* const slot0 = kv_pool_lds + 2 * kCodeBuf;
+        auto code = [&](int c) { return code0 + (c & 1) * kCodeBuf; };
+        auto slot = [&](int c) { return slot0 + (c & (kF8Ring - 1)) * kF8Slot; };
+        // waits until this wave's gathers of the chunk due next have landed, `ahead` later chunks staying in
+        // flight (each wave issues at most kF8LoadsPerWave per chunk, at least kF8LoadsPerWave - 1)
+        auto wait_f8 = [&](const int ahead) __attribute__((always_inline)) {
+          switch (ahead) {
+            case 0: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kF8LoadsPerWave - 1)); break;
+            default: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * (kF8LoadsPerWave - 1))); break;
+          }
+        };
+        __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
+        for (int c = 0; c < kF8Ring - 1 && c < nch; ++c)
+          gather_chunk_f8(kv8, prow_lds + c * kCW, dummy, slot(c), wave, lane);
+        wait_f8(min(nch - 1, kF8Ring - 2));
         lds_barrier();
-        chunk(c, kv_lds[c % kBufW], qk_only);
-        lds_barrier();  // every wave is done with this buffer before a gather overwrites it
-        if (c + kDepth < nch)
-          gather_chunk_wide<NW>(kv, prow_lds + (c + kDepth) * kCW, dummy, kv_lds[(c + kDepth) % kBufW], wave, lane);
+        convert_chunk_f8(slot(0), code(0), threadIdx.x);
+        for (int c = 0; c < nch; ++c) {
+          if (c + 1 < nch) wait_f8(min(nch - 2 - c, kF8Ring - 3));
+          lds_barrier();
+          if (c + kF8Ring - 1 < nch)
+            gather_chunk_f8(kv8, prow_lds + (c + kF8Ring - 1) * kCW, dummy, slot(c + kF8Ring - 1), wave, lane);
+          if (c + 1 < nch) convert_chunk_f8(slot(c + 1), code(c + 1), threadIdx.x);
+          chunk(c, code(c), slot(c), qk_only);
+        }
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
+        for (int c = 0; c < kDepth && c < nch; ++c)
+          gather_chunk_wide<NW>(kv, prow_lds + c * kCW, dummy, buf(c), wave, lane);
+        for (int c = 0; c < nch; ++c) {
+          wait_chunk(min(nch - 1 - c, kDepth - 1));
+          lds_barrier();
+          chunk(c, buf(c), nullptr, qk_only);
+          lds_barrier();  // every wave is done with this buffer before a gather overwrites it
+          if (c + kDepth < nch) gather_chunk_wide<NW>(kv, prow_lds + (c + kDepth) * kCW, dummy, buf(c + kDepth), wave, lane);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     };
 #pragma unroll
     for (int dt = 0; dt < kDC / 32; ++dt) o[dt] = v16f{};
@@ -1012,8 +1226,9 @@ AttnPlan plan(const Geo& g) {
   AttnPlan p{1, chunks * kNC, 0};
   if (g.kv_dtype == 0 /* F32 */) return p;
   const int nw = g.H % 128 == 0 ? 4 : g.H % 64 == 0 ? 2 : 1;  // waves per block divide the 64 gathers of a chunk
-  // the all-heads kernel reads bf16 latent rows only; FP8 entries always take the 16-head kernel
-  if (g.kv_dtype == 1 && g.H % 32 == 0 && (int64_t)g.R * (g.H / (32 * nw)) * chunks >= 128) {
+  // FP8 entries take the all-heads kernel with four waves only (128 heads per block)
+  const bool wide_ok = g.kv_dtype == 1 ? g.H % 32 == 0 : g.H % 128 == 0;
+  if (wide_ok && (int64_t)g.R * (g.H / (32 * nw)) * chunks >= 128) {
     // all-heads kernel: one block per (row, head group of <= 128, split), one block per CU at a time; split
     // the selection only as far as needed to give every CU a block.  With fewer than 128 (row, group, chunk)
     // units it could not spread over the chip, and the 16-head kernel below runs instead.
@@ -1062,22 +1277,22 @@ Partials carve_partials(const Geo& g, int nsplit, void* workspace) {
   return w;
 }
 
-template <int NW>
+template <int NW, bool kFp8>
 void launch_mqa(const Geo& g, const AttnPlan& p, const unsigned short* qp, const unsigned short* kp,
                 const int32_t* topk_idx, const int32_t* pool_rows, void* out, float* lse, const Partials& pt,
                 float scale_log2, hipStream_t stream) {
   const int64_t units = (int64_t)g.R * (g.H / (32 * NW));
   const int nblocks = work_blocks((int64_t)g.R * p.nsplit, g.H / (32 * NW));
   if (p.nsplit == 1)
-    attn_bf16_mqa_kernel<NW, false><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H, 1,
-        (int)units,
-        p.split_len, scale_log2, static_cast<unsigned short*>(out), lse, nullptr, nullptr, nullptr);
+    attn_bf16_mqa_kernel<NW, false, kFp8><<<nblocks, NW * 64, 0, stream>>>(
+        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages,
+        g.num_pages, g.log2ps, g.H, 1, (int)units, p.split_len, scale_log2, static_cast<unsigned short*>(out), lse,
+        nullptr, nullptr, nullptr);
   else
-    attn_bf16_mqa_kernel<NW, true><<<nblocks, NW * 64, 0, stream>>>(
-        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps, g.H,
-        p.nsplit,
-        (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex, pt.lse);
+    attn_bf16_mqa_kernel<NW, true, kFp8><<<nblocks, NW * 64, 0, stream>>>(
+        qp, kp, topk_idx, g.k, pool_rows, g.row_len, g.max_row_len, g.row_seq, g.page_table, g.S, g.max_pages,
+        g.num_pages, g.log2ps, g.H, p.nsplit, (int)units, p.split_len, scale_log2, nullptr, nullptr, pt.o, pt.ex,
+        pt.lse);
 }
 
 }  // namespace
@@ -1102,9 +1317,12 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* kv_pool, const i
     const Partials pt = carve_partials(g, p.nsplit, workspace);
     if (p.nw > 0) {
       switch (p.nw) {
-        case 1: launch_mqa<1>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
-        case 2: launch_mqa<2>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
-        default: launch_mqa<4>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
+        case 1: launch_mqa<1, false>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
+        case 2: launch_mqa<2, false>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream); break;
+        default:
+          if (fp8) launch_mqa<4, true>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream);
+          else launch_mqa<4, false>(g, p, qp, kp, topk_idx, pool_rows, out, lse, pt, scale_log2, stream);
+          break;
       }
     } else {
       const int64_t units = (int64_t)g.R * (g.H / kHG);

@@ -275,13 +275,16 @@ def _large_fp8_latents(prob, seed=41):
     prob.kv_pool[:, 512:528] = np.full((n, 4), 1.0 / 60.0, np.float32).view(np.uint8)
 
 
-def test_fp8_latent_large_values_one_and_two_positions():
+@pytest.mark.parametrize("batch,H", [(4, 16), (128, 128)])
+def test_fp8_latent_large_values_one_and_two_positions(batch, H):
     # Rows of one and two positions over entries whose dequantised latent values lie in [4, 8): a one-position row's
     # output is its latent row, a two-position row's a convex combination of two.  Every product of a probability
     # and a tile scale reaches the MFMAs unrounded, so the only error left is the bf16 rounding of the output, at
     # most half a bf16 ulp of |o| (1/64 in [4, 8)); rounding those products to bf16 would add up to 8 * 2^-9.
-    prob = synth.make_problem(synth.get("batched_paged", batch=4, lengths=[1, 2, 1, 2], anchors=0, recent=0,
-                                        kv_dtype="f8", H=16, k=64, seed=40))
+    # 4 rows of 16 heads run the 16-head kernel; 128 rows of 128 heads (128 row-chunks) the all-heads kernel.
+    say(f"case large fp8 latents batch={batch} H={H}")
+    prob = synth.make_problem(synth.get("batched_paged", batch=batch, lengths=[1, 2] * (batch // 2), anchors=0,
+                                        recent=0, kv_dtype="f8", H=H, k=64, seed=40))
     _large_fp8_latents(prob)
     res = gpu_step(prob)
     ref_o, ref_lse = oracle.sparse_attn_fp8(prob.q, prob.kv_pool, res.idx, prob.row_seq, prob.page_table,
@@ -309,6 +312,30 @@ def test_fp8_latent_with_prefill_rows_and_wide_index_keys():
 def test_fp8_latent_full_size():
     # the 128K decode workload over fp8 entries, checked element by element against the oracle
     _sampled("decode_128k_fp8kv", lambda p: [0])
+
+
+def test_fp8_latent_all_heads_kernel():
+    # 128 heads over fp8 entries with at least 128 (row, chunk) units run the all-heads kernel: a paged batch with
+    # an empty, a one-position and a short row (160 units), and logits spanning hundreds of units, where a later
+    # chunk's maximum far above the first chunk's forces the recompute against exact per-head maxima (128 units)
+    _run(synth.get("batched_paged", batch=5, lengths=[0, 1, 1500, 6000, 9000], anchors=8, recent=8, kv_dtype="f8",
+                   H=128))
+    _run(synth.get("batched_paged", batch=4, length_range=(6000, 9000), softmax_scale=60.0, anchors=16, recent=32,
+                   kv_dtype="f8", H=128))
+
+
+def test_fp8_latent_all_heads_dense():
+    # dense attention over fp8 entries through the all-heads kernel (every visible position of each row)
+    _dense(synth.get("batched_paged", batch=4, lengths=[9000, 3000, 0, 1], H=128, anchors=8, recent=8,
+                     kv_dtype="f8"))
+
+
+def test_batched_paged_fp8kv_full_size():
+    # 64 paged sequences over fp8 entries (the all-heads kernel with four splits per row), sampled rows
+    def rows(p):
+        order = np.argsort(p.row_len)
+        return sorted({int(order[0]), int(order[-1]), 7, 40})
+    _sampled("batched_paged_fp8kv", rows)
 
 
 # ------------------------------------------------------------------------------- top-k on crafted scores
