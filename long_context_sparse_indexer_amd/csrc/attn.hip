@@ -571,11 +571,13 @@ template <int NW>  // waves per block: 32 * NW heads
 __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restrict__ kv, const int32_t* prow,
                                                   int dummy, char* buf, int wave, int lane) {
   constexpr int kRows = kCW / NW;
+  int prs[kRows];  // every row id first: one LDS round trip rather than one per load (the asm clobbers memory)
+#pragma unroll
+  for (int t = 0; t < kRows; ++t) prs[t] = prow[wave * kRows + t];
 #pragma unroll
   for (int t = 0; t < kRows; ++t) {
     const int rr = wave * kRows + t;
-    int pr = prow[rr];
-    if (pr < 0) pr = dummy;
+    const int pr = prs[t] < 0 ? dummy : prs[t];
     const unsigned short* src = kv + (int64_t)pr * kDC + lane * 8;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(buf + rr * kRowW)));
@@ -583,88 +585,225 @@ __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restri
   }
 }
 
-// FP8 entries in the all-heads kernel.  A chunk's 32 entries (656 bytes each, 1312 16-byte pieces) are gathered
-// raw by LDS-DMA into one of four staging slots, packed at 656-byte strides: load i of a chunk moves pieces
-// 64 i .. 64 i + 63, wave w issuing loads w, w + 4, ...; the lanes past the last piece reread a piece of a selected
-// entry into the slot's padding.  One chunk ahead of its use, every thread widens 64 codes of the staged chunk to
-// bf16 (exact: an e4m3 value has a 4-bit significand) into a code buffer laid out like the bf16 rows, and the
-// first four lanes of each row copy its tile scales into a table [tile][slot parity][slot / 2], from which a lane
-// reads the scales of its 16 S^T rows as four 16-byte loads.  The scales are applied outside the MFMAs: QK
-// accumulates each 128-dim tile on its own and adds it in with the slot's scale; PV multiplies each probability by
-// its slot's scale for the tile of the output columns and splits that product into a bf16 head and a bf16 rest,
-// both of which go through the MFMA.  No dequantised value is rounded.  The RoPE dims are read by QK straight from
-// the staging slot (656 bytes = 164 dwords, 4 banks mod 32 like the code rows, so the permuted A rows stay
-// conflict-free).
+// FP8 entries in the all-heads kernel.  A chunk's 32 entries (656 bytes each) are gathered raw by LDS-DMA into
+// one of four staging slots, packed at 656-byte strides, one load of 41 lanes per entry (wave w gathers entries
+// 8 w .. 8 w + 7).  Loads that each cover 64 16-byte pieces, crossing entries, took twice as long to issue per
+// byte.  One chunk ahead of its use, every thread widens 64 codes of the staged chunk to
+// bf16 (exact: an e4m3 value has a 4-bit significand) into a code buffer laid out like the bf16 rows.  The tile
+// scales are applied outside the MFMAs: QK accumulates each 128-dim tile on its own and adds it in with the slot's
+// scale; PV multiplies each probability by its slot's scale for the tile of the output columns and splits that
+// product into a bf16 head and a bf16 rest, both of which go through the MFMA.  No dequantised value is rounded.
+// Register i of an S^T tile holds slot 8 (i >> 2) + 2 (i & 3) + half in every lane of a lane half, so lane l
+// loads the four scales of the slot that register l % 16 holds in its half, and a DPP row_newbcast:i move hands
+// register i's scale to every lane of the row (rows 0-1 are half 0, rows 2-3 half 1).  The RoPE dims and the
+// scales are read straight from the staging slot (656 bytes = 164 dwords, 4 banks mod 32 like the code rows, so
+// the permuted A rows stay conflict-free).
 constexpr int kF8RopeByte = kDC + 16;          // RoPE values follow the codes and the four scales
-constexpr int kF8Pieces = kCW * kF8Entry / 16;  // 1312
-constexpr int kF8Loads = (kF8Pieces + 63) / 64;  // 21 LDS-DMA loads per chunk
-constexpr int kF8LoadsPerWave = (kF8Loads + 3) / 4;  // wave 0 issues 6, waves 1..3 issue 5
-constexpr int kF8Slot = kF8Loads * 1024;         // staging slot bytes
+constexpr int kF8Pieces = kF8Entry / 16;        // 41 16-byte pieces per entry: one LDS-DMA load of 41 lanes
+constexpr int kF8RowsPerWave = kCW / 4;          // rows (loads) each of the four waves gathers per chunk
+constexpr int kF8Slot = kCW * kF8Entry;          // staging slot bytes
 constexpr int kF8Ring = 4;                       // staging slots: converting, computing (RoPE), two in flight
-constexpr int kCodeTab = kCW * kRowW;            // offset of the scale table in a code buffer
-constexpr int kCodeBuf = kCodeTab + 4 * kCW * 4;
-static_assert(kF8Entry % 16 == 0 && kF8Pieces <= kF8Loads * 64, "pieces fit the loads");
+constexpr int kCodeBuf = kCW * kRowW;            // a code buffer: 32 rows of bf16 codes
+static_assert(kF8Entry % 16 == 0 && kF8Pieces <= 64, "an entry fits one load");
 
 __device__ __forceinline__ void gather_chunk_f8(const uint8_t* __restrict__ kv, const int32_t* prow, int dummy,
                                                 char* slot, int wave, int lane) {
-  // The load index and the LDS address are wave-uniform (scalar registers), and the lane's piece is recomputed
-  // per call: hoisted out of the chunk loop, the per-load offsets had been kept in vector registers and spilled,
-  // and a spill reload waits for every gather in flight (vmcnt counts both).
+  // The row ids first (one LDS round trip: the asm statements clobber memory), then one load per row.  The LDS
+  // address is wave-uniform (scalar registers).
   const int w = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t base = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)slot));
-  asm volatile("" : "+v"(lane));
+  int pr[kF8RowsPerWave];
 #pragma unroll
-  for (int j = 0; j < kF8LoadsPerWave; ++j) {
-    const int i = w + 4 * j;
-    if (i < kF8Loads) {
-      const int pc = 64 * i + lane;
-      int row = pc / (kF8Entry / 16), piece = pc - row * (kF8Entry / 16);
-      int pr = dummy;
-      if (pc < kF8Pieces) {
-        pr = prow[row];
-        if (pr < 0) pr = dummy;
-      } else {
-        piece = 0;
-      }
-      const uint8_t* src = kv + (int64_t)pr * kF8Entry + 16 * piece;
-      const uint32_t lds = base + 1024u * (uint32_t)i;
+  for (int t = 0; t < kF8RowsPerWave; ++t) pr[t] = prow[w * kF8RowsPerWave + t];
+#pragma unroll
+  for (int t = 0; t < kF8RowsPerWave; ++t) {
+    const int r = pr[t] < 0 ? dummy : pr[t];
+    const uint8_t* src = kv + (int64_t)r * kF8Entry + 16 * min(lane, kF8Pieces - 1);
+    const uint32_t lds = base + (uint32_t)((w * kF8RowsPerWave + t) * kF8Entry);
+    if (lane < kF8Pieces)
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-    }
   }
 }
 
 // Thread t widens codes 16 g + 128 j (g = t % 8, j = 0..3) of row t / 8: the eight lanes of a row read 128
 // contiguous bytes per load, and write 32 bytes each per tile as two 16-byte stores, lanes 4..7 of a row in the
 // opposite order so that the eight lanes of one store cover all 32 banks.
+__device__ __forceinline__ v4i convert_load_f8(const char* slot, int t, int j) {
+  const int row = t >> 3, g = t & 7;
+  return *reinterpret_cast<const v4i*>(slot + row * kF8Entry + 16 * g + 128 * j);
+}
+__device__ __forceinline__ void convert_store_f8(char* code, int t, int j, const v4i c) {
+  const int row = t >> 3, g = t & 7, sw = (g >> 2) & 1;
+  v4i w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const uint32_t d = (uint32_t)c[2 * h + x];
+      const v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, false);
+      const v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, true);
+      w[h][2 * x] = (int)__builtin_bit_cast(uint32_t, lo);
+      w[h][2 * x + 1] = (int)__builtin_bit_cast(uint32_t, hi);
+    }
+  char* dst = code + row * kRowW + 256 * j + 32 * g;
+  const v4i w0 = sw ? w[1] : w[0], w1 = sw ? w[0] : w[1];  // select whole vectors: no per-lane indexing
+  *reinterpret_cast<v4i*>(dst + 16 * sw) = w0;
+  *reinterpret_cast<v4i*>(dst + 16 * (1 - sw)) = w1;
+}
 __device__ __forceinline__ void convert_chunk_f8(const char* slot, char* code, int t) {
   asm volatile("" : "+v"(t));  // recomputed per call, like the gather offsets
-  const int row = t >> 3, g = t & 7, sw = (g >> 2) & 1;
-  const char* src = slot + row * kF8Entry;
   v4i c[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const v4i*>(src + 16 * g + 128 * j);
-  float sc = 0.f;
-  if (g < 4) sc = *reinterpret_cast<const float*>(src + kDC + 4 * g);
+  for (int j = 0; j < 4; ++j) c[j] = convert_load_f8(slot, t, j);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v4i w[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const uint32_t d = (uint32_t)c[j][2 * h + x];
-        const v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, false);
-        const v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, true);
-        w[h][2 * x] = (int)__builtin_bit_cast(uint32_t, lo);
-        w[h][2 * x + 1] = (int)__builtin_bit_cast(uint32_t, hi);
-      }
-    char* dst = code + row * kRowW + 256 * j + 32 * g;
-    const v4i w0 = sw ? w[1] : w[0], w1 = sw ? w[0] : w[1];  // select whole vectors: no per-lane indexing
-    *reinterpret_cast<v4i*>(dst + 16 * sw) = w0;
-    *reinterpret_cast<v4i*>(dst + 16 * (1 - sw)) = w1;
+  for (int j = 0; j < 4; ++j) convert_store_f8(code, t, j, c[j]);
+}
+
+// Register i's value of a per-row quantity held by lanes 16 r + i, applied through the DPP row_newbcast:i source
+// of a VOP2 instruction, two registers (2 e, 2 e + 1) at a time: bcast_mul2 gives x = bcast_i(s) * st[i], and
+// bcast_fma2 adds bcast_i(s) * a[i] to st[i].  Written out because the compiler kept a separate DPP move per use;
+// two at a time so that the work can sit between MFMAs.  The s_nop covers the VALU-write-to-DPP-read hazard on s.
+// All 64 lanes must be active.
+template <int kE>
+__device__ __forceinline__ void bcast_mul2(float& x0, float& x1, float s, float st0, float st1);
+template <int kE>
+__device__ __forceinline__ void bcast_fma2(float& st0, float& st1, float s, float a0, float a1);
+template <>
+__device__ __forceinline__ void bcast_mul2<0>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<0>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<1>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<1>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<2>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:5 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<2>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:5 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<3>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<3>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<4>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:9 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<4>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:9 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<5>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<5>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<6>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<6>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+template <>
+__device__ __forceinline__ void bcast_mul2<7>(float& x0, float& x1, float s, float st0, float st1) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %2, %3 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %2, %4 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "=&v"(x0), "=&v"(x1) : "v"(s), "v"(st0), "v"(st1));
+}
+template <>
+__device__ __forceinline__ void bcast_fma2<7>(float& st0, float& st1, float s, float a0, float a1) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(st0), "+v"(st1) : "v"(s), "v"(a0), "v"(a1));
+}
+
+// Registers 2 e, 2 e + 1 of tile scale s times the probabilities st, split into a bf16 head (the top 16 bits) and
+// a bf16 rest (the exact remainder, rounded): dword e & 3 of the K-step e >> 2 operands hp and lp.
+template <int kE>
+__device__ __forceinline__ void split_pair(const v16f& st, float s, v4i (&hp)[2], v4i (&lp)[2]) {
+  float x0, x1;
+  bcast_mul2<kE>(x0, x1, s, st[2 * kE], st[2 * kE + 1]);
+  const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+  const float l0 = x0 - __uint_as_float(b0 & 0xffff0000u), l1 = x1 - __uint_as_float(b1 & 0xffff0000u);
+  hp[kE >> 2][kE & 3] = (int)__builtin_amdgcn_perm(b1, b0, 0x07060302u);  // top halves of b0, b1
+  const v2bf lb = v2bf{(__bf16)l0, (__bf16)l1};
+  lp[kE >> 2][kE & 3] = (int)__builtin_bit_cast(uint32_t, lb);
+}
+__device__ __forceinline__ void split_pair_n(int e, const v16f& st, float s, v4i (&hp)[2], v4i (&lp)[2]) {
+  switch (e) {  // e is a constant wherever this is inlined
+    case 0: split_pair<0>(st, s, hp, lp); break;
+    case 1: split_pair<1>(st, s, hp, lp); break;
+    case 2: split_pair<2>(st, s, hp, lp); break;
+    case 3: split_pair<3>(st, s, hp, lp); break;
+    case 4: split_pair<4>(st, s, hp, lp); break;
+    case 5: split_pair<5>(st, s, hp, lp); break;
+    case 6: split_pair<6>(st, s, hp, lp); break;
+    default: split_pair<7>(st, s, hp, lp); break;
   }
-  if (g < 4) reinterpret_cast<float*>(code + kCodeTab)[g * kCW + (row & 1) * (kCW / 2) + (row >> 1)] = sc;
+}
+__device__ __forceinline__ void fold_pair_n(int e, v16f& st, const v16f& a, float s) {
+  float s0 = st[2 * e], s1 = st[2 * e + 1];
+  switch (e) {
+    case 0: bcast_fma2<0>(s0, s1, s, a[0], a[1]); break;
+    case 1: bcast_fma2<1>(s0, s1, s, a[2], a[3]); break;
+    case 2: bcast_fma2<2>(s0, s1, s, a[4], a[5]); break;
+    case 3: bcast_fma2<3>(s0, s1, s, a[6], a[7]); break;
+    case 4: bcast_fma2<4>(s0, s1, s, a[8], a[9]); break;
+    case 5: bcast_fma2<5>(s0, s1, s, a[10], a[11]); break;
+    case 6: bcast_fma2<6>(s0, s1, s, a[12], a[13]); break;
+    default: bcast_fma2<7>(s0, s1, s, a[14], a[15]); break;
+  }
+  st[2 * e] = s0;
+  st[2 * e + 1] = s1;
 }
 
 // kFp8: the latent rows are 656-byte FP8 entries (four waves only), dequantised into hi and lo bf16 rows; the
@@ -682,6 +821,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   static_assert(!kFp8 || NW == 4, "FP8 entries: eight rows per wave and chunk");
   args_to_sgprs(q, kv, topk_idx, k, pool_rows, row_len, max_row_len, row_seq, page_table, num_seqs, max_pages,
                 num_pages, log2ps, H, nsplit, units, split_len);
+  DSA_STAMP(5, 0);
   constexpr int kRows = kCW / NW;  // rows each wave gathers per chunk
   // chunks gathered ahead: at the wait for chunk c, the kDepth - 1 chunks after it may still be in flight,
   // which must fit vmcnt (at most 63 outstanding loads per wave)
@@ -715,8 +855,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   {
     constexpr int kQW = kFp8 ? kDC + kRope : kDC;  // query row width
     const unsigned short* qrow = q + ((int64_t)r * H + hw + col) * kQW + 8 * half;
+    // FP8 entries: K-step ks takes, in lane half h, dims 32 (ks >> 1) + 16 h + 8 (ks & 1) .. +8, so that one
+    // 16-byte read of a staged row's codes serves two K-steps
 #pragma unroll
-    for (int ks = 0; ks < kDC / 16; ++ks) qb[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
+    for (int ks = 0; ks < kDC / 16; ++ks)
+      qb[ks] = *reinterpret_cast<const v8bf*>(kFp8 ? qrow + 8 * half + 32 * (ks >> 1) + 8 * (ks & 1) : qrow + 16 * ks);
     if constexpr (kFp8)
 #pragma unroll
       for (int ks = 0; ks < kRope / 16; ++ks) qr[ks] = *reinterpret_cast<const v8bf*>(qrow + kDC + 16 * ks);
@@ -771,6 +914,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     if (threadIdx.x == 0) overflow = 0;
   }
   __syncthreads();
+  DSA_STAMP(5, 1);
   int first_valid = wave_first[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) first_valid = min(first_valid, wave_first[w]);
@@ -793,45 +937,48 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
       // kQkDepth K-steps ahead of their MFMAs; sched_barrier keeps the compiler from hoisting further.
       v16f st = {};
       const int arow_i = 8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1);  // the slot this lane's A row holds
+      // FP8: the four tile scales of the slot register (lane % 16) holds in this lane's half
+      v4f sc = {};
       if constexpr (kFp8) {
-        // each 128-dim tile of codes on an accumulator of its own, added in with the scales of this lane's rows
-        // (register i holds slot 8 (i >> 2) + 2 (i & 3) + half, whose scale sits at entry i of the half's table
-        // row), then the RoPE K-steps straight onto st.  Three K-steps of A operands ahead: with four, one Q
-        // register was spilled, and its reload (vmcnt) waited for every gather in flight.
-        constexpr int kQkDepth = 3;
-        const char* arow = cur + arow_i * kRowW + 16 * half;
-        const float* tab = reinterpret_cast<const float*>(cur + kCodeTab) + half * (kCW / 2);
-        v8bf abuf[kQkDepth];
+        const int sl = 8 * ((lane & 15) >> 2) + 2 * (lane & 3) + half;
+        sc = *reinterpret_cast<const v4f*>(raw + sl * kF8Entry + kDC);
+      }
+      if constexpr (kFp8) {
+        // Each 128-dim tile of codes on an accumulator of its own, added in with the scales of this lane's rows
+        // (row_newbcast:i gives register i's), then the RoPE K-steps straight onto st.  The A operands are read
+        // from the staged entries as e4m3 codes, 16 bytes (two K-steps) per read, and widened to bf16 in
+        // registers: half the LDS bytes of reading the widened rows, which the four waves' QK reads saturate.
+        constexpr int kQkDepth = 2;  // reads (K-step pairs) ahead
+        const char* araw = raw + arow_i * kF8Entry + 16 * half;
+        v4i abuf[kQkDepth];
 #pragma unroll
-        for (int ks = 0; ks < kQkDepth; ++ks) abuf[ks] = *reinterpret_cast<const v8bf*>(arow + 32 * ks);
+        for (int j = 0; j < kQkDepth; ++j) abuf[j] = *reinterpret_cast<const v4i*>(araw + 32 * j);
+        auto widen = [](v4i c, int odd) __attribute__((always_inline)) {  // codes of K-step 2 j + odd
+          const uint32_t d0 = (uint32_t)c[2 * odd], d1 = (uint32_t)c[2 * odd + 1];
+          const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, false);
+          const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, true);
+          const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, false);
+          const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, true);
+          return v8bf{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+        };
         v16f acc[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v16f& at = acc[t & 1];
-          at = v16f{};
+        for (int t = 0; t < 5; ++t) {
+          // tile t's K-steps, each followed by a quarter of the previous tile's fold (two registers), so that
+          // the fold's VALU work runs while the MFMAs do
+          if (t < 4) acc[t & 1] = v16f{};
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) {
-            const int ks = 8 * t + kk;
-            at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kQkDepth], qb[ks], at, 0, 0, 0);
-            if (ks + kQkDepth < kDC / 16)
-              abuf[ks % kQkDepth] = *reinterpret_cast<const v8bf*>(arow + 32 * (ks + kQkDepth));
+            const int ks = 8 * t + kk, j = ks >> 1;
+            if (t < 4) {
+              acc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen(abuf[j % kQkDepth], ks & 1), qb[ks],
+                                                                   acc[t & 1], 0, 0, 0);
+              if ((ks & 1) && j + kQkDepth < kDC / 32)
+                abuf[j % kQkDepth] = *reinterpret_cast<const v4i*>(araw + 32 * (j + kQkDepth));
+            }
+            if (t > 0) fold_pair_n(kk, st, acc[(t - 1) & 1], sc[t - 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (t > 0) {  // the previous tile, while this one's MFMAs run
-            const v16f& ap = acc[(t - 1) & 1];
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-              const v4f s4 = *reinterpret_cast<const v4f*>(tab + (t - 1) * kCW + 4 * a4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) st[4 * a4 + e] = fmaf(ap[4 * a4 + e], s4[e], st[4 * a4 + e]);
-            }
-          }
-        }
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const v4f s4 = *reinterpret_cast<const v4f*>(tab + 3 * kCW + 4 * a4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st[4 * a4 + e] = fmaf(acc[1][4 * a4 + e], s4[e], st[4 * a4 + e]);
         }
         const char* rrow = raw + arow_i * kF8Entry + kF8RopeByte + 16 * half;
 #pragma unroll
@@ -876,8 +1023,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
         float rs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          st[i] = exp2f(st[i] - m_use);
+        for (int i = 0; i < 16; ++i) {  // v_exp_f32: 2^x for x <= kHeadroom, 0 for -inf
+          st[i] = __builtin_amdgcn_exp2f(st[i] - m_use);
           rs += st[i];
         }
         {
@@ -898,36 +1045,33 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         };
         if constexpr (kFp8) {
           // tile t of the output columns (dt = 4 t .. 4 t + 3): each probability times its slot's scale for the
-          // tile, as a bf16 head and a bf16 rest, on two MFMAs per (K-step, column tile)
-          const float* tab = reinterpret_cast<const float*>(cur + kCodeTab) + half * (kCW / 2);
-          constexpr int kTileSteps = (kCW / 16) * 4;  // (K-step, column tile) pairs of one tile
+          // tile, x, as the bf16 head h = x cut to its top 16 bits and the rest x - h (exact) rounded to bf16
+          // (together x to 2^-16 relative), on two MFMAs per (K-step, column tile)
+          constexpr int kTileSteps = (kCW / 16) * 4;  // (K-step, column tile) pairs of one tile, K-step major
           v8bf bbuf[kPvDepth];
           auto pvb = [&](int v) __attribute__((always_inline)) {  // v: tile-major index of the pairs
             const int t = v / kTileSteps, w = v % kTileSteps;
-            return bread((w & 1) * (kDC / 32) + 4 * t + (w >> 1));
+            return bread((w >> 2) * (kDC / 32) + 4 * t + (w & 3));
           };
 #pragma unroll
           for (int v = 0; v < kPvDepth; ++v) bbuf[v] = pvb(v);
+          // hp / lp [K-step]: bf16 pairs (2 e, 2 e + 1) of registers 8 ks ..  Skewed so that one set suffices:
+          // while a tile's K-step 0 MFMAs run, its K-step 1 operands are made (the previous tile's are spent);
+          // while its K-step 1 MFMAs run, the next tile's K-step 0 operands.
+          v4i hp[2], lp[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split_pair_n(e, st, sc[0], hp, lp);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            v8bf ph[kCW / 16], pl[kCW / 16];
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-              const v4f s4 = *reinterpret_cast<const v4f*>(tab + t * kCW + 4 * a4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int i = 4 * a4 + e;
-                const float x = st[i] * s4[e];
-                const __bf16 h = (__bf16)x;
-                ph[i >> 3][i & 7] = h;
-                pl[i >> 3][i & 7] = (__bf16)(x - (float)h);  // x - h is exact
-              }
-            }
 #pragma unroll
             for (int w = 0; w < kTileSteps; ++w) {
-              const int v = t * kTileSteps + w, ks = w & 1, dt = 4 * t + (w >> 1);
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[ks], bbuf[v % kPvDepth], o[dt], 0, 0, 0);
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[ks], bbuf[v % kPvDepth], o[dt], 0, 0, 0);
+              const int v = t * kTileSteps + w, ks = w >> 2, dt = 4 * t + (w & 3);
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, hp[ks]), bbuf[v % kPvDepth],
+                                                              o[dt], 0, 0, 0);
+              if (w < 4) split_pair_n(4 + w, st, sc[t], hp, lp);
+              else if (t < 3) split_pair_n(w - 4, st, sc[t + 1], hp, lp);
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lp[ks]), bbuf[v % kPvDepth],
+                                                              o[dt], 0, 0, 0);
               if (v + kPvDepth < 4 * kTileSteps) bbuf[v % kPvDepth] = pvb(v + kPvDepth);
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -966,7 +1110,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     // after the barrier that ends chunk c, chunk c + kDepth is gathered into a buffer no wave still reads.
     // FP8 entries: at the barrier that opens chunk c, chunk c + 1 has landed in its staging slot and every wave is
     // done with chunk c - 1; chunk c + 3 is then gathered into chunk c - 1's slot and chunk c + 1 converted into
-    // chunk c - 1's code buffer, before chunk c is computed from the buffer converted one chunk earlier.
+    // chunk c - 1's code buffer (read by PV), before chunk c is computed.
     auto run = [&](const bool qk_only) __attribute__((always_inline)) {
       if constexpr (kFp8) {
         const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
@@ -975,13 +1119,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         auto code = [&](int c) { return code0 + (c & 1) * kCodeBuf; };
         auto slot = [&](int c) { return slot0 + (c & (kF8Ring - 1)) * kF8Slot; };
         // waits until this wave's gathers of the chunk due next have landed, `ahead` later chunks staying in
-        // flight (each wave issues at most kF8LoadsPerWave per chunk, at least kF8LoadsPerWave - 1)
+        // flight (kF8RowsPerWave loads per chunk)
         auto wait_f8 = [&](const int ahead) __attribute__((always_inline)) {
-          switch (ahead) {
-            case 0: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0)); break;
-            case 1: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kF8LoadsPerWave - 1)); break;
-            default: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * (kF8LoadsPerWave - 1))); break;
-          }
+          if (ahead == 0) __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0));
+          else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kF8RowsPerWave));
+          else __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * kF8RowsPerWave));
         };
         __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
         for (int c = 0; c < kF8Ring - 1 && c < nch; ++c)
@@ -989,6 +1131,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         wait_f8(min(nch - 1, kF8Ring - 2));
         lds_barrier();
         convert_chunk_f8(slot(0), code(0), threadIdx.x);
+        DSA_STAMP(5, 2);
         for (int c = 0; c < nch; ++c) {
           if (c + 1 < nch) wait_f8(min(nch - 2 - c, kF8Ring - 3));
           lds_barrier();
@@ -996,6 +1139,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
             gather_chunk_f8(kv8, prow_lds + (c + kF8Ring - 1) * kCW, dummy, slot(c + kF8Ring - 1), wave, lane);
           if (c + 1 < nch) convert_chunk_f8(slot(c + 1), code(c + 1), threadIdx.x);
           chunk(c, code(c), slot(c), qk_only);
+          if ((c & 3) == 3 && c < 16) DSA_STAMP(5, 3 + (c >> 2));
         }
         __syncthreads();
       } else {
@@ -1006,6 +1150,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
           wait_chunk(min(nch - 1 - c, kDepth - 1));
           lds_barrier();
           chunk(c, buf(c), nullptr, qk_only);
+          if ((c & 3) == 3 && c < 16) DSA_STAMP(5, 3 + (c >> 2));
           lds_barrier();  // every wave is done with this buffer before a gather overwrites it
           if (c + kDepth < nch) gather_chunk_wide<NW>(kv, prow_lds + (c + kDepth) * kCW, dummy, buf(c + kDepth), wave, lane);
         }
@@ -1025,6 +1170,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     }
   }
 
+  DSA_STAMP(5, 7);
   // finish: normalise O rows by their head's sum (held in lane (0, head))
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   const bool any = first_valid != 0x7fffffff;
@@ -1058,6 +1204,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     else if (lse)
       lse[(int64_t)r * H + hw + col] = lz;
   }
+  DSA_STAMP(5, 8);
 }
 
 // Merge the per-split (o, lse) pairs of one (row, head): o = sum_s exp(lse_s - L) o_s, L = log sum exp lse_s,
