@@ -521,17 +521,28 @@ struct BitmapScratch {
   alignas(16) uint32_t wt[2 * 16];
   uint32_t bin, above, nb, nlow, neq, T, need;
 };
-template <int kWpt>
+struct NoPre {
+  __device__ void operator()() const {}
+};
+// pre(): work of the caller's that runs while the candidates load (its LDS writes must be visible after the
+// first barrier).
+template <int kWpt, class Pre = NoPre>
 __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const uint64_t* __restrict__ list,
-                              const ListSink& sink, uint32_t* bits, uint32_t* h, BitmapScratch& S) {
+                              const ListSink& sink, uint32_t* bits, uint32_t* h, BitmapScratch& S,
+                              const Pre& pre = Pre{}) {
   constexpr int NT = 1024, NW = NT / 64;
   constexpr int kPer = kCap / NT;  // candidates per thread
   static_assert(kWpt >= 1 && kWpt % 4 == 0 && kPer * NT == kCap, "bitmap and list split evenly");
   const int t = threadIdx.x, lane = t & 63;
-  if (c < (uint32_t)keff || c > (uint32_t)kCap || n > kWpt * NT * 32) return false;
+  if (c < (uint32_t)keff || c > (uint32_t)kCap || n > kWpt * NT * 32) {
+    pre();
+    return false;
+  }
+  DSA_STAMP(1, 10);
   uint64_t e[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) e[j] = list[min(j * NT + t, (int)c - 1)];  // entries past c dropped below
+  pre();
   for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
 #pragma unroll
   for (int q = 0; q < kWpt; ++q) bits[t * kWpt + q] = 0u;
@@ -566,6 +577,7 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
     }
   }
   __syncthreads();
+  DSA_STAMP(1, 11);
   const uint32_t bin = S.bin, nb = S.nb;
   if (bin == kTopkBins - 1) return false;  // uniform: the threshold lies in the open-ended top bin
   const uint32_t prefix = fl + bin;
@@ -579,10 +591,12 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
     }
     __syncthreads();
     if (t < 64) {
+      // every low part against every other: lane y's value reaches all lanes through v_readlane, so the loop
+      // runs in registers (an LDS read per step had made it a chain of LDS round trips)
       const uint32_t dx = lane < (int)nb ? S.low[lane] : 0u;
       uint32_t gt = 0, ge = 0;
       for (uint32_t y = 0; y < nb; ++y) {
-        const uint32_t dy = S.low[y];
+        const uint32_t dy = (uint32_t)__builtin_amdgcn_readlane((int)dx, (int)y);
         gt += dy > dx;
         ge += dy >= dx;
       }
@@ -618,6 +632,7 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
     }
   }
   __syncthreads();
+  DSA_STAMP(1, 12);
   const uint32_t T = S.T;
   need = S.need;  // keys equal to T to take, lowest positions first
   // mark the keys above T; list the keys equal to T
@@ -643,6 +658,7 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
     if (rank < need) atomicOr(&bits[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
+  DSA_STAMP(1, 13);
   // slots in position order: thread t owns bitmap words t kWpt .. +kWpt
   uint32_t w[kWpt], cntw = 0;
 #pragma unroll
@@ -656,6 +672,7 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
   }
   uint32_t tot;
   uint32_t slot = block_scan1<NT>(cntw, S.wt, tot);
+  DSA_STAMP(1, 14);
 #pragma unroll
   for (int q = 0; q < kWpt; ++q) {
     uint32_t b = w[q];

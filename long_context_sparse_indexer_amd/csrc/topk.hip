@@ -45,6 +45,76 @@ __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ c
   if (r < R) reinterpret_cast<v4i*>(cnt)[r] = v4i{0, 0, 0, 0};
 }
 
+constexpr int kRes = 1024;  // threads of the resolve block
+
+// Where the fused step wants the pool row of every selected slot ([R, k] int32, -1 for padding); `out` NULL
+// when no pool rows are wanted.
+struct PoolRows {
+  int32_t* out;
+  const int32_t* row_seq;
+  const int32_t* page_table;
+  int num_seqs, max_pages, num_pages, log2ps;
+};
+
+// LDS of a bitmap resolve over rows of at most 2^kBitsLog2 positions.
+template <int kBitsLog2>
+struct BitmapLds {
+  static constexpr int kWords = (1 << kBitsLog2) / 32;
+  static constexpr bool kStagePages = kBitsLog2 <= 17;
+  alignas(16) uint32_t bits[kWords];
+  alignas(16) int32_t pt[kStagePages ? kResPages : 1];
+};
+
+// The selection of row r (1024 threads): a row no longer than its budget is written whole; otherwise select.h's
+// bitmap_select settles it from the candidate list (`count` candidates above the floor fl), and a row the list
+// cannot settle (the sample overshot, the list overflowed, heavy ties) is selected over its stored scores.  The
+// list is written in increasing position order, padded with -1, with the pool row of each slot when asked; the
+// page ids of the row's sequence are staged in LDS when they fit.  h: kTopkBins words of LDS.
+template <int kBitsLog2>
+__device__ __forceinline__ void bitmap_resolve_row(const float* __restrict__ scores, int64_t ld, int r, int n, int k,
+                                                   uint32_t fl, uint32_t count, const uint64_t* __restrict__ cand,
+                                                   int32_t* __restrict__ topk_idx, const PoolRows& pr,
+                                                   BitmapLds<kBitsLog2>& L, uint32_t* h, BitmapScratch& S) {
+  const int t = threadIdx.x, keff = min(k, n);
+  const int32_t* gpt = pr.out ? pr.page_table + (int64_t)clamp_seq(pr.row_seq[r], pr.num_seqs) * pr.max_pages : nullptr;
+  const bool pt_lds = BitmapLds<kBitsLog2>::kStagePages && pr.out && pr.max_pages <= kResPages;
+  const ListSink sink{topk_idx + (int64_t)r * k, pr.out ? pr.out + (int64_t)r * k : nullptr,
+                      RowMap{pt_lds ? L.pt : gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
+  if (keff >= n) {
+    const ListSink gsink{sink.out, sink.rows_out, RowMap{gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
+    for (int i = t; i < k; i += kRes) gsink.put_or_pad(i, i < n ? i : -1);
+    return;
+  }
+  DSA_STAMP(1, 3);
+  // the page ids are staged while the candidates load (visible after bitmap_select's first barrier)
+  auto stage = [&]() { if (pt_lds) stage_page_row<kRes>(L.pt, gpt, pr.max_pages); };
+  if (!bitmap_select<BitmapLds<kBitsLog2>::kWords / kRes>(n, keff, fl, count, cand + (int64_t)r * kCap, sink, L.bits,
+                                                           h, S, stage)) {
+    __syncthreads();
+    select_and_write<kRes>(RowList{scores + (int64_t)r * ld}, n, (uint32_t)keff, keff, sink, h, S.wt);
+  }
+  DSA_STAMP(1, 4);
+  for (int i = keff + t; i < k; i += kRes) sink.put_or_pad(i, -1);
+  DSA_STAMP(1, 5);
+}
+
+// The filter blocks of a row that participate (cpb chunks each), and the hand-over to the last of them: every
+// thread waits for its candidate stores, then one acquire-release atomic per block (device scope) counts the
+// block in, so that one write-back of the cache per block publishes the block's stores; the block that completes
+// the count has acquired the others' and resolves the row in place of a resolve launch.  (A device-scope fence
+// in every thread made the hand-over cost more than the launch it saves.)
+__device__ __forceinline__ bool last_filter_block(uint32_t* cnt_done, int parts, uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(cnt_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(parts - 1);
+  __syncthreads();
+  return *flag != 0u;
+}
+__device__ __forceinline__ uint32_t load_count(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The kEpt = 4 consecutive scores of this thread in chunk c, as one 16-byte load with no branch: the row's
 // stride is a multiple of 4 and at least n, so a 4-aligned offset below n can always be read whole; past the
 // row's end offset 0 is read instead and the values are marked invalid where they are used.  Keeping the raw
@@ -194,17 +264,23 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
   return (b1 << 8) | s[2];
 }
 
+// kFuse: rows of at most 2^17 positions are resolved by their last filter block (bitmap_resolve_row), and a row
+// no longer than its budget is written whole by block 0.
+template <bool kFuse>
 __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
                                                            const int32_t* __restrict__ row_len, int max_row_len,
                                                            int k, uint32_t* __restrict__ cnt,
                                                            uint32_t* __restrict__ thr,
                                                            uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
-                                                           int nblk_max, int cpb) {
+                                                           int nblk_max, int cpb, int32_t* __restrict__ topk_idx,
+                                                           PoolRows pr) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
   __shared__ __attribute__((aligned(16))) uint32_t h2[256];
-  __shared__ uint32_t seg_base, s_f[4];
+  __shared__ uint32_t seg_base, s_f[4], s_last;
+  __shared__ BitmapLds<kFuse ? 17 : 5> bl;  // used when kFuse
+  __shared__ BitmapScratch bs[1];  // used when kFuse
   args_to_sgprs(scores, ld, row_len, max_row_len, k, cnt, thr, seg_cnt, seg_off, cand, nblk_max, cpb);
   DSA_STAMP(1, 0);
   const int r = blockIdx.y;
@@ -212,6 +288,12 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const int keff = min(k, n);
   const int nchunk = (n + kCh - 1) / kCh;
   const int c0 = (int)blockIdx.x * cpb;
+  if constexpr (kFuse) {
+    if (keff >= n) {  // the whole row, by one block
+      if (blockIdx.x == 0) bitmap_resolve_row<17>(scores, ld, r, n, k, 0u, 0u, cand, topk_idx, pr, bl, h, bs[0]);
+      return;
+    }
+  }
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
@@ -258,6 +340,10 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
     filter(ch + 1, xb);
   }
   DSA_STAMP(1, 2);
+  if constexpr (kFuse) {
+    if (last_filter_block(&cnt[4 * r + 3], (nchunk + cpb - 1) / cpb, &s_last))
+      bitmap_resolve_row<17>(scores, ld, r, n, k, fl, load_count(&cnt[4 * r + 2]), cand, topk_idx, pr, bl, h, bs[0]);
+  }
 }
 
 // Filter for blocks that cover several chunks (long rows, large batches).  The chunk loop stages each chunk's
@@ -268,23 +354,34 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
 constexpr int kStageCap = 6144;  // staged candidates per block (48 KiB; two 1024-thread blocks fit a CU)
 static_assert(kCh <= kStageCap, "one chunk always fits an empty stage");
 
+// kFuse as for topk_filter_kernel; the resolve's bitmap and page ids take the stage's LDS once it is flushed.
+template <bool kFuse>
 __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int max_row_len, int k,
     uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
     uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand, int nblk_max,
-    int cpb) {
+    int cpb, int32_t* __restrict__ topk_idx, PoolRows pr) {
+  static_assert(sizeof(BitmapLds<17>) <= kStageCap * sizeof(uint64_t), "the resolve's LDS fits the stage");
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
-  __shared__ uint64_t stage[kStageCap];
+  __shared__ __attribute__((aligned(16))) uint64_t stage[kStageCap];
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];  // the sample's histograms
   __shared__ __attribute__((aligned(16))) uint32_t h2[256];
   __shared__ uint32_t chunk_n[kTopkMaxBlocksPerRow];  // candidates of each staged chunk
-  __shared__ uint32_t seg_base, s_f[4];
+  __shared__ uint32_t seg_base, s_f[4], s_last;
+  __shared__ BitmapScratch bs[1];  // used when kFuse
   args_to_sgprs(scores, ld, row_len, max_row_len, k, cnt, thr, seg_cnt, seg_off, cand, nblk_max, cpb);
+  auto& bl = *reinterpret_cast<BitmapLds<17>*>(stage);
   const int r = blockIdx.y;
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
   const int nchunk = (n + kCh - 1) / kCh;
   const int c0 = (int)blockIdx.x * cpb;
+  if constexpr (kFuse) {
+    if (keff >= n) {  // the whole row, by one block
+      if (blockIdx.x == 0) bitmap_resolve_row<17>(scores, ld, r, n, k, 0u, 0u, cand, topk_idx, pr, bl, h, bs[0]);
+      return;
+    }
+  }
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
@@ -339,18 +436,12 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   }
   __syncthreads();  // the stage and chunk counts are complete
   flush(c1);
+  if constexpr (kFuse) {
+    if (last_filter_block(&cnt[4 * r + 3], (nchunk + cpb - 1) / cpb, &s_last))  // its barriers end the flush
+      bitmap_resolve_row<17>(scores, ld, r, n, k, fl, load_count(&cnt[4 * r + 2]), cand, topk_idx, pr, bl, h, bs[0]);
+  }
 }
 
-constexpr int kRes = 1024;  // threads of the resolve block
-
-// Where the fused step wants the pool row of every selected slot ([R, k] int32, -1 for padding); `out` NULL
-// when no pool rows are wanted.
-struct PoolRows {
-  int32_t* out;
-  const int32_t* row_seq;
-  const int32_t* page_table;
-  int num_seqs, max_pages, num_pages, log2ps;
-};
 
 // One block per row: the selection of the row (select.h), written as the list of selected positions in increasing
 // position order, padded with -1, and, when asked, the pool row of each.
@@ -409,33 +500,14 @@ __global__ __launch_bounds__(kRes) void topk_bitmap_resolve_kernel(const float* 
                                                                    const uint64_t* __restrict__ cand,
                                                                    int32_t* __restrict__ topk_idx, PoolRows pr) {
   static_assert(kRes == 1024, "bitmap_select runs on 1024 threads");
-  constexpr int kWords = (1 << kBitsLog2) / 32;
-  constexpr bool kStagePages = kBitsLog2 <= 17;
-  __shared__ __attribute__((aligned(16))) uint32_t bits[kWords];
+  __shared__ BitmapLds<kBitsLog2> bl;
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
   __shared__ BitmapScratch S;
-  __shared__ int32_t pt[kStagePages ? kResPages : 1];
   args_to_sgprs(scores, ld, row_len, max_row_len, k, thr, cnt, cand, topk_idx, pr.out, pr.row_seq, pr.page_table,
                 pr.num_seqs, pr.max_pages, pr.num_pages, pr.log2ps);
-  const int r = blockIdx.x, t = threadIdx.x;
+  const int r = blockIdx.x;
   const int n = clamp_len(row_len[r], max_row_len);
-  const int keff = min(k, n);
-  const int32_t* gpt = pr.out ? pr.page_table + (int64_t)clamp_seq(pr.row_seq[r], pr.num_seqs) * pr.max_pages : nullptr;
-  const bool pt_lds = kStagePages && pr.out && pr.max_pages <= kResPages;
-  const ListSink sink{topk_idx + (int64_t)r * k, pr.out ? pr.out + (int64_t)r * k : nullptr,
-                      RowMap{pt_lds ? pt : gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
-  if (keff >= n) {
-    const ListSink gsink{sink.out, sink.rows_out, RowMap{gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
-    for (int i = t; i < k; i += kRes) gsink.put_or_pad(i, i < n ? i : -1);
-    return;
-  }
-  if (pt_lds) stage_page_row<kRes>(pt, gpt, pr.max_pages);  // visible after bitmap_select's first barrier
-  if (!bitmap_select<kWords / kRes>(n, keff, thr[4 * r], cnt[4 * r + 2], cand + (int64_t)r * kCap, sink, bits, h,
-                                    S)) {
-    __syncthreads();
-    select_and_write<kRes>(RowList{scores + (int64_t)r * ld}, n, (uint32_t)keff, keff, sink, h, S.wt);
-  }
-  for (int i = keff + t; i < k; i += kRes) sink.put_or_pad(i, -1);
+  bitmap_resolve_row<kBitsLog2>(scores, ld, r, n, k, thr[4 * r], cnt[4 * r + 2], cand, topk_idx, pr, bl, h, S);
 }
 
 }  // namespace
@@ -473,17 +545,20 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const Ws w = carve(g, workspace);
   const int cpb = chunks_per_block(g, w.nblk);
   dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
-  if (cpb > 1)
-    topk_filter_staged_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr,
-                                                         w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
-  else
-    topk_filter_kernel<<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr,
-                                                  w.seg_cnt, w.seg_off, w.cand, w.nblk, cpb);
   const PoolRows pr{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps};
-  if (g.max_row_len <= (1 << 17))
-    topk_bitmap_resolve_kernel<17><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
-                                                             w.cand, topk_idx, pr);
-  else if (g.max_row_len <= (1 << 20))
+  // rows of at most 2^17 positions: the last filter block of each row resolves it (one launch fewer)
+  const bool fuse = g.max_row_len <= (1 << 17);
+#define DSA_FILTER(KERN, F)                                                                                     \
+  KERN<F><<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr, w.seg_cnt, w.seg_off, \
+                                     w.cand, w.nblk, cpb, topk_idx, pr)
+  if (cpb > 1) {
+    if (fuse) DSA_FILTER(topk_filter_staged_kernel, true); else DSA_FILTER(topk_filter_staged_kernel, false);
+  } else {
+    if (fuse) DSA_FILTER(topk_filter_kernel, true); else DSA_FILTER(topk_filter_kernel, false);
+  }
+#undef DSA_FILTER
+  if (fuse) return hipGetLastError();
+  if (g.max_row_len <= (1 << 20))
     topk_bitmap_resolve_kernel<20><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
                                                              w.cand, topk_idx, pr);
   else
