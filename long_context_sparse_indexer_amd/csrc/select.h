@@ -39,10 +39,9 @@ struct RowList {
   __device__ int32_t p(int i) const { return i; }
 };
 
-// Pool row of a position of the row's sequence.  The row's page table is read from LDS when it was staged there,
-// else from global memory.
+// Pool row of a position of the row's sequence, from the global row of its page table.
 struct RowMap {
-  const int32_t* pt;  // page ids of the row's sequence: LDS copy or global row of the page table
+  const int32_t* pt;
   int max_pages, num_pages, log2ps;
   __device__ int32_t row(int32_t pos) const {
     const int lp = min(pos >> log2ps, max_pages - 1);
@@ -50,6 +49,20 @@ struct RowMap {
     return (page << log2ps) | (pos & ((1 << log2ps) - 1));
   }
 };
+// The same from the row's page ids staged in LDS.  A sink whose page-table reads may be global or LDS makes them
+// flat loads, and a loop of stores and flat loads waits for every store it issued: the two are kept apart.
+struct LdsRowMap {
+  const __attribute__((address_space(3))) int32_t* pt;
+  int max_pages, num_pages, log2ps;
+  __device__ int32_t row(int32_t pos) const {
+    const int lp = min(pos >> log2ps, max_pages - 1);
+    const int page = min(max(pt[lp], 0), num_pages - 1);
+    return (page << log2ps) | (pos & ((1 << log2ps) - 1));
+  }
+};
+__device__ __forceinline__ const __attribute__((address_space(3))) int32_t* lds_ptr(const int32_t* p) {
+  return reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+}
 
 // Copies the page ids of a row's sequence (max_pages <= kResPages) into LDS: every load is issued before the first
 // store, from an in-range address.  Called by all NT threads; the copy is visible after the caller's next barrier.
@@ -66,11 +79,12 @@ __device__ __forceinline__ void stage_page_row(int32_t* __restrict__ dst, const 
 }
 
 // Sink of the standalone selection: the whole list of selected positions and, when rows_out is non-NULL, the pool
-// row of each.
-struct ListSink {
+// row of each (Map: RowMap or LdsRowMap).
+template <class Map>
+struct ListSinkT {
   int32_t* out;
   int32_t* rows_out;
-  RowMap map;
+  Map map;
   __device__ bool wants(uint32_t, uint32_t) const { return true; }
   __device__ void put(uint32_t slot, int32_t pos) const {
     out[slot] = pos;
@@ -81,6 +95,8 @@ struct ListSink {
     if (rows_out) rows_out[slot] = pos >= 0 ? map.row(pos) : -1;
   }
 };
+using ListSink = ListSinkT<RowMap>;
+using LdsListSink = ListSinkT<LdsRowMap>;
 
 // Exclusive prefix over the block of one value per thread, and the block total, with one barrier: every wave
 // scans its lanes and publishes its total in wt[0 .. NW), then every thread adds the totals of the waves before
@@ -526,9 +542,9 @@ struct NoPre {
 };
 // pre(): work of the caller's that runs while the candidates load (its LDS writes must be visible after the
 // first barrier).
-template <int kWpt, class Pre = NoPre>
+template <int kWpt, class Sink, class Pre = NoPre>
 __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const uint64_t* __restrict__ list,
-                              const ListSink& sink, uint32_t* bits, uint32_t* h, BitmapScratch& S,
+                              const Sink& sink, uint32_t* bits, uint32_t* h, BitmapScratch& S,
                               const Pre& pre = Pre{}) {
   constexpr int NT = 1024, NW = NT / 64;
   constexpr int kPer = kCap / NT;  // candidates per thread

@@ -78,23 +78,28 @@ __device__ __forceinline__ void bitmap_resolve_row(const float* __restrict__ sco
   const int t = threadIdx.x, keff = min(k, n);
   const int32_t* gpt = pr.out ? pr.page_table + (int64_t)clamp_seq(pr.row_seq[r], pr.num_seqs) * pr.max_pages : nullptr;
   const bool pt_lds = BitmapLds<kBitsLog2>::kStagePages && pr.out && pr.max_pages <= kResPages;
-  const ListSink sink{topk_idx + (int64_t)r * k, pr.out ? pr.out + (int64_t)r * k : nullptr,
-                      RowMap{pt_lds ? L.pt : gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
+  int32_t* const out = topk_idx + (int64_t)r * k;
+  int32_t* const rows_out = pr.out ? pr.out + (int64_t)r * k : nullptr;
+  const ListSink gsink{out, rows_out, RowMap{gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
   if (keff >= n) {
-    const ListSink gsink{sink.out, sink.rows_out, RowMap{gpt, pr.max_pages, pr.num_pages, pr.log2ps}};
     for (int i = t; i < k; i += kRes) gsink.put_or_pad(i, i < n ? i : -1);
     return;
   }
   DSA_STAMP(1, 3);
-  // the page ids are staged while the candidates load (visible after bitmap_select's first barrier)
-  auto stage = [&]() { if (pt_lds) stage_page_row<kRes>(L.pt, gpt, pr.max_pages); };
-  if (!bitmap_select<BitmapLds<kBitsLog2>::kWords / kRes>(n, keff, fl, count, cand + (int64_t)r * kCap, sink, L.bits,
-                                                           h, S, stage)) {
-    __syncthreads();
-    select_and_write<kRes>(RowList{scores + (int64_t)r * ld}, n, (uint32_t)keff, keff, sink, h, S.wt);
-  }
-  DSA_STAMP(1, 4);
-  for (int i = keff + t; i < k; i += kRes) sink.put_or_pad(i, -1);
+  auto finish = [&](const auto& sink, auto pre) __attribute__((always_inline)) {
+    if (!bitmap_select<BitmapLds<kBitsLog2>::kWords / kRes>(n, keff, fl, count, cand + (int64_t)r * kCap, sink,
+                                                             L.bits, h, S, pre)) {
+      __syncthreads();
+      select_and_write<kRes>(RowList{scores + (int64_t)r * ld}, n, (uint32_t)keff, keff, gsink, h, S.wt);
+    }
+    DSA_STAMP(1, 4);
+    for (int i = keff + t; i < k; i += kRes) gsink.put_or_pad(i, -1);
+  };
+  if (pt_lds)  // the page ids are staged while the candidates load (visible after bitmap_select's first barrier)
+    finish(LdsListSink{out, rows_out, LdsRowMap{lds_ptr(L.pt), pr.max_pages, pr.num_pages, pr.log2ps}},
+           [&]() { stage_page_row<kRes>(L.pt, gpt, pr.max_pages); });
+  else
+    finish(gsink, NoPre{});
   DSA_STAMP(1, 5);
 }
 
@@ -129,40 +134,37 @@ __device__ __forceinline__ v4f load_raw(const float* __restrict__ row, int c, in
 // 128K-position decode step, 8% more for a 4096-row prefill chunk, from the extra candidates).
 constexpr int kSampleDiv = 32;
 
-// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, found by wave 0
-// alone in two levels: lane l sums the kBins/64 bins (63 - l) * kBins/64 .. (lane 0 the top ones) with 16-byte
-// reads and a DPP scan over the lanes picks the lane L holding the bin; then lanes g < kBins/256 take L's groups
-// of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
-// number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
-// Called by wave 0 only; the caller publishes the result with a barrier.
-template <int kBins>
-__device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
-  constexpr int kPer = kBins / 64, kGroups = kPer / 4;
-  static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
-  const int lane = threadIdx.x;
-  const v4i* hb = reinterpret_cast<const v4i*>(h);
-  uint32_t local = 0;
+// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, and the number of
+// entries above it, into *b and *above_out (left as preset when the histogram holds fewer than `need`).  Thread t
+// owns bins (NT - 1 - t) * kPer .. +kPer (kPer = kBins / NT, at least one; threads past the bins own none), a
+// block scan counts the entries above each thread's bins, and the thread holding the need-th largest walks its
+// bins.  (Wave 0 alone, with two levels of lane scans, took 1.1 us for 4096 bins at a 128K-position decode.)  One
+// barrier inside the scan; the caller publishes with another.  wt: NT / 64 words of LDS.
+template <int NT, int kBins>
+__device__ __forceinline__ void block_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* wt, uint32_t* b,
+                                                    uint32_t* above_out) {
+  constexpr int kPer = kBins >= NT ? kBins / NT : 1;
+  static_assert(kBins % kPer == 0 && kPer <= 4, "a thread's bins in one 16-byte read");
+  const int t = threadIdx.x;
+  const bool owns = (t + 1) * kPer <= kBins;
+  uint32_t hv[kPer], local = 0;
+  const int b0 = kBins - (t + 1) * kPer;  // this thread's lowest bin
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
-    const v4i x = hb[(63 - lane) * kGroups + q];
-    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  for (int e = 0; e < kPer; ++e) {
+    hv[e] = owns ? h[b0 + e] : 0u;
+    local += hv[e];
   }
   uint32_t tot;
-  const uint32_t above = wave_exclusive_scan(local, tot);
-  const uint64_t hit = __ballot(above < need && above + local >= need);
-  if (!hit) return;  // uniform: fewer than `need` entries
-  const int L = __builtin_ctzll(hit);
-  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
-  const v4i z = {0, 0, 0, 0};
-  const v4i x = lane < kGroups ? hb[(63 - L) * kGroups + (kGroups - 1 - lane)] : z;
-  const uint32_t gsum = (uint32_t)(x[0] + x[1] + x[2] + x[3]);
-  uint32_t tot2;
-  uint32_t a = above_l + wave_exclusive_scan(gsum, tot2);
-  if (lane < kGroups && a < need && a + gsum >= need) {
-    int e = 3;
-    while (e > 0 && a + (uint32_t)x[e] < need) a += (uint32_t)x[e--];
-    *b = (uint32_t)((63 - L) * kPer + 4 * (kGroups - 1 - lane) + e);
-    *above_out = a;
+  uint32_t above = block_scan1<NT>(local, wt, tot);
+  if (owns && above < need && above + local >= need) {
+    for (int e = kPer - 1; e >= 0; --e) {
+      if (above + hv[e] >= need) {
+        *b = (uint32_t)(b0 + e);
+        *above_out = above;
+        break;
+      }
+      above += hv[e];
+    }
   }
 }
 
@@ -181,7 +183,7 @@ __device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t n
 // a barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, uint32_t* h,
-                                                 uint32_t* h2, uint32_t* s) {
+                                                 uint32_t* h2, uint32_t* s, uint32_t* wt) {
   constexpr int kGroup = 4;  // 16-byte pieces per thread held in registers: all of them up to S = 16384
   // piece j (16 bytes) lies at `start(j)`: in a short row the row itself, piece after piece; in a sampled row the
   // j % 4-th quarter of run j / 4, which starts at a multiple of 4 below n - 16 (step >= 128), so every load lies
@@ -252,14 +254,14 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
   round(h, 20, 12, 0u, false);
   __syncthreads();
   DSA_STAMP(1, 7);
-  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins>(h, (uint32_t)m, &s[0], &s[1]);
+  block_threshold_bin<NT, kTopkBins>(h, (uint32_t)m, wt, &s[0], &s[1]);
   __syncthreads();
   DSA_STAMP(1, 8);
   const uint32_t b1 = s[0];
   round(h2, 12, 8, b1, ngroups > 1);
   __syncthreads();
   DSA_STAMP(1, 9);
-  if (threadIdx.x < 64) wave_threshold_bin<256>(h2, (uint32_t)m - s[1], &s[2], &s[3]);
+  block_threshold_bin<NT, 256>(h2, (uint32_t)m - s[1], wt, &s[2], &s[3]);
   __syncthreads();
   return (b1 << 8) | s[2];
 }
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const float* row = scores + (int64_t)r * ld;
   v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
   // every block ranks the sample itself instead of waiting for one block to publish the floor
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f, scan);
   DSA_STAMP(1, 1);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f, scan);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
