@@ -586,24 +586,21 @@ __device__ __forceinline__ void gather_chunk_wide(const unsigned short* __restri
 }
 
 // FP8 entries in the all-heads kernel.  A chunk's 32 entries (656 bytes each) are gathered raw by LDS-DMA into
-// one of four staging slots, packed at 656-byte strides, one load of 41 lanes per entry (wave w gathers entries
-// 8 w .. 8 w + 7).  Loads that each cover 64 16-byte pieces, crossing entries, took twice as long to issue per
-// byte.  One chunk ahead of its use, every thread widens 64 codes of the staged chunk to
-// bf16 (exact: an e4m3 value has a 4-bit significand) into a code buffer laid out like the bf16 rows.  The tile
-// scales are applied outside the MFMAs: QK accumulates each 128-dim tile on its own and adds it in with the slot's
-// scale; PV multiplies each probability by its slot's scale for the tile of the output columns and splits that
-// product into a bf16 head and a bf16 rest, both of which go through the MFMA.  No dequantised value is rounded.
-// Register i of an S^T tile holds slot 8 (i >> 2) + 2 (i & 3) + half in every lane of a lane half, so lane l
-// loads the four scales of the slot that register l % 16 holds in its half, and a DPP row_newbcast:i move hands
-// register i's scale to every lane of the row (rows 0-1 are half 0, rows 2-3 half 1).  The RoPE dims and the
-// scales are read straight from the staging slot (656 bytes = 164 dwords, 4 banks mod 32 like the code rows, so
-// the permuted A rows stay conflict-free).
+// one of kF8Ring staging slots, packed at 656-byte strides, one load of 41 lanes per entry (wave w gathers entries
+// 8 w .. 8 w + 7); loads that each cover 64 16-byte pieces, crossing entries, took twice as long to issue per byte.
+// Both products read the e4m3 codes straight from the staging slot and widen them to bf16 in registers (exact: an
+// e4m3 value has a 4-bit significand): QK with 16-byte reads that serve two K-steps, PV with transposed 8-bit
+// reads.  The tile scales are applied outside the MFMAs: QK accumulates each 128-dim tile on its own and adds it in
+// with the slot's scale; PV multiplies each probability by its slot's scale for the tile of the output columns and
+// splits that product into a bf16 head and a bf16 rest, both of which go through the MFMA.  No dequantised value
+// is rounded.  Register i of an S^T tile holds the same slot in every lane of a lane half, so lane l loads the four
+// scales of the slot that register l % 16 holds in its half, and a DPP row_newbcast:i hands register i's scale to
+// every lane of the row (rows 0-1 are half 0, rows 2-3 half 1).  The RoPE dims are read by QK from the slot too.
 constexpr int kF8RopeByte = kDC + 16;          // RoPE values follow the codes and the four scales
 constexpr int kF8Pieces = kF8Entry / 16;        // 41 16-byte pieces per entry: one LDS-DMA load of 41 lanes
 constexpr int kF8RowsPerWave = kCW / 4;          // rows (loads) each of the four waves gathers per chunk
 constexpr int kF8Slot = kCW * kF8Entry;          // staging slot bytes
-constexpr int kF8Ring = 4;                       // staging slots: converting, computing (RoPE), two in flight
-constexpr int kCodeBuf = kCW * kRowW;            // a code buffer: 32 rows of bf16 codes
+constexpr int kF8Ring = 4;                       // staging slots: the chunk computed, three in flight (six spilled)
 static_assert(kF8Entry % 16 == 0 && kF8Pieces <= 64, "an entry fits one load");
 
 __device__ __forceinline__ void gather_chunk_f8(const uint8_t* __restrict__ kv, const int32_t* prow, int dummy,
@@ -626,39 +623,11 @@ __device__ __forceinline__ void gather_chunk_f8(const uint8_t* __restrict__ kv, 
   }
 }
 
-// Thread t widens codes 16 g + 128 j (g = t % 8, j = 0..3) of row t / 8: the eight lanes of a row read 128
-// contiguous bytes per load, and write 32 bytes each per tile as two 16-byte stores, lanes 4..7 of a row in the
-// opposite order so that the eight lanes of one store cover all 32 banks.
-__device__ __forceinline__ v4i convert_load_f8(const char* slot, int t, int j) {
-  const int row = t >> 3, g = t & 7;
-  return *reinterpret_cast<const v4i*>(slot + row * kF8Entry + 16 * g + 128 * j);
-}
-__device__ __forceinline__ void convert_store_f8(char* code, int t, int j, const v4i c) {
-  const int row = t >> 3, g = t & 7, sw = (g >> 2) & 1;
-  v4i w[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const uint32_t d = (uint32_t)c[2 * h + x];
-      const v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, false);
-      const v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.f, true);
-      w[h][2 * x] = (int)__builtin_bit_cast(uint32_t, lo);
-      w[h][2 * x + 1] = (int)__builtin_bit_cast(uint32_t, hi);
-    }
-  char* dst = code + row * kRowW + 256 * j + 32 * g;
-  const v4i w0 = sw ? w[1] : w[0], w1 = sw ? w[0] : w[1];  // select whole vectors: no per-lane indexing
-  *reinterpret_cast<v4i*>(dst + 16 * sw) = w0;
-  *reinterpret_cast<v4i*>(dst + 16 * (1 - sw)) = w1;
-}
-__device__ __forceinline__ void convert_chunk_f8(const char* slot, char* code, int t) {
-  asm volatile("" : "+v"(t));  // recomputed per call, like the gather offsets
-  v4i c[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = convert_load_f8(slot, t, j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) convert_store_f8(code, t, j, c[j]);
-}
+// Slot order of the FP8 path: MFMA row m (an A row of QK, a K index of PV) holds slot f8_slot(m), which swaps
+// rows 8..11 with 12..15 in each 16.  With 656-byte (164-dword, 4 banks mod 32) rows, the eight lanes of a 16-byte
+// QK read (rows f8_slot(0..7), or f8_slot(8..15)) and the sixteen lanes of a PV transposed read (the rows of K
+// indices 8 kh + 0..7, two 8-byte pieces each) then cover all 32 banks.
+__device__ __forceinline__ int f8_slot(int m) { return m ^ (((m >> 3) & 1) << 2); }
 
 // Register i's value of a per-row quantity held by lanes 16 r + i, applied through the DPP row_newbcast:i source
 // of a VOP2 instruction, two registers (2 e, 2 e + 1) at a time: bcast_mul2 gives x = bcast_i(s) * st[i], and
@@ -827,8 +796,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   // which must fit vmcnt (at most 63 outstanding loads per wave)
   constexpr int kDepth = kBufW < 63 / kRows + 1 ? kBufW : 63 / kRows + 1;
   static_assert(kDepth >= 2 && (kDepth - 1) * kRows <= 63, "gathers in flight fit vmcnt");
-  // bf16 rows: a ring of kBufW chunks filled by LDS-DMA; FP8 entries: two code buffers, then kF8Ring staging slots
-  constexpr int kPool = kFp8 ? 2 * kCodeBuf + kF8Ring * kF8Slot : kBufW * kCW * kRowW;
+  // bf16 rows: a ring of kBufW chunks filled by LDS-DMA; FP8 entries: a ring of kF8Ring staging slots
+  constexpr int kPool = kFp8 ? kF8Ring * kF8Slot : kBufW * kCW * kRowW;
   __shared__ __attribute__((aligned(16))) char kv_pool_lds[kPool];
   __shared__ int32_t prow_lds[kWideMaxSplitLen];           // physical row of every slot, -1 = no position
   __shared__ uint32_t valid_lds[kWideMaxSplitLen / 32];    // bit per slot: it has a position
@@ -936,11 +905,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
       // S^T: slots 0..31 of the chunk (A rows) x this wave's 32 heads (B columns).  The A operands are read
       // kQkDepth K-steps ahead of their MFMAs; sched_barrier keeps the compiler from hoisting further.
       v16f st = {};
-      const int arow_i = 8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1);  // the slot this lane's A row holds
+      // the slot this lane's A row holds (FP8: see f8_slot)
+      const int arow_i = kFp8 ? f8_slot(col) : 8 * (col >> 3) + 2 * (col & 3) + ((col >> 2) & 1);
       // FP8: the four tile scales of the slot register (lane % 16) holds in this lane's half
       v4f sc = {};
       if constexpr (kFp8) {
-        const int sl = 8 * ((lane & 15) >> 2) + 2 * (lane & 3) + half;
+        const int sl = f8_slot(8 * ((lane & 15) >> 2) + 4 * half + (lane & 3));
         sc = *reinterpret_cast<const v4f*>(raw + sl * kF8Entry + kDC);
       }
       if constexpr (kFp8) {
@@ -1004,9 +974,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[i] *= scale_log2;
       if (vw != ~0u) {  // uniform: a chunk with slots that hold no position
-        const uint32_t w = vw >> half;  // register i holds row 8 (i >> 2) + 2 (i & 3) + half
+        // register i holds slot 8 (i >> 2) + 2 (i & 3) + half (bf16 rows), f8_slot(8 (i >> 2) + 4 half + (i & 3))
+        // (FP8 entries)
+        if constexpr (kFp8) {
+          // register 4 a + b holds slot 8 a + 4 (half ^ (a & 1)) + b: gather those nibbles of vw into bits 4 a ..
+          uint32_t wp = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[i] = (w >> (8 * (i >> 2) + 2 * (i & 3))) & 1u ? st[i] : -INFINITY;
+          for (int a = 0; a < 4; ++a) wp |= ((vw >> (8 * a + 4 * (half ^ (a & 1)))) & 0xfu) << (4 * a);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[i] = (wp >> i) & 1u ? st[i] : -INFINITY;
+        } else {
+          const uint32_t w = vw >> half;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[i] = (w >> (8 * (i >> 2) + 2 * (i & 3))) & 1u ? st[i] : -INFINITY;
+        }
       }
       float mx = st[0];
 #pragma unroll
@@ -1046,12 +1027,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
         if constexpr (kFp8) {
           // tile t of the output columns (dt = 4 t .. 4 t + 3): each probability times its slot's scale for the
           // tile, x, as the bf16 head h = x cut to its top 16 bits and the rest x - h (exact) rounded to bf16
-          // (together x to 2^-16 relative), on two MFMAs per (K-step, column tile)
+          // (together x to 2^-16 relative), on two MFMAs per (K-step, column tile).  The B operands come straight
+          // from the staged codes: ds_read_b64_tr_b8 gives lane (n, kh) the codes of column n in the eight slots
+          // of K indices 8 kh .., widened to bf16 in registers.  In each 16-lane group lane 2 e + hh addresses
+          // slot f8_slot(16 ks + 8 (e >> 2) + 4 kh + (e & 3)), columns 16 nh + 8 hh .. +8 of the tile; lane l of
+          // the group receives byte l & 7 of the addresses of lanes 2 e + (l >> 3), e = 0..7.
           constexpr int kTileSteps = (kCW / 16) * 4;  // (K-step, column tile) pairs of one tile, K-step major
+          const char* pb8;
+          {
+            const int g = lane >> 4, L = lane & 15, e = L >> 1, hh = L & 1, kh = g >> 1, nh = g & 1;
+            pb8 = raw + f8_slot(8 * (e >> 2) + 4 * kh + (e & 3)) * kF8Entry + 16 * nh + 8 * hh;
+          }
+          auto bread8 = [&](int ks, int dt) __attribute__((always_inline)) {
+            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)((__attribute__((address_space(3))) char*)(
+                    const_cast<char*>(pb8 + 16 * kF8Entry * ks + 32 * dt))));
+            const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c.x, 1.f, false);
+            const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c.x, 1.f, true);
+            const v2bf x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c.y, 1.f, false);
+            const v2bf x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c.y, 1.f, true);
+            return v8bf{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+          };
           v8bf bbuf[kPvDepth];
           auto pvb = [&](int v) __attribute__((always_inline)) {  // v: tile-major index of the pairs
             const int t = v / kTileSteps, w = v % kTileSteps;
-            return bread((w >> 2) * (kDC / 32) + 4 * t + (w & 3));
+            return bread8(w >> 2, 4 * t + (w & 3));
           };
 #pragma unroll
           for (int v = 0; v < kPvDepth; ++v) bbuf[v] = pvb(v);
@@ -1108,37 +1108,36 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     };
     // One pass over the chunks.  bf16 rows: kDepth chunks are gathered ahead into a ring of kBufW LDS buffers;
     // after the barrier that ends chunk c, chunk c + kDepth is gathered into a buffer no wave still reads.
-    // FP8 entries: at the barrier that opens chunk c, chunk c + 1 has landed in its staging slot and every wave is
-    // done with chunk c - 1; chunk c + 3 is then gathered into chunk c - 1's slot and chunk c + 1 converted into
-    // chunk c - 1's code buffer (read by PV), before chunk c is computed.
+    // FP8 entries: kF8Ring - 1 chunks are gathered ahead into a ring of kF8Ring staging slots; at the barrier that
+    // opens chunk c, chunk c has landed and every wave is done with chunk c - 1, whose slot takes chunk
+    // c + kF8Ring - 1.
     auto run = [&](const bool qk_only) __attribute__((always_inline)) {
       if constexpr (kFp8) {
         const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
-        char* const code0 = kv_pool_lds;
-        char* const slot0 = kv_pool_lds + 2 * kCodeBuf;
-        auto code = [&](int c) { return code0 + (c & 1) * kCodeBuf; };
-        auto slot = [&](int c) { return slot0 + (c & (kF8Ring - 1)) * kF8Slot; };
-        // waits until this wave's gathers of the chunk due next have landed, `ahead` later chunks staying in
-        // flight (kF8RowsPerWave loads per chunk)
+        auto slot = [&](int c) { return kv_pool_lds + (c % kF8Ring) * kF8Slot; };
+        // waits until this wave's gathers of chunk c have landed, `ahead` later chunks staying in flight
+        // (kF8RowsPerWave loads per chunk)
         auto wait_f8 = [&](const int ahead) __attribute__((always_inline)) {
-          if (ahead == 0) __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0));
-          else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kF8RowsPerWave));
-          else __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * kF8RowsPerWave));
+          static_assert((kF8Ring - 2) * kF8RowsPerWave <= 63, "gathers in flight fit vmcnt");
+          switch (ahead) {
+            case 0: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(kF8RowsPerWave)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(2 * kF8RowsPerWave)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(3 * kF8RowsPerWave)); break;
+            default: __builtin_amdgcn_s_waitcnt(kWaitVmOnly(4 * kF8RowsPerWave)); break;
+          }
         };
+        static_assert(kF8Ring - 2 <= 4, "wait_f8 covers the ring");
         __builtin_amdgcn_s_waitcnt(0);  // from here the gathers are the only loads in flight
         for (int c = 0; c < kF8Ring - 1 && c < nch; ++c)
           gather_chunk_f8(kv8, prow_lds + c * kCW, dummy, slot(c), wave, lane);
-        wait_f8(min(nch - 1, kF8Ring - 2));
-        lds_barrier();
-        convert_chunk_f8(slot(0), code(0), threadIdx.x);
         DSA_STAMP(5, 2);
         for (int c = 0; c < nch; ++c) {
-          if (c + 1 < nch) wait_f8(min(nch - 2 - c, kF8Ring - 3));
+          wait_f8(min(nch - 1 - c, kF8Ring - 2));
           lds_barrier();
           if (c + kF8Ring - 1 < nch)
             gather_chunk_f8(kv8, prow_lds + (c + kF8Ring - 1) * kCW, dummy, slot(c + kF8Ring - 1), wave, lane);
-          if (c + 1 < nch) convert_chunk_f8(slot(c + 1), code(c + 1), threadIdx.x);
-          chunk(c, code(c), slot(c), qk_only);
+          chunk(c, nullptr, slot(c), qk_only);
           if ((c & 3) == 3 && c < 16) DSA_STAMP(5, 3 + (c >> 2));
         }
         __syncthreads();
