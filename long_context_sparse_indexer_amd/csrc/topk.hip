@@ -134,37 +134,40 @@ __device__ __forceinline__ v4f load_raw(const float* __restrict__ row, int c, in
 // 128K-position decode step, 8% more for a 4096-row prefill chunk, from the extra candidates).
 constexpr int kSampleDiv = 32;
 
-// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, and the number of
-// entries above it, into *b and *above_out (left as preset when the histogram holds fewer than `need`).  Thread t
-// owns bins (NT - 1 - t) * kPer .. +kPer (kPer = kBins / NT, at least one; threads past the bins own none), a
-// block scan counts the entries above each thread's bins, and the thread holding the need-th largest walks its
-// bins.  (Wave 0 alone, with two levels of lane scans, took 1.1 us for 4096 bins at a 128K-position decode.)  One
-// barrier inside the scan; the caller publishes with another.  wt: NT / 64 words of LDS.
-template <int NT, int kBins>
-__device__ __forceinline__ void block_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* wt, uint32_t* b,
-                                                    uint32_t* above_out) {
-  constexpr int kPer = kBins >= NT ? kBins / NT : 1;
-  static_assert(kBins % kPer == 0 && kPer <= 4, "a thread's bins in one 16-byte read");
-  const int t = threadIdx.x;
-  const bool owns = (t + 1) * kPer <= kBins;
-  uint32_t hv[kPer], local = 0;
-  const int b0 = kBins - (t + 1) * kPer;  // this thread's lowest bin
+// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, found by wave 0
+// alone in two levels: lane l sums the kBins/64 bins (63 - l) * kBins/64 .. (lane 0 the top ones) with 16-byte
+// reads and a DPP scan over the lanes picks the lane L holding the bin; then lanes g < kBins/256 take L's groups
+// of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
+// number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
+// Called by wave 0 only; the caller publishes the result with a barrier.
+template <int kBins>
+__device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
+  constexpr int kPer = kBins / 64, kGroups = kPer / 4;
+  static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
+  const int lane = threadIdx.x;
+  const v4i* hb = reinterpret_cast<const v4i*>(h);
+  uint32_t local = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    hv[e] = owns ? h[b0 + e] : 0u;
-    local += hv[e];
+  for (int q = 0; q < kGroups; ++q) {
+    const v4i x = hb[(63 - lane) * kGroups + q];
+    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
   }
   uint32_t tot;
-  uint32_t above = block_scan1<NT>(local, wt, tot);
-  if (owns && above < need && above + local >= need) {
-    for (int e = kPer - 1; e >= 0; --e) {
-      if (above + hv[e] >= need) {
-        *b = (uint32_t)(b0 + e);
-        *above_out = above;
-        break;
-      }
-      above += hv[e];
-    }
+  const uint32_t above = wave_exclusive_scan(local, tot);
+  const uint64_t hit = __ballot(above < need && above + local >= need);
+  if (!hit) return;  // uniform: fewer than `need` entries
+  const int L = __builtin_ctzll(hit);
+  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+  const v4i z = {0, 0, 0, 0};
+  const v4i x = lane < kGroups ? hb[(63 - L) * kGroups + (kGroups - 1 - lane)] : z;
+  const uint32_t gsum = (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  uint32_t tot2;
+  uint32_t a = above_l + wave_exclusive_scan(gsum, tot2);
+  if (lane < kGroups && a < need && a + gsum >= need) {
+    int e = 3;
+    while (e > 0 && a + (uint32_t)x[e] < need) a += (uint32_t)x[e--];
+    *b = (uint32_t)((63 - L) * kPer + 4 * (kGroups - 1 - lane) + e);
+    *above_out = a;
   }
 }
 
@@ -183,7 +186,7 @@ __device__ __forceinline__ void block_threshold_bin(const uint32_t* h, uint32_t 
 // a barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, int n, int keff, uint32_t* h,
-                                                 uint32_t* h2, uint32_t* s, uint32_t* wt) {
+                                                 uint32_t* h2, uint32_t* s) {
   constexpr int kGroup = 4;  // 16-byte pieces per thread held in registers: all of them up to S = 16384
   // piece j (16 bytes) lies at `start(j)`: in a short row the row itself, piece after piece; in a sampled row the
   // j % 4-th quarter of run j / 4, which starts at a multiple of 4 below n - 16 (step >= 128), so every load lies
@@ -254,14 +257,14 @@ __device__ __forceinline__ uint32_t floor_prefix(const float* __restrict__ row, 
   round(h, 20, 12, 0u, false);
   __syncthreads();
   DSA_STAMP(1, 7);
-  block_threshold_bin<NT, kTopkBins>(h, (uint32_t)m, wt, &s[0], &s[1]);
+  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins>(h, (uint32_t)m, &s[0], &s[1]);
   __syncthreads();
   DSA_STAMP(1, 8);
   const uint32_t b1 = s[0];
   round(h2, 12, 8, b1, ngroups > 1);
   __syncthreads();
   DSA_STAMP(1, 9);
-  block_threshold_bin<NT, 256>(h2, (uint32_t)m - s[1], wt, &s[2], &s[3]);
+  if (threadIdx.x < 64) wave_threshold_bin<256>(h2, (uint32_t)m - s[1], &s[2], &s[3]);
   __syncthreads();
   return (b1 << 8) | s[2];
 }
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   const float* row = scores + (int64_t)r * ld;
   v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
   // every block ranks the sample itself instead of waiting for one block to publish the floor
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f, scan);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   DSA_STAMP(1, 1);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
   v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f, scan);
+  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
@@ -548,8 +551,10 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const int cpb = chunks_per_block(g, w.nblk);
   dim3 grid((w.nblk + cpb - 1) / cpb, g.R);
   const PoolRows pr{pool_rows, g.row_seq, g.page_table, g.S, g.max_pages, g.num_pages, g.log2ps};
-  // rows of at most 2^17 positions: the last filter block of each row resolves it (one launch fewer)
-  const bool fuse = g.max_row_len <= (1 << 17);
+  // a single row of at most 2^17 positions: the last filter block resolves it (one launch fewer).  With many rows
+  // the resolves, a few microseconds each, would hold filter blocks' CUs while other rows' filter blocks wait
+  // (64 rows of the batched decode: 20 -> 41 us), so they take a launch of their own.
+  const bool fuse = g.R == 1 && g.max_row_len <= (1 << 17);
 #define DSA_FILTER(KERN, F)                                                                                     \
   KERN<F><<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr, w.seg_cnt, w.seg_off, \
                                      w.cand, w.nblk, cpb, topk_idx, pr)
@@ -560,7 +565,10 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   }
 #undef DSA_FILTER
   if (fuse) return hipGetLastError();
-  if (g.max_row_len <= (1 << 20))
+  if (g.max_row_len <= (1 << 17))
+    topk_bitmap_resolve_kernel<17><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
+                                                             w.cand, topk_idx, pr);
+  else if (g.max_row_len <= (1 << 20))
     topk_bitmap_resolve_kernel<20><<<g.R, kRes, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.thr, w.cnt,
                                                              w.cand, topk_idx, pr);
   else
