@@ -527,7 +527,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     for (int j = 0; j < 4; ++j) {
       const int piece = j * 64 + lane, hh = piece >> 4, c8 = piece & 15;  // head, 8-column piece
       const v4i x = *reinterpret_cast<const v4i*>(stg + hh * kStgRow + c8 * 8);
-      *reinterpret_cast<v4i*>(part_o + (prow0 + hh) * kDC + wave * 128 + c8 * 8) = x;
+      // non-temporal: the combine reads the partials next, and dirty lines left in the L2 lengthen the kernel's
+      // end (-0.3 us per 128K step)
+      __builtin_nontemporal_store(x, reinterpret_cast<v4i*>(part_o + (prow0 + hh) * kDC + wave * 128 + c8 * 8));
     }
   }
   if (wave == 0 && g == 0) {
@@ -1187,7 +1189,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
       const int64_t prow = ((int64_t)r * nsplit + split) * H + hw + hh;
 #pragma unroll
       for (int dt = 0; dt < kDC / 32; ++dt)
-        part_o[prow * kDC + 32 * dt + col] = part_bits(any ? o[dt][i] * inv : 0.f, ex);
+        __builtin_nontemporal_store(part_bits(any ? o[dt][i] * inv : 0.f, ex), part_o + prow * kDC + 32 * dt + col);
       if (col == 0) part_exp[prow] = ex;
     } else {
       const int64_t orow = (int64_t)r * H + hw + hh;
