@@ -176,6 +176,18 @@ def test_attention_wide_logit_range(batch):
                    recent=32))
 
 
+@pytest.mark.parametrize("batch,H,k", [(8, 128, 2048), (16, 128, 2048), (32, 128, 2048), (64, 128, 2048),
+                                         (64, 16, 4096)])
+def test_split_merge_one_wave_per_row_head(batch, H, k):
+    # 1024 or more (row, head) pairs.  The all-heads kernel splits each row 32, 16, 8 and 4 ways at 8, 16, 32 and
+    # 64 rows; up to 16 splits are merged by one wave per pair, 32 by a block per pair.  The 16-head kernel
+    # splits a 4096-slot budget 64 ways (block-per-pair merge)
+    def rows(p):
+        return [0, p.R // 2, p.R - 1]
+    _sampled("batched_paged", rows, batch=batch, length_range=(k + 300, 2 * k + 700), H=H, k=k, anchors=16,
+             recent=32)
+
+
 def test_paged_equals_contiguous_bit_for_bit():
     cfg = synth.get("batched_paged", batch=3, length_range=(2500, 7000), H=32)
     a = gpu_step(synth.make_problem(cfg))
