@@ -248,7 +248,8 @@ dsa_status_t decode_step(const dsa::Geo& g, const void* q_idx, const float* q_id
   // the top-k hands the bf16 attention the pool row of every selected slot, sparing it the page-table lookup
   int32_t* pool_rows = g.kv_dtype == DSA_BF16 ? pool_rows_ws : nullptr;
   if (fuse) {
-    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK)
+    if ((st = hip_status(dsa::launch_topk_select(g, scores, ld, idx, tail, pool_rows, dsa::indexer_floor_blocks(g), s),
+                         "top-k launch")) != DSA_OK)
       return st;
   } else if ((st = hip_status(dsa::launch_topk(g, scores, ld, idx, tail, pool_rows, s), "top-k launch")) != DSA_OK) {
     return st;

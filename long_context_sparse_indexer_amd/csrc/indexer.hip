@@ -206,19 +206,157 @@ __device__ __forceinline__ void index_row_tiles(
 }
 
 
+// The fused step's top-k floor of row r, ranked from the row's own keys by one extra block while the rest of the
+// grid scores the row, so that the filter only compares (the sample used to be ranked again by every filter block
+// after this kernel).  The block scores kFloorSample positions, 256 runs of four consecutive positions spread
+// evenly over the row (a run lies in one page), with the tiles' contraction and epilogue: group g of wave w is 32
+// positions, eight runs, each lane loading its own position's page id.  The keys are ranked through LDS histograms
+// (bits 31..20, then bits 19..12 in the bin found) to the 20-bit prefix of the m-th largest sampled score, with
+// m = mu + 4 sqrt(mu) + 8 and mu = k_eff S / n the expected number of sampled scores among the row's k_eff
+// largest: about n m / S scores reach it (5.1 K at n = 128K, k = 2048), and a sample holds m scores above the
+// k_eff-th largest with probability below 1e-6 at these sizes.  Whatever floor comes out, the selection stays
+// exact: a row whose floor admits fewer than k_eff candidates, or more than its list holds, is selected over its
+// stored scores.  Rows outside indexer_floor_row return at once.
+template <int HB, int KB>
+__device__ __forceinline__ void sample_row_floor(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
+    int num_pages, int log2ps, int max_row_len, int k, uint32_t* __restrict__ thr, int r) {
+  constexpr int H_I = 32 * HB, D_I = 64 * KB;
+  constexpr int kGroups = kFloorSample / (4 * 32);  // 32-position groups per wave
+  constexpr int kRuns = kFloorSample / 4;
+  static_assert(kGroups % 2 == 0, "groups are finished in pairs");
+  __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h2[256];
+  __shared__ uint32_t s[4];
+  const int n = clamp_len(row_len[r], max_row_len);
+  const int keff = min(k, n);
+  if (!indexer_floor_row(n, keff)) return;  // uniform over the block
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int seq = clamp_seq(row_seq[r], num_seqs);
+  // pool rows of the lane's positions (run j = 8 (kGroups wave + g) + col / 4 starts at j n / kRuns, rounded down
+  // to a multiple of 4; the last run ends below n since n >= kFloorMinLen), then their keys and scales
+  int64_t prow[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int j = 8 * (kGroups * wave + g) + (col >> 2);
+    const int pos = (int)(((int64_t)j * n / kRuns) & ~3) + (col & 3);
+    const int lp = min(pos >> log2ps, max_pages - 1);
+    const int page = min(max(page_table[(int64_t)seq * max_pages + lp], 0), num_pages - 1);
+    prow[g] = ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
+  }
+  // the row's query operands and epilogue weights, laid out as in index_row_tiles
+  v8i a[HB][KB];
+  float wq[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      a[hb][kb] =
+          *reinterpret_cast<const v8i*>(q_idx + ((int64_t)r * H_I + hb * 32 + col) * D_I + kb * 64 + half * 32);
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const int64_t h0 = (int64_t)r * H_I + hb * 32 + half * 4 + 8 * m4;
+      const v4f w4 = *reinterpret_cast<const v4f*>(head_w + h0);
+      const v4f s4 = *reinterpret_cast<const v4f*>(q_scale + h0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wq[hb][4 * m4 + e] = w4[e] * s4[e];
+    }
+  }
+  // histograms cleared while the loads are in flight
+  for (int i = threadIdx.x; i < kTopkBins; i += 256) h[i] = 0u;
+  h2[threadIdx.x] = 0u;
+  if (threadIdx.x < 4) s[threadIdx.x] = 0u;  // a floor of 0 keeps every key, should the rank fail
+  // scores, in rounds of kRound groups whose keys are loaded together (d_I = 128 keys take two rounds: eight groups
+  // of 64-byte operands would not fit the registers); within a round the MFMA of unit u + 1 is issued before the
+  // epilogue of unit u, as in the tiles, and lane half h ends with the score of group 2 p + h at position col
+  constexpr int kRound = KB == 1 ? kGroups : kGroups / 2;
+  constexpr int kUnits = kRound * HB;
+  uint32_t key[kGroups / 2];
+#pragma unroll
+  for (int g0 = 0; g0 < kGroups; g0 += kRound) {
+    v8i b[kRound][KB];
+    float sk[kRound];
+#pragma unroll
+    for (int g = 0; g < kRound; ++g) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        b[g][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[g0 + g] * D_I + kb * 64 + half * 32);
+      sk[g] = k_scale[prow[g0 + g]];
+    }
+    auto unit_mfma = [&](int u) __attribute__((always_inline)) {
+      v16f acc = {};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u % HB][kb], b[u / HB][kb], acc, 0, 0, 0, 0, 0, 0);
+      return acc;
+    };
+    v16f acc = unit_mfma(0);
+    float lin = 0.f, ab = 0.f, part[2];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int g = u / HB, hb = u % HB;
+      v16f nxt;
+      if (u + 1 < kUnits) nxt = unit_mfma(u + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        lin = fmaf(wq[hb][i], acc[i], lin);
+        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+      }
+      if (hb == HB - 1) {
+        part[g % 2] = lin + ab;
+        lin = 0.f;
+        ab = 0.f;
+      }
+      if (hb == HB - 1 && g % 2 == 1) {
+        const auto sw =
+            __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+        const float skp = half ? sk[g] : sk[g - 1];
+        key[(g0 + g) / 2] = order_key(skp * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1]))));
+      }
+      if (u + 1 < kUnits) acc = nxt;
+    }
+  }
+  const float mu = (float)keff * (float)kFloorSample / (float)n;
+  const uint32_t m = (uint32_t)min(kFloorSample, (int)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kGroups / 2; ++p) atomicAdd(&h[key[p] >> 20], 1u);
+  __syncthreads();
+  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins>(h, m, &s[0], &s[1]);
+  __syncthreads();
+  const uint32_t b1 = s[0];
+#pragma unroll
+  for (int p = 0; p < kGroups / 2; ++p)
+    if ((key[p] >> 20) == b1) atomicAdd(&h2[(key[p] >> 12) & 255u], 1u);
+  __syncthreads();
+  if (threadIdx.x < 64) wave_threshold_bin<256>(h2, m - s[1], &s[2], &s[3]);
+  __syncthreads();
+  if (threadIdx.x == 0) thr[4 * r + 1] = (b1 << 8) | s[2];
+}
+
 template <int HB, int KB>
 __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
     const uint8_t* __restrict__ k_pool, const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, float* __restrict__ scores, int64_t ld, TopkState clear,
-    int tiles_per_block) {
+    int tiles_per_block, int floor_col) {
   args_to_sgprs(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages, num_pages,
-                log2ps, max_row_len, scores, ld, clear.cnt, tiles_per_block);
+                log2ps, max_row_len, scores, ld, clear.cnt, clear.thr, clear.k, tiles_per_block, floor_col);
   DSA_STAMP(0, 0);
+  // column 0 of a grid with floor blocks ranks the rows' top-k floors (dispatched first, so it starts with the tiles)
+  if (floor_col && blockIdx.x == 0) {
+    sample_row_floor<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs,
+                             max_pages, num_pages, log2ps, max_row_len, clear.k, clear.thr, (int)blockIdx.y);
+    return;
+  }
   index_row_tiles<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages,
                           num_pages, log2ps, max_row_len, scores, ld, clear, tiles_per_block, (int)blockIdx.y,
-                          (int)blockIdx.x);
+                          (int)blockIdx.x - floor_col);
 }
 
 // Chunked prefill: consecutive rows of one sequence score the same keys, so the contraction is a real GEMM
@@ -634,10 +772,11 @@ void launch_f8(const Geo& g, const uint8_t* qp, const float* q_idx_scale, const 
   const int tiles_row = (g.max_row_len + kIdxTile - 1) / kIdxTile;
   const int64_t tiles = (int64_t)tiles_row * g.R;
   const int per = (int)std::max<int64_t>(1, std::min<int64_t>(tiles_row, tiles / kIdxTargetBlocks));
-  dim3 grid((tiles_row + per - 1) / per, g.R);
+  const int floor_col = fuse && indexer_floor_blocks(g) ? 1 : 0;
+  dim3 grid((tiles_row + per - 1) / per + floor_col, g.R);
   indexer_f8_kernel<HB, KB><<<grid, 256, 0, stream>>>(
       qp, q_idx_scale, head_w, kp, k_idx_scale, g.row_seq, g.row_len, g.page_table, g.S, g.max_pages, g.num_pages,
-      g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr}, per);
+      g.log2ps, g.max_row_len, scores, ld, fuse ? *fuse : TopkState{nullptr, nullptr, 0}, per, floor_col);
 }
 
 // Grid-wide barrier of a persistent launch whose blocks are all resident: each block adds one to *bar when it
@@ -739,6 +878,10 @@ void launch_tiled_mode(const Geo& g, const void* q_idx, const float* q_idx_scale
 // fp8 rows that come in groups sharing a sequence take the tiled kernel (d_I = 64 or 128)
 bool indexer_tiled(const Geo& g) {
   return g.idx_dtype == 2 /* F8E4M3 */ && (g.d_I == 64 || g.d_I == 128) && g.rows_per_seq >= kTiledMinRows;
+}
+
+bool indexer_floor_blocks(const Geo& g) {
+  return g.idx_dtype == 2 /* F8E4M3 */ && !indexer_tiled(g) && g.max_row_len >= kFloorMinLen && g.k <= 4096;
 }
 
 hipError_t launch_indexer(const Geo& g, const void* q_idx, const float* q_idx_scale, const float* head_w,

@@ -22,10 +22,15 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Per-row top-k state that must start at zero: the candidate counters.  In the fused step the indexer clears
-// them (block 0 of each row, after its scores), sparing the top-k a zeroing launch.
+// them (block 0 of each row, after its scores), sparing the top-k a zeroing launch, and ranks the top-k floor of
+// the rows of indexer_floor_row into thr (an extra block per row).
 struct TopkState {
   uint32_t* cnt;  // [R, 4]
+  uint32_t* thr;  // [R, 4]; entry 1 receives the floor
+  int k;
 };
+// Whether the fused step's indexer launch carries the floor blocks (some row may have indexer_floor_row).
+bool indexer_floor_blocks(const Geo& g);
 
 // indexer.hip.  fp8 problems whose rows come in groups of at least kTiledMinRows per sequence (chunked prefill)
 // run the tiled GEMM kernel, which takes no `fuse`.  Otherwise, with `fuse` non-NULL the indexer also clears the
@@ -77,9 +82,9 @@ TopkState topk_state(const Geo& g, void* workspace);
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream);
 // Selection over stored scores whose top-k state is already zero (launch_topk_zero, or the fused indexer).
 // pool_rows: if non-NULL, [R, k] int32 receiving the pool row of every selected slot (-1 for padding), for the
-// attention.
+// attention.  indexer_floors: the fused indexer ranked the floors of the rows of indexer_floor_row.
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              int32_t* pool_rows, hipStream_t stream);
+                              int32_t* pool_rows, bool indexer_floors, hipStream_t stream);
 hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
                        int32_t* pool_rows, hipStream_t stream);
 

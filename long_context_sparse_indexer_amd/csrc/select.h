@@ -26,6 +26,43 @@ constexpr int kCh = kTopkChunk;   // scores per filter chunk
 constexpr int kCap = 12288;       // candidate entries a row keeps for the resolve step
 constexpr int kResPages = 4096;   // page-table entries a resolving block stages in LDS
 
+// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, found by wave 0
+// alone in two levels: lane l sums the kBins/64 bins (63 - l) * kBins/64 .. (lane 0 the top ones) with 16-byte
+// reads and a DPP scan over the lanes picks the lane L holding the bin; then lanes g < kBins/256 take L's groups
+// of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
+// number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
+// Called by wave 0 only; the caller publishes the result with a barrier.
+template <int kBins>
+__device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
+  constexpr int kPer = kBins / 64, kGroups = kPer / 4;
+  static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
+  const int lane = threadIdx.x;
+  const v4i* hb = reinterpret_cast<const v4i*>(h);
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const v4i x = hb[(63 - lane) * kGroups + q];
+    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  }
+  uint32_t tot;
+  const uint32_t above = wave_exclusive_scan(local, tot);
+  const uint64_t hit = __ballot(above < need && above + local >= need);
+  if (!hit) return;  // uniform: fewer than `need` entries
+  const int L = __builtin_ctzll(hit);
+  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+  const v4i z = {0, 0, 0, 0};
+  const v4i x = lane < kGroups ? hb[(63 - L) * kGroups + (kGroups - 1 - lane)] : z;
+  const uint32_t gsum = (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  uint32_t tot2;
+  uint32_t a = above_l + wave_exclusive_scan(gsum, tot2);
+  if (lane < kGroups && a < need && a + gsum >= need) {
+    int e = 3;
+    while (e > 0 && a + (uint32_t)x[e] < need) a += (uint32_t)x[e--];
+    *b = (uint32_t)((63 - L) * kPer + 4 * (kGroups - 1 - lane) + e);
+    *above_out = a;
+  }
+}
+
 // Candidate access for the resolve step: entries of the LDS list, or every position of the stored row.
 struct LdsList {
   const uint32_t* key;

@@ -6,7 +6,8 @@
 // Scores become order-preserving 32-bit keys.  Every hand-over between blocks happens at a kernel boundary:
 //   filter   grid (4096-score chunks, rows): every block first finds the row's floor, the 20-bit key prefix of a
 //            sampled score that comfortably more than k_eff scores of the row exceed.  The sample is a fixed set
-//            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram.  The
+//            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram (in the
+//            fused step the indexer has already ranked the floor of most decode rows from the keys).  The
 //            block then writes the keys whose first 20 bits reach the floor, in position order, into a segment of
 //            the row's candidate list.
 //   resolve  one 1024-thread block per row runs the resolve step of select.h and writes the list (and, in the
@@ -134,43 +135,6 @@ __device__ __forceinline__ v4f load_raw(const float* __restrict__ row, int c, in
 // 128K-position decode step, 8% more for a 4096-row prefill chunk, from the extra candidates).
 constexpr int kSampleDiv = 32;
 
-// The bin of an LDS histogram holding the need-th largest entry, counting from the top bin, found by wave 0
-// alone in two levels: lane l sums the kBins/64 bins (63 - l) * kBins/64 .. (lane 0 the top ones) with 16-byte
-// reads and a DPP scan over the lanes picks the lane L holding the bin; then lanes g < kBins/256 take L's groups
-// of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
-// number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
-// Called by wave 0 only; the caller publishes the result with a barrier.
-template <int kBins>
-__device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
-  constexpr int kPer = kBins / 64, kGroups = kPer / 4;
-  static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
-  const int lane = threadIdx.x;
-  const v4i* hb = reinterpret_cast<const v4i*>(h);
-  uint32_t local = 0;
-#pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
-    const v4i x = hb[(63 - lane) * kGroups + q];
-    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
-  }
-  uint32_t tot;
-  const uint32_t above = wave_exclusive_scan(local, tot);
-  const uint64_t hit = __ballot(above < need && above + local >= need);
-  if (!hit) return;  // uniform: fewer than `need` entries
-  const int L = __builtin_ctzll(hit);
-  const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
-  const v4i z = {0, 0, 0, 0};
-  const v4i x = lane < kGroups ? hb[(63 - L) * kGroups + (kGroups - 1 - lane)] : z;
-  const uint32_t gsum = (uint32_t)(x[0] + x[1] + x[2] + x[3]);
-  uint32_t tot2;
-  uint32_t a = above_l + wave_exclusive_scan(gsum, tot2);
-  if (lane < kGroups && a < need && a + gsum >= need) {
-    int e = 3;
-    while (e > 0 && a + (uint32_t)x[e] < need) a += (uint32_t)x[e--];
-    *b = (uint32_t)((63 - L) * kPer + 4 * (kGroups - 1 - lane) + e);
-    *above_out = a;
-  }
-}
-
 // The row's floor: the first 20 bits of the m-th largest score of a sample of the row, ranked in two rounds of an
 // LDS histogram: bits 31..20 of every sampled key (4096 bins in h), then bits 19..12 of those in the bin found
 // (256 bins in h2), each ranked by one wave.  The sample is S scores in S/16 runs of sixteen consecutive scores
@@ -279,7 +243,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
                                                            uint32_t* __restrict__ seg_cnt,
                                                            uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand,
                                                            int nblk_max, int cpb, int32_t* __restrict__ topk_idx,
-                                                           PoolRows pr) {
+                                                           PoolRows pr, const uint32_t* __restrict__ pre_floor) {
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
   __shared__ __attribute__((aligned(16))) uint32_t h2[256];
@@ -301,9 +265,11 @@ __global__ __launch_bounds__(kTpb) void topk_filter_kernel(const float* __restri
   }
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
-  v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample
-  // every block ranks the sample itself instead of waiting for one block to publish the floor
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
+  v4f xa = load_raw(row, c0, n), xb;  // the first chunk loads together with the sample (or the indexer's floor)
+  // every block ranks the sample itself instead of waiting for one block to publish the floor, unless the fused
+  // indexer ranked it
+  const uint32_t fl = pre_floor && indexer_floor_row(n, keff) ? pre_floor[4 * r]
+                                                              : floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   DSA_STAMP(1, 1);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
@@ -365,7 +331,7 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int max_row_len, int k,
     uint32_t* __restrict__ cnt, uint32_t* __restrict__ thr,
     uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ seg_off, uint64_t* __restrict__ cand, int nblk_max,
-    int cpb, int32_t* __restrict__ topk_idx, PoolRows pr) {
+    int cpb, int32_t* __restrict__ topk_idx, PoolRows pr, const uint32_t* __restrict__ pre_floor) {
   static_assert(sizeof(BitmapLds<17>) <= kStageCap * sizeof(uint64_t), "the resolve's LDS fits the stage");
   __shared__ __attribute__((aligned(16))) uint32_t scan[kTpb / 64 + 1];
   __shared__ __attribute__((aligned(16))) uint64_t stage[kStageCap];
@@ -389,8 +355,9 @@ __global__ __launch_bounds__(kTpb) void topk_filter_staged_kernel(
   }
   if (keff >= n || c0 >= nchunk) return;
   const float* row = scores + (int64_t)r * ld;
-  v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample
-  const uint32_t fl = floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
+  v4f x = load_raw(row, c0, n);  // the first chunk loads together with the sample (or the indexer's floor)
+  const uint32_t fl = pre_floor && indexer_floor_row(n, keff) ? pre_floor[4 * r]
+                                                              : floor_prefix<kTpb>(row, n, keff, h, h2, s_f);
   if (blockIdx.x == 0 && threadIdx.x == 0) thr[4 * r + 0] = fl;
   const int c1 = min(nchunk, c0 + cpb);
   // staged chunks [cs, ch) hold `staged` candidates
@@ -525,7 +492,7 @@ size_t topk_workspace_bytes(const Geo& g) {
 
 TopkState topk_state(const Geo& g, void* workspace) {
   const Ws w = carve(g, workspace);
-  return TopkState{w.cnt};
+  return TopkState{w.cnt, w.thr, g.k};
 }
 
 hipError_t launch_topk_zero(const Geo& g, void* workspace, hipStream_t stream) {
@@ -545,7 +512,7 @@ int chunks_per_block(const Geo& g, int nblk) {
 }
 
 hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int32_t* topk_idx, void* workspace,
-                              int32_t* pool_rows, hipStream_t stream) {
+                              int32_t* pool_rows, bool indexer_floors, hipStream_t stream) {
   if (g.R == 0) return hipSuccess;
   const Ws w = carve(g, workspace);
   const int cpb = chunks_per_block(g, w.nblk);
@@ -557,7 +524,7 @@ hipError_t launch_topk_select(const Geo& g, const float* scores, int64_t ld, int
   const bool fuse = g.R == 1 && g.max_row_len <= (1 << 17);
 #define DSA_FILTER(KERN, F)                                                                                     \
   KERN<F><<<grid, kTpb, 0, stream>>>(scores, ld, g.row_len, g.max_row_len, g.k, w.cnt, w.thr, w.seg_cnt, w.seg_off, \
-                                     w.cand, w.nblk, cpb, topk_idx, pr)
+                                     w.cand, w.nblk, cpb, topk_idx, pr, indexer_floors ? w.thr + 1 : nullptr)
   if (cpb > 1) {
     if (fuse) DSA_FILTER(topk_filter_staged_kernel, true); else DSA_FILTER(topk_filter_staged_kernel, false);
   } else {
@@ -580,7 +547,7 @@ hipError_t launch_topk(const Geo& g, const float* scores, int64_t ld, int32_t* t
                        int32_t* pool_rows, hipStream_t stream) {
   hipError_t e = launch_topk_zero(g, workspace, stream);
   if (e != hipSuccess) return e;
-  return launch_topk_select(g, scores, ld, topk_idx, workspace, pool_rows, stream);
+  return launch_topk_select(g, scores, ld, topk_idx, workspace, pool_rows, false, stream);
 }
 
 }  // namespace dsa

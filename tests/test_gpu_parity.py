@@ -61,6 +61,37 @@ def test_batched_short_empty_and_tiny_rows():
     _run(synth.get("batched_paged", batch=4, lengths=[0, 1, 1500, 6000], anchors=8, recent=8))
 
 
+def test_indexer_ranked_floor_rows():
+    # rows of 16K..256K positions take the top-k floor that the fused step's indexer ranks from 1024 sampled keys
+    # (the separate calls rank the filter's own sample, and the two selections must agree bit for bit): the
+    # shortest such row and one just below it, k = 4096 at 2^17 and k = 2048 at 2^18 (the rule's edges), and a
+    # paged batch with rows on both sides of 16K
+    _run(synth.get("decode_128k", lengths=[16384], H=16, anchors=64, recent=96))
+    _run(synth.get("decode_128k", lengths=[16383], H=16, anchors=64, recent=96))
+    _run(synth.get("decode_128k", lengths=[1 << 17], k=4096, H=16))
+    _run(synth.get("decode_128k", lengths=[1 << 18], H=16))
+    _run(synth.get("batched_paged", batch=4, lengths=[9000, 16384, 40000, 70001], H=32))
+
+
+def _scale_sampled_keys(prob, factor):
+    """Multiplies the key scale of the 1024 positions the fused indexer samples for a row's floor (256 runs of
+    four, run j at j n / 256 rounded down to a multiple of four): every score there scales by `factor`."""
+    n = int(prob.row_len[0])
+    pos = np.array([((j * n) // 256) // 4 * 4 + c for j in range(256) for c in range(4)])
+    ps = prob.page_size
+    phys = prob.page_table[prob.row_seq[0], pos // ps].astype(np.int64) * ps + pos % ps
+    prob.k_idx_scale[phys] *= np.float32(factor)
+
+
+def test_indexer_floor_misjudged_either_way():
+    # sampled keys scaled up 8x: the floor sits above all but about 40 scores, fewer than k, so the row is selected
+    # over its stored scores; scaled down 8x: nearly every score reaches the floor, the candidate list overflows,
+    # and the same rescan settles it.  Both stay exact.
+    _run(synth.get("decode_128k", lengths=[1 << 17], H=16), mutate=lambda p: _scale_sampled_keys(p, 8.0))
+    _run(synth.get("decode_128k", lengths=[40000], H=16, anchors=64, recent=96),
+         mutate=lambda p: _scale_sampled_keys(p, 0.125))
+
+
 def test_index_heads_32_and_small_budgets():
     _run(synth.get("decode_128k", lengths=[9000], H_I=32, k=100, anchors=16, recent=32))
     _run(synth.get("decode_128k", lengths=[5000], k=1, H=16, anchors=16, recent=32))
