@@ -206,17 +206,33 @@ __device__ __forceinline__ void index_row_tiles(
 }
 
 
+// Largest value over the 64 lanes of a wave (DPP within rows, then lane swaps between rows).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
 // The fused step's top-k floor of row r, ranked from the row's own keys by one extra block while the rest of the
 // grid scores the row, so that the filter only compares (the sample used to be ranked again by every filter block
-// after this kernel).  The block scores kFloorSample positions, 256 runs of four consecutive positions spread
-// evenly over the row (a run lies in one page), with the tiles' contraction and epilogue: group g of wave w is 32
-// positions, eight runs, each lane loading its own position's page id.  The keys are ranked through LDS histograms
-// (bits 31..20, then bits 19..12 in the bin found) to the 20-bit prefix of the m-th largest sampled score, with
-// m = mu + 4 sqrt(mu) + 8 and mu = k_eff S / n the expected number of sampled scores among the row's k_eff
-// largest: about n m / S scores reach it (5.1 K at n = 128K, k = 2048), and a sample holds m scores above the
-// k_eff-th largest with probability below 1e-6 at these sizes.  Whatever floor comes out, the selection stays
-// exact: a row whose floor admits fewer than k_eff candidates, or more than its list holds, is selected over its
-// stored scores.  Rows outside indexer_floor_row return at once.
+// after this kernel).  The block scores S sampled positions, S / 4 runs of four consecutive positions spread
+// evenly over the row (a run lies in one page), with the tiles' contraction and epilogue: each wave takes rounds of
+// four 32-position groups (eight runs each, every lane loading its own position's page id).  S = 512 (one round)
+// for a single row of up to 2^17 positions with k_eff <= 2048, where this block is the last to finish, else 1024
+// (with several rows the block hides behind the other rows' tiles, and the larger sample admits fewer candidates).  The floor is the 20-bit prefix of the m-th
+// largest sampled score, m = mu + 4 sqrt(mu) + 8 with mu = k_eff S / n the expected number of sampled scores
+// among the row's k_eff largest: about n m / S scores reach it (7.2 K at n = 128K, k = 2048), and a sample holds m
+// scores at or above the k_eff-th largest with probability below 1e-6 at these sizes.  One LDS histogram ranks
+// the sample: bin 4095 - d counts the keys whose 20-bit prefix lies d below the sample's largest (d clamped to
+// 4095), so the m-th largest is found without a second round unless it lies 4095 or more prefixes down (a
+// spread of more than a factor of four), when the floor keeps every key.  Whatever floor comes out, the
+// selection stays exact: a row whose floor admits fewer than k_eff candidates, or more than its list holds, is
+// selected over its stored scores.  Rows outside indexer_floor_row return at once.
 template <int HB, int KB>
 __device__ __forceinline__ void sample_row_floor(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ head_w,
@@ -224,29 +240,34 @@ __device__ __forceinline__ void sample_row_floor(
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, int k, uint32_t* __restrict__ thr, int r) {
   constexpr int H_I = 32 * HB, D_I = 64 * KB;
-  constexpr int kGroups = kFloorSample / (4 * 32);  // 32-position groups per wave
-  constexpr int kRuns = kFloorSample / 4;
-  static_assert(kGroups % 2 == 0, "groups are finished in pairs");
+  constexpr int kRound = 4;                                        // groups per wave and round (512 positions)
+  constexpr int kMaxGroups = kFloorSample / (4 * 32);              // groups per wave at S = kFloorSample
+  constexpr int kLoad = kRound;                                    // groups whose keys are in flight together
+  static_assert(kMaxGroups % kLoad == 0 && kLoad % kRound == 0, "rounds tile the groups");
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
-  __shared__ __attribute__((aligned(16))) uint32_t h2[256];
-  __shared__ uint32_t s[4];
+  __shared__ uint32_t s[8];
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
   if (!indexer_floor_row(n, keff)) return;  // uniform over the block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
-  // pool rows of the lane's positions (run j = 8 (kGroups wave + g) + col / 4 starts at j n / kRuns, rounded down
-  // to a multiple of 4; the last run ends below n since n >= kFloorMinLen), then their keys and scales
-  int64_t prow[kGroups];
+  const int S = gridDim.y == 1 && n <= (1 << 17) && keff <= 2048 ? 4 * 32 * kRound : kFloorSample;
+  const int G = S / (4 * 32);  // groups per wave
+  const int runs = S / 4;
+  // pool rows of the lane's positions: group g of wave w holds runs 8 (G w + g) + col / 4; run j starts at j n / runs
+  // rounded down to a multiple of 4 (the last run ends below n since n >= kFloorMinLen)
+  int64_t prow[kMaxGroups];
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    const int j = 8 * (kGroups * wave + g) + (col >> 2);
-    const int pos = (int)(((int64_t)j * n / kRuns) & ~3) + (col & 3);
+  for (int g = 0; g < kMaxGroups; ++g) {
+    if (g >= G) break;  // uniform
+    const int j = 8 * (G * wave + g) + (col >> 2);
+    const int pos = (int)(((int64_t)j * n / runs) & ~3) + (col & 3);
     const int lp = min(pos >> log2ps, max_pages - 1);
     const int page = min(max(page_table[(int64_t)seq * max_pages + lp], 0), num_pages - 1);
     prow[g] = ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
   }
+  DSA_STAMP(0, 4);
   // the row's query operands and epilogue weights, laid out as in index_row_tiles
   v8i a[HB][KB];
   float wq[HB][16];
@@ -265,77 +286,88 @@ __device__ __forceinline__ void sample_row_floor(
       for (int e = 0; e < 4; ++e) wq[hb][4 * m4 + e] = w4[e] * s4[e];
     }
   }
-  // histograms cleared while the loads are in flight
+  // histogram cleared while the loads are in flight
   for (int i = threadIdx.x; i < kTopkBins; i += 256) h[i] = 0u;
-  h2[threadIdx.x] = 0u;
-  if (threadIdx.x < 4) s[threadIdx.x] = 0u;  // a floor of 0 keeps every key, should the rank fail
-  // scores, in rounds of kRound groups whose keys are loaded together (d_I = 128 keys take two rounds: eight groups
-  // of 64-byte operands would not fit the registers); within a round the MFMA of unit u + 1 is issued before the
-  // epilogue of unit u, as in the tiles, and lane half h ends with the score of group 2 p + h at position col
-  constexpr int kRound = KB == 1 ? kGroups : kGroups / 2;
-  constexpr int kUnits = kRound * HB;
-  uint32_t key[kGroups / 2];
+  if (threadIdx.x < 8) s[threadIdx.x] = 0u;  // a floor of 0 keeps every key, should the rank fail
+  // scores, one round of four groups at a time (the keys of eight groups would not fit the registers beside the
+  // tiles' budget); the MFMA of unit u + 1 is issued before the epilogue of unit u, as in the tiles, and lane half
+  // h ends with the score of group 2 p + h at position col
+  uint32_t key[kMaxGroups / 2];
 #pragma unroll
-  for (int g0 = 0; g0 < kGroups; g0 += kRound) {
-    v8i b[kRound][KB];
-    float sk[kRound];
+  for (int i = 0; i < kMaxGroups / 2; ++i) key[i] = 0u;
 #pragma unroll
-    for (int g = 0; g < kRound; ++g) {
+  for (int g0 = 0; g0 < kMaxGroups; g0 += kLoad) {
+    if (g0 >= G) break;  // uniform
+    v8i b[kLoad][KB];
+    float sk[kLoad];
+#pragma unroll
+    for (int g = 0; g < kLoad; ++g) {
+      if (g0 + g >= G) break;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         b[g][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[g0 + g] * D_I + kb * 64 + half * 32);
       sk[g] = k_scale[prow[g0 + g]];
     }
-    auto unit_mfma = [&](int u) __attribute__((always_inline)) {
-      v16f acc = {};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u % HB][kb], b[u / HB][kb], acc, 0, 0, 0, 0, 0, 0);
-      return acc;
-    };
-    v16f acc = unit_mfma(0);
-    float lin = 0.f, ab = 0.f, part[2];
+    for (int q0 = 0; q0 < kLoad; q0 += kRound) {
+      if (g0 + q0 >= G) break;  // uniform
+      auto unit_mfma = [&](int u) __attribute__((always_inline)) {
+        v16f acc = {};
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int g = u / HB, hb = u % HB;
-      v16f nxt;
-      if (u + 1 < kUnits) nxt = unit_mfma(u + 1);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int kb = 0; kb < KB; ++kb)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u % HB][kb], b[q0 + u / HB][kb], acc, 0, 0, 0, 0,
+                                                                0, 0);
+        return acc;
+      };
+      constexpr int kUnits = kRound * HB;
+      v16f acc = unit_mfma(0);
+      float lin = 0.f, ab = 0.f, part[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        lin = fmaf(wq[hb][i], acc[i], lin);
-        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+      for (int u = 0; u < kUnits; ++u) {
+        const int g = u / HB, hb = u % HB;
+        v16f nxt;
+        if (u + 1 < kUnits) nxt = unit_mfma(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          lin = fmaf(wq[hb][i], acc[i], lin);
+          ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
+        }
+        if (hb == HB - 1) {
+          part[g % 2] = lin + ab;
+          lin = 0.f;
+          ab = 0.f;
+        }
+        if (hb == HB - 1 && g % 2 == 1) {
+          const auto sw =
+              __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+          const float skp = half ? sk[q0 + g] : sk[q0 + g - 1];
+          key[(g0 + q0 + g) / 2] = order_key(skp * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1]))));
+        }
+        if (u + 1 < kUnits) acc = nxt;
       }
-      if (hb == HB - 1) {
-        part[g % 2] = lin + ab;
-        lin = 0.f;
-        ab = 0.f;
-      }
-      if (hb == HB - 1 && g % 2 == 1) {
-        const auto sw =
-            __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-        const float skp = half ? sk[g] : sk[g - 1];
-        key[(g0 + g) / 2] = order_key(skp * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1]))));
-      }
-      if (u + 1 < kUnits) acc = nxt;
     }
   }
-  const float mu = (float)keff * (float)kFloorSample / (float)n;
-  const uint32_t m = (uint32_t)min(kFloorSample, (int)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
-  __syncthreads();
+  DSA_STAMP(0, 5);
+  const float mu = (float)keff * (float)S / (float)n;
+  const uint32_t m = (uint32_t)min(S, (int)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
+  // the sample's largest key (keys of groups past G stay 0 and never exceed it), then one histogram of distances
+  uint32_t mx = 0u;
 #pragma unroll
-  for (int p = 0; p < kGroups / 2; ++p) atomicAdd(&h[key[p] >> 20], 1u);
+  for (int i = 0; i < kMaxGroups / 2; ++i) mx = max(mx, key[i]);
+  mx = wave_max_u32(mx);
+  if (lane == 0) s[4 + wave] = mx;
   __syncthreads();
-  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins>(h, m, &s[0], &s[1]);
-  __syncthreads();
-  const uint32_t b1 = s[0];
+  const uint32_t top = max(max(s[4], s[5]), max(s[6], s[7])) >> 12;
 #pragma unroll
-  for (int p = 0; p < kGroups / 2; ++p)
-    if ((key[p] >> 20) == b1) atomicAdd(&h2[(key[p] >> 12) & 255u], 1u);
+  for (int i = 0; i < kMaxGroups / 2; ++i)
+    if (2 * i < G) atomicAdd(&h[kTopkBins - 1 - min(top - (key[i] >> 12), (uint32_t)kTopkBins - 1)], 1u);
   __syncthreads();
-  if (threadIdx.x < 64) wave_threshold_bin<256>(h2, m - s[1], &s[2], &s[3]);
+  DSA_STAMP(0, 6);
+  if (threadIdx.x < 64) wave_threshold_bin<kTopkBins, 16>(h, m, &s[0], &s[1]);
   __syncthreads();
-  if (threadIdx.x == 0) thr[4 * r + 1] = (b1 << 8) | s[2];
+  if (threadIdx.x == 0) thr[4 * r + 1] = s[0] > 0u ? top - (kTopkBins - 1 - s[0]) : 0u;
+  DSA_STAMP(0, 7);
 }
 
 template <int HB, int KB>
@@ -348,15 +380,22 @@ __global__ __launch_bounds__(256, KB == 1 ? 3 : 2) void indexer_f8_kernel(
   args_to_sgprs(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages, num_pages,
                 log2ps, max_row_len, scores, ld, clear.cnt, clear.thr, clear.k, tiles_per_block, floor_col);
   DSA_STAMP(0, 0);
-  // column 0 of a grid with floor blocks ranks the rows' top-k floors (dispatched first, so it starts with the tiles)
-  if (floor_col && blockIdx.x == 0) {
-    sample_row_floor<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs,
-                             max_pages, num_pages, log2ps, max_row_len, clear.k, clear.thr, (int)blockIdx.y);
-    return;
+  // a grid with floor blocks has one extra column: the first R blocks in dispatch order (linear id, x fastest) rank
+  // the rows' top-k floors, so that they start with the first tiles even in a batch, and the other blocks take the
+  // rows' tiles in row-major order
+  int r = (int)blockIdx.y, bx = (int)blockIdx.x;
+  if (floor_col) {
+    const int lin = (int)(blockIdx.x + blockIdx.y * gridDim.x), R = (int)gridDim.y, cols = (int)gridDim.x - 1;
+    if (lin < R) {
+      sample_row_floor<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs,
+                               max_pages, num_pages, log2ps, max_row_len, clear.k, clear.thr, lin);
+      return;
+    }
+    r = (lin - R) / cols;
+    bx = (lin - R) % cols;
   }
   index_row_tiles<HB, KB>(q_idx, q_scale, head_w, k_pool, k_scale, row_seq, row_len, page_table, num_seqs, max_pages,
-                          num_pages, log2ps, max_row_len, scores, ld, clear, tiles_per_block, (int)blockIdx.y,
-                          (int)blockIdx.x - floor_col);
+                          num_pages, log2ps, max_row_len, scores, ld, clear, tiles_per_block, r, bx);
 }
 
 // Chunked prefill: consecutive rows of one sequence score the same keys, so the contraction is a real GEMM

@@ -32,17 +32,27 @@ constexpr int kResPages = 4096;   // page-table entries a resolving block stages
 // of four bins, top group first, a second scan picks the group, and its lane walks the four bins.  The bin and the
 // number of entries above it land in *b, *above (left as preset when the histogram holds fewer than `need`).
 // Called by wave 0 only; the caller publishes the result with a barrier.
-template <int kBins>
+template <int kBins, int kInFlight = 4>
 __device__ __forceinline__ void wave_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* b, uint32_t* above_out) {
   constexpr int kPer = kBins / 64, kGroups = kPer / 4;
   static_assert(kPer % 4 == 0 && kGroups <= 64, "16-byte reads of a lane's bins");
   const int lane = threadIdx.x;
   const v4i* hb = reinterpret_cast<const v4i*>(h);
+  // lane l reads its kGroups 16-byte words starting at word l % kGroups (in the plain order every lane would hit the
+  // same banks at once, a kGroups * 16-byte lane stride), kInFlight of them issued before any is summed: a running
+  // sum over the reads had the compiler keep two in flight, eight LDS round trips in a row
+  static_assert((kGroups & (kGroups - 1)) == 0, "the rotation wraps with a mask");
+  constexpr int kBatch = kInFlight < kGroups ? kInFlight : kGroups;
+  static_assert(kGroups % kBatch == 0, "batches tile the words");
   uint32_t local = 0;
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
-    const v4i x = hb[(63 - lane) * kGroups + q];
-    local += (uint32_t)(x[0] + x[1] + x[2] + x[3]);
+  for (int q0 = 0; q0 < kGroups; q0 += kBatch) {
+    v4i xs[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) xs[q] = hb[(63 - lane) * kGroups + ((q0 + q + lane) & (kGroups - 1))];
+    __builtin_amdgcn_sched_barrier(0);  // the batch's reads issued before the first sum
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) local += (uint32_t)(xs[q][0] + xs[q][1] + xs[q][2] + xs[q][3]);
   }
   uint32_t tot;
   const uint32_t above = wave_exclusive_scan(local, tot);

@@ -74,17 +74,19 @@ def test_indexer_ranked_floor_rows():
 
 
 def _scale_sampled_keys(prob, factor):
-    """Multiplies the key scale of the 1024 positions the fused indexer samples for a row's floor (256 runs of
-    four, run j at j n / 256 rounded down to a multiple of four): every score there scales by `factor`."""
+    """Multiplies the key scale of the positions the fused indexer samples for a row's floor (runs of four, run j
+    of `runs` at j n / runs rounded down to a multiple of four; 128 runs for a single row of up to 2^17 positions
+    with k <= 2048, else 256): every score of row 0 there scales by `factor`."""
     n = int(prob.row_len[0])
-    pos = np.array([((j * n) // 256) // 4 * 4 + c for j in range(256) for c in range(4)])
+    runs = 128 if prob.R == 1 and n <= (1 << 17) and min(prob.k, n) <= 2048 else 256
+    pos = np.array([((j * n) // runs) // 4 * 4 + c for j in range(runs) for c in range(4)])
     ps = prob.page_size
     phys = prob.page_table[prob.row_seq[0], pos // ps].astype(np.int64) * ps + pos % ps
     prob.k_idx_scale[phys] *= np.float32(factor)
 
 
 def test_indexer_floor_misjudged_either_way():
-    # sampled keys scaled up 8x: the floor sits above all but about 40 scores, fewer than k, so the row is selected
+    # sampled keys scaled up 8x: the floor sits above all but a few dozen scores, fewer than k, so the row is selected
     # over its stored scores; scaled down 8x: nearly every score reaches the floor, the candidate list overflows,
     # and the same rescan settles it.  Both stay exact.
     _run(synth.get("decode_128k", lengths=[1 << 17], H=16), mutate=lambda p: _scale_sampled_keys(p, 8.0))
