@@ -221,16 +221,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // The fused step's top-k floor of row r, ranked from the row's own keys by one extra block while the rest of the
 // grid scores the row, so that the filter only compares (the sample used to be ranked again by every filter block
 // after this kernel).  The block scores S sampled positions, S / 4 runs of four consecutive positions spread
-// evenly over the row (a run lies in one page), with the tiles' contraction and epilogue: each wave takes rounds of
-// four 32-position groups (eight runs each, every lane loading its own position's page id).  S = 512 (one round)
-// for a single row of up to 2^17 positions with k_eff <= 2048, where this block is the last to finish, else 1024
-// (with several rows the block hides behind the other rows' tiles, and the larger sample admits fewer candidates).  The floor is the 20-bit prefix of the m-th
-// largest sampled score, m = mu + 4 sqrt(mu) + 8 with mu = k_eff S / n the expected number of sampled scores
-// among the row's k_eff largest: about n m / S scores reach it (7.2 K at n = 128K, k = 2048), and a sample holds m
-// scores at or above the k_eff-th largest with probability below 1e-6 at these sizes.  One LDS histogram ranks
-// the sample: bin 4095 - d counts the keys whose 20-bit prefix lies d below the sample's largest (d clamped to
-// 4095), so the m-th largest is found without a second round unless it lies 4095 or more prefixes down (a
-// spread of more than a factor of four), when the floor keeps every key.  Whatever floor comes out, the
+// evenly over the row (a run lies in one page), with the tiles' contraction and epilogue, in rounds of four
+// 32-position groups per wave (eight runs each, every lane loading its own position's page id); the keys go to
+// LDS.  S = 512 (one round) for a single row of up to 2^17 positions with k_eff <= 2048, where this block is the
+// last to finish; 1024 up to 2^18 positions (with several rows the block hides behind the other rows' tiles, and
+// the larger sample admits fewer candidates); 4096 up to 2^20.  The floor is the 20-bit prefix of the m-th largest
+// sampled score, m = mu + 4 sqrt(mu) + 8 with mu = k_eff S / n the expected number of sampled scores among the row's
+// k_eff largest: about n m / S scores reach it (7.2 K at n = 128K, k = 2048, S = 512; 7.2 K at n = 2^20), and a
+// sample holds m scores at or above the k_eff-th largest with probability below 1e-6 at these sizes.  One LDS
+// histogram ranks the sample: bin 4095 - d counts the keys whose 20-bit prefix lies d below the sample's largest
+// (d clamped to 4095), so the m-th largest is found without a second round unless it lies 4095 or more prefixes
+// down (a spread of more than a factor of four), when the floor keeps every key.  Whatever floor comes out, the
 // selection stays exact: a row whose floor admits fewer than k_eff candidates, or more than its list holds, is
 // selected over its stored scores.  Rows outside indexer_floor_row return at once.
 template <int HB, int KB>
@@ -240,11 +241,9 @@ __device__ __forceinline__ void sample_row_floor(
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ page_table, int num_seqs, int max_pages,
     int num_pages, int log2ps, int max_row_len, int k, uint32_t* __restrict__ thr, int r) {
   constexpr int H_I = 32 * HB, D_I = 64 * KB;
-  constexpr int kRound = 4;                                        // groups per wave and round (512 positions)
-  constexpr int kMaxGroups = kFloorSample / (4 * 32);              // groups per wave at S = kFloorSample
-  constexpr int kLoad = kRound;                                    // groups whose keys are in flight together
-  static_assert(kMaxGroups % kLoad == 0 && kLoad % kRound == 0, "rounds tile the groups");
+  constexpr int kRound = 4;  // groups per wave and round (512 positions per block)
   __shared__ __attribute__((aligned(16))) uint32_t h[kTopkBins];
+  __shared__ uint32_t keys[kFloorSample];
   __shared__ uint32_t s[8];
   const int n = clamp_len(row_len[r], max_row_len);
   const int keff = min(k, n);
@@ -252,22 +251,11 @@ __device__ __forceinline__ void sample_row_floor(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int seq = clamp_seq(row_seq[r], num_seqs);
-  const int S = gridDim.y == 1 && n <= (1 << 17) && keff <= 2048 ? 4 * 32 * kRound : kFloorSample;
+  const int S = gridDim.y == 1 && n <= (1 << 17) && keff <= 2048 ? 4 * 32 * kRound
+                : n <= (1 << 18)                                 ? 1024
+                                                                 : kFloorSample;
   const int G = S / (4 * 32);  // groups per wave
   const int runs = S / 4;
-  // pool rows of the lane's positions: group g of wave w holds runs 8 (G w + g) + col / 4; run j starts at j n / runs
-  // rounded down to a multiple of 4 (the last run ends below n since n >= kFloorMinLen)
-  int64_t prow[kMaxGroups];
-#pragma unroll
-  for (int g = 0; g < kMaxGroups; ++g) {
-    if (g >= G) break;  // uniform
-    const int j = 8 * (G * wave + g) + (col >> 2);
-    const int pos = (int)(((int64_t)j * n / runs) & ~3) + (col & 3);
-    const int lp = min(pos >> log2ps, max_pages - 1);
-    const int page = min(max(page_table[(int64_t)seq * max_pages + lp], 0), num_pages - 1);
-    prow[g] = ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
-  }
-  DSA_STAMP(0, 4);
   // the row's query operands and epilogue weights, laid out as in index_row_tiles
   v8i a[HB][KB];
   float wq[HB][16];
@@ -286,82 +274,83 @@ __device__ __forceinline__ void sample_row_floor(
       for (int e = 0; e < 4; ++e) wq[hb][4 * m4 + e] = w4[e] * s4[e];
     }
   }
-  // histogram cleared while the loads are in flight
+  // histogram cleared while the first loads are in flight
   for (int i = threadIdx.x; i < kTopkBins; i += 256) h[i] = 0u;
   if (threadIdx.x < 8) s[threadIdx.x] = 0u;  // a floor of 0 keeps every key, should the rank fail
-  // scores, one round of four groups at a time (the keys of eight groups would not fit the registers beside the
-  // tiles' budget); the MFMA of unit u + 1 is issued before the epilogue of unit u, as in the tiles, and lane half
-  // h ends with the score of group 2 p + h at position col
-  uint32_t key[kMaxGroups / 2];
+  // rounds of four groups: group g of wave w holds runs 8 (G w + g) + col / 4, run j starting at j n / runs rounded
+  // down to a multiple of 4 (the last run ends below n since n >= kFloorMinLen); page ids, then keys and scales;
+  // the MFMA of unit u + 1 is issued before the epilogue of unit u, as in the tiles, and lane half h ends with the
+  // score of group 2 p + h at position col
+#pragma unroll 1
+  for (int g0 = 0; g0 < G; g0 += kRound) {
+    int64_t prow[kRound];
 #pragma unroll
-  for (int i = 0; i < kMaxGroups / 2; ++i) key[i] = 0u;
+    for (int g = 0; g < kRound; ++g) {
+      const int j = 8 * (G * wave + g0 + g) + (col >> 2);
+      const int pos = (int)(((int64_t)j * n / runs) & ~3) + (col & 3);
+      const int lp = min(pos >> log2ps, max_pages - 1);
+      const int page = min(max(page_table[(int64_t)seq * max_pages + lp], 0), num_pages - 1);
+      prow[g] = ((int64_t)page << log2ps) | (pos & ((1 << log2ps) - 1));
+    }
+    DSA_STAMP(0, 4);
+    v8i b[kRound][KB];
+    float sk[kRound];
 #pragma unroll
-  for (int g0 = 0; g0 < kMaxGroups; g0 += kLoad) {
-    if (g0 >= G) break;  // uniform
-    v8i b[kLoad][KB];
-    float sk[kLoad];
-#pragma unroll
-    for (int g = 0; g < kLoad; ++g) {
-      if (g0 + g >= G) break;
+    for (int g = 0; g < kRound; ++g) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        b[g][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[g0 + g] * D_I + kb * 64 + half * 32);
-      sk[g] = k_scale[prow[g0 + g]];
+        b[g][kb] = *reinterpret_cast<const v8i*>(k_pool + prow[g] * D_I + kb * 64 + half * 32);
+      sk[g] = k_scale[prow[g]];
     }
+    auto unit_mfma = [&](int u) __attribute__((always_inline)) {
+      v16f acc = {};
 #pragma unroll
-    for (int q0 = 0; q0 < kLoad; q0 += kRound) {
-      if (g0 + q0 >= G) break;  // uniform
-      auto unit_mfma = [&](int u) __attribute__((always_inline)) {
-        v16f acc = {};
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u % HB][kb], b[u / HB][kb], acc, 0, 0, 0, 0, 0, 0);
+      return acc;
+    };
+    constexpr int kUnits = kRound * HB;
+    v16f acc = unit_mfma(0);
+    float lin = 0.f, ab = 0.f, part[2];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u % HB][kb], b[q0 + u / HB][kb], acc, 0, 0, 0, 0,
-                                                                0, 0);
-        return acc;
-      };
-      constexpr int kUnits = kRound * HB;
-      v16f acc = unit_mfma(0);
-      float lin = 0.f, ab = 0.f, part[2];
+    for (int u = 0; u < kUnits; ++u) {
+      const int g = u / HB, hb = u % HB;
+      v16f nxt;
+      if (u + 1 < kUnits) nxt = unit_mfma(u + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kUnits; ++u) {
-        const int g = u / HB, hb = u % HB;
-        v16f nxt;
-        if (u + 1 < kUnits) nxt = unit_mfma(u + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          lin = fmaf(wq[hb][i], acc[i], lin);
-          ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
-        }
-        if (hb == HB - 1) {
-          part[g % 2] = lin + ab;
-          lin = 0.f;
-          ab = 0.f;
-        }
-        if (hb == HB - 1 && g % 2 == 1) {
-          const auto sw =
-              __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-          const float skp = half ? sk[q0 + g] : sk[q0 + g - 1];
-          key[(g0 + q0 + g) / 2] = order_key(skp * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1]))));
-        }
-        if (u + 1 < kUnits) acc = nxt;
+      for (int i = 0; i < 16; ++i) {
+        lin = fmaf(wq[hb][i], acc[i], lin);
+        ab = fmaf(wq[hb][i], fabsf(acc[i]), ab);
       }
+      if (hb == HB - 1) {
+        part[g % 2] = lin + ab;
+        lin = 0.f;
+        ab = 0.f;
+      }
+      if (hb == HB - 1 && g % 2 == 1) {
+        const auto sw =
+            __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+        const float skp = half ? sk[g] : sk[g - 1];
+        keys[(G * wave + g0 + g - 1 + half) * 32 + col] =
+            order_key(skp * (0.5f * (__uint_as_float(sw[0]) + __uint_as_float(sw[1]))));
+      }
+      if (u + 1 < kUnits) acc = nxt;
     }
   }
   DSA_STAMP(0, 5);
   const float mu = (float)keff * (float)S / (float)n;
   const uint32_t m = (uint32_t)min(S, (int)ceilf(mu + 4.f * sqrtf(mu) + 8.f));
-  // the sample's largest key (keys of groups past G stay 0 and never exceed it), then one histogram of distances
+  __syncthreads();  // the keys are in LDS
+  // the sample's largest key, then one histogram of distances below it
   uint32_t mx = 0u;
-#pragma unroll
-  for (int i = 0; i < kMaxGroups / 2; ++i) mx = max(mx, key[i]);
+  for (int i = threadIdx.x; i < S; i += 256) mx = max(mx, keys[i]);
   mx = wave_max_u32(mx);
   if (lane == 0) s[4 + wave] = mx;
   __syncthreads();
   const uint32_t top = max(max(s[4], s[5]), max(s[6], s[7])) >> 12;
-#pragma unroll
-  for (int i = 0; i < kMaxGroups / 2; ++i)
-    if (2 * i < G) atomicAdd(&h[kTopkBins - 1 - min(top - (key[i] >> 12), (uint32_t)kTopkBins - 1)], 1u);
+  for (int i = threadIdx.x; i < S; i += 256)
+    atomicAdd(&h[kTopkBins - 1 - min(top - (keys[i] >> 12), (uint32_t)kTopkBins - 1)], 1u);
   __syncthreads();
   DSA_STAMP(0, 6);
   if (threadIdx.x < 64) wave_threshold_bin<kTopkBins, 16>(h, m, &s[0], &s[1]);

@@ -8,15 +8,15 @@ namespace dsa {
 constexpr int kTopkBins = 4096;  // bins of a 12-bit key digit, and of the resolve's candidate histogram
 
 // Rows whose top-k floor the fused step's indexer ranks from the row's own keys while the rest of its grid scores
-// the row (indexer.hip), leaving it in the row's thr[4 r + 1] for the filter: rows of 16K..256K positions with
-// k_eff <= 4096 (k_eff <= 2048 past 128K), so that about n m / S <= 8192 scores reach a floor ranked from
-// S = 512 samples (a single row of up to 128K with k_eff <= 2048) or S = kFloorSample, with margin
-// m = mu + 4 sqrt(mu) + 8.
-// Other rows rank the filter's own sample.  One rule, evaluated on both sides of the kernel boundary.
-constexpr int kFloorSample = 1024;     // most sampled positions: 256 runs of four
+// the row (indexer.hip), leaving it in the row's thr[4 r + 1] for the filter: rows of 16K..2^20 positions with
+// k_eff <= 2048, and up to 2^17 positions with k_eff <= 4096, so that about n m / S <= 8192 scores reach a floor
+// ranked from S samples with margin m = mu + 4 sqrt(mu) + 8 (S = 512 for a single row of up to 2^17 positions with
+// k_eff <= 2048, 1024 up to 2^18 positions, else kFloorSample).  Other rows rank the filter's own sample.  One
+// rule, evaluated on both sides of the kernel boundary.
+constexpr int kFloorSample = 4096;     // most sampled positions: 1024 runs of four
 constexpr int kFloorMinLen = 16384;
 __host__ __device__ inline bool indexer_floor_row(int n, int keff) {
-  return keff < n && n >= kFloorMinLen && n <= (1 << 18) && keff <= 4096 && (keff <= 2048 || n <= (1 << 17));
+  return keff < n && n >= kFloorMinLen && ((n <= (1 << 17) && keff <= 4096) || (n <= (1 << 20) && keff <= 2048));
 }
 
 struct Ws {

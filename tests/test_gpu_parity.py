@@ -62,7 +62,7 @@ def test_batched_short_empty_and_tiny_rows():
 
 
 def test_indexer_ranked_floor_rows():
-    # rows of 16K..256K positions take the top-k floor that the fused step's indexer ranks from 1024 sampled keys
+    # rows of 16K..2^20 positions take the top-k floor that the fused step's indexer ranks from sampled keys
     # (the separate calls rank the filter's own sample, and the two selections must agree bit for bit): the
     # shortest such row and one just below it, k = 4096 at 2^17 and k = 2048 at 2^18 (the rule's edges), and a
     # paged batch with rows on both sides of 16K
@@ -70,15 +70,16 @@ def test_indexer_ranked_floor_rows():
     _run(synth.get("decode_128k", lengths=[16383], H=16, anchors=64, recent=96))
     _run(synth.get("decode_128k", lengths=[1 << 17], k=4096, H=16))
     _run(synth.get("decode_128k", lengths=[1 << 18], H=16))
+    _run(synth.get("decode_128k", lengths=[600001], H=16))  # 4096 samples, taken in eight rounds
     _run(synth.get("batched_paged", batch=4, lengths=[9000, 16384, 40000, 70001], H=32))
 
 
 def _scale_sampled_keys(prob, factor):
     """Multiplies the key scale of the positions the fused indexer samples for a row's floor (runs of four, run j
     of `runs` at j n / runs rounded down to a multiple of four; 128 runs for a single row of up to 2^17 positions
-    with k <= 2048, else 256): every score of row 0 there scales by `factor`."""
+    with k <= 2048, 256 up to 2^18 positions, else 1024): every score of row 0 there scales by `factor`."""
     n = int(prob.row_len[0])
-    runs = 128 if prob.R == 1 and n <= (1 << 17) and min(prob.k, n) <= 2048 else 256
+    runs = 128 if prob.R == 1 and n <= (1 << 17) and min(prob.k, n) <= 2048 else 256 if n <= (1 << 18) else 1024
     pos = np.array([((j * n) // runs) // 4 * 4 + c for j in range(runs) for c in range(4)])
     ps = prob.page_size
     phys = prob.page_table[prob.row_seq[0], pos // ps].astype(np.int64) * ps + pos % ps
@@ -92,6 +93,7 @@ def test_indexer_floor_misjudged_either_way():
     _run(synth.get("decode_128k", lengths=[1 << 17], H=16), mutate=lambda p: _scale_sampled_keys(p, 8.0))
     _run(synth.get("decode_128k", lengths=[40000], H=16, anchors=64, recent=96),
          mutate=lambda p: _scale_sampled_keys(p, 0.125))
+    _run(synth.get("decode_128k", lengths=[1 << 19], H=16), mutate=lambda p: _scale_sampled_keys(p, 8.0))
 
 
 def test_index_heads_32_and_small_budgets():
