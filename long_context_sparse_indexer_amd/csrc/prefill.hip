@@ -141,6 +141,7 @@ __global__ __launch_bounds__(1024) void pf_resolve_kernel(const int32_t* __restr
     for (int i = t; i < k; i += 1024) sink.put_or_pad(i, i < n ? i : -1);
     return;
   }
+  static_assert(kPfCap == kCap, "bitmap_select reads a whole list of kCap entries");
   const bool ok = bitmap_select<kWords / 1024>(n, keff, sel.floor[r], sel.cnt[r], sel.cand + (int64_t)r * kPfCap,
                                                sink, bits, h, S);
   if (!ok) {  // uniform

@@ -90,22 +90,22 @@ struct RowList {
 struct RowMap {
   const int32_t* pt;
   int max_pages, num_pages, log2ps;
-  __device__ int32_t row(int32_t pos) const {
+  __device__ int32_t base(int32_t pos) const {  // pool row of the first position of pos's page
     const int lp = min(pos >> log2ps, max_pages - 1);
-    const int page = min(max(pt[lp], 0), num_pages - 1);
-    return (page << log2ps) | (pos & ((1 << log2ps) - 1));
+    return min(max(pt[lp], 0), num_pages - 1) << log2ps;
   }
+  __device__ int32_t row(int32_t pos) const { return base(pos) | (pos & ((1 << log2ps) - 1)); }
 };
 // The same from the row's page ids staged in LDS.  A sink whose page-table reads may be global or LDS makes them
 // flat loads, and a loop of stores and flat loads waits for every store it issued: the two are kept apart.
 struct LdsRowMap {
   const __attribute__((address_space(3))) int32_t* pt;
   int max_pages, num_pages, log2ps;
-  __device__ int32_t row(int32_t pos) const {
+  __device__ int32_t base(int32_t pos) const {
     const int lp = min(pos >> log2ps, max_pages - 1);
-    const int page = min(max(pt[lp], 0), num_pages - 1);
-    return (page << log2ps) | (pos & ((1 << log2ps) - 1));
+    return min(max(pt[lp], 0), num_pages - 1) << log2ps;
   }
+  __device__ int32_t row(int32_t pos) const { return base(pos) | (pos & ((1 << log2ps) - 1)); }
 };
 __device__ __forceinline__ const __attribute__((address_space(3))) int32_t* lds_ptr(const int32_t* p) {
   return reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(reinterpret_cast<uintptr_t>(p));
@@ -140,6 +140,13 @@ struct ListSinkT {
   __device__ void put_or_pad(uint32_t slot, int32_t pos) const {  // pos -1: a padding slot
     out[slot] = pos;
     if (rows_out) rows_out[slot] = pos >= 0 ? map.row(pos) : -1;
+  }
+  // A 32-aligned word of positions lies in one page (pages hold >= 32 positions): its page's first pool row, read
+  // once, serves every position of the word (put_in_word), so that a loop over the word reads no page table.
+  __device__ int32_t word_base(int32_t pos0) const { return rows_out ? map.base(pos0) : 0; }
+  __device__ void put_in_word(uint32_t slot, int32_t pos, int32_t base) const {
+    out[slot] = pos;
+    if (rows_out) rows_out[slot] = base | (pos & ((1 << map.log2ps) - 1));
   }
 };
 using ListSink = ListSinkT<RowMap>;
@@ -575,8 +582,9 @@ __device__ void resolve_finish(const float* __restrict__ row, int n, int keff, c
 // still needed, are marked in the bitmap, and a popcount scan of the bitmap hands every selected position to the
 // sink at its slot, in increasing position order.  Returns false, having handed over nothing, when the list cannot
 // settle the row: fewer than k_eff or more than kCap candidates, a threshold in the open-ended top bin, or more than
-// kMaxTies keys equal to T.  Called by all 1024 threads (the result is uniform); `bits` holds kWpt * 1024 words,
-// covering the row's n positions, h kTopkBins words.
+// kMaxTies keys equal to T.  Called by all 1024 threads (the result is uniform); `list` is the row's whole list of
+// kCap entries (c of them written), `bits` holds kWpt * 1024 words, covering the row's n positions, h kTopkBins
+// words.
 constexpr int kMaxTies = 1024;
 struct BitmapScratch {
   int32_t eq_pos[kMaxTies];
@@ -597,14 +605,16 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
   constexpr int kPer = kCap / NT;  // candidates per thread
   static_assert(kWpt >= 1 && kWpt % 4 == 0 && kPer * NT == kCap, "bitmap and list split evenly");
   const int t = threadIdx.x, lane = t & 63;
+  // the whole list (kCap entries per row) is loaded whatever the count, so that the loads go out together with the
+  // count's own and need not wait for its round trip; entries past c are ignored below
+  uint64_t e[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) e[j] = list[j * NT + t];
   if (c < (uint32_t)keff || c > (uint32_t)kCap || n > kWpt * NT * 32) {
     pre();
     return false;
   }
   DSA_STAMP(1, 10);
-  uint64_t e[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) e[j] = list[min(j * NT + t, (int)c - 1)];  // entries past c dropped below
   pre();
   for (int i = t; i < kTopkBins; i += NT) h[i] = 0u;
 #pragma unroll
@@ -733,6 +743,11 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
       cntw += (uint32_t)__popc((uint32_t)y[x]);
     }
   }
+  // each word's page base is read before the writes (one read per word, all in flight together): a read per
+  // selected position had made the loop a chain of LDS round trips
+  int32_t wbase[kWpt];
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) wbase[q] = sink.word_base((t * kWpt + q) * 32);
   uint32_t tot;
   uint32_t slot = block_scan1<NT>(cntw, S.wt, tot);
   DSA_STAMP(1, 14);
@@ -742,7 +757,7 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
     while (b) {
       const int bit = __builtin_ctz(b);
       b &= b - 1;
-      if (slot < (uint32_t)keff) sink.put(slot, (t * kWpt + q) * 32 + bit);
+      if (slot < (uint32_t)keff) sink.put_in_word(slot, (t * kWpt + q) * 32 + bit, wbase[q]);
       ++slot;
     }
   }
