@@ -605,11 +605,13 @@ __device__ bool bitmap_select(int n, int keff, uint32_t fl, uint32_t c, const ui
   constexpr int kPer = kCap / NT;  // candidates per thread
   static_assert(kWpt >= 1 && kWpt % 4 == 0 && kPer * NT == kCap, "bitmap and list split evenly");
   const int t = threadIdx.x, lane = t & 63;
-  // the whole list (kCap entries per row) is loaded whatever the count, so that the loads go out together with the
-  // count's own and need not wait for its round trip; entries past c are ignored below
+  // a grid of at most 1024 blocks loads the whole list (kCap entries per row) whatever the count, so that the loads go
+  // out together with the count's own and need not wait for its round trip (entries past c are ignored below);
+  // thousands of rows (a prefill chunk) load only their c entries, since the extra bytes would then add up
+  const bool speculate = gridDim.x * gridDim.y <= 1024u;
   uint64_t e[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) e[j] = list[j * NT + t];
+  for (int j = 0; j < kPer; ++j) e[j] = list[speculate ? j * NT + t : min(j * NT + t, max((int)c, 1) - 1)];
   if (c < (uint32_t)keff || c > (uint32_t)kCap || n > kWpt * NT * 32) {
     pre();
     return false;
