@@ -269,8 +269,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       if (len > 0)
 #pragma unroll
         for (int j = 0; j < kSlotsPerThread; ++j) {
+          // only the rounds that hold slots of the split load (uniform): a 64-slot split takes one, not sixteen
           const int s = j * 256 + threadIdx.x;
-          const int v = src.list[min(s, len - 1)];
+          const int v = j * 256 < len ? src.list[min(s, len - 1)] : -1;
           pr[j] = s < len ? v : -1;
         }
       else
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       const int32_t* pt = page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages;
       int pg[kSlotsPerThread];
 #pragma unroll
-      for (int j = 0; j < kSlotsPerThread; ++j) pg[j] = pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)];
+      for (int j = 0; j < kSlotsPerThread; ++j)
+        pg[j] = j * 256 < len ? pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)] : 0;
 #pragma unroll
       for (int j = 0; j < kSlotsPerThread; ++j)
         pr[j] = pr[j] >= 0 ? (min(max(pg[j], 0), num_pages - 1) << log2ps) | (pr[j] & ((1 << log2ps) - 1)) : -1;
@@ -846,8 +848,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
   if (src.list && len > 0) {
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j) {
+      // only the rounds that hold slots of the split load (uniform over the block)
       const int sl = (j * NW + wave) * 64 + lane;
-      const int v = src.list[min(sl, len - 1)];
+      const int v = j * NW * 64 < len ? src.list[min(sl, len - 1)] : -1;
       pr[j] = sl < len ? v : -1;
     }
   } else {
@@ -861,7 +864,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_mqa_kernel(
     const int32_t* pt = page_table + (int64_t)clamp_seq(row_seq[r], num_seqs) * max_pages;
     int pg[kSlotsPerThread];
 #pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) pg[j] = pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)];
+    for (int j = 0; j < kSlotsPerThread; ++j)
+      pg[j] = j * NW * 64 < len ? pt[min(max(pr[j], 0) >> log2ps, max_pages - 1)] : 0;
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j)
       pr[j] = pr[j] >= 0 ? (min(max(pg[j], 0), num_pages - 1) << log2ps) | (pr[j] & ((1 << log2ps) - 1)) : -1;
