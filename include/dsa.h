@@ -112,6 +112,10 @@ dsa_status_t dsa_indexer_scores(const dsa_problem_t *problem, const dsa_layout_t
  *   topk_idx  [R, k] int32 out: the selected positions in increasing position order, then -1 padding
  *   workspace >= dsa_workspace_bytes(problem, DSA_OP_TOPK) bytes of device memory, 256-byte aligned
  * Scores are ranked by an order-preserving integer key of their fp32 value (+0 and -0 are equal).
+ * Cost: every row is exact, but a row settles fast only when its candidate list (the scores at or above a
+ * sampled floor, about k + 8 sqrt(32 k) + 512 of them at n = 128K) fits 12288 entries, i.e. up to k of about 8K
+ * at 128K; a larger budget, or heavy ties at the threshold, takes a whole-row radix select that is several times
+ * slower.
  */
 dsa_status_t dsa_topk(const dsa_problem_t *problem, const dsa_layout_t *layout, const float *scores,
                       int64_t scores_ld, int32_t *topk_idx, void *workspace, size_t workspace_bytes, void *stream);
