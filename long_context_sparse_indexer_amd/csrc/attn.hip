@@ -495,23 +495,40 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     }
     __syncthreads();
   }
+  DSA_STAMP(3, 10);
   // split partials go out as 16-byte stores: each wave stages its 16 heads x 128 columns of fp16 bits in LDS
   // (rows padded to 136 halves so the four heads of one write land on different banks), then every lane stores
   // four 8-column pieces; the chunk buffers are free once the last chunk's barrier has passed
   constexpr int kStgRow = 136;
   unsigned short* stg = reinterpret_cast<unsigned short*>(kv_lds0) + wave * (kHG * kStgRow);
+  // the four heads' sums and largest magnitudes are read before any is used (one LDS round trip, not four), and
+  // each head's power-of-two partial scale folds into its 1 / l: o (2^-e / l) equals 2^-e (o / l) but for
+  // subnormal values
+  float lvs[4], mxs[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) lvs[v] = __shfl(l, g * 4 + v, 64);
+  if (kSplit) {
+    const float* wmax = &s_lds[0][0];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int hh = g * 4 + v;
+      mxs[v] = fmaxf(fmaxf(wmax[hh], wmax[kHG + hh]), fmaxf(wmax[2 * kHG + hh], wmax[3 * kHG + hh]));
+    }
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int hh = g * 4 + v;
-    const float lv = __shfl(l, hh, 64);
+    const float lv = lvs[v];
     const float inv = lv > 0.f ? 1.f / lv : 0.f;
     if (kSplit) {
-      const float* wmax = &s_lds[0][0];
-      const float mx = fmaxf(fmaxf(wmax[hh], wmax[kHG + hh]), fmaxf(wmax[2 * kHG + hh], wmax[3 * kHG + hh]));
-      const int e = part_exponent(mx * inv);
+      // l >= 1 (the largest term is 1), so 2^-e / l stays finite with e clamped at -100; values below 2^-100
+      // then store as smaller fp16 codes against the same exponent
+      const int e = max(part_exponent(mxs[v] * inv), -100);
+      const float sc = ldexpf(inv, -e);
       const int64_t prow = ((int64_t)r * nsplit + split) * H + grp16 * kHG + hh;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) stg[hh * kStgRow + dt * 16 + i] = part_bits(o[dt][v] * inv, e);
+      for (int dt = 0; dt < 8; ++dt)
+        stg[hh * kStgRow + dt * 16 + i] = __builtin_bit_cast(unsigned short, (_Float16)(o[dt][v] * sc));
       if (wave == 0 && i == 0) part_exp[prow] = e;
     } else {
 #pragma unroll
@@ -524,6 +541,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     // the empty asm keeps the compiler from moving the 16-byte reads above the 2-byte writes
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("" ::: "memory");
+    DSA_STAMP(3, 11);
     const int64_t prow0 = ((int64_t)r * nsplit + split) * H + grp16 * kHG;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
