@@ -3,7 +3,8 @@
 // row shorter than the budget is read in full).  Equal scores are taken lowest position first; the result
 // is written in increasing position order, padded with -1.
 //
-// Scores become order-preserving 32-bit keys.  Every hand-over between blocks happens at a kernel boundary:
+// Scores become order-preserving 32-bit keys.  Hand-overs between blocks happen at kernel boundaries, except that
+// a single row of at most 2^17 positions is resolved by its last filter block (one acquire-release counter):
 //   filter   grid (4096-score chunks, rows): every block first finds the row's floor, the 20-bit key prefix of a
 //            sampled score that comfortably more than k_eff scores of the row exceed.  The sample is a fixed set
 //            of evenly spaced runs of the row, the same in every block, ranked through an LDS histogram (in the
